@@ -1,0 +1,152 @@
+"""Reference ("oracle") integrator for hash-blocked TSDF fusion.
+
+TEST INFRASTRUCTURE ONLY.  A plain, single-threaded C++ implementation
+(``tsdf_oracle.cpp``, a ``std::map`` keyed by block coordinate) that the
+tests, the smoke check and the benchmark's CPU-baseline leg use to check and
+time the HIP library.  The HIP library and its Python binding never import,
+load or call anything here, and share no code with it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Iterable, Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "tsdf_oracle.cpp")
+LIBRARY = os.path.join(HERE, "libtsdf_oracle.so")
+
+# Strict IEEE single precision: no contraction into FMA, no fast-math, SSE
+# arithmetic (x86-64 default) so no excess precision.
+CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
+            "-fno-fast-math", "-mfpmath=sse", "-fno-finite-math-only"]
+
+TRACK_TOUCHED = 1
+WATCH_ONLY = 2
+
+
+def build(source: str = SOURCE, output: str = LIBRARY, extra_flags: Iterable[str] = ()) -> str:
+    """Compile the oracle (or a copy of its source) into a shared library."""
+    tmp = output + f".tmp{os.getpid()}"
+    cmd = ["g++", *CXXFLAGS, *extra_flags, "-o", tmp, source]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, output)
+    return output
+
+
+class _FrameStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "pixels", "points_valid", "near_skipped", "out_of_range", "cells_visited",
+        "voxel_updates", "blocks_touched", "blocks_new", "voxels_touched",
+        "update_misses", "pool_overflow_new")]
+
+
+class _Totals(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "blocks", "pool_overflow", "update_misses", "points_valid", "near_skipped",
+        "out_of_range", "voxel_updates", "frames")]
+
+
+_LIBS: Dict[str, ctypes.CDLL] = {}
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    if path in _LIBS:
+        return _LIBS[path]
+    if not os.path.exists(path):
+        if path != LIBRARY:
+            raise FileNotFoundError(path)
+        build()
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.oracle_create.restype = P
+    lib.oracle_create.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_int64, ctypes.c_int32]
+    lib.oracle_destroy.argtypes = [P]
+    lib.oracle_watch.argtypes = [P, P, ctypes.c_int64]
+    lib.oracle_integrate.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                     P, P, ctypes.POINTER(_FrameStats)]
+    lib.oracle_get_totals.argtypes = [P, ctypes.POINTER(_Totals)]
+    lib.oracle_block_count.restype = ctypes.c_int64
+    lib.oracle_block_count.argtypes = [P]
+    lib.oracle_block_coords.argtypes = [P, P]
+    lib.oracle_block_sums.restype = ctypes.c_int64
+    lib.oracle_block_sums.argtypes = [P, P, ctypes.c_int64, P, P, P, P, P]
+    _LIBS[path] = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+class Oracle:
+    """One volume integrated by the reference implementation.
+
+    pool_capacity bounds the number of blocks; keys beyond it are refused and
+    counted.  track_touched enables the per-frame distinct-voxel count U;
+    watch (n x 3 block coordinates) keeps sums only for those blocks."""
+
+    def __init__(self, voxel_size: float, trunc: float, pool_capacity: int,
+                 track_touched: bool = False, watch: Optional[np.ndarray] = None,
+                 library: str = LIBRARY):
+        self._lib = load(library)
+        flags = (TRACK_TOUCHED if track_touched else 0) | (WATCH_ONLY if watch is not None else 0)
+        self._h = self._lib.oracle_create(voxel_size, trunc, int(pool_capacity), flags)
+        if not self._h:
+            raise ValueError("invalid oracle parameters")
+        if watch is not None:
+            w = np.ascontiguousarray(watch, np.int32).reshape(-1, 3)
+            if self._lib.oracle_watch(self._h, _ptr(w), w.shape[0]) != 0:
+                raise RuntimeError("oracle_watch after integration")
+        self.frame_stats = []
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.oracle_destroy(h)
+            self._h = None
+
+    def integrate(self, frame) -> dict:
+        depth = np.ascontiguousarray(frame.depth, np.float32)
+        rgb = np.ascontiguousarray(frame.rgb, np.uint8)
+        H, W = depth.shape
+        assert rgb.shape == (H, W, 3)
+        R = np.ascontiguousarray(frame.R, np.float32).reshape(9)
+        t = np.ascontiguousarray(frame.t, np.float32).reshape(3)
+        st = _FrameStats()
+        rc = self._lib.oracle_integrate(self._h, _ptr(depth), _ptr(rgb), W, H,
+                                        frame.fx, frame.fy, frame.cx, frame.cy,
+                                        _ptr(R), _ptr(t), ctypes.byref(st))
+        if rc != 0:
+            raise RuntimeError(f"oracle_integrate failed ({rc})")
+        d = {n: int(getattr(st, n)) for n, _ in _FrameStats._fields_}
+        self.frame_stats.append(d)
+        return d
+
+    def totals(self) -> dict:
+        t = _Totals()
+        self._lib.oracle_get_totals(self._h, ctypes.byref(t))
+        return {n: int(getattr(t, n)) for n, _ in _Totals._fields_}
+
+    def block_count(self) -> int:
+        return int(self._lib.oracle_block_count(self._h))
+
+    def block_coords(self) -> np.ndarray:
+        n = self.block_count()
+        out = np.empty((n, 3), np.int32)
+        if n:
+            self._lib.oracle_block_coords(self._h, _ptr(out))
+        return out
+
+    def block_sums(self, coords: np.ndarray) -> Dict[str, np.ndarray]:
+        c = np.ascontiguousarray(coords, np.int32).reshape(-1, 3)
+        n = c.shape[0]
+        out = {k: np.empty((n, 512), np.float64) for k in ("tsdf", "weight", "r", "g", "b")}
+        if n:
+            self._lib.oracle_block_sums(self._h, _ptr(c), n, _ptr(out["tsdf"]), _ptr(out["weight"]),
+                                        _ptr(out["r"]), _ptr(out["g"]), _ptr(out["b"]))
+        return out

@@ -1,0 +1,75 @@
+"""Write the stored expected counts under tests/golden/ by running ONLY the
+oracle on the seeded synthetic workloads.
+
+    python tests/golden/make_golden.py [workload ...]
+
+For each workload it writes <name>_counts.json: per frame the SHA-256 of the
+generated inputs and the oracle's exact integer counts (valid points, voxel
+updates V, distinct voxels U, blocks touched B_t, new blocks B_n, cells
+visited) plus the running block count.  The load-factor tests pick their
+pool sizes and frame prefixes from the running block count, and the
+benchmark takes its algorithmic byte counts (depth/colour per pixel, one
+16-byte table entry per touched block, one more per new block, five floats
+read and written per touched voxel) from these numbers.
+"""
+from __future__ import annotations
+
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from hash_table_amd import scenes  # noqa: E402
+
+
+def frame_sha(f) -> str:
+    return scenes.frame_digest([f])
+
+
+def make_counts(name: str, n_frames=None) -> dict:
+    wl = scenes.workload(name)
+    n = wl.n_frames if n_frames is None else min(n_frames, wl.n_frames)
+    o = oracle.Oracle(wl.voxel_size, wl.trunc, wl.pool_capacity, track_touched=True)
+    frames = []
+    t_oracle = 0.0
+    for i in range(n):
+        f = wl.frame(i)
+        t0 = time.perf_counter()
+        st = o.integrate(f)
+        t_oracle += time.perf_counter() - t0
+        st["blocks_total"] = o.block_count()
+        st["sha256"] = frame_sha(f)
+        frames.append(st)
+        print(f"{name} frame {i}: V={st['voxel_updates']} U={st['voxels_touched']} "
+              f"B_t={st['blocks_touched']} blocks={st['blocks_total']}", flush=True)
+    return {
+        "workload": name,
+        "voxel_size": wl.voxel_size, "trunc": wl.trunc,
+        "pool_capacity": wl.pool_capacity, "table_entries": wl.table_entries,
+        "width": wl.width, "height": wl.height, "n_frames": n,
+        "totals": o.totals(),
+        "oracle_seconds_here": round(t_oracle, 2),
+        "frames": frames,
+        "written_by": "tests/golden/make_golden.py (oracle only)",
+    }
+
+
+def main(argv):
+    names = argv or ["room640x480", "cube640x480", "spherewall320x240", "plane64x48"]
+    for name in names:
+        out = make_counts(name)
+        path = os.path.join(HERE, f"{name}_counts.json")
+        with open(path, "w") as fh:
+            json.dump(out, fh, indent=1)
+        print("wrote", path)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

@@ -1,0 +1,347 @@
+"""Checks that pin the oracle to facts other than itself.
+
+Each ``*_failures(lib)`` function integrates with the oracle library at
+``lib`` and returns a list of failure messages (empty = pinned).  They are
+shared by the oracle tests and by the mutation tests, which build copies of
+the oracle with a planted mistake and require that some check fails.
+
+Run as a script (used by the mutation tests, in a subprocess, so that a
+planted mistake that crashes cannot take the test runner down):
+    python tests/oracle_pins.py LIB PIN[,PIN...]
+prints one JSON object {pin: [failures]}.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from hash_table_amd import scenes  # noqa: E402
+
+try:
+    from tests import bruteforce  # noqa: E402
+except ImportError:                # run as a script from tests/
+    import bruteforce  # type: ignore  # noqa: E402
+
+PLANE_BLOCKS = {(bx, by, 12) for bx in range(-9, 9) for by in range(-7, 6)}
+
+
+def _voxel_table(o, coords=None):
+    """(global voxel index (n,3) int64, sums dict of flat arrays) for every
+    voxel with weight > 0."""
+    if coords is None:
+        coords = o.block_coords()
+    s = o.block_sums(coords)
+    w = s["weight"]
+    bi, li = np.nonzero(w > 0)
+    local = np.stack([li % 8, (li // 8) % 8, li // 64], 1)
+    k = coords[bi].astype(np.int64) * 8 + local
+    flat = {n: a[bi, li] for n, a in s.items()}
+    return k, flat
+
+
+def plane_failures(lib=oracle.LIBRARY):
+    """Fronto-parallel plane at z = 1 m, identity pose, vs = 1 cm, trunc = 4 cm.
+
+    Closed form: kept voxels are exactly the layers kz = 96..103 (centres
+    0.965..1.035 m, neighbours fail the band by half a voxel); the mean TSDF of
+    a voxel is (1 - zc)/0.04; the blocks are {(bx, by, 12): -9 <= bx <= 8,
+    -7 <= by <= 5} (the rays of columns 0 and 63 and row 0 reach the outer
+    blocks inside the band, row 47 does not reach by = 6)."""
+    f = []
+    wl = scenes.workload("plane64x48")
+    o = oracle.Oracle(wl.voxel_size, wl.trunc, wl.pool_capacity, library=lib)
+    st = o.integrate(wl.frame(0))
+    blocks = {tuple(int(x) for x in b) for b in o.block_coords()}
+    if blocks != PLANE_BLOCKS:
+        f.append(f"plane block set: {len(blocks)} blocks, missing {sorted(PLANE_BLOCKS - blocks)[:4]}, "
+                 f"extra {sorted(blocks - PLANE_BLOCKS)[:4]}")
+        return f
+    k, s = _voxel_table(o)
+    layers = set(np.unique(k[:, 2]).tolist())
+    if layers != set(range(96, 104)):
+        f.append(f"plane layers {sorted(layers)} != 96..103")
+    mean = s["tsdf"] / s["weight"]
+    zc = (k[:, 2] + 0.5) * 0.01
+    expect = (1.0 - zc) / 0.04
+    err = np.abs(mean - expect).max() if mean.size else 1.0
+    if not err < 2e-5:
+        f.append(f"plane mean TSDF off closed form by {err:.3g}")
+    if np.any(s["weight"] != np.round(s["weight"])):
+        f.append("non-integer weight")
+    if int(s["weight"].sum()) != st["voxel_updates"]:
+        f.append("sum of weights != voxel updates")
+    # linear zero crossing between layers 99 (+0.125) and 100 (-0.125)
+    m99 = mean[k[:, 2] == 99].mean()
+    m100 = mean[k[:, 2] == 100].mean()
+    zx = 0.995 + 0.01 * m99 / (m99 - m100)
+    if not abs(zx - 1.0) < 1e-5:
+        f.append(f"plane zero crossing {zx:.7f} != 1.0")
+    if st["blocks_touched"] != len(PLANE_BLOCKS) or st["blocks_new"] != len(PLANE_BLOCKS):
+        f.append("plane block counters")
+    if st["points_valid"] != 64 * 48:
+        f.append("plane valid points")
+    return f
+
+
+def _single_pixel(frame, u, v):
+    depth = np.zeros_like(frame.depth)
+    depth[v, u] = frame.depth[v, u]
+    return scenes.Frame(depth, frame.rgb, frame.fx, frame.fy, frame.cx, frame.cy, frame.R, frame.t)
+
+
+def _bf_cases():
+    cases = []
+    for seed in range(6):
+        vs = (0.01, 0.013, 0.005)[seed % 3]
+        tr = vs * (4.0, 2.5, 6.0)[seed % 3]
+        cases.append((scenes.random_frame(seed, W=7, H=5, translation_scale=0.5), vs, tr))
+    return cases
+
+
+def bruteforce_failures(lib=oracle.LIBRARY, tol=1e-4):
+    """Per point and per frame, the oracle's voxels, weights and sums equal a
+    brute-force enumeration of the band voxels in double precision (points
+    with a decision too close to call in float32 are skipped and counted)."""
+    f = []
+    n_points = n_ties = 0
+    for frame, vs, tr in _bf_cases():
+        H, W = frame.depth.shape
+        tie_mask = np.zeros((H, W), bool)
+        for v in range(H):
+            for u in range(W):
+                want, tie = bruteforce.point_voxels(frame, u, v, vs, tr)
+                if want is None:
+                    continue
+                n_points += 1
+                if tie:
+                    n_ties += 1
+                    tie_mask[v, u] = True
+                    continue
+                o = oracle.Oracle(vs, tr, 1 << 20, library=lib)
+                o.integrate(_single_pixel(frame, u, v))
+                k, s = _voxel_table(o)
+                got = {tuple(int(x) for x in kk): i for i, kk in enumerate(k)}
+                if set(got) != set(want):
+                    f.append(f"point ({u},{v}) vs={vs}: voxel set differs "
+                             f"({len(set(got) - set(want))} extra, {len(set(want) - set(got))} missing)")
+                    continue
+                for kk, (ts, r, g, b) in want.items():
+                    i = got[kk]
+                    if s["weight"][i] != 1.0:
+                        f.append(f"point ({u},{v}): weight {s['weight'][i]}")
+                        break
+                    d = max(abs(s["tsdf"][i] - ts), abs(s["r"][i] - r), abs(s["g"][i] - g), abs(s["b"][i] - b))
+                    if not d < tol:
+                        f.append(f"point ({u},{v}) voxel {kk}: sums off by {d:.3g}")
+                        break
+                if len(f) > 10:
+                    return f
+        # whole frame, tie points removed: aggregated weights exact, sums close
+        depth = frame.depth.copy()
+        depth[tie_mask] = 0.0
+        fr = scenes.Frame(depth, frame.rgb, frame.fx, frame.fy, frame.cx, frame.cy, frame.R, frame.t)
+        want, _ = bruteforce.frame_voxels(fr, vs, tr)
+        o = oracle.Oracle(vs, tr, 1 << 20, library=lib)
+        o.integrate(fr)
+        k, s = _voxel_table(o)
+        got = {tuple(int(x) for x in kk): i for i, kk in enumerate(k)}
+        if set(got) != set(want):
+            f.append(f"frame vs={vs}: voxel sets differ")
+            continue
+        for kk, acc in want.items():
+            i = got[kk]
+            if s["weight"][i] != acc[1]:
+                f.append(f"frame voxel {kk}: weight {s['weight'][i]} != {acc[1]}")
+                break
+            d = max(abs(s[n][i] - acc[j]) for j, n in ((0, "tsdf"), (2, "r"), (3, "g"), (4, "b")))
+            if not d < tol * acc[1]:
+                f.append(f"frame voxel {kk}: sums off by {d:.3g}")
+                break
+    if n_points < 150:
+        f.append(f"only {n_points} brute-force points")
+    if n_ties > 0.05 * n_points:
+        f.append(f"{n_ties} of {n_points} points are ties")
+    return f
+
+
+def sphere_failures(lib=oracle.LIBRARY, frames=range(10)):
+    """Analytic sphere r = 0.5 m at (0, 0, 1.5), noise-free depth: along each
+    voxel column near the optical axis the linear zero crossing of the mean
+    TSDF lies within a quarter voxel of the sphere surface (the paper's
+    analytic gate; a half-voxel bias in where the distance is evaluated shows
+    up here as a 5 mm error)."""
+    f = []
+    wl = scenes.workload("spherewall320x240_noisefree")
+    o = oracle.Oracle(wl.voxel_size, wl.trunc, wl.pool_capacity, library=lib)
+    for i in frames:
+        o.integrate(wl.frame(i))
+    k, s = _voxel_table(o)
+    mean = s["tsdf"] / s["weight"]
+    vs = wl.voxel_size
+    worst = 0.0
+    n_cols = 0
+    for ix in range(-4, 4):
+        for iy in range(-4, 4):
+            sel = (k[:, 0] == ix) & (k[:, 1] == iy) & (k[:, 2] < 120)
+            kz = k[sel, 2]
+            m = mean[sel]
+            order = np.argsort(kz)
+            kz, m = kz[order], m[order]
+            cross = None
+            for j in range(len(kz) - 1):
+                if kz[j + 1] == kz[j] + 1 and m[j] > 0 >= m[j + 1]:
+                    z0 = (kz[j] + 0.5) * vs
+                    cross = z0 + vs * m[j] / (m[j] - m[j + 1])
+                    break
+            if cross is None:
+                f.append(f"no zero crossing in column ({ix},{iy})")
+                continue
+            xc, yc = (ix + 0.5) * vs, (iy + 0.5) * vs
+            surface = 1.5 - math.sqrt(0.25 - xc * xc - yc * yc)
+            worst = max(worst, abs(cross - surface))
+            n_cols += 1
+    if not worst <= vs / 4:
+        f.append(f"sphere zero crossing off by {worst * 1000:.3f} mm (> {vs / 4 * 1000:.2f} mm)")
+    if n_cols < 60:
+        f.append(f"only {n_cols} columns")
+    return f
+
+
+def invariant_failures(lib=oracle.LIBRARY):
+    """Order independence (sums commute), exact pool-exhaustion accounting,
+    re-integration, value ranges and count consistency."""
+    f = []
+    wl = scenes.workload("spherewall320x240")
+    frames = [wl.frame(i) for i in (0, 4, 9)]
+    vs, tr = wl.voxel_size, wl.trunc
+
+    a = oracle.Oracle(vs, tr, 1 << 20, track_touched=True, library=lib)
+    st0 = a.integrate(frames[0])
+    ka, sa = _voxel_table(a)
+    if st0["voxels_touched"] != len(ka):
+        f.append("U != voxels with weight after one frame")
+    if st0["blocks_touched"] != a.block_count() or st0["blocks_new"] != a.block_count():
+        f.append("B_t / B_n != blocks after one frame")
+    for fr in frames[1:]:
+        a.integrate(fr)
+    b = oracle.Oracle(vs, tr, 1 << 20, library=lib)
+    for fr in (frames[2], frames[0], frames[1]):
+        b.integrate(fr)
+    ca, cb = a.block_coords(), b.block_coords()
+    if not np.array_equal(ca, cb):
+        f.append("block set depends on frame order")
+    else:
+        sa, sb = a.block_sums(ca), b.block_sums(cb)
+        if not np.array_equal(sa["weight"], sb["weight"]):
+            f.append("weights depend on frame order")
+        for n in ("tsdf", "r", "g", "b"):
+            if not np.allclose(sa[n], sb[n], rtol=0, atol=1e-9):
+                f.append(f"{n} sums depend on frame order")
+        w = sa["weight"]
+        if np.any(w.max(1) <= 0):
+            f.append("a block without any contribution")
+        tot = a.totals()
+        if int(w.sum()) != tot["voxel_updates"]:
+            f.append("sum of weights != voxel updates")
+        m = w > 0
+        mt = sa["tsdf"][m] / w[m]
+        if mt.min() < -1 - 1e-12 or mt.max() > 1 + 1e-12:
+            f.append("mean TSDF outside [-1, 1]")
+        for n in ("r", "g", "b"):
+            mc = sa[n][m] / w[m]
+            if mc.min() < 0 or mc.max() > 1 + 1e-12:
+                f.append(f"mean {n} outside [0, 1]")
+
+    # pool exhaustion: exactly N - cap keys refused, misses account for the rest
+    n_blocks = a.block_count()
+    cap = n_blocks - 7
+    c = oracle.Oracle(vs, tr, cap, library=lib)
+    for fr in frames:
+        c.integrate(fr)
+    tc = c.totals()
+    if tc["blocks"] != cap or tc["pool_overflow"] != 7:
+        f.append(f"exhaustion: blocks {tc['blocks']} overflow {tc['pool_overflow']} (want {cap}, 7)")
+    wc = c.block_sums(c.block_coords())["weight"]
+    if int(wc.sum()) + tc["update_misses"] != tc["voxel_updates"]:
+        f.append("exhaustion: weights + misses != voxel updates")
+    if tc["voxel_updates"] != a.totals()["voxel_updates"]:
+        f.append("exhaustion changed the voxel-update count")
+
+    # the same frame twice: no new blocks, weights double
+    d = oracle.Oracle(vs, tr, 1 << 20, library=lib)
+    d.integrate(frames[0])
+    w1 = d.block_sums(d.block_coords())["weight"].copy()
+    st = d.integrate(frames[0])
+    w2 = d.block_sums(d.block_coords())["weight"]
+    if st["blocks_new"] != 0 or not np.array_equal(w2, 2 * w1):
+        f.append("re-integrating a frame changed the block set or did not double weights")
+    return f
+
+
+def edge_failures(lib=oracle.LIBRARY):
+    """Empty, invalid, near and out-of-range inputs."""
+    f = []
+    base = scenes.random_frame(11, W=9, H=6)
+    vs, tr = 0.01, 0.04
+
+    def run(depth, t=None):
+        o = oracle.Oracle(vs, tr, 1 << 16, library=lib)
+        fr = scenes.Frame(np.ascontiguousarray(depth, np.float32), base.rgb[: depth.shape[0], : depth.shape[1]]
+                          if depth.size else np.zeros(depth.shape + (3,), np.uint8),
+                          base.fx, base.fy, base.cx, base.cy, base.R,
+                          base.t if t is None else np.asarray(t, np.float32))
+        return o.integrate(fr), o
+
+    st, o = run(np.zeros((6, 9)))
+    if st["points_valid"] or o.block_count():
+        f.append("all-zero frame produced points")
+    st, o = run(np.zeros((0, 0)))
+    if st["points_valid"] or o.block_count():
+        f.append("empty frame produced points")
+    d = np.full((6, 9), np.nan)
+    d[0, :3] = [np.inf, -np.inf, -1.0]
+    st, o = run(d)
+    if st["points_valid"] or st["near_skipped"] or o.block_count():
+        f.append("non-finite / negative depths were used")
+    d = np.full((6, 9), 0.03)              # 0 < d <= trunc
+    d[1, 1] = tr
+    st, o = run(d)
+    if st["near_skipped"] != 54 or st["points_valid"]:
+        f.append(f"near points: {st['near_skipped']} skipped")
+    st, o = run(base.depth, t=[1e5, 0.0, 0.0])   # 10^7 voxels from the origin
+    if st["out_of_range"] != 54 or st["points_valid"] or o.block_count():
+        f.append(f"out of range: {st['out_of_range']}")
+    st, o = run(base.depth, t=[80000.0, 0.0, 0.0])  # inside the key range
+    if st["out_of_range"] or st["points_valid"] != 54:
+        f.append("in-range far points rejected")
+    return f
+
+
+PINS = {
+    "plane": plane_failures,
+    "bruteforce": bruteforce_failures,
+    "sphere": sphere_failures,
+    "invariants": invariant_failures,
+    "edges": edge_failures,
+}
+
+
+if __name__ == "__main__":
+    lib_path = sys.argv[1]
+    names = sys.argv[2].split(",")
+    out = {}
+    for n in names:
+        try:
+            out[n] = PINS[n](lib_path)
+        except Exception as e:           # a planted mistake may break a check outright
+            out[n] = [f"exception: {type(e).__name__}: {e}"]
+    print(json.dumps(out))

@@ -1,0 +1,93 @@
+"""The oracle against what the pages and geometry fix (CPU only).
+
+Every check lives in tests/oracle_pins.py so that the mutation tests can run
+the same checks against copies of the oracle with a planted mistake.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_oracle():
+    oracle.build()
+
+
+@pytest.mark.parametrize("pin", sorted(oracle_pins.PINS))
+def test_pin(pin):
+    failures = oracle_pins.PINS[pin]()
+    assert failures == [], failures
+
+
+def test_plane_every_voxel_single_ray():
+    # 2 cm pixel footprint on 1 cm voxels: every kept voxel receives one ray,
+    # so its colour is exactly one pixel's colour / 255
+    from hash_table_amd import scenes
+    wl = scenes.workload("plane64x48")
+    o = oracle.Oracle(wl.voxel_size, wl.trunc, wl.pool_capacity)
+    o.integrate(wl.frame(0))
+    s = o.block_sums(o.block_coords())
+    w = s["weight"]
+    assert set(np.unique(w[w > 0])) == {1.0}
+    vals = np.round(s["r"][w > 0] * 255.0, 9)
+    assert np.all(vals == np.round(vals))
+
+
+# ---------------------------------------------------------------------------
+# mutation tests: each plants one plausible mistake in a copy of the oracle
+# source; some pin must fail (or the mutant must crash).
+# ---------------------------------------------------------------------------
+MUTATIONS = [
+    # (name, original text, replacement, occurrences, pins expected to notice)
+    ("distance at cell corner, not centre", "((float)k[i] + 0.5f) * vs", "((float)k[i] + 0.0f) * vs", 1,
+     "plane,sphere"),
+    ("sdf sign flipped", "const float sdf = d - zc;", "const float sdf = zc - d;", 1, "plane"),
+    ("occlusion test dropped", "if (sdf >= -trunc && sdf <= trunc)", "if (sdf <= trunc)", 1,
+     "plane,bruteforce"),
+    ("band test dropped", "if (sdf >= -trunc && sdf <= trunc)", "if (sdf >= -trunc)", 1, "plane,bruteforce"),
+    ("walk skips cells", "k[m] += step[m];", "k[m] += 2 * step[m];", 1, "bruteforce,plane"),
+    ("wrong first boundary", "tmax[i] = ((float)(k[i] + 1) - gA[i]) * inv[i];",
+     "tmax[i] = ((float)k[i] - gA[i]) * inv[i];", 1, "bruteforce"),
+    ("walk stops half way", "if (!(tmax[m] <= 1.0f)) break;", "if (!(tmax[m] <= 0.5f)) break;", 1,
+     "bruteforce,plane"),
+    ("rotation transposed", "((R[3 * i + 0] * a[0] + R[3 * i + 1] * a[1]) + R[3 * i + 2] * a[2])",
+     "((R[i] * a[0] + R[3 + i] * a[1]) + R[6 + i] * a[2])", 1, "bruteforce"),
+    ("fx used for rows", "((float)v - cy) / fy", "((float)v - cy) / fx", 1, "bruteforce"),
+    ("tsdf not normalised", "(double)sdf / (double)o->trunc", "(double)sdf", 1, "plane,bruteforce"),
+    ("colour scale", "(double)col[0] / 255.0", "(double)col[0] / 256.0", 1, "bruteforce"),
+    ("block index truncates toward zero", "if (k % kBlockEdge != 0 && k < 0) q -= 1;", "", 1, "plane"),
+    ("capacity off by one", "(int64_t)o->blocks.size() >= o->capacity", "(int64_t)o->blocks.size() > o->capacity",
+     1, "invariants"),
+    ("near points used", "if (d <= trunc) { s.near_skipped++; continue; }", "", 1, "edges"),
+    ("range check dropped", "in_range = false;", "in_range = true;", 1, "edges"),
+    ("voxel index axes swapped", "(k[0] - kBlockEdge * bc.x) + kBlockEdge * (k[1] - kBlockEdge * bc.y) +\n"
+     "                      kBlockEdge * kBlockEdge * (k[2] - kBlockEdge * bc.z)",
+     "(k[2] - kBlockEdge * bc.z) + kBlockEdge * (k[1] - kBlockEdge * bc.y) +\n"
+     "                      kBlockEdge * kBlockEdge * (k[0] - kBlockEdge * bc.x)", 1, "plane"),
+    ("weight of two", "S.weight[local] += 1.0;", "S.weight[local] += 2.0;", 1, "plane,bruteforce"),
+]
+
+
+@pytest.mark.parametrize("name,old,new,count,pins", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutant_is_caught(tmp_path, name, old, new, count, pins):
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == count, f"mutation target not found: {old!r}"
+    mutant = tmp_path / "mutant.cpp"
+    mutant.write_text(src.replace(old, new))
+    lib = oracle.build(str(mutant), str(tmp_path / "libmutant.so"))
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "oracle_pins.py"), lib, pins],
+                          capture_output=True, text=True, timeout=300, cwd=ROOT)
+    if proc.returncode != 0:
+        return                                     # the mutant crashed: caught
+    result = json.loads(proc.stdout.strip().splitlines()[-1])
+    caught = {p: f for p, f in result.items() if f}
+    assert caught, f"mutation '{name}' passed every pin: {result}"
