@@ -1,0 +1,276 @@
+"""Benchmark of the integrate path (allocate + update) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload room640x480]
+
+A step integrates the whole 100-frame, 640 x 480 room sequence (one
+tsdf_allocate and one tsdf_update per frame) into a freshly reset volume;
+inputs are resident in device memory before timing starts.  Timing is gated
+on parity: the run first checks the volume against the oracle's stored
+counts for the same seeded frames.  Per-kernel durations come from HIP
+events recorded on the launch stream around every kernel of the timed
+steps.  Prints one JSON line.
+
+Roofline: the path is HBM- and atomic-bound (no dense contraction).  The
+algorithmic bytes of a frame (per frame counts from the oracle) are
+  allocate  4 P + 16 B_t + 16 B_n
+  update    7 P + 16 B_t + 40 U
+with P valid... pixels (depth 4 B, colour 3 B per pixel), B_t blocks touched
+(one 16-byte table entry read), B_n new blocks (one entry written), U
+distinct voxels touched (five floats read and written).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pct(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return float("nan")
+    i = min(len(xs) - 1, max(0, int(round(q / 100.0 * (len(xs) - 1)))))
+    return xs[i]
+
+
+def load_counts(name):
+    path = os.path.join(ROOT, "tests", "golden", f"{name}_counts.json")
+    with open(path) as fh:
+        return json.load(fh)
+
+
+def frame_bytes(fr):
+    P = fr["pixels"]
+    alloc = 4 * P + 16 * fr["blocks_touched"] + 16 * fr["blocks_new"]
+    upd = 7 * P + 16 * fr["blocks_touched"] + 40 * fr["voxels_touched"]
+    return alloc, upd
+
+
+def microbench(torch, tsdf, stream):
+    """Copy bandwidth and atomic / CAS rates (events on the launch stream)."""
+    out = {}
+    s = stream.cuda_stream
+
+    def timed(fn, reps=5):
+        ts = []
+        for _ in range(reps + 1):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return statistics.median(ts[1:])
+
+    nbytes = 4 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t = timed(lambda: tsdf.tsdf_mb_copy(src.data_ptr(), dst.data_ptr(), nbytes, s))
+    out["copy_GBps"] = round(2 * nbytes / t / 1e9, 1)
+    del src, dst
+    n = 1 << 28                                     # 1 GiB of floats
+    buf = torch.zeros(n, dtype=torch.float32, device="cuda")
+    ops = 1 << 28
+    for name, pat in (("coalesced", tsdf.MB_COALESCED), ("block_row", tsdf.MB_BLOCK_ROW),
+                      ("random", tsdf.MB_RANDOM), ("same_wave", tsdf.MB_SAME_WAVE)):
+        t = timed(lambda: tsdf.tsdf_mb_atomic_add_f32(buf.data_ptr(), n, ops, pat, 7, s))
+        out[f"atomic_add_f32_{name}_Gops"] = round(ops / t / 1e9, 2)
+    del buf
+    n = 1 << 24
+    cbuf = torch.zeros(n, dtype=torch.int64, device="cuda")
+    ops = 1 << 26
+    t = timed(lambda: tsdf.tsdf_mb_cas_u64(cbuf.data_ptr(), n, ops, 3, s))
+    out["cas_u64_random_Gops"] = round(ops / t / 1e9, 2)
+    del cbuf
+    return out
+
+
+def cpu_baseline(wl, n_frames):
+    """The oracle, single-threaded, on the first n_frames of the workload."""
+    import oracle
+    oracle.build()
+    frames = [wl.frame(i) for i in range(n_frames)]
+    o = oracle.Oracle(wl.voxel_size, wl.trunc, wl.pool_capacity)
+    t0 = time.perf_counter()
+    for f in frames:
+        o.integrate(f)
+    dt = time.perf_counter() - t0
+    tot = o.totals()
+    return {
+        "value": round(tot["points_valid"] / dt, 1),
+        "unit": "points/s",
+        "voxel_updates_per_s": round(tot["voxel_updates"] / dt, 1),
+        "cores": 1,
+        "host_cores": os.cpu_count(),
+        "cpu": platform.processor() or platform.machine(),
+        "kind": "oracle",
+        "sample": f"first {n_frames} of {wl.n_frames} frames ({tot['points_valid']} points), {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="room640x480")
+    ap.add_argument("--cpu-frames", type=int, default=40)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-microbench", action="store_true")
+    ap.add_argument("--no-events", action="store_true", help="time whole steps only")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see the sharding note in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hash_table_amd import scenes, tsdf
+    tsdf.load()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    wl = scenes.workload(args.workload)
+    counts = load_counts(args.workload)
+    log(f"generating {wl.n_frames} frames of {wl.name}")
+    host_frames = [wl.frame(i) for i in range(wl.n_frames)]
+    for i in (0, wl.n_frames - 1):
+        if scenes.frame_digest([host_frames[i]]) != counts["frames"][i]["sha256"]:
+            raise SystemExit("generated frames differ from the stored oracle counts")
+    frames = [tsdf.DeviceFrame(f) for f in host_frames]
+    vol = tsdf.Volume(wl.voxel_size, wl.trunc, wl.pool_capacity, wl.table_entries)
+    torch.cuda.synchronize()
+
+    # --- parity gate: one full pass against the oracle's stored counts --------
+    for f in frames:
+        vol.integrate(f)
+    st = vol.stats()
+    tot = counts["totals"]
+    gate = {
+        "blocks": st["pool_used"] == tot["blocks"],
+        "voxel_updates": st["voxel_updates"] == tot["voxel_updates"],
+        "points_valid": st["points_valid"] == tot["points_valid"],
+        "no_loss": st["pool_overflow"] == st["table_full"] == st["update_misses"] == st["walk_guard"] == 0,
+    }
+    log("parity gate", gate)
+    if not all(gate.values()):
+        raise SystemExit(f"parity gate failed: {gate} stats={ {k: v for k, v in st.items() if 'hist' not in k} }")
+
+    use_events = not args.no_events
+    ev = []
+
+    def step(record):
+        vol.reset()
+        for i, f in enumerate(frames):
+            if record:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record(stream)
+                tsdf.tsdf_allocate(vol.handle, f.desc, sh)
+                e[1].record(stream)
+                tsdf.tsdf_update(vol.handle, f.desc, sh)
+                e[2].record(stream)
+                ev.append((i, e))
+            else:
+                tsdf.tsdf_integrate(vol.handle, f.desc, sh)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(use_events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = vol.stats()
+
+    n_frames = wl.n_frames
+    pts = tot["points_valid"]
+    vox = tot["voxel_updates"]
+    ms_per_step = wall / args.steps * 1e3
+    out = {
+        "metric": "integrated points/s and voxel-updates/s (allocate+update), % of HBM roofline",
+        "value": round(pts * args.steps / wall, 1),
+        "unit": "points/s",
+        "voxel_updates_per_s": round(vox * args.steps / wall, 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "frames_per_step": n_frames, "width": wl.width, "height": wl.height,
+                   "voxel_size": wl.voxel_size, "trunc": wl.trunc, "pool_capacity": wl.pool_capacity,
+                   "table_entries": wl.table_entries, "points_per_step": pts, "voxel_updates_per_step": vox,
+                   "step": "reset used pool + table, then allocate+update for every frame"},
+        "parity_gate": gate,
+    }
+    if use_events:
+        t_alloc, t_upd = [], []
+        b_alloc, b_upd = [], []
+        for i, e in ev:
+            t_alloc.append(e[0].elapsed_time(e[1]) * 1e-3)
+            t_upd.append(e[1].elapsed_time(e[2]) * 1e-3)
+            a, u = frame_bytes(counts["frames"][i])
+            b_alloc.append(a)
+            b_upd.append(u)
+        ta, tu = sum(t_alloc), sum(t_upd)
+        steps = args.steps
+        per = {
+            "allocate": {"points_per_s": pts * steps / ta, "voxel_updates_per_s": vox * steps / ta,
+                         "GBps": sum(b_alloc) / ta / 1e9,
+                         "us_median": 1e6 * statistics.median(t_alloc), "us_p95": 1e6 * pct(t_alloc, 95),
+                         "us_p99": 1e6 * pct(t_alloc, 99)},
+            "update": {"points_per_s": pts * steps / tu, "voxel_updates_per_s": vox * steps / tu,
+                       "GBps": sum(b_upd) / tu / 1e9,
+                       "us_median": 1e6 * statistics.median(t_upd), "us_p95": 1e6 * pct(t_upd, 95),
+                       "us_p99": 1e6 * pct(t_upd, 99)},
+            "integrate_kernels": {"points_per_s": pts * steps / (ta + tu),
+                                  "voxel_updates_per_s": vox * steps / (ta + tu),
+                                  "GBps": (sum(b_alloc) + sum(b_upd)) / (ta + tu) / 1e9},
+            "launches": len(t_alloc),
+        }
+        for k in ("allocate", "update", "integrate_kernels"):
+            per[k]["hbm_frac"] = per[k]["GBps"] / HBM_PEAK_GBS
+            per[k] = {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in per[k].items()}
+        out["kernels"] = per
+        dom = "update" if tu >= ta else "allocate"
+        t_dom = tu if dom == "update" else ta
+        b_dom = sum(b_upd) if dom == "update" else sum(b_alloc)
+        achieved = b_dom / t_dom / 1e9
+        out["roofline"] = {"kernel": f"k_{dom}", "bound": "hbm", "achieved": round(achieved, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": None,
+                           "bytes_per_launch": round(b_dom / len(t_upd)),
+                           "avg_launch_us": round(t_dom / len(t_upd) * 1e6, 3)}
+    out["loss_counters"] = {k: st[k] for k in ("pool_overflow", "table_full", "update_misses", "walk_guard")}
+    if not args.no_microbench:
+        log("microbenchmarks")
+        out["microbench"] = microbench(torch, tsdf, stream)
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_frames} frames")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_frames)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,275 @@
+"""ctypes binding of libtsdf_hip.so (include/tsdf.h, include/tsdf_microbench.h).
+
+Argument marshalling only: every step of the integrate path runs in the HIP
+kernels of the library.  The functions keep the C names; a status other than
+TSDF_OK raises TsdfError.  PyTorch supplies device memory and streams
+(``stream`` is an integer hipStream_t, e.g. ``torch.cuda.current_stream().cuda_stream``).
+
+There is no fallback: if the library is not built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libtsdf_hip.so")
+
+TSDF_OK, TSDF_EINVAL, TSDF_EALIGN, TSDF_EHIP, TSDF_ESMALL = 0, -1, -2, -3, -4
+TSDF_PROBE_BINS = 32
+TSDF_MAX_POOL_BLOCKS = 1 << 30
+TSDF_MAX_TABLE_ENTRIES = 1 << 31
+BLOCK_VOXELS = 512
+MB_COALESCED, MB_RANDOM, MB_SAME_WAVE, MB_BLOCK_ROW = 0, 1, 2, 3
+
+# every symbol the headers declare
+EXPORTS = [
+    "tsdf_table_entries_for", "tsdf_counters_bytes", "tsdf_create", "tsdf_reset", "tsdf_allocate",
+    "tsdf_update", "tsdf_integrate", "tsdf_export_blocks", "tsdf_get_stats", "tsdf_destroy",
+    "tsdf_status_str", "tsdf_mb_copy", "tsdf_mb_atomic_add_f32", "tsdf_mb_cas_u64",
+]
+
+
+class TsdfError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call} failed: {_status_name(status)} ({status})")
+
+
+class tsdf_config(ctypes.Structure):
+    _fields_ = [("voxel_size", ctypes.c_float), ("trunc", ctypes.c_float),
+                ("pool_capacity", ctypes.c_int64), ("table_entries", ctypes.c_int64)]
+
+
+class tsdf_buffers(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("table", "tsdf", "weight", "r", "g", "b", "counters")]
+
+
+class tsdf_frame(ctypes.Structure):
+    _fields_ = [("depth", ctypes.c_void_p), ("rgb", ctypes.c_void_p),
+                ("width", ctypes.c_int32), ("height", ctypes.c_int32),
+                ("fx", ctypes.c_float), ("fy", ctypes.c_float), ("cx", ctypes.c_float), ("cy", ctypes.c_float),
+                ("R", ctypes.c_float * 9), ("t", ctypes.c_float * 3)]
+
+
+class tsdf_stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "pool_used", "pool_overflow", "table_full", "update_misses", "out_of_range", "near_skipped",
+        "points_valid", "voxel_updates", "walk_guard", "probe_max")] + [
+        ("probe_hist_alloc", ctypes.c_uint64 * TSDF_PROBE_BINS),
+        ("probe_hist_update", ctypes.c_uint64 * TSDF_PROBE_BINS)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load the HIP library (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m hash_table_amd.build` "
+                           "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sigs = {
+        "tsdf_table_entries_for": (I64, [I64]),
+        "tsdf_counters_bytes": (SZ, []),
+        "tsdf_create": (I32, [ctypes.POINTER(tsdf_config), ctypes.POINTER(tsdf_buffers), P, ctypes.POINTER(P)]),
+        "tsdf_reset": (I32, [P, P]),
+        "tsdf_allocate": (I32, [P, ctypes.POINTER(tsdf_frame), P]),
+        "tsdf_update": (I32, [P, ctypes.POINTER(tsdf_frame), P]),
+        "tsdf_integrate": (I32, [P, ctypes.POINTER(tsdf_frame), P]),
+        "tsdf_export_blocks": (I32, [P, P, P, P, P, P, P, I64, ctypes.POINTER(I64), P]),
+        "tsdf_get_stats": (I32, [P, ctypes.POINTER(tsdf_stats), P]),
+        "tsdf_destroy": (None, [P]),
+        "tsdf_status_str": (ctypes.c_char_p, [I32]),
+        "tsdf_mb_copy": (I32, [P, P, SZ, P]),
+        "tsdf_mb_atomic_add_f32": (I32, [P, SZ, SZ, ctypes.c_int, ctypes.c_uint32, P]),
+        "tsdf_mb_cas_u64": (I32, [P, SZ, SZ, ctypes.c_uint32, P]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _status_name(status: int) -> str:
+    try:
+        return load().tsdf_status_str(status).decode()
+    except Exception:
+        return str(status)
+
+
+def _check(status: int, call: str) -> None:
+    if status != TSDF_OK:
+        raise TsdfError(status, call)
+
+
+# ---------------------------------------------------------------------------
+# C entry points, same names
+# ---------------------------------------------------------------------------
+def tsdf_table_entries_for(pool_capacity: int) -> int:
+    return int(load().tsdf_table_entries_for(pool_capacity))
+
+
+def tsdf_counters_bytes() -> int:
+    return int(load().tsdf_counters_bytes())
+
+
+def tsdf_status_str(status: int) -> str:
+    return load().tsdf_status_str(status).decode()
+
+
+def tsdf_create(config: tsdf_config, buffers: tsdf_buffers, stream: int = 0) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(load().tsdf_create(ctypes.byref(config), ctypes.byref(buffers), ctypes.c_void_p(stream),
+                              ctypes.byref(h)), "tsdf_create")
+    return h
+
+
+def tsdf_reset(volume, stream: int = 0) -> None:
+    _check(load().tsdf_reset(volume, ctypes.c_void_p(stream)), "tsdf_reset")
+
+
+def tsdf_allocate(volume, frame: tsdf_frame, stream: int = 0) -> None:
+    _check(load().tsdf_allocate(volume, ctypes.byref(frame), ctypes.c_void_p(stream)), "tsdf_allocate")
+
+
+def tsdf_update(volume, frame: tsdf_frame, stream: int = 0) -> None:
+    _check(load().tsdf_update(volume, ctypes.byref(frame), ctypes.c_void_p(stream)), "tsdf_update")
+
+
+def tsdf_integrate(volume, frame: tsdf_frame, stream: int = 0) -> None:
+    _check(load().tsdf_integrate(volume, ctypes.byref(frame), ctypes.c_void_p(stream)), "tsdf_integrate")
+
+
+def tsdf_export_blocks(volume, coords: int, tsdf: int, weight: int, r: int, g: int, b: int,
+                       max_blocks: int, stream: int = 0) -> int:
+    n = ctypes.c_int64(0)
+    st = load().tsdf_export_blocks(volume, *(ctypes.c_void_p(p) for p in (coords, tsdf, weight, r, g, b)),
+                                   max_blocks, ctypes.byref(n), ctypes.c_void_p(stream))
+    if st == TSDF_ESMALL:
+        raise TsdfError(st, f"tsdf_export_blocks ({n.value} blocks > {max_blocks})")
+    _check(st, "tsdf_export_blocks")
+    return int(n.value)
+
+
+def tsdf_get_stats(volume, stream: int = 0) -> Dict[str, object]:
+    s = tsdf_stats()
+    _check(load().tsdf_get_stats(volume, ctypes.byref(s), ctypes.c_void_p(stream)), "tsdf_get_stats")
+    out: Dict[str, object] = {n: int(getattr(s, n)) for n, _ in tsdf_stats._fields_[:10]}
+    out["probe_hist_alloc"] = np.array(s.probe_hist_alloc[:], np.int64)
+    out["probe_hist_update"] = np.array(s.probe_hist_update[:], np.int64)
+    return out
+
+
+def tsdf_destroy(volume) -> None:
+    if volume:
+        load().tsdf_destroy(volume)
+
+
+def tsdf_mb_copy(src: int, dst: int, nbytes: int, stream: int = 0) -> None:
+    _check(load().tsdf_mb_copy(src, dst, nbytes, ctypes.c_void_p(stream)), "tsdf_mb_copy")
+
+
+def tsdf_mb_atomic_add_f32(buf: int, n: int, n_ops: int, pattern: int, seed: int = 1, stream: int = 0) -> None:
+    _check(load().tsdf_mb_atomic_add_f32(buf, n, n_ops, pattern, seed, ctypes.c_void_p(stream)),
+           "tsdf_mb_atomic_add_f32")
+
+
+def tsdf_mb_cas_u64(buf: int, n: int, n_ops: int, seed: int = 1, stream: int = 0) -> None:
+    _check(load().tsdf_mb_cas_u64(buf, n, n_ops, seed, ctypes.c_void_p(stream)), "tsdf_mb_cas_u64")
+
+
+# ---------------------------------------------------------------------------
+# torch-backed convenience wrappers (memory and streams only)
+# ---------------------------------------------------------------------------
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+class DeviceFrame:
+    """A frame uploaded to device memory, with its tsdf_frame descriptor."""
+
+    def __init__(self, frame, device="cuda"):
+        import torch
+        self.depth = torch.from_numpy(np.ascontiguousarray(frame.depth, np.float32)).to(device)
+        self.rgb = torch.from_numpy(np.ascontiguousarray(frame.rgb, np.uint8)).to(device)
+        H, W = self.depth.shape
+        f = tsdf_frame()
+        f.depth = self.depth.data_ptr() if self.depth.numel() else None
+        f.rgb = self.rgb.data_ptr() if self.rgb.numel() else None
+        f.width, f.height = W, H
+        f.fx, f.fy, f.cx, f.cy = frame.fx, frame.fy, frame.cx, frame.cy
+        R = np.ascontiguousarray(frame.R, np.float32).reshape(9)
+        t = np.ascontiguousarray(frame.t, np.float32).reshape(3)
+        f.R = (ctypes.c_float * 9)(*R.tolist())
+        f.t = (ctypes.c_float * 3)(*t.tolist())
+        self.desc = f
+        self.valid_hint = None
+
+
+class Volume:
+    """A TSDF volume whose table, pool and counters are torch CUDA tensors."""
+
+    def __init__(self, voxel_size: float, trunc: float, pool_capacity: int, table_entries: int = 0,
+                 device="cuda", stream=None):
+        import torch
+        entries = table_entries or tsdf_table_entries_for(pool_capacity)
+        if entries <= 0:
+            raise TsdfError(TSDF_EINVAL, "tsdf_table_entries_for")
+        self.voxel_size, self.trunc = voxel_size, trunc
+        self.pool_capacity, self.table_entries = int(pool_capacity), int(entries)
+        self.device = device
+        n = int(pool_capacity) * BLOCK_VOXELS
+        self.table = torch.empty(int(entries) * 2, dtype=torch.int64, device=device)
+        self.pool = {k: torch.empty(n, dtype=torch.float32, device=device) for k in ("tsdf", "weight", "r", "g", "b")}
+        self.counters = torch.empty((tsdf_counters_bytes() + 7) // 8, dtype=torch.int64, device=device)
+        self._cfg = tsdf_config(voxel_size, trunc, int(pool_capacity), int(table_entries))
+        self._buf = tsdf_buffers(self.table.data_ptr(), *(self.pool[k].data_ptr() for k in
+                                 ("tsdf", "weight", "r", "g", "b")), self.counters.data_ptr())
+        self.handle = tsdf_create(self._cfg, self._buf, _stream_handle(stream))
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            tsdf_destroy(h)
+            self.handle = None
+
+    def reset(self, stream=None):
+        tsdf_reset(self.handle, _stream_handle(stream))
+
+    def allocate(self, frame: DeviceFrame, stream=None):
+        tsdf_allocate(self.handle, frame.desc, _stream_handle(stream))
+
+    def update(self, frame: DeviceFrame, stream=None):
+        tsdf_update(self.handle, frame.desc, _stream_handle(stream))
+
+    def integrate(self, frame: DeviceFrame, stream=None):
+        tsdf_integrate(self.handle, frame.desc, _stream_handle(stream))
+
+    def stats(self, stream=None) -> Dict[str, object]:
+        return tsdf_get_stats(self.handle, _stream_handle(stream))
+
+    def export(self, stream=None, arrays=("tsdf", "weight", "r", "g", "b")):
+        """All pool blocks as host numpy arrays: coords (n, 3) int32 and
+        {name: (n, 512) float32}, in pool-index order."""
+        import torch
+        n = int(self.stats(stream)["pool_used"])
+        coords = torch.empty((max(n, 1), 3), dtype=torch.int32, device=self.device)
+        outs = {k: torch.empty((max(n, 1), BLOCK_VOXELS), dtype=torch.float32, device=self.device) for k in arrays}
+        ptr = {k: (outs[k].data_ptr() if k in outs else 0) for k in ("tsdf", "weight", "r", "g", "b")}
+        got = tsdf_export_blocks(self.handle, coords.data_ptr(), ptr["tsdf"], ptr["weight"], ptr["r"], ptr["g"],
+                                 ptr["b"], max(n, 1), _stream_handle(stream))
+        assert got == n, (got, n)
+        return coords[:n].cpu().numpy(), {k: v[:n].cpu().numpy() for k, v in outs.items()}

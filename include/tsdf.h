@@ -1,0 +1,170 @@
+/*
+ * tsdf.h -- C ABI of libtsdf_hip.so, the MI355X (gfx950) implementation of
+ * the integrate path of hash-blocked TSDF fusion.
+ *
+ * The method is the one in "What Irregularity Costs: CUDA C++, Rust, and
+ * Triton on a Hash-Blocked GPU Workload" (section 3): voxels are grouped in
+ * blocks of 8^3 = 512; an open-addressed, linear-probing hash table of
+ * 16-byte entries (64-bit packed key, 32-bit block index, 4 bytes padding)
+ * maps block coordinates to indices in a flat pool of five parallel float
+ * arrays (TSDF sum, weight, R, G, B sums); integration is two kernels over
+ * the same points, `allocate` (walk the band, insert missing blocks with one
+ * 64-bit compare-exchange per key) and `update` (look blocks up, five atomic
+ * additions per voxel, storing sums rather than means).  As in the paper's
+ * section 3a harness, all memory is allocated by the caller and handed over
+ * as plain pointers; the library never allocates, frees or reshapes it.
+ *
+ * Conventions for every entry point:
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *     call that launches work enqueues it on `stream` and returns without
+ *     waiting, except tsdf_export_blocks and tsdf_get_stats, which wait.
+ *   - Invalid arguments return a negative status synchronously and enqueue
+ *     nothing.  A failed HIP launch or copy returns TSDF_EHIP.
+ *   - Data loss is never a status code: pool exhaustion, a full table and
+ *     misses are counters read back by tsdf_get_stats (the paper's
+ *     section 3a requires pool-exhaustion reporting, section 7 shows why
+ *     probe exhaustion must be reported too).  No block is ever dropped
+ *     without being counted.
+ *   - A volume is used from one stream at a time; calls on one volume must
+ *     not overlap.  Frame memory must stay valid until the enqueued work
+ *     has run.
+ */
+#ifndef TSDF_H
+#define TSDF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TSDF_OK = 0,
+    TSDF_EINVAL = -1,   /* invalid argument: null pointer, bad size or parameter */
+    TSDF_EALIGN = -2,   /* a buffer is not 16-byte aligned */
+    TSDF_EHIP = -3,     /* a HIP launch or copy failed */
+    TSDF_ESMALL = -4    /* the caller's output buffers are too small */
+} tsdf_status;
+
+/* Largest pool, in blocks; the pool index of a block must fit 32 bits with
+ * two sentinel values left over. */
+#define TSDF_MAX_POOL_BLOCKS (1LL << 30)
+/* Largest table, in entries. */
+#define TSDF_MAX_TABLE_ENTRIES (1LL << 31)
+/* Largest number of cells one point's band walk may visit (a frame whose
+ * intrinsics allow more is rejected with TSDF_EINVAL). */
+#define TSDF_MAX_WALK 4096
+/* Bins of the probe-depth histograms: bin i counts probes of i+1 slots,
+ * the last bin counts TSDF_PROBE_BINS slots or more. */
+#define TSDF_PROBE_BINS 32
+
+typedef struct tsdf_volume tsdf_volume;     /* opaque host-side handle */
+
+typedef struct {
+    float voxel_size;       /* metres, finite, > 0 */
+    float trunc;            /* truncation distance, metres, finite, > 0 */
+    int64_t pool_capacity;  /* blocks, 1 .. TSDF_MAX_POOL_BLOCKS */
+    int64_t table_entries;  /* 0: tsdf_table_entries_for(pool_capacity); otherwise a power of
+                               two >= 2 * pool_capacity (so the table is at most half full)
+                               and <= TSDF_MAX_TABLE_ENTRIES */
+} tsdf_config;
+
+/* Device memory owned by the caller, all 16-byte aligned. */
+typedef struct {
+    void* table;            /* table_entries * 16 bytes; entry = {uint64 key, uint32 index, uint32 pad} */
+    float* tsdf;            /* pool_capacity * 512 floats each: per-voxel sums of the */
+    float* weight;          /*   normalised signed distance (sdf / trunc), of the weight, */
+    float* r;               /*   and of the colour channels (0..1).  Voxel v of block i is */
+    float* g;               /*   element i * 512 + v, v = x + 8 y + 64 z within the block. */
+    float* b;
+    void* counters;         /* tsdf_counters_bytes() bytes */
+} tsdf_buffers;
+
+/* One depth frame.  Pointers are device memory. */
+typedef struct {
+    const float* depth;     /* height * width floats, row-major, metres of camera z;
+                               0, negative or non-finite = no measurement */
+    const uint8_t* rgb;     /* height * width * 3 bytes, row-major, R G B interleaved;
+                               needed by update and integrate, ignored by allocate */
+    int32_t width, height;  /* >= 0; an empty frame is a no-op */
+    float fx, fy, cx, cy;   /* pinhole intrinsics, pixels; pixel (u, v) looks along
+                               ((u - cx) / fx, (v - cy) / fy, 1) in camera coordinates */
+    float R[9];             /* camera-to-world rotation, row-major */
+    float t[3];             /* camera position in the world, metres */
+} tsdf_frame;
+
+/* Counters accumulated since tsdf_create / tsdf_reset. */
+typedef struct {
+    int64_t pool_used;       /* blocks holding a pool index (<= pool_capacity) */
+    int64_t pool_overflow;   /* distinct keys inserted after the pool was full */
+    int64_t table_full;      /* insertions that probed every table slot without room */
+    int64_t update_misses;   /* kept voxel contributions whose block has no pool index */
+    int64_t out_of_range;    /* update-pass points whose band leaves +-2^23 voxels */
+    int64_t near_skipped;    /* update-pass points with 0 < depth <= trunc */
+    int64_t points_valid;    /* update-pass points whose band was walked */
+    int64_t voxel_updates;   /* kept (point, voxel) pairs of the update pass */
+    int64_t walk_guard;      /* walks cut at TSDF_MAX_WALK (never expected: always 0) */
+    int64_t probe_max;       /* longest probe sequence seen, slots */
+    uint64_t probe_hist_alloc[TSDF_PROBE_BINS];   /* allocate: slots per table operation */
+    uint64_t probe_hist_update[TSDF_PROBE_BINS];  /* update: slots per lookup */
+} tsdf_stats;
+
+/* Default table size for a pool: the smallest power of two >= 2 * pool_capacity
+ * (section 3 of the paper: at most half full).  Returns -1 for an invalid capacity. */
+int64_t tsdf_table_entries_for(int64_t pool_capacity);
+
+/* Size of the counters buffer. */
+size_t tsdf_counters_bytes(void);
+
+/* Validate the configuration and buffers, then enqueue the initialisation of
+ * the volume on `stream`: every table entry empty (all bits set), counters
+ * zero, the whole pool zero.  On success *out receives a new handle. */
+tsdf_status tsdf_create(const tsdf_config* config, const tsdf_buffers* buffers, void* stream,
+                        tsdf_volume** out);
+
+/* Enqueue a reset to the state tsdf_create leaves: the used part of the pool
+ * is zeroed, the table emptied and the counters cleared. */
+tsdf_status tsdf_reset(tsdf_volume* volume, void* stream);
+
+/* The allocate kernel (paper, section 3): for every point, walk its
+ * truncation band; for each kept voxel make sure its block is in the table,
+ * inserting it with a single 64-bit compare-exchange of the packed key and
+ * taking the next pool index.  The probe has no fixed bound: it stops at the
+ * key, at an empty slot it wins, or after trying every slot (table_full).  A
+ * key inserted after the pool is full gets no index (pool_overflow). */
+tsdf_status tsdf_allocate(tsdf_volume* volume, const tsdf_frame* frame, void* stream);
+
+/* The update kernel (paper, section 3): the same walk and occlusion test;
+ * for each kept voxel look its block up and add, with five float atomic
+ * additions, sdf/trunc, 1, R/255, G/255, B/255 to the five pool arrays.
+ * Blocks without an index count as update_misses.  Call after tsdf_allocate
+ * of the same frame (stream order is the only ordering needed). */
+tsdf_status tsdf_update(tsdf_volume* volume, const tsdf_frame* frame, void* stream);
+
+/* tsdf_allocate then tsdf_update of one frame. */
+tsdf_status tsdf_integrate(tsdf_volume* volume, const tsdf_frame* frame, void* stream);
+
+/* Copy every block holding a pool index to caller device memory, in pool
+ * index order: coords (n x 3 int32 block coordinates) and, for each non-null
+ * array pointer, n * 512 floats of that pool array.  *n_blocks receives n
+ * (host memory).  Returns TSDF_ESMALL, copying nothing, if n > max_blocks.
+ * Waits for the stream. */
+tsdf_status tsdf_export_blocks(tsdf_volume* volume, int32_t* coords, float* tsdf, float* weight,
+                               float* r, float* g, float* b, int64_t max_blocks, int64_t* n_blocks,
+                               void* stream);
+
+/* Read the counters into *stats (host memory).  Waits for the stream. */
+tsdf_status tsdf_get_stats(tsdf_volume* volume, tsdf_stats* stats, void* stream);
+
+/* Free the handle.  Never frees caller memory. */
+void tsdf_destroy(tsdf_volume* volume);
+
+/* Name of a status code. */
+const char* tsdf_status_str(tsdf_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSDF_H */
