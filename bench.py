@@ -134,6 +134,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-microbench", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="time whole steps only")
+    ap.add_argument("--mode", default="owner", choices=["owner", "rays"], help="update organisation")
+    ap.add_argument("--no-variant", action="store_true", help="skip timing the other update mode")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -155,54 +157,84 @@ def main():
         if scenes.frame_digest([host_frames[i]]) != counts["frames"][i]["sha256"]:
             raise SystemExit("generated frames differ from the stored oracle counts")
     frames = [tsdf.DeviceFrame(f) for f in host_frames]
-    vol = tsdf.Volume(wl.voxel_size, wl.trunc, wl.pool_capacity, wl.table_entries)
-    torch.cuda.synchronize()
-
-    # --- parity gate: one full pass against the oracle's stored counts --------
-    for f in frames:
-        vol.integrate(f)
-    st = vol.stats()
     tot = counts["totals"]
-    gate = {
-        "blocks": st["pool_used"] == tot["blocks"],
-        "voxel_updates": st["voxel_updates"] == tot["voxel_updates"],
-        "points_valid": st["points_valid"] == tot["points_valid"],
-        "no_loss": st["pool_overflow"] == st["table_full"] == st["update_misses"] == st["walk_guard"] == 0,
-    }
-    log("parity gate", gate)
-    if not all(gate.values()):
-        raise SystemExit(f"parity gate failed: {gate} stats={ {k: v for k, v in st.items() if 'hist' not in k} }")
-
-    use_events = not args.no_events
-    ev = []
-
-    def step(record):
-        vol.reset()
-        for i, f in enumerate(frames):
-            if record:
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-                e[0].record(stream)
-                tsdf.tsdf_allocate(vol.handle, f.desc, sh)
-                e[1].record(stream)
-                tsdf.tsdf_update(vol.handle, f.desc, sh)
-                e[2].record(stream)
-                ev.append((i, e))
-            else:
-                tsdf.tsdf_integrate(vol.handle, f.desc, sh)
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(use_events)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    st = vol.stats()
-
-    n_frames = wl.n_frames
     pts = tot["points_valid"]
     vox = tot["voxel_updates"]
+
+    def measure(mode, steps, warmup, use_events):
+        """Parity gate, then `steps` timed steps; returns (wall seconds,
+        per-launch allocate and update seconds and frame indices, stats, gate)."""
+        vol = tsdf.Volume(wl.voxel_size, wl.trunc, wl.pool_capacity, wl.table_entries, update_mode=mode)
+        torch.cuda.synchronize()
+        for f in frames:                       # parity gate: one full pass vs the oracle's counts
+            vol.integrate(f)
+        st = vol.stats()
+        gate = {
+            "blocks": st["pool_used"] == tot["blocks"],
+            "voxel_updates": st["voxel_updates"] == tot["voxel_updates"],
+            "points_valid": st["points_valid"] == tot["points_valid"],
+            "no_loss": st["pool_overflow"] == st["table_full"] == st["update_misses"] == st["walk_guard"] == 0,
+        }
+        log(f"[{mode}] parity gate", gate)
+        if not all(gate.values()):
+            raise SystemExit(f"parity gate failed ({mode}): {gate}")
+        ev = []
+
+        def step(record):
+            vol.reset()
+            for i, f in enumerate(frames):
+                if record:
+                    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                    e[0].record(stream)
+                    tsdf.tsdf_allocate(vol.handle, f.desc, sh)
+                    e[1].record(stream)
+                    tsdf.tsdf_update(vol.handle, f.desc, sh)
+                    e[2].record(stream)
+                    ev.append((i, e))
+                else:
+                    tsdf.tsdf_integrate(vol.handle, f.desc, sh)
+
+        for _ in range(warmup):
+            step(False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step(use_events)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        st = vol.stats()
+        t_alloc = [e[0].elapsed_time(e[1]) * 1e-3 for _, e in ev]
+        t_upd = [e[1].elapsed_time(e[2]) * 1e-3 for _, e in ev]
+        idx = [i for i, _ in ev]
+        del vol
+        torch.cuda.empty_cache()
+        return wall, t_alloc, t_upd, idx, st, gate
+
+    def kernel_report(t_alloc, t_upd, idx, steps):
+        b_alloc = [frame_bytes(counts["frames"][i])[0] for i in idx]
+        b_upd = [frame_bytes(counts["frames"][i])[1] for i in idx]
+        ta, tu = sum(t_alloc), sum(t_upd)
+        per = {
+            "allocate": {"points_per_s": pts * steps / ta, "voxel_updates_per_s": vox * steps / ta,
+                         "GBps": sum(b_alloc) / ta / 1e9, "us_median": 1e6 * statistics.median(t_alloc),
+                         "us_p95": 1e6 * pct(t_alloc, 95), "us_p99": 1e6 * pct(t_alloc, 99)},
+            "update": {"points_per_s": pts * steps / tu, "voxel_updates_per_s": vox * steps / tu,
+                       "GBps": sum(b_upd) / tu / 1e9, "us_median": 1e6 * statistics.median(t_upd),
+                       "us_p95": 1e6 * pct(t_upd, 95), "us_p99": 1e6 * pct(t_upd, 99)},
+            "integrate_kernels": {"points_per_s": pts * steps / (ta + tu),
+                                  "voxel_updates_per_s": vox * steps / (ta + tu),
+                                  "GBps": (sum(b_alloc) + sum(b_upd)) / (ta + tu) / 1e9},
+            "launches": len(t_alloc),
+        }
+        for k in ("allocate", "update", "integrate_kernels"):
+            per[k]["hbm_frac"] = per[k]["GBps"] / HBM_PEAK_GBS
+            per[k] = {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in per[k].items()}
+        return per, ta, tu, sum(b_alloc), sum(b_upd)
+
+    use_events = not args.no_events
+    wall, t_alloc, t_upd, idx, st, gate = measure(args.mode, args.steps, args.warmup, use_events)
+
+    n_frames = wl.n_frames
     ms_per_step = wall / args.steps * 1e3
     out = {
         "metric": "integrated points/s and voxel-updates/s (allocate+update), % of HBM roofline",
@@ -220,48 +252,29 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "frames_per_step": n_frames, "width": wl.width, "height": wl.height,
                    "voxel_size": wl.voxel_size, "trunc": wl.trunc, "pool_capacity": wl.pool_capacity,
-                   "table_entries": wl.table_entries, "points_per_step": pts, "voxel_updates_per_step": vox,
+                   "table_entries": wl.table_entries, "update_mode": args.mode, "points_per_step": pts,
+                   "voxel_updates_per_step": vox,
                    "step": "reset used pool + table, then allocate+update for every frame"},
         "parity_gate": gate,
     }
     if use_events:
-        t_alloc, t_upd = [], []
-        b_alloc, b_upd = [], []
-        for i, e in ev:
-            t_alloc.append(e[0].elapsed_time(e[1]) * 1e-3)
-            t_upd.append(e[1].elapsed_time(e[2]) * 1e-3)
-            a, u = frame_bytes(counts["frames"][i])
-            b_alloc.append(a)
-            b_upd.append(u)
-        ta, tu = sum(t_alloc), sum(t_upd)
-        steps = args.steps
-        per = {
-            "allocate": {"points_per_s": pts * steps / ta, "voxel_updates_per_s": vox * steps / ta,
-                         "GBps": sum(b_alloc) / ta / 1e9,
-                         "us_median": 1e6 * statistics.median(t_alloc), "us_p95": 1e6 * pct(t_alloc, 95),
-                         "us_p99": 1e6 * pct(t_alloc, 99)},
-            "update": {"points_per_s": pts * steps / tu, "voxel_updates_per_s": vox * steps / tu,
-                       "GBps": sum(b_upd) / tu / 1e9,
-                       "us_median": 1e6 * statistics.median(t_upd), "us_p95": 1e6 * pct(t_upd, 95),
-                       "us_p99": 1e6 * pct(t_upd, 99)},
-            "integrate_kernels": {"points_per_s": pts * steps / (ta + tu),
-                                  "voxel_updates_per_s": vox * steps / (ta + tu),
-                                  "GBps": (sum(b_alloc) + sum(b_upd)) / (ta + tu) / 1e9},
-            "launches": len(t_alloc),
-        }
-        for k in ("allocate", "update", "integrate_kernels"):
-            per[k]["hbm_frac"] = per[k]["GBps"] / HBM_PEAK_GBS
-            per[k] = {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in per[k].items()}
+        per, ta, tu, ba, bu = kernel_report(t_alloc, t_upd, idx, args.steps)
         out["kernels"] = per
-        dom = "update" if tu >= ta else "allocate"
-        t_dom = tu if dom == "update" else ta
-        b_dom = sum(b_upd) if dom == "update" else sum(b_alloc)
+        upd_name = "k_update_owner" if args.mode == "owner" else "k_update_rays"
+        dom, t_dom, b_dom = (upd_name, tu, bu) if tu >= ta else ("k_allocate", ta, ba)
         achieved = b_dom / t_dom / 1e9
-        out["roofline"] = {"kernel": f"k_{dom}", "bound": "hbm", "achieved": round(achieved, 1),
+        out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                            "traffic": None,
                            "bytes_per_launch": round(b_dom / len(t_upd)),
                            "avg_launch_us": round(t_dom / len(t_upd) * 1e6, 3)}
+    if not args.no_variant:
+        other = "rays" if args.mode == "owner" else "owner"
+        w2, a2, u2, i2, _, g2 = measure(other, max(1, args.steps // 2), 1, True)
+        per2, *_ = kernel_report(a2, u2, i2, max(1, args.steps // 2))
+        out["variants"] = {other: {"points_per_s": round(pts * max(1, args.steps // 2) / w2, 1),
+                                   "ms_per_step": round(w2 / max(1, args.steps // 2) * 1e3, 4),
+                                   "kernels": per2, "parity_gate": g2}}
     out["loss_counters"] = {k: st[k] for k in ("pool_overflow", "table_full", "update_misses", "walk_guard")}
     if not args.no_microbench:
         log("microbenchmarks")

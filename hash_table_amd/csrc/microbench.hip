@@ -34,10 +34,14 @@ __global__ __launch_bounds__(kThreads) void k_atomic_add(float* buf, unsigned lo
             case 0: a = i & mask; break;
             case 1: a = mix32((unsigned int)i ^ seed) & mask; break;
             case 2: a = mix32((unsigned int)(i >> 6) ^ seed) & mask; break;
-            default: {
+            case 3: {
                 const unsigned int h = mix32((unsigned int)(i >> 6) ^ seed);
                 a = (((unsigned long long)(h >> 3) * 512ull + (h & 7u) * 64ull) & mask & ~63ull) + (i & 63);
+                break;
             }
+            default:       // one lane per wave, on one of n / 32 counters (a 128-byte line each)
+                if (i & 63) continue;
+                a = ((i >> 6) * 32ull) & mask;
         }
         unsafeAtomicAdd(buf + a, 1.0f);
     }
@@ -73,7 +77,8 @@ tsdf_status tsdf_mb_copy(const void* src, void* dst, size_t bytes, void* stream)
 }
 
 tsdf_status tsdf_mb_atomic_add_f32(float* buf, size_t n, size_t n_ops, int pattern, uint32_t seed, void* stream) {
-    if (!buf || !pow2(n) || pattern < 0 || pattern > 3 || (pattern == 3 && n < 512)) return TSDF_EINVAL;
+    if (!buf || !pow2(n) || pattern < 0 || pattern > 4 || (pattern == 3 && n < 512) || (pattern == 4 && n < 32))
+        return TSDF_EINVAL;
     if (!n_ops) return TSDF_OK;
     hipLaunchKernelGGL(k_atomic_add, dim3(grid_for(n_ops)), dim3(kThreads), 0, static_cast<hipStream_t>(stream), buf,
                        (unsigned long long)(n - 1), (unsigned long long)n_ops, pattern, seed);

@@ -1,0 +1,370 @@
+// tsdf_capi.hip -- the C ABI of libtsdf_hip.so (include/tsdf.h): argument
+// validation, the host-side volume handle, and kernel dispatch.  Memory is
+// always the caller's ("What Irregularity Costs", section 3a: the harness
+// allocates once and hands pointers through a C ABI).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "../../include/tsdf.h"
+#include "tsdf_kernels.hpp"
+
+using namespace tsdf;
+
+namespace {
+
+constexpr int kOwnerGrid = 4096;                     // single-wavefront workgroups of the owner update
+constexpr int64_t kDefaultFramePixels = 1 << 20;    // owner-mode record buffers, per frame
+constexpr int64_t kRunsPerPixel = 4;                // record capacity per pixel (a room frame needs ~2.7)
+
+// Owner-mode scratch layout: per-frame counters, per-table-entry arrays,
+// then the per-frame segment and record buffers (kParts partitions each).
+struct ScratchLayout {
+    size_t fc, desc, segs, recs, sorted, items, items_spill, item_of, rec_count, bytes;
+    unsigned int item_part_cap, seg_part_cap, rec_part_cap;
+};
+
+ScratchLayout scratch_layout(int64_t entries, int64_t frame_pixels) {
+    ScratchLayout L;
+    const int64_t px = frame_pixels > 0 ? frame_pixels : kDefaultFramePixels;
+    L.item_part_cap = (unsigned int)std::max<int64_t>(64, entries / (kParts / 2));
+    L.seg_part_cap = (unsigned int)((px + kParts - 1) / kParts);
+    L.rec_part_cap = (unsigned int)((kRunsPerPixel * px + kParts - 1) / kParts);
+    size_t o = 0;
+    L.fc = o;                         // 16-byte aligned pieces first
+    o += 2 * sizeof(FrameCounters);
+    L.desc = o;
+    o += sizeof(ItemDesc) * (size_t)entries;
+    L.segs = o;
+    o += sizeof(Segment) * (size_t)kParts * L.seg_part_cap;
+    L.recs = o;
+    o += sizeof(uint2) * (size_t)kParts * L.rec_part_cap;
+    L.sorted = o;
+    o += sizeof(uint2) * (size_t)kParts * L.rec_part_cap;
+    L.items = o;
+    o += 4 * (size_t)kParts * L.item_part_cap;
+    L.items_spill = o;
+    o += 4 * (size_t)entries;
+    L.item_of = o;
+    o += 4 * (size_t)entries;
+    L.rec_count = o;
+    o += 4 * (size_t)entries;
+    L.bytes = o;
+    return L;
+}
+
+}  // namespace
+
+struct tsdf_volume {
+    tsdf_config cfg;
+    tsdf_buffers buf;
+    unsigned int mask;
+    unsigned int serial;        // allocate calls so far (frame stamp source)
+    bool pending;               // an owner-mode allocate whose update has not run yet
+    tsdf_frame last;            // the frame of that allocate
+};
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int64_t resolved_entries(const tsdf_config* c) {
+    return c->table_entries ? c->table_entries : tsdf_table_entries_for(c->pool_capacity);
+}
+
+VolumeArgs volume_args(const tsdf_volume* h) {
+    VolumeArgs a;
+    a.table = static_cast<Entry*>(h->buf.table);
+    a.mask = h->mask;
+    a.capacity = (unsigned long long)h->cfg.pool_capacity;
+    a.tsdf = h->buf.tsdf;
+    a.weight = h->buf.weight;
+    a.r = h->buf.r;
+    a.g = h->buf.g;
+    a.b = h->buf.b;
+    a.counters = static_cast<unsigned long long*>(h->buf.counters);
+    a.vs = h->cfg.voxel_size;
+    a.inv_vs = 1.0f / h->cfg.voxel_size;
+    a.trunc = h->cfg.trunc;
+    a.inv_trunc = 1.0f / h->cfg.trunc;
+    return a;
+}
+
+OwnerArgs owner_args(const tsdf_volume* h, unsigned int serial) {
+    OwnerArgs o;
+    std::memset(&o, 0, sizeof(o));
+    o.build_items = h->cfg.update_mode == TSDF_UPDATE_OWNER;
+    o.parity = serial & 1u;
+    o.stamp = serial;
+    if (!o.build_items) return o;
+    const ScratchLayout L = scratch_layout(h->cfg.table_entries, h->cfg.max_frame_pixels);
+    char* base = static_cast<char*>(h->buf.scratch);
+    o.fc = reinterpret_cast<FrameCounters*>(base + L.fc);
+    o.items = reinterpret_cast<unsigned int*>(base + L.items);
+    o.items_spill = reinterpret_cast<unsigned int*>(base + L.items_spill);
+    o.item_of = reinterpret_cast<unsigned int*>(base + L.item_of);
+    o.rec_count = reinterpret_cast<unsigned int*>(base + L.rec_count);
+    o.desc = reinterpret_cast<ItemDesc*>(base + L.desc);
+    o.segs = reinterpret_cast<Segment*>(base + L.segs);
+    o.recs = reinterpret_cast<uint2*>(base + L.recs);
+    o.sorted = reinterpret_cast<uint2*>(base + L.sorted);
+    o.item_part_cap = L.item_part_cap;
+    o.seg_part_cap = L.seg_part_cap;
+    o.rec_part_cap = L.rec_part_cap;
+    return o;
+}
+
+// init arguments: the owner-mode arrays that must start zeroed
+bool init_volume(const tsdf_volume* h, bool whole_pool, hipStream_t s) {
+    const OwnerArgs own = owner_args(h, 0);
+    return launch_init(volume_args(h), (unsigned long long)h->cfg.table_entries, whole_pool,
+                       own.build_items ? &own : nullptr, s);
+}
+
+// Validate a frame and fill the launch arguments.  *empty is set for a frame
+// without pixels (nothing to launch).
+tsdf_status frame_args(const tsdf_volume* h, const tsdf_frame* fr, bool need_rgb, FrameArgs* a, bool* empty) {
+    if (!fr) return TSDF_EINVAL;
+    if (fr->width < 0 || fr->height < 0) return TSDF_EINVAL;
+    const int64_t pixels = (int64_t)fr->width * fr->height;
+    if (pixels > ((int64_t)1 << 31) - 1) return TSDF_EINVAL;
+    *empty = pixels == 0;
+    if (*empty) return TSDF_OK;
+    if (!fr->depth || (need_rgb && !fr->rgb)) return TSDF_EINVAL;
+    if (!std::isfinite(fr->fx) || !std::isfinite(fr->fy) || fr->fx == 0.0f || fr->fy == 0.0f) return TSDF_EINVAL;
+    if (!std::isfinite(fr->cx) || !std::isfinite(fr->cy)) return TSDF_EINVAL;
+    for (int i = 0; i < 9; ++i)
+        if (!std::isfinite(fr->R[i])) return TSDF_EINVAL;
+    for (int i = 0; i < 3; ++i)
+        if (!std::isfinite(fr->t[i])) return TSDF_EINVAL;
+    // R must be a rotation (to float precision): the update maps world
+    // points back to pixels with its transpose
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) {
+            double dot = 0.0;
+            for (int k = 0; k < 3; ++k) dot += (double)fr->R[3 * i + k] * fr->R[3 * j + k];
+            if (std::fabs(dot - (i == j ? 1.0 : 0.0)) > 1e-4) return TSDF_EINVAL;
+        }
+    // Bound on the cells one walk can visit: 1 + (crossings per axis <=
+    // |extent| + 2), extent_i = sum_j |R_ij| |b_j - a_j| / vs with
+    // |b - a| = 2 trunc (|xn|, |yn|, 1) at the image corners; + 8 of slack.
+    const double mx = std::max(std::fabs(0.0 - fr->cx), std::fabs(fr->width - 1.0 - fr->cx)) / std::fabs(fr->fx);
+    const double my = std::max(std::fabs(0.0 - fr->cy), std::fabs(fr->height - 1.0 - fr->cy)) / std::fabs(fr->fy);
+    const double span[3] = {mx, my, 1.0};
+    double bound = 1.0 + 6.0 + 8.0;
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j)
+            bound += std::fabs((double)fr->R[3 * i + j]) * 2.0 * h->cfg.trunc * span[j] / h->cfg.voxel_size;
+    if (!(bound <= TSDF_MAX_WALK)) return TSDF_EINVAL;
+
+    a->depth = fr->depth;
+    a->rgb = fr->rgb;
+    a->width = fr->width;
+    a->height = fr->height;
+    a->fx = fr->fx;
+    a->fy = fr->fy;
+    a->cx = fr->cx;
+    a->cy = fr->cy;
+    std::memcpy(a->R, fr->R, sizeof(a->R));
+    std::memcpy(a->t, fr->t, sizeof(a->t));
+    a->max_visits = (int)std::ceil(bound);
+    a->tiles_x = (fr->width + 15) / 16;
+    const int tiles_y = (fr->height + 15) / 16;
+    a->n_tiles = a->tiles_x * tiles_y;
+    a->tiles_per_xcd = (a->n_tiles + 7) / 8;
+    return TSDF_OK;
+}
+
+bool same_frame(const tsdf_frame& a, const tsdf_frame& b) { return std::memcmp(&a, &b, sizeof(a)) == 0; }
+
+tsdf_status do_allocate(tsdf_volume* h, const tsdf_frame* frame, const FrameArgs& fa, hipStream_t s) {
+    if (h->pending && !launch_discard(volume_args(h), owner_args(h, h->serial), s)) return TSDF_EHIP;
+    h->pending = false;
+    const unsigned int serial = h->serial + 1 == 0xFFFFFFFFu ? 1u : h->serial + 1;
+    if (!launch_allocate(fa, volume_args(h), owner_args(h, serial), s)) return TSDF_EHIP;
+    h->serial = serial;
+    if (h->cfg.update_mode == TSDF_UPDATE_OWNER) {
+        h->pending = true;
+        h->last = *frame;
+    }
+    return TSDF_OK;
+}
+
+tsdf_status do_update(tsdf_volume* h, const tsdf_frame* frame, const FrameArgs& fa, hipStream_t s) {
+    if (h->cfg.update_mode == TSDF_UPDATE_RAYS) return launch_update_rays(fa, volume_args(h), s) ? TSDF_OK : TSDF_EHIP;
+    if (!h->pending || !same_frame(h->last, *frame)) return TSDF_EINVAL;
+    if (!launch_update_owner(fa, volume_args(h), owner_args(h, h->serial), kOwnerGrid, s)) return TSDF_EHIP;
+    h->pending = false;
+    return TSDF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t tsdf_table_entries_for(int64_t pool_capacity) {
+    if (pool_capacity < 1 || pool_capacity > TSDF_MAX_POOL_BLOCKS) return -1;
+    int64_t t = 1;
+    while (t < 2 * pool_capacity) t <<= 1;
+    return t;
+}
+
+size_t tsdf_counters_bytes(void) { return sizeof(unsigned long long) * kReplicas * kCounterWords; }
+
+size_t tsdf_scratch_bytes(const tsdf_config* config) {
+    if (!config || config->update_mode != TSDF_UPDATE_OWNER) return 0;
+    const int64_t entries = resolved_entries(config);
+    if (entries <= 0 || config->max_frame_pixels < 0 || config->max_frame_pixels > ((int64_t)1 << 28)) return 0;
+    return scratch_layout(entries, config->max_frame_pixels).bytes;
+}
+
+tsdf_status tsdf_create(const tsdf_config* config, const tsdf_buffers* buffers, void* stream, tsdf_volume** out) {
+    if (!config || !buffers || !out) return TSDF_EINVAL;
+    *out = nullptr;
+    if (!finite_pos(config->voxel_size) || !finite_pos(config->trunc)) return TSDF_EINVAL;
+    if (config->pool_capacity < 1 || config->pool_capacity > TSDF_MAX_POOL_BLOCKS) return TSDF_EINVAL;
+    if (config->update_mode != TSDF_UPDATE_OWNER && config->update_mode != TSDF_UPDATE_RAYS) return TSDF_EINVAL;
+    if (config->max_frame_pixels < 0 || config->max_frame_pixels > ((int64_t)1 << 28)) return TSDF_EINVAL;
+    const int64_t entries = resolved_entries(config);
+    if (!is_pow2(entries) || entries < 2 * config->pool_capacity || entries > TSDF_MAX_TABLE_ENTRIES)
+        return TSDF_EINVAL;
+    const tsdf_buffers& b = *buffers;
+    if (!b.table || !b.tsdf || !b.weight || !b.r || !b.g || !b.b || !b.counters) return TSDF_EINVAL;
+    if (config->update_mode == TSDF_UPDATE_OWNER && !b.scratch) return TSDF_EINVAL;
+    if (!aligned16(b.table) || !aligned16(b.tsdf) || !aligned16(b.weight) || !aligned16(b.r) ||
+        !aligned16(b.g) || !aligned16(b.b) || !aligned16(b.counters) || !aligned16(b.scratch))
+        return TSDF_EALIGN;
+
+    tsdf_volume* h = new (std::nothrow) tsdf_volume;
+    if (!h) return TSDF_EINVAL;
+    std::memset(h, 0, sizeof(*h));
+    h->cfg = *config;
+    h->cfg.table_entries = entries;
+    h->buf = b;
+    h->mask = (unsigned int)(entries - 1);
+    if (!init_volume(h, true, static_cast<hipStream_t>(stream))) {
+        delete h;
+        return TSDF_EHIP;
+    }
+    *out = h;
+    return TSDF_OK;
+}
+
+tsdf_status tsdf_reset(tsdf_volume* h, void* stream) {
+    if (!h) return TSDF_EINVAL;
+    h->pending = false;
+    return init_volume(h, false, static_cast<hipStream_t>(stream)) ? TSDF_OK : TSDF_EHIP;
+}
+
+tsdf_status tsdf_allocate(tsdf_volume* h, const tsdf_frame* frame, void* stream) {
+    if (!h) return TSDF_EINVAL;
+    FrameArgs fa;
+    bool empty = false;
+    const tsdf_status st = frame_args(h, frame, false, &fa, &empty);
+    if (st != TSDF_OK || empty) return st;
+    return do_allocate(h, frame, fa, static_cast<hipStream_t>(stream));
+}
+
+tsdf_status tsdf_update(tsdf_volume* h, const tsdf_frame* frame, void* stream) {
+    if (!h) return TSDF_EINVAL;
+    FrameArgs fa;
+    bool empty = false;
+    const tsdf_status st = frame_args(h, frame, true, &fa, &empty);
+    if (st != TSDF_OK || empty) return st;
+    return do_update(h, frame, fa, static_cast<hipStream_t>(stream));
+}
+
+tsdf_status tsdf_integrate(tsdf_volume* h, const tsdf_frame* frame, void* stream) {
+    if (!h) return TSDF_EINVAL;
+    FrameArgs fa;
+    bool empty = false;
+    const tsdf_status st = frame_args(h, frame, true, &fa, &empty);
+    if (st != TSDF_OK || empty) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const tsdf_status a = do_allocate(h, frame, fa, s);
+    if (a != TSDF_OK) return a;
+    return do_update(h, frame, fa, s);
+}
+
+tsdf_status tsdf_get_stats(tsdf_volume* h, tsdf_stats* out, void* stream) {
+    if (!h || !out) return TSDF_EINVAL;
+    static thread_local unsigned long long c[kReplicas * kCounterWords];
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(c, h->buf.counters, sizeof(c), hipMemcpyDeviceToHost, s) != hipSuccess) return TSDF_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return TSDF_EHIP;
+    unsigned long long sum[kCounterWords] = {0};
+    for (int r = 0; r < kReplicas; ++r)
+        for (int k = 0; k < kCounterWords; ++k) {
+            const unsigned long long v = c[r * kCounterWords + k];
+            sum[k] = k == kProbeMax ? std::max(sum[k], v) : sum[k] + v;
+        }
+    const unsigned long long cap = (unsigned long long)h->cfg.pool_capacity;
+    const unsigned long long used = c[kBlockCounter];          // copy 0 holds the pool-index counter
+    std::memset(out, 0, sizeof(*out));
+    out->pool_used = (int64_t)(used < cap ? used : cap);
+    out->pool_overflow = (int64_t)(used > cap ? used - cap : 0);
+    out->table_full = (int64_t)sum[kTableFull];
+    out->update_misses = (int64_t)sum[kUpdateMisses];
+    out->out_of_range = (int64_t)sum[kOutOfRange];
+    out->near_skipped = (int64_t)sum[kNearSkipped];
+    out->points_valid = (int64_t)sum[kPointsValid];
+    out->voxel_updates = (int64_t)sum[kVoxelUpdates];
+    out->walk_guard = (int64_t)sum[kWalkGuard];
+    out->probe_max = (int64_t)sum[kProbeMax];
+    out->fallback_blocks = (int64_t)sum[kFallbackBlocks];
+    for (int i = 0; i < kProbeBins; ++i) {
+        out->probe_hist_alloc[i] = sum[kHistAlloc + i];
+        out->probe_hist_update[i] = sum[kHistUpdate + i];
+    }
+    return TSDF_OK;
+}
+
+tsdf_status tsdf_export_blocks(tsdf_volume* h, int32_t* coords, float* tsdf, float* weight, float* r, float* g,
+                               float* b, int64_t max_blocks, int64_t* n_blocks, void* stream) {
+    if (!h || !n_blocks || max_blocks < 0) return TSDF_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned long long used = 0;
+    const unsigned long long* dc = static_cast<const unsigned long long*>(h->buf.counters);
+    if (hipMemcpyAsync(&used, dc + kBlockCounter, sizeof(used), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return TSDF_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return TSDF_EHIP;
+    const unsigned long long cap = (unsigned long long)h->cfg.pool_capacity;
+    const int64_t n = (int64_t)(used < cap ? used : cap);
+    *n_blocks = n;
+    if (n > max_blocks) return TSDF_ESMALL;
+    if (n == 0) return TSDF_OK;
+    if (!coords) return TSDF_EINVAL;
+    if (!launch_export_coords(volume_args(h), (unsigned long long)h->cfg.table_entries, (unsigned long long)n,
+                              coords, s))
+        return TSDF_EHIP;
+    const size_t bytes = (size_t)n * kBlockVoxels * sizeof(float);
+    float* dst[5] = {tsdf, weight, r, g, b};
+    const float* src[5] = {h->buf.tsdf, h->buf.weight, h->buf.r, h->buf.g, h->buf.b};
+    for (int i = 0; i < 5; ++i)
+        if (dst[i] && hipMemcpyAsync(dst[i], src[i], bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return TSDF_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return TSDF_EHIP;
+    return TSDF_OK;
+}
+
+void tsdf_destroy(tsdf_volume* h) { delete h; }
+
+const char* tsdf_status_str(tsdf_status st) {
+    switch (st) {
+        case TSDF_OK: return "TSDF_OK";
+        case TSDF_EINVAL: return "TSDF_EINVAL";
+        case TSDF_EALIGN: return "TSDF_EALIGN";
+        case TSDF_EHIP: return "TSDF_EHIP";
+        case TSDF_ESMALL: return "TSDF_ESMALL";
+    }
+    return "TSDF_UNKNOWN";
+}
+
+}  // extern "C"

@@ -26,9 +26,12 @@ constexpr float kStillAxis = 1e-30f;                // |direction| at or below: 
 constexpr int kBlockVoxels = 512;
 constexpr int kProbeBins = 32;
 
-// Counter words (uint64) at the start of the caller's counters buffer.
+// Counter words (uint64) of one replica of the caller's counters buffer.
+// Statistics are spread over kReplicas copies (workgroup w adds to copy
+// w mod kReplicas) because same-address atomics serialise; readers sum the
+// copies.  The pool-index counter lives in copy 0 only.
 enum CounterWord {
-    kBlockCounter = 0,   // next pool index; may run past the capacity
+    kBlockCounter = 0,   // next pool index; may run past the capacity (copy 0 only)
     kTableFull,
     kUpdateMisses,
     kOutOfRange,
@@ -37,15 +40,87 @@ enum CounterWord {
     kVoxelUpdates,
     kWalkGuard,
     kProbeMax,
+    kFallbackBlocks,     // owner update: blocks rescanned because their runs did not fit
     kHistAlloc = 16,
     kHistUpdate = kHistAlloc + kProbeBins,
     kCounterWords = kHistUpdate + kProbeBins,
 };
+constexpr int kReplicas = 64;
 
+__device__ __forceinline__ unsigned long long* replica(unsigned long long* counters) {
+    return counters + (size_t)(blockIdx.x % kReplicas) * kCounterWords;
+}
+
+// 16-byte table entry: packed key, pool index, and (in the 4 bytes the
+// paper's entry leaves as padding) the serial of the last frame whose
+// allocate pass touched the block, so each touched block is handed to the
+// update pass exactly once per frame.
 struct __align__(16) Entry {
     unsigned long long key;
     unsigned int idx;
-    unsigned int pad;
+    unsigned int stamp;
+};
+
+constexpr unsigned int kNoSlot = 0xFFFFFFFFu;
+constexpr unsigned int kSegOverflow = 0x80000000u;   // block's runs did not all fit: rescan it
+constexpr float kNearPlane = 1e-4f;                 // block corners closer than this: whole image
+
+// One run of a walk inside one block: the pixel, the first cell the walk
+// visits in the block (voxel index), the cells it visits there and how many
+// of them pass the occlusion test.
+__device__ __forceinline__ unsigned int pack_run(int entry, int cells, int kept) {
+    return (unsigned int)entry | ((unsigned int)cells << 9) | ((unsigned int)kept << 15);
+}
+__device__ __forceinline__ int run_entry(unsigned int info) { return (int)(info & 511u); }
+__device__ __forceinline__ int run_cells(unsigned int info) { return (int)((info >> 9) & 63u); }
+__device__ __forceinline__ int run_kept(unsigned int info) { return (int)((info >> 15) & 63u); }
+
+// A wavefront's runs through one block, as recorded by allocate.
+struct __align__(16) Segment {
+    unsigned int slot;        // table slot of the block
+    unsigned int rec_base;    // its first record in the unsorted record buffer
+    unsigned int runs;        // records
+    unsigned int block_off;   // where its records start among the block's records
+};
+
+// A block touched by the frame, as the owner update reads it.
+struct __align__(16) ItemDesc {
+    unsigned long long key;
+    unsigned int idx;         // pool index (>= capacity: none)
+    unsigned int rec_first;   // first record in the block-ordered buffer
+    unsigned int rec_count;   // | kSegOverflow: records did not fit, rescan
+    unsigned int pad[3];
+};
+
+// Per-frame counters of the owner update, in the caller's scratch buffer,
+// one set per frame parity.  Items and run records are reserved in
+// kParts partitions (wavefront w uses partition w mod kParts) so that no
+// single counter takes every wavefront's atomic.
+constexpr int kParts = 64;
+struct FrameCounters {
+    unsigned long long segrec[kParts];  // segments << 32 | records reserved, per partition
+    unsigned int items[kParts];         // blocks first touched, per partition
+    unsigned int items_spill;           // blocks beyond their partition's share
+    unsigned int items_total;           // all blocks (set when the blocks are placed)
+    unsigned long long placed;          // records given to blocks
+    unsigned long long pad[6];
+};
+
+// Owner-update bookkeeping in the caller's scratch buffer.
+struct OwnerArgs {
+    FrameCounters* fc;         // [2] by frame parity
+    unsigned int* items;       // [kParts * item_part_cap] first-touched slots, by partition
+    unsigned int* items_spill; // [table entries] slots beyond a partition's share
+    unsigned int* item_of;     // [table entries] slot -> its item this frame
+    unsigned int* rec_count;   // [table entries] runs per slot this frame (| kSegOverflow)
+    ItemDesc* desc;            // [table entries] per item
+    Segment* segs;             // [kParts * seg_part_cap]
+    uint2* recs;               // [kParts * rec_part_cap] (pixel, packed run), allocate order
+    uint2* sorted;             // [kParts * rec_part_cap] the same records grouped by block
+    unsigned int item_part_cap, seg_part_cap, rec_part_cap;
+    unsigned int parity;       // frame serial & 1
+    unsigned int stamp;        // frame serial, never 0xFFFFFFFF
+    int build_items;           // 0: ray-parallel update, nothing recorded
 };
 
 // Per-launch frame arguments (passed by value; lands in SGPRs).
@@ -85,6 +160,11 @@ struct BandWalk {
     float tm0, tm1, tm2;
     int k0, k1, k2;
     int s0, s1, s2;
+    // cells the walk can visit lie in [span_lo - 1, span_hi + 1] per axis
+    // (the start and end cells, plus one for a final step that lands on a
+    // boundary exactly)
+    int span_lo0, span_lo1, span_lo2;
+    int span_hi0, span_hi1, span_hi2;
 };
 
 __device__ __forceinline__ void setup_axis(float gA, float gB, int& k, int& s, float& inv, float& tm) {
@@ -136,6 +216,13 @@ __device__ __forceinline__ int setup_walk(BandWalk& w, float d, int u, int v, co
     setup_axis(gA0, gB0, w.k0, w.s0, w.inv0, w.tm0);
     setup_axis(gA1, gB1, w.k1, w.s1, w.inv1, w.tm1);
     setup_axis(gA2, gB2, w.k2, w.s2, w.inv2, w.tm2);
+    const int e0 = (int)floorf(gB0), e1 = (int)floorf(gB1), e2 = (int)floorf(gB2);
+    w.span_lo0 = min(w.k0, e0);
+    w.span_lo1 = min(w.k1, e1);
+    w.span_lo2 = min(w.k2, e2);
+    w.span_hi0 = max(w.k0, e0);
+    w.span_hi1 = max(w.k1, e1);
+    w.span_hi2 = max(w.k2, e2);
     return kValid;
 }
 
@@ -179,6 +266,22 @@ __device__ __forceinline__ bool advance(BandWalk& w) {
     return true;
 }
 
+// Put the walk at cell k.  A walk's next-boundary parameters depend only on
+// its current cell (advance recomputes them with this formula), so a walk
+// resumed at a cell it visits continues exactly as the full walk would.
+__device__ __forceinline__ float boundary_param(int k, int s, float gA, float inv) {
+    return s > 0 ? ((float)(k + 1) - gA) * inv : (s < 0 ? ((float)k - gA) * inv : __builtin_inff());
+}
+
+__device__ __forceinline__ void resume_at(BandWalk& w, int k0, int k1, int k2) {
+    w.k0 = k0;
+    w.k1 = k1;
+    w.k2 = k2;
+    w.tm0 = boundary_param(k0, w.s0, w.gA0, w.inv0);
+    w.tm1 = boundary_param(k1, w.s1, w.gA1, w.inv1);
+    w.tm2 = boundary_param(k2, w.s2, w.gA2, w.inv2);
+}
+
 // 64-bit key: block coordinate (cell >> 3, i.e. floor(cell / 8)) + 2^20 per
 // axis, x in bits 0-20, y in 21-41, z in 42-62; bit 63 stays clear, so no
 // key equals the empty marker.
@@ -206,34 +309,51 @@ __device__ __forceinline__ unsigned int home_slot(unsigned long long key, unsign
 // Make sure `key` is in the table.  Linear probing from its home slot with
 // no fixed bound: it ends at the key, at an empty slot won by the one 64-bit
 // compare-exchange, or after every slot was tried (counted as table_full).
-// The winner takes the next pool index and publishes it (or kNoIndex once
-// the pool is full).  Keys are read with plain loads: a slot only ever goes
-// from empty to a key, so a stale empty read just leads to a compare-exchange
-// whose returned value is authoritative.  Returns the slots probed.
-__device__ __forceinline__ unsigned int insert_key(const VolumeArgs& vol, unsigned long long key) {
+// Keys are read with plain loads: a slot only ever goes from empty to a
+// key, so a stale empty read just leads to a compare-exchange whose returned
+// value is authoritative.  Returns the slot (kNoSlot if the table is full);
+// `won` tells whether this call inserted the key (the caller then takes a
+// pool index for it and publishes it), `probes` the slots probed.
+__device__ __forceinline__ unsigned int insert_key(const VolumeArgs& vol, unsigned long long key, bool& won,
+                                                   unsigned int& probes) {
     unsigned int slot = home_slot(key, vol.mask);
-    unsigned int probes = 1;
+    probes = 1;
+    won = false;
     for (;;) {
         const unsigned long long cur = vol.table[slot].key;
-        if (cur == key) break;
+        if (cur == key) return slot;
         if (cur == kEmptyKey) {
             const unsigned long long prev = atomicCAS(&vol.table[slot].key, kEmptyKey, key);
             if (prev == kEmptyKey) {
-                const unsigned long long idx = atomicAdd(vol.counters + kBlockCounter, 1ull);
-                const unsigned int pub = idx < vol.capacity ? (unsigned int)idx : kNoIndex;
-                __hip_atomic_store(&vol.table[slot].idx, pub, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
+                won = true;
+                return slot;
             }
-            if (prev == key) break;
+            if (prev == key) return slot;
         }
         if (probes > vol.mask) {       // every slot tried
-            atomicAdd(vol.counters + kTableFull, 1ull);
-            break;
+            atomicAdd(replica(vol.counters) + kTableFull, 1ull);
+            return kNoSlot;
         }
         slot = (slot + 1) & vol.mask;
         ++probes;
     }
-    return probes;
+}
+
+// The lanes of a wavefront that inserted keys take consecutive pool indices
+// with one atomic, and publish them (kNoIndex once the pool is full).  Must
+// be called by the whole wavefront.
+__device__ __forceinline__ void claim_pool_indices(const VolumeArgs& vol, bool won, unsigned int slot) {
+    const unsigned long long m = __ballot(won);
+    if (!m) return;
+    const int lane = threadIdx.x & 63;
+    unsigned long long base = 0;
+    if (lane == 0) base = atomicAdd(vol.counters + kBlockCounter, (unsigned long long)__popcll(m));
+    base = __shfl(base, 0, 64);
+    if (won) {
+        const unsigned long long idx = base + (unsigned long long)__popcll(m & ((1ull << lane) - 1ull));
+        const unsigned int pub = idx < vol.capacity ? (unsigned int)idx : kNoIndex;
+        __hip_atomic_store(&vol.table[slot].idx, pub, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // Look `key` up after allocation has completed (a kernel boundary earlier on
@@ -260,5 +380,74 @@ __device__ __forceinline__ unsigned int wave_sum(unsigned int x) {
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
     return x;
 }
+
+__device__ __forceinline__ void unpack_key(unsigned long long key, int& bx, int& by, int& bz) {
+    bx = (int)(key & 0x1FFFFFull) - kKeyBias;
+    by = (int)((key >> 21) & 0x1FFFFFull) - kKeyBias;
+    bz = (int)((key >> 42) & 0x1FFFFFull) - kKeyBias;
+}
+
+// Pixels (inclusive rectangle) whose band can reach block (bx, by, bz), and
+// the camera-depth range of that reach.  The block's cells grown by one cell
+// on every side (covering rounding of the walk at cell boundaries) are
+// projected corner by corner; every point of a pixel's band segment projects
+// to that pixel, so a pixel whose walk enters the block lies in the bounding
+// box of the corner projections, widened by one pixel for rounding.  A box
+// reaching the camera plane covers the whole image.
+struct PixelRect {
+    int u0, v0, u1, v1;
+    float zmin, zmax;
+};
+
+__device__ __forceinline__ PixelRect block_rect(int bx, int by, int bz, const FrameArgs& f, float vs) {
+    const float lo[3] = {(float)(8 * bx - 1) * vs, (float)(8 * by - 1) * vs, (float)(8 * bz - 1) * vs};
+    const float hi[3] = {(float)(8 * bx + 9) * vs, (float)(8 * by + 9) * vs, (float)(8 * bz + 9) * vs};
+    float umin = __builtin_inff(), umax = -__builtin_inff();
+    float vmin = __builtin_inff(), vmax = -__builtin_inff();
+    float zmin = __builtin_inff(), zmax = -__builtin_inff();
+    bool behind = false;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const float d0 = ((c & 1) ? hi[0] : lo[0]) - f.t[0];
+        const float d1 = ((c & 2) ? hi[1] : lo[1]) - f.t[1];
+        const float d2 = ((c & 4) ? hi[2] : lo[2]) - f.t[2];
+        const float xc = f.R[0] * d0 + f.R[3] * d1 + f.R[6] * d2;
+        const float yc = f.R[1] * d0 + f.R[4] * d1 + f.R[7] * d2;
+        const float zc = f.R[2] * d0 + f.R[5] * d1 + f.R[8] * d2;
+        zmin = fminf(zmin, zc);
+        zmax = fmaxf(zmax, zc);
+        if (!(zc > kNearPlane)) {
+            behind = true;
+        } else {
+            const float u = f.fx * (xc / zc) + f.cx;
+            const float v = f.fy * (yc / zc) + f.cy;
+            umin = fminf(umin, u);
+            umax = fmaxf(umax, u);
+            vmin = fminf(vmin, v);
+            vmax = fmaxf(vmax, v);
+        }
+    }
+    PixelRect r;
+    r.zmin = zmin;
+    r.zmax = zmax;
+    if (behind) {
+        r.u0 = 0;
+        r.v0 = 0;
+        r.u1 = f.width - 1;
+        r.v1 = f.height - 1;
+        return r;
+    }
+    const float W = (float)f.width, H = (float)f.height;
+    r.u0 = (int)floorf(fminf(fmaxf(umin, -2.0f), W + 2.0f)) - 1;
+    r.u1 = (int)ceilf(fminf(fmaxf(umax, -2.0f), W + 2.0f)) + 1;
+    r.v0 = (int)floorf(fminf(fmaxf(vmin, -2.0f), H + 2.0f)) - 1;
+    r.v1 = (int)ceilf(fminf(fmaxf(vmax, -2.0f), H + 2.0f)) + 1;
+    r.u0 = max(r.u0, 0);
+    r.v0 = max(r.v0, 0);
+    r.u1 = min(r.u1, f.width - 1);
+    r.v1 = min(r.v1, f.height - 1);
+    return r;
+}
+
 
 }  // namespace tsdf

@@ -1,0 +1,788 @@
+// tsdf_kernels.hip -- gfx950 kernels of the integrate path and their host
+// launch wrappers (declared in tsdf_kernels.hpp).
+//
+// The integrate path of hash-blocked TSDF fusion as "What Irregularity
+// Costs: CUDA C++, Rust, and Triton on a Hash-Blocked GPU Workload"
+// describes it in section 3: two kernels over the same points, `allocate`
+// (the irregular stage: probe, compare-exchange, insert) and `update` (the
+// regular stage: accumulate sums into the blocks).  Both apply the same
+// occlusion test and produce the same per-voxel sums; how the update is
+// organised is this library's choice for the MI355X memory system:
+//
+//   * owner update (default): allocate hands every block its frame touched
+//     to the update exactly once (a per-frame stamp in the entry padding),
+//     with the pixel rectangle its band can be seen through.  One workgroup
+//     per block replays the exact walk of every candidate pixel, sums the
+//     block's contributions in LDS and then read-modify-writes the five pool
+//     arrays with plain coalesced loads and stores: a block has one writer
+//     per frame, so no device-scope float atomics are needed.  Blocks whose
+//     rectangle is split over several workgroups add with coalesced atomics.
+//   * ray-parallel update: the shape the paper describes (one thread per
+//     point, a lookup per block run, five no-return f32 atomic additions per
+//     voxel), kept as a variant.
+//
+// Launch geometry of the per-point kernels: one thread per pixel; a
+// 256-thread workgroup (four wave64 wavefronts) covers a 16 x 16 tile, each
+// wavefront an 8 x 8 sub-tile, so a wave's rays mostly touch the same blocks.
+// Workgroups go to the eight XCDs round-robin; the workgroup -> tile remap
+// gives each XCD a contiguous run of tiles so neighbouring tiles share an L2.
+#include <hip/hip_runtime.h>
+
+#include "tsdf_kernels.hpp"
+
+namespace tsdf {
+namespace {
+
+constexpr int kTile = 16;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kXcds = 8;
+constexpr int kListCap = 256;     // block runs a wavefront buffers before de-duplicating
+constexpr int kSetCap = 256;      // per-wavefront LDS hash set (power of two, >= kListCap)
+constexpr float kInv255 = 1.0f / 255.0f;
+
+__device__ __forceinline__ bool workgroup_tile(const FrameArgs& f, int& tile_u0, int& tile_v0) {
+    const int wg = blockIdx.x;
+    const int tile = (wg % kXcds) * f.tiles_per_xcd + wg / kXcds;
+    if (tile >= f.n_tiles) return false;
+    tile_u0 = (tile % f.tiles_x) * kTile;
+    tile_v0 = (tile / f.tiles_x) * kTile;
+    return true;
+}
+
+__device__ __forceinline__ void thread_pixel(int tile_u0, int tile_v0, int& u, int& v) {
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    u = tile_u0 + (wave & 1) * 8 + (lane & 7);
+    v = tile_v0 + (wave >> 1) * 8 + (lane >> 3);
+}
+
+__device__ __forceinline__ void hist_add(unsigned int* s_hist, unsigned int* s_pmax, unsigned int probes) {
+    atomicAdd(s_hist + (probes < (unsigned)kProbeBins ? probes - 1 : kProbeBins - 1), 1u);
+    atomicMax(s_pmax, probes);
+}
+
+__device__ __forceinline__ void flush_hist(const unsigned int* s_hist, const unsigned int* s_pmax,
+                                           unsigned long long* counters, int base) {
+    const int t = threadIdx.x;
+    unsigned long long* c = replica(counters);
+    if (t < kProbeBins && s_hist[t]) atomicAdd(c + base + t, (unsigned long long)s_hist[t]);
+    if (t == kProbeBins && *s_pmax) atomicMax(c + kProbeMax, (unsigned long long)*s_pmax);
+}
+
+// order the wavefront's LDS accesses (LDS operations of one wavefront
+// complete in order once issued; this keeps the compiler from moving them)
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// ---------------------------------------------------------------------------
+// allocate.  Each lane walks its ray and cuts it into runs, one per block it
+// crosses (a ray enters a block once); runs with at least one kept voxel are
+// compacted by ballot into a per-wavefront LDS list.  A full list is
+// de-duplicated by block key in a per-wavefront LDS hash set, and one lane
+// per distinct key probes the global table, all of the wavefront's distinct
+// keys in flight together.  For the owner update each (wavefront, block)
+// group of runs is then stored as a segment of run records.  Also counts
+// the point classes and the kept (point, voxel) pairs.
+// ---------------------------------------------------------------------------
+constexpr unsigned int kNoBase = 0xFFFFFFFFu;     // runs not recorded (block rescanned)
+constexpr unsigned int kNoKeyBase = 0xFFFFFFFEu;  // runs of a key the full table refused
+
+struct AllocLds {
+    unsigned long long lkey[kWaves][kListCap];    // run list: block key,
+    unsigned int lpix[kWaves][kListCap];          //   pixel index,
+    unsigned int linfo[kWaves][kListCap];         //   packed run,
+    unsigned short lset[kWaves][kListCap];        //   its set slot
+    unsigned long long skey[kWaves][kSetCap];     // set: key,
+    unsigned int sruns[kWaves][kSetCap];          //   runs,
+    unsigned int sbase[kWaves][kSetCap];          //   first record,
+    unsigned int sfill[kWaves][kSetCap];          //   records written
+    unsigned short suniq[kWaves][kSetCap];        // occupied set slots, compacted
+    unsigned int nuniq[kWaves];
+    unsigned int hist[kProbeBins];
+    unsigned int pmax;
+    unsigned int cnt[6];
+};
+
+__device__ void flush_runs(AllocLds& L, int wave, int lane, int n, const VolumeArgs& vol, const OwnerArgs& own,
+                           unsigned int& misses) {
+    for (int i = lane; i < kSetCap; i += 64) {
+        L.skey[wave][i] = kEmptyKey;
+        L.sruns[wave][i] = 0;
+        L.sfill[wave][i] = 0;
+    }
+    if (lane == 0) L.nuniq[wave] = 0;
+    wave_lds_fence();
+    for (int i = lane; i < n; i += 64) {
+        const unsigned long long key = L.lkey[wave][i];
+        unsigned int h = home_slot(key, kSetCap - 1);
+        for (;;) {     // n <= kSetCap distinct keys at most: the probe always finds room
+            const unsigned long long prev = atomicCAS(&L.skey[wave][h], kEmptyKey, key);
+            if (prev == kEmptyKey) {
+                L.suniq[wave][atomicAdd(&L.nuniq[wave], 1u)] = (unsigned short)h;
+                break;
+            }
+            if (prev == key) break;
+            h = (h + 1) & (kSetCap - 1);
+        }
+        L.lset[wave][i] = (unsigned short)h;
+        atomicAdd(&L.sruns[wave][h], 1u);
+    }
+    wave_lds_fence();
+    const int nu = (int)L.nuniq[wave];
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const unsigned int part = (blockIdx.x * kWaves + wave) % kParts;
+    FrameCounters* fc = own.fc + own.parity;         // owner mode only
+    for (int j0 = 0; j0 < nu; j0 += 64) {           // wavefront-uniform
+        const int j = j0 + lane;
+        const bool has = j < nu;
+        int h = 0;
+        unsigned int slot = kNoSlot;
+        bool won = false;
+        if (has) {
+            h = L.suniq[wave][j];
+            unsigned int probes;
+            slot = insert_key(vol, L.skey[wave][h], won, probes);
+            hist_add(L.hist, &L.pmax, probes);
+        }
+        claim_pool_indices(vol, won, slot);
+        if (!own.build_items) continue;             // the ray-parallel update needs nothing more
+        // first touch of the block this frame: the stamp exchange lets one
+        // caller per frame through; the wavefront's new blocks take item
+        // numbers in its partition with one atomic
+        bool first = false;
+        if (has && slot != kNoSlot && vol.table[slot].stamp != own.stamp)
+            first = atomicExch(&vol.table[slot].stamp, own.stamp) != own.stamp;
+        const unsigned long long fm = __ballot(first);
+        if (fm) {
+            unsigned int ib = 0;
+            if (lane == 0) ib = atomicAdd(&fc->items[part], (unsigned int)__popcll(fm));
+            ib = __shfl(ib, 0, 64);
+            if (first) {
+                const unsigned int k = ib + (unsigned int)__popcll(fm & below);
+                if (k < own.item_part_cap)
+                    own.items[(size_t)part * own.item_part_cap + k] = slot;
+                else                                 // beyond the partition's share (rare)
+                    own.items_spill[atomicAdd(&fc->items_spill, 1u)] = slot;
+            }
+        }
+        // segments and records: one reservation for the whole wavefront
+        const bool rsv = has && slot != kNoSlot;
+        const unsigned int runs = rsv ? L.sruns[wave][h] : 0u;
+        unsigned int x = runs;                       // inclusive prefix of runs over the lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        const unsigned int total = __shfl(x, 63, 64);
+        const unsigned long long rm = __ballot(rsv);
+        unsigned long long r0 = 0;
+        if (rm) {
+            if (lane == 0) r0 = atomicAdd(&fc->segrec[part], ((unsigned long long)__popcll(rm) << 32) | total);
+            r0 = __shfl(r0, 0, 64);
+        }
+        if (rsv) {
+            const unsigned int seg = (unsigned int)(r0 >> 32) + (unsigned int)__popcll(rm & below);
+            const unsigned int rec = (unsigned int)r0 + (x - runs);
+            Segment* segs = own.segs + (size_t)part * own.seg_part_cap;
+            if (seg < own.seg_part_cap && (unsigned long long)rec + runs <= own.rec_part_cap) {
+                Segment sg;
+                sg.slot = slot;
+                sg.rec_base = part * own.rec_part_cap + rec;
+                sg.runs = runs;
+                sg.block_off = atomicAdd(own.rec_count + slot, runs) & ~kSegOverflow;
+                segs[seg] = sg;
+                L.sbase[wave][h] = sg.rec_base;
+            } else {                                 // out of space: the update rescans the block
+                if (seg < own.seg_part_cap) {        // the scatter reads every reserved segment
+                    Segment sg;
+                    sg.slot = kNoSlot;
+                    sg.rec_base = 0;
+                    sg.runs = 0;
+                    sg.block_off = 0;
+                    segs[seg] = sg;
+                }
+                atomicOr(own.rec_count + slot, kSegOverflow);
+                L.sbase[wave][h] = kNoBase;
+            }
+        } else if (has) {                            // the full table refused the key: its
+            L.sbase[wave][h] = kNoKeyBase;           // kept visits are lost, counted below
+        }
+    }
+    wave_lds_fence();
+    if (own.build_items) {
+        for (int i = lane; i < n; i += 64) {
+            const int h = L.lset[wave][i];
+            const unsigned int base = L.sbase[wave][h];
+            if (base == kNoKeyBase) {
+                misses += (unsigned int)run_kept(L.linfo[wave][i]);
+            } else if (base != kNoBase) {
+                const unsigned int pos = atomicAdd(&L.sfill[wave][h], 1u);
+                own.recs[base + pos] = make_uint2(L.lpix[wave][i], L.linfo[wave][i]);
+            }
+        }
+    }
+    wave_lds_fence();
+}
+
+__global__ __launch_bounds__(kThreads) void k_allocate(FrameArgs f, VolumeArgs vol, OwnerArgs own) {
+    __shared__ AllocLds L;
+    if (blockIdx.x == 0 && own.build_items) {
+        // clear the next frame's counters (their last users finished before
+        // this kernel started)
+        unsigned long long* next = reinterpret_cast<unsigned long long*>(own.fc + (own.parity ^ 1));
+        for (int i = threadIdx.x; i < (int)(sizeof(FrameCounters) / 8); i += kThreads) next[i] = 0;
+    }
+    int tu, tv;
+    if (!workgroup_tile(f, tu, tv)) return;
+    if (threadIdx.x < kProbeBins) L.hist[threadIdx.x] = 0;
+    if (threadIdx.x < 6) L.cnt[threadIdx.x] = 0;
+    if (threadIdx.x == 0) L.pmax = 0;
+    __syncthreads();
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int u, v;
+    thread_pixel(tu, tv, u, v);
+    const unsigned int pix = (unsigned int)v * (unsigned int)f.width + (unsigned int)u;
+    BandWalk w;
+    int cls = kInvalid;
+    if (u < f.width && v < f.height) cls = setup_walk(w, f.depth[pix], u, v, f, vol.trunc, vol.inv_vs);
+    bool alive = cls == kValid;
+    unsigned long long cur = kEmptyKey;       // block of the current run
+    int entry = 0, cells = 0, kept = 0;       // the current run
+    unsigned int n_upd = 0, n_guard = 0, misses = 0;
+    int visits = 0;
+    int base = 0;                             // wavefront-uniform fill of the run list
+
+    for (;;) {
+        const bool any_alive = __any(alive);
+        bool emit = false;
+        unsigned long long ekey = kEmptyKey;
+        unsigned int einfo = 0;
+        if (alive) {
+            const unsigned long long key = block_key(w.k0, w.k1, w.k2);
+            if (key != cur) {                 // a new block: close the previous run
+                emit = kept > 0;
+                ekey = cur;
+                einfo = pack_run(entry, cells, kept);
+                cur = key;
+                entry = voxel_in_block(w.k0, w.k1, w.k2);
+                cells = 0;
+                kept = 0;
+            }
+            ++cells;
+            float sdf;
+            if (centre_test(w, f, vol.vs, vol.trunc, sdf)) {
+                ++kept;
+                ++n_upd;
+            }
+            if (++visits >= f.max_visits) {
+                n_guard += advance(w) ? 1u : 0u;
+                alive = false;
+            } else {
+                alive = advance(w);
+            }
+        } else if (!any_alive && cur != kEmptyKey) {   // after the last step: the last run
+            emit = kept > 0;
+            ekey = cur;
+            einfo = pack_run(entry, cells, kept);
+            cur = kEmptyKey;
+        }
+        const unsigned long long m = __ballot(emit);
+        if (m) {
+            if (base + 64 > kListCap) {
+                flush_runs(L, wave, lane, base, vol, own, misses);
+                base = 0;
+            }
+            if (emit) {
+                const int pos = base + __popcll(m & below);
+                L.lkey[wave][pos] = ekey;
+                L.lpix[wave][pos] = pix;
+                L.linfo[wave][pos] = einfo;
+            }
+            base += __popcll(m);
+        }
+        if (!any_alive) break;
+    }
+    if (base > 0) flush_runs(L, wave, lane, base, vol, own, misses);
+
+    const unsigned int c_valid = wave_sum(cls == kValid);
+    const unsigned int c_near = wave_sum(cls == kNear);
+    const unsigned int c_oor = wave_sum(cls == kOutside);
+    const unsigned int c_upd = wave_sum(n_upd);
+    const unsigned int c_guard = wave_sum(n_guard);
+    const unsigned int c_miss = wave_sum(misses);
+    if (lane == 0) {
+        if (c_valid) atomicAdd(L.cnt + 0, c_valid);
+        if (c_near) atomicAdd(L.cnt + 1, c_near);
+        if (c_oor) atomicAdd(L.cnt + 2, c_oor);
+        if (c_upd) atomicAdd(L.cnt + 3, c_upd);
+        if (c_guard) atomicAdd(L.cnt + 4, c_guard);
+        if (c_miss) atomicAdd(L.cnt + 5, c_miss);
+    }
+    __syncthreads();
+    flush_hist(L.hist, &L.pmax, vol.counters, kHistAlloc);
+    if (threadIdx.x < 6 && L.cnt[threadIdx.x]) {
+        const int word = threadIdx.x == 0 ? kPointsValid
+                       : threadIdx.x == 1 ? kNearSkipped
+                       : threadIdx.x == 2 ? kOutOfRange
+                       : threadIdx.x == 3 ? kVoxelUpdates
+                       : threadIdx.x == 4 ? kWalkGuard
+                                          : kUpdateMisses;
+        atomicAdd(replica(vol.counters) + word, (unsigned long long)L.cnt[threadIdx.x]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// grouping the frame's run records by block.  k_place_items gives every
+// touched block a descriptor and a contiguous record range (one atomic per
+// 256 blocks); k_scatter_records copies each segment's records into its
+// block's range (the segment knows its offset there).
+// ---------------------------------------------------------------------------
+// prefix over the partitions' counts (+ the spill list): pre[p] = first
+// global index of partition p, pre[kParts + 1] = total
+__device__ void partition_prefix(const unsigned int* counts, unsigned int cap, unsigned int spill, unsigned int* pre) {
+    if (threadIdx.x == 0) {
+        unsigned int acc = 0;
+        for (int p = 0; p < kParts; ++p) {
+            pre[p] = acc;
+            acc += min(counts[p], cap);
+        }
+        pre[kParts] = acc;
+        pre[kParts + 1] = acc + spill;
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ int find_partition(const unsigned int* pre, unsigned int i) {
+    int a = 0, b = kParts;                   // largest p with pre[p] <= i (p = kParts: spill)
+    while (a < b) {
+        const int m = (a + b + 1) >> 1;
+        if (pre[m] <= i) a = m; else b = m - 1;
+    }
+    return a;
+}
+
+__global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerArgs own) {
+    __shared__ unsigned int s_pre[kParts + 2];
+    __shared__ unsigned int s_wave[kWaves];
+    __shared__ unsigned int s_base;
+    FrameCounters& fc = own.fc[own.parity];
+    partition_prefix(fc.items, own.item_part_cap, fc.items_spill, s_pre);
+    const unsigned int n = s_pre[kParts + 1];
+    if (blockIdx.x == 0 && threadIdx.x == 0) fc.items_total = n;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (unsigned int b = blockIdx.x * kThreads; b < n; b += gridDim.x * kThreads) {
+        const unsigned int i = b + tid;
+        unsigned int slot = 0, rc = 0, cnt = 0;
+        if (i < n) {
+            const int p = find_partition(s_pre, i);
+            slot = p < kParts ? own.items[(size_t)p * own.item_part_cap + (i - s_pre[p])]
+                              : own.items_spill[i - s_pre[kParts]];
+            rc = own.rec_count[slot];
+            cnt = (rc & kSegOverflow) ? 0u : rc;
+        }
+        unsigned int x = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) s_wave[wave] = x;
+        __syncthreads();
+        if (tid == 0) {
+            unsigned int acc = 0;
+            for (int k = 0; k < kWaves; ++k) {
+                const unsigned int t = s_wave[k];
+                s_wave[k] = acc;
+                acc += t;
+            }
+            s_base = (unsigned int)atomicAdd(&fc.placed, (unsigned long long)acc);
+        }
+        __syncthreads();
+        if (i < n) {
+            const ulonglong2 e = *reinterpret_cast<const ulonglong2*>(vol.table + slot);
+            ItemDesc d;
+            d.key = e.x;
+            d.idx = (unsigned int)e.y;
+            d.rec_first = s_base + s_wave[wave] + x - cnt;
+            d.rec_count = rc;
+            d.pad[0] = slot;
+            d.pad[1] = 0;
+            d.pad[2] = 0;
+            own.desc[i] = d;
+            own.item_of[slot] = i;
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_scatter_records(VolumeArgs vol, OwnerArgs own) {
+    __shared__ unsigned int s_cnt[kParts];
+    __shared__ unsigned int s_pre[kParts + 2];
+    FrameCounters& fc = own.fc[own.parity];
+    if (threadIdx.x < kParts) s_cnt[threadIdx.x] = (unsigned int)(fc.segrec[threadIdx.x] >> 32);
+    __syncthreads();
+    partition_prefix(s_cnt, own.seg_part_cap, 0, s_pre);
+    const unsigned int n = s_pre[kParts];
+    const int lane = threadIdx.x & 63;
+    const unsigned int waves = gridDim.x * kWaves;
+    for (unsigned int j = blockIdx.x * kWaves + (threadIdx.x >> 6); j < n; j += waves) {
+        const int p = find_partition(s_pre, j);
+        const Segment sg = own.segs[(size_t)p * own.seg_part_cap + (j - s_pre[p])];
+        if (sg.slot == kNoSlot) continue;                       // refused for lack of space
+        const ItemDesc d = own.desc[own.item_of[sg.slot]];
+        if (d.rec_count & kSegOverflow) continue;               // the block is rescanned
+        for (unsigned int r = lane; r < sg.runs; r += 64)
+            own.sorted[d.rec_first + sg.block_off + r] = own.recs[sg.rec_base + r];
+    }
+}
+
+// Drop a frame's records without updating (an allocate that no update
+// followed): clear the per-block run counts it left.
+__global__ __launch_bounds__(kThreads) void k_discard_items(VolumeArgs vol, OwnerArgs own) {
+    __shared__ unsigned int s_pre[kParts + 2];
+    FrameCounters& fc = own.fc[own.parity];
+    partition_prefix(fc.items, own.item_part_cap, fc.items_spill, s_pre);
+    const unsigned int n = s_pre[kParts + 1];
+    for (unsigned int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+        const int p = find_partition(s_pre, i);
+        const unsigned int slot = p < kParts ? own.items[(size_t)p * own.item_part_cap + (i - s_pre[p])]
+                                             : own.items_spill[i - s_pre[kParts]];
+        own.rec_count[slot] = 0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// owner update: one wavefront per touched block (blocks handed out
+// statically, no shared counter).  The block's runs are replayed from their
+// recorded first cell (the exact walk state there follows from the cell),
+// kept voxels add into LDS (signed distance as f32, weight and colour bytes
+// as integer sums), and the block's touched voxels are then read, added to
+// and written with plain coalesced loads and stores: the block has no other
+// writer this frame.  A block whose runs did not fit the record buffers is
+// rescanned instead: every pixel of the rectangle its band can be seen
+// through replays its walk.
+// ---------------------------------------------------------------------------
+constexpr int kOwnerThreads = 64;
+
+struct UpdateLds {
+    float tsdf[kBlockVoxels];
+    unsigned long long wr[kBlockVoxels];          // weight | R sum << 32
+    unsigned long long gb[kBlockVoxels];          // G sum | B sum << 32
+};
+
+__device__ __forceinline__ void accumulate(UpdateLds& L, const BandWalk& w, const FrameArgs& f,
+                                           const VolumeArgs& vol, unsigned long long c_wr, unsigned long long c_gb,
+                                           unsigned int& n_kept) {
+    float sdf;
+    if (centre_test(w, f, vol.vs, vol.trunc, sdf)) {
+        const int j = voxel_in_block(w.k0, w.k1, w.k2);
+        atomicAdd(L.tsdf + j, sdf * vol.inv_trunc);
+        atomicAdd(L.wr + j, c_wr);
+        atomicAdd(L.gb + j, c_gb);
+        ++n_kept;
+    }
+}
+
+__device__ __forceinline__ void colour_words(const FrameArgs& f, size_t pix, unsigned long long& c_wr,
+                                             unsigned long long& c_gb) {
+    c_wr = 1ull | ((unsigned long long)f.rgb[3 * pix + 0] << 32);
+    c_gb = (unsigned long long)f.rgb[3 * pix + 1] | ((unsigned long long)f.rgb[3 * pix + 2] << 32);
+}
+
+// rescan: every pixel of the block's rectangle replays its walk through the block
+__device__ void rescan_block(UpdateLds& L, const FrameArgs& f, const VolumeArgs& vol, int bx, int by, int bz,
+                             unsigned int& n_kept) {
+    const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
+    const PixelRect r = block_rect(bx, by, bz, f, vol.vs);
+    if (r.u0 > r.u1 || r.v0 > r.v1) return;
+    const int rw = r.u1 - r.u0 + 1;
+    const long long area = (long long)rw * (r.v1 - r.v0 + 1);
+    const float zlo = r.zmin - vol.vs, zhi = r.zmax + vol.vs;
+    for (long long p = threadIdx.x; p < area; p += blockDim.x) {
+        const int u = r.u0 + (int)(p % rw);
+        const int v = r.v0 + (int)(p / rw);
+        const size_t pix = (size_t)v * f.width + u;
+        const float d = f.depth[pix];
+        if (!(d - vol.trunc <= zhi && d + vol.trunc >= zlo)) continue;      // band cannot reach the block
+        BandWalk w;
+        if (setup_walk(w, d, u, v, f, vol.trunc, vol.inv_vs) != kValid) continue;
+        if (w.span_hi0 < lo0 - 1 || w.span_lo0 > lo0 + 8 || w.span_hi1 < lo1 - 1 || w.span_lo1 > lo1 + 8 ||
+            w.span_hi2 < lo2 - 1 || w.span_lo2 > lo2 + 8)
+            continue;                                                        // cell span misses the block
+        unsigned long long c_wr, c_gb;
+        colour_words(f, pix, c_wr, c_gb);
+        bool inside = false;
+        for (int visits = 0;;) {
+            if ((unsigned)(w.k0 - lo0) < 8u && (unsigned)(w.k1 - lo1) < 8u && (unsigned)(w.k2 - lo2) < 8u) {
+                inside = true;
+                accumulate(L, w, f, vol, c_wr, c_gb, n_kept);
+            } else if (inside) {
+                break;                                                       // a walk crosses a block once
+            }
+            if (++visits >= f.max_visits || !advance(w)) break;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kOwnerThreads) void k_update_owner(FrameArgs f, VolumeArgs vol, OwnerArgs own) {
+    __shared__ UpdateLds L;
+    const int tid = threadIdx.x;
+    const unsigned int n_items = own.fc[own.parity].items_total;
+    unsigned int misses = 0, fallbacks = 0;
+
+    for (unsigned int it = blockIdx.x; it < n_items; it += gridDim.x) {
+        const ItemDesc d = own.desc[it];
+        int bx, by, bz;
+        unpack_key(d.key, bx, by, bz);
+        for (int j = tid; j < kBlockVoxels; j += kOwnerThreads) {
+            L.tsdf[j] = 0.0f;
+            L.wr[j] = 0;
+            L.gb[j] = 0;
+        }
+        __syncthreads();
+        unsigned int n_kept = 0;
+        if (d.rec_count & kSegOverflow) {
+            rescan_block(L, f, vol, bx, by, bz, n_kept);
+            fallbacks += tid == 0;
+        } else {
+            const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
+            for (unsigned int r = tid; r < d.rec_count; r += kOwnerThreads) {
+                const uint2 rec = own.sorted[d.rec_first + r];
+                const unsigned int pix = rec.x;
+                const int u = (int)(pix % (unsigned int)f.width), v = (int)(pix / (unsigned int)f.width);
+                BandWalk w;
+                if (setup_walk(w, f.depth[pix], u, v, f, vol.trunc, vol.inv_vs) != kValid) continue;  // cannot happen
+                unsigned long long c_wr, c_gb;
+                colour_words(f, pix, c_wr, c_gb);
+                const int e = run_entry(rec.y);
+                resume_at(w, lo0 + (e & 7), lo1 + ((e >> 3) & 7), lo2 + (e >> 6));
+                const int cells = run_cells(rec.y);
+                for (int q = 0;;) {
+                    accumulate(L, w, f, vol, c_wr, c_gb, n_kept);
+                    if (++q >= cells || !advance(w)) break;
+                }
+            }
+        }
+        __syncthreads();
+        if (d.idx < vol.capacity) {
+            const size_t base = (size_t)d.idx * kBlockVoxels;
+            for (int j = tid; j < kBlockVoxels; j += kOwnerThreads) {
+                const unsigned long long wr = L.wr[j];
+                const unsigned int cnt = (unsigned int)wr;
+                if (!cnt) continue;
+                const unsigned long long gb = L.gb[j];
+                const size_t off = base + j;
+                const float t0 = vol.tsdf[off], w0 = vol.weight[off], r0 = vol.r[off], g0 = vol.g[off],
+                            b0 = vol.b[off];
+                vol.tsdf[off] = t0 + L.tsdf[j];
+                vol.weight[off] = w0 + (float)cnt;
+                vol.r[off] = r0 + (float)(unsigned int)(wr >> 32) * kInv255;
+                vol.g[off] = g0 + (float)(unsigned int)gb * kInv255;
+                vol.b[off] = b0 + (float)(unsigned int)(gb >> 32) * kInv255;
+            }
+        } else {
+            misses += n_kept;               // block refused a pool index: counted, not stored
+        }
+        if (tid == 0) own.rec_count[d.pad[0]] = 0;
+        __syncthreads();
+    }
+    const unsigned int c_miss = wave_sum(misses);
+    if (tid == 0 && c_miss) atomicAdd(replica(vol.counters) + kUpdateMisses, (unsigned long long)c_miss);
+    if (tid == 0 && fallbacks) atomicAdd(replica(vol.counters) + kFallbackBlocks, (unsigned long long)fallbacks);
+}
+
+// ---------------------------------------------------------------------------
+// ray-parallel update: walk, test, look the block up once per block run of
+// the ray, add with five no-return f32 atomics into the SoA pool.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_update_rays(FrameArgs f, VolumeArgs vol) {
+    __shared__ unsigned int s_hist[kProbeBins];
+    __shared__ unsigned int s_pmax;
+    __shared__ unsigned int s_miss;
+    int tu, tv;
+    if (!workgroup_tile(f, tu, tv)) return;
+    if (threadIdx.x < kProbeBins) s_hist[threadIdx.x] = 0;
+    if (threadIdx.x == 0) {
+        s_pmax = 0;
+        s_miss = 0;
+    }
+    __syncthreads();
+
+    int u, v;
+    thread_pixel(tu, tv, u, v);
+    BandWalk w;
+    int cls = kInvalid;
+    float cr = 0.f, cg = 0.f, cb = 0.f;
+    if (u < f.width && v < f.height) {
+        const size_t pix = (size_t)v * f.width + u;
+        cls = setup_walk(w, f.depth[pix], u, v, f, vol.trunc, vol.inv_vs);
+        if (cls == kValid) {
+            cr = (float)f.rgb[3 * pix + 0] * kInv255;
+            cg = (float)f.rgb[3 * pix + 1] * kInv255;
+            cb = (float)f.rgb[3 * pix + 2] * kInv255;
+        }
+    }
+    unsigned int n_miss = 0;
+    if (cls == kValid) {
+        unsigned long long cur = kEmptyKey;
+        unsigned int idx = kNoIndex;
+        int visits = 0;
+        for (;;) {
+            float sdf;
+            if (centre_test(w, f, vol.vs, vol.trunc, sdf)) {
+                const unsigned long long key = block_key(w.k0, w.k1, w.k2);
+                if (key != cur) {
+                    unsigned int probes;
+                    idx = lookup_key(vol, key, probes);
+                    cur = key;
+                    hist_add(s_hist, &s_pmax, probes);
+                }
+                if (idx != kNoIndex) {
+                    const size_t off = (size_t)idx * kBlockVoxels + voxel_in_block(w.k0, w.k1, w.k2);
+                    unsafeAtomicAdd(vol.tsdf + off, sdf * vol.inv_trunc);
+                    unsafeAtomicAdd(vol.weight + off, 1.0f);
+                    unsafeAtomicAdd(vol.r + off, cr);
+                    unsafeAtomicAdd(vol.g + off, cg);
+                    unsafeAtomicAdd(vol.b + off, cb);
+                } else {
+                    ++n_miss;
+                }
+            }
+            if (++visits >= f.max_visits || !advance(w)) break;
+        }
+    }
+    const unsigned int c_miss = wave_sum(n_miss);
+    if ((threadIdx.x & 63) == 0 && c_miss) atomicAdd(&s_miss, c_miss);
+    __syncthreads();
+    flush_hist(s_hist, &s_pmax, vol.counters, kHistUpdate);
+    if (threadIdx.x == 0 && s_miss) atomicAdd(replica(vol.counters) + kUpdateMisses, (unsigned long long)s_miss);
+}
+
+// ---------------------------------------------------------------------------
+// initialisation, reset and export
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_fill_table(uint4* table, unsigned long long n) {
+    const uint4 empty = make_uint4(~0u, ~0u, ~0u, ~0u);
+    for (unsigned long long i = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (unsigned long long)gridDim.x * blockDim.x)
+        table[i] = empty;
+}
+
+// Zero the first `capacity` pool blocks of all five arrays or, with
+// use_counter, only min(block counter, capacity) blocks (the used part).
+__global__ __launch_bounds__(kThreads) void k_zero_pool(float4* a0, float4* a1, float4* a2, float4* a3,
+                                                         float4* a4, const unsigned long long* counters,
+                                                         unsigned long long capacity, int use_counter) {
+    unsigned long long blocks = capacity;
+    if (use_counter) {
+        const unsigned long long used = counters[kBlockCounter];
+        blocks = used < capacity ? used : capacity;
+    }
+    const unsigned long long n = blocks * (kBlockVoxels / 4);
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (unsigned long long i = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (unsigned long long)gridDim.x * blockDim.x) {
+        a0[i] = z;
+        a1[i] = z;
+        a2[i] = z;
+        a3[i] = z;
+        a4[i] = z;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_zero_words(unsigned int* a, unsigned long long n) {
+    for (unsigned long long i = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (unsigned long long)gridDim.x * blockDim.x)
+        a[i] = 0;
+}
+
+__global__ __launch_bounds__(kThreads) void k_zero_counters(unsigned long long* counters) {
+    for (int i = threadIdx.x; i < kReplicas * kCounterWords; i += blockDim.x) counters[i] = 0;
+}
+
+__global__ __launch_bounds__(kThreads) void k_export_coords(const Entry* table, unsigned long long n_entries,
+                                                             unsigned long long n_blocks, int* coords) {
+    for (unsigned long long i = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; i < n_entries;
+         i += (unsigned long long)gridDim.x * blockDim.x) {
+        const ulonglong2 e = *reinterpret_cast<const ulonglong2*>(table + i);
+        const unsigned int idx = (unsigned int)e.y;
+        if (e.x == kEmptyKey || idx >= n_blocks) continue;
+        int bx, by, bz;
+        unpack_key(e.x, bx, by, bz);
+        coords[3 * (size_t)idx + 0] = bx;
+        coords[3 * (size_t)idx + 1] = by;
+        coords[3 * (size_t)idx + 2] = bz;
+    }
+}
+
+unsigned int grid_for(unsigned long long n) {
+    unsigned long long g = (n + kThreads - 1) / kThreads;
+    if (g < 1) g = 1;
+    if (g > 8192) g = 8192;
+    return (unsigned int)g;
+}
+
+bool launched() { return hipGetLastError() == hipSuccess; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launch wrappers
+// ---------------------------------------------------------------------------
+int tile_grid(const FrameArgs& f) { return f.tiles_per_xcd * kXcds; }
+
+bool launch_allocate(const FrameArgs& f, const VolumeArgs& v, const OwnerArgs& o, hipStream_t s) {
+    hipLaunchKernelGGL(k_allocate, dim3(tile_grid(f)), dim3(kThreads), 0, s, f, v, o);
+    return launched();
+}
+
+bool launch_update_owner(const FrameArgs& f, const VolumeArgs& v, const OwnerArgs& o, int grid, hipStream_t s) {
+    hipLaunchKernelGGL(k_place_items, dim3(256), dim3(kThreads), 0, s, v, o);
+    hipLaunchKernelGGL(k_scatter_records, dim3(2048), dim3(kThreads), 0, s, v, o);
+    hipLaunchKernelGGL(k_update_owner, dim3(grid), dim3(kOwnerThreads), 0, s, f, v, o);
+    return launched();
+}
+
+bool launch_discard(const VolumeArgs& v, const OwnerArgs& o, hipStream_t s) {
+    hipLaunchKernelGGL(k_discard_items, dim3(64), dim3(kThreads), 0, s, v, o);
+    return launched();
+}
+
+bool launch_update_rays(const FrameArgs& f, const VolumeArgs& v, hipStream_t s) {
+    hipLaunchKernelGGL(k_update_rays, dim3(tile_grid(f)), dim3(kThreads), 0, s, f, v);
+    return launched();
+}
+
+bool launch_init(const VolumeArgs& v, unsigned long long table_entries, bool whole_pool, const OwnerArgs* own,
+                 hipStream_t s) {
+    if (own) {
+        hipLaunchKernelGGL(k_zero_words, dim3(grid_for(table_entries)), dim3(kThreads), 0, s, own->rec_count,
+                           table_entries);
+        hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(kThreads), 0, s, reinterpret_cast<unsigned int*>(own->fc),
+                           (unsigned long long)(2 * sizeof(FrameCounters) / 4));
+    }
+    const unsigned long long cap = v.capacity;
+    hipLaunchKernelGGL(k_zero_pool, dim3(grid_for(cap * (kBlockVoxels / 4))), dim3(kThreads), 0, s,
+                       (float4*)v.tsdf, (float4*)v.weight, (float4*)v.r, (float4*)v.g, (float4*)v.b,
+                       (const unsigned long long*)v.counters, cap, whole_pool ? 0 : 1);
+    hipLaunchKernelGGL(k_fill_table, dim3(grid_for(table_entries)), dim3(kThreads), 0, s, (uint4*)v.table,
+                       table_entries);
+    hipLaunchKernelGGL(k_zero_counters, dim3(1), dim3(kThreads), 0, s, v.counters);
+    return launched();
+}
+
+bool launch_export_coords(const VolumeArgs& v, unsigned long long table_entries, unsigned long long n_blocks,
+                          int* coords, hipStream_t s) {
+    hipLaunchKernelGGL(k_export_coords, dim3(grid_for(table_entries)), dim3(kThreads), 0, s, v.table, table_entries,
+                       n_blocks, coords);
+    return launched();
+}
+
+}  // namespace tsdf

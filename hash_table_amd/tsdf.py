@@ -19,15 +19,17 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libtsdf_hip.so")
 
 TSDF_OK, TSDF_EINVAL, TSDF_EALIGN, TSDF_EHIP, TSDF_ESMALL = 0, -1, -2, -3, -4
+TSDF_UPDATE_OWNER, TSDF_UPDATE_RAYS = 0, 1
+UPDATE_MODES = {"owner": TSDF_UPDATE_OWNER, "rays": TSDF_UPDATE_RAYS}
 TSDF_PROBE_BINS = 32
 TSDF_MAX_POOL_BLOCKS = 1 << 30
 TSDF_MAX_TABLE_ENTRIES = 1 << 31
 BLOCK_VOXELS = 512
-MB_COALESCED, MB_RANDOM, MB_SAME_WAVE, MB_BLOCK_ROW = 0, 1, 2, 3
+MB_COALESCED, MB_RANDOM, MB_SAME_WAVE, MB_BLOCK_ROW, MB_COUNTERS = 0, 1, 2, 3, 4
 
 # every symbol the headers declare
 EXPORTS = [
-    "tsdf_table_entries_for", "tsdf_counters_bytes", "tsdf_create", "tsdf_reset", "tsdf_allocate",
+    "tsdf_table_entries_for", "tsdf_counters_bytes", "tsdf_scratch_bytes", "tsdf_create", "tsdf_reset", "tsdf_allocate",
     "tsdf_update", "tsdf_integrate", "tsdf_export_blocks", "tsdf_get_stats", "tsdf_destroy",
     "tsdf_status_str", "tsdf_mb_copy", "tsdf_mb_atomic_add_f32", "tsdf_mb_cas_u64",
 ]
@@ -41,11 +43,12 @@ class TsdfError(RuntimeError):
 
 class tsdf_config(ctypes.Structure):
     _fields_ = [("voxel_size", ctypes.c_float), ("trunc", ctypes.c_float),
-                ("pool_capacity", ctypes.c_int64), ("table_entries", ctypes.c_int64)]
+                ("pool_capacity", ctypes.c_int64), ("table_entries", ctypes.c_int64),
+                ("update_mode", ctypes.c_int32), ("max_frame_pixels", ctypes.c_int64)]
 
 
 class tsdf_buffers(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("table", "tsdf", "weight", "r", "g", "b", "counters")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("table", "tsdf", "weight", "r", "g", "b", "counters", "scratch")]
 
 
 class tsdf_frame(ctypes.Structure):
@@ -58,7 +61,7 @@ class tsdf_frame(ctypes.Structure):
 class tsdf_stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "pool_used", "pool_overflow", "table_full", "update_misses", "out_of_range", "near_skipped",
-        "points_valid", "voxel_updates", "walk_guard", "probe_max")] + [
+        "points_valid", "voxel_updates", "walk_guard", "probe_max", "fallback_blocks")] + [
         ("probe_hist_alloc", ctypes.c_uint64 * TSDF_PROBE_BINS),
         ("probe_hist_update", ctypes.c_uint64 * TSDF_PROBE_BINS)]
 
@@ -79,6 +82,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     sigs = {
         "tsdf_table_entries_for": (I64, [I64]),
         "tsdf_counters_bytes": (SZ, []),
+        "tsdf_scratch_bytes": (SZ, [ctypes.POINTER(tsdf_config)]),
         "tsdf_create": (I32, [ctypes.POINTER(tsdf_config), ctypes.POINTER(tsdf_buffers), P, ctypes.POINTER(P)]),
         "tsdf_reset": (I32, [P, P]),
         "tsdf_allocate": (I32, [P, ctypes.POINTER(tsdf_frame), P]),
@@ -123,6 +127,10 @@ def tsdf_counters_bytes() -> int:
     return int(load().tsdf_counters_bytes())
 
 
+def tsdf_scratch_bytes(config: tsdf_config) -> int:
+    return int(load().tsdf_scratch_bytes(ctypes.byref(config)))
+
+
 def tsdf_status_str(status: int) -> str:
     return load().tsdf_status_str(status).decode()
 
@@ -164,7 +172,7 @@ def tsdf_export_blocks(volume, coords: int, tsdf: int, weight: int, r: int, g: i
 def tsdf_get_stats(volume, stream: int = 0) -> Dict[str, object]:
     s = tsdf_stats()
     _check(load().tsdf_get_stats(volume, ctypes.byref(s), ctypes.c_void_p(stream)), "tsdf_get_stats")
-    out: Dict[str, object] = {n: int(getattr(s, n)) for n, _ in tsdf_stats._fields_[:10]}
+    out: Dict[str, object] = {n: int(getattr(s, n)) for n, _ in tsdf_stats._fields_[:11]}
     out["probe_hist_alloc"] = np.array(s.probe_hist_alloc[:], np.int64)
     out["probe_hist_update"] = np.array(s.probe_hist_update[:], np.int64)
     return out
@@ -220,24 +228,30 @@ class DeviceFrame:
 
 
 class Volume:
-    """A TSDF volume whose table, pool and counters are torch CUDA tensors."""
+    """A TSDF volume whose table, pool, counters and scratch are torch CUDA
+    tensors.  update_mode: "owner" (default) or "rays"."""
 
     def __init__(self, voxel_size: float, trunc: float, pool_capacity: int, table_entries: int = 0,
-                 device="cuda", stream=None):
+                 update_mode: str = "owner", max_frame_pixels: int = 0, device="cuda", stream=None):
         import torch
         entries = table_entries or tsdf_table_entries_for(pool_capacity)
         if entries <= 0:
             raise TsdfError(TSDF_EINVAL, "tsdf_table_entries_for")
         self.voxel_size, self.trunc = voxel_size, trunc
         self.pool_capacity, self.table_entries = int(pool_capacity), int(entries)
+        self.update_mode = update_mode
         self.device = device
+        self._cfg = tsdf_config(voxel_size, trunc, int(pool_capacity), int(table_entries), UPDATE_MODES[update_mode],
+                                int(max_frame_pixels))
         n = int(pool_capacity) * BLOCK_VOXELS
         self.table = torch.empty(int(entries) * 2, dtype=torch.int64, device=device)
         self.pool = {k: torch.empty(n, dtype=torch.float32, device=device) for k in ("tsdf", "weight", "r", "g", "b")}
         self.counters = torch.empty((tsdf_counters_bytes() + 7) // 8, dtype=torch.int64, device=device)
-        self._cfg = tsdf_config(voxel_size, trunc, int(pool_capacity), int(table_entries))
+        scratch = tsdf_scratch_bytes(self._cfg)
+        self.scratch = torch.empty((scratch + 7) // 8, dtype=torch.int64, device=device) if scratch else None
         self._buf = tsdf_buffers(self.table.data_ptr(), *(self.pool[k].data_ptr() for k in
-                                 ("tsdf", "weight", "r", "g", "b")), self.counters.data_ptr())
+                                 ("tsdf", "weight", "r", "g", "b")), self.counters.data_ptr(),
+                                 self.scratch.data_ptr() if scratch else None)
         self.handle = tsdf_create(self._cfg, self._buf, _stream_handle(stream))
 
     def __del__(self):

@@ -61,6 +61,17 @@ typedef enum {
 
 typedef struct tsdf_volume tsdf_volume;     /* opaque host-side handle */
 
+/* How tsdf_update adds a frame's contributions (both give the same sums):
+ *   TSDF_UPDATE_OWNER  each block the frame touched is handed to one
+ *                      workgroup, which replays the band walks that reach it,
+ *                      sums them in LDS and read-modify-writes the block's
+ *                      voxels with plain coalesced loads and stores (blocks
+ *                      split over several workgroups add atomically);
+ *   TSDF_UPDATE_RAYS   one thread per point walks its band, looks each block
+ *                      run up and adds with five f32 atomics per voxel (the
+ *                      paper's section 3 shape). */
+typedef enum { TSDF_UPDATE_OWNER = 0, TSDF_UPDATE_RAYS = 1 } tsdf_update_mode;
+
 typedef struct {
     float voxel_size;       /* metres, finite, > 0 */
     float trunc;            /* truncation distance, metres, finite, > 0 */
@@ -68,17 +79,24 @@ typedef struct {
     int64_t table_entries;  /* 0: tsdf_table_entries_for(pool_capacity); otherwise a power of
                                two >= 2 * pool_capacity (so the table is at most half full)
                                and <= TSDF_MAX_TABLE_ENTRIES */
+    int32_t update_mode;    /* tsdf_update_mode */
+    int64_t max_frame_pixels; /* owner mode: frame size the per-frame record buffers are sized
+                               for (0: 2^20); larger frames still integrate exactly, but
+                               blocks whose records do not fit are rescanned (slower) */
 } tsdf_config;
 
 /* Device memory owned by the caller, all 16-byte aligned. */
 typedef struct {
-    void* table;            /* table_entries * 16 bytes; entry = {uint64 key, uint32 index, uint32 pad} */
+    void* table;            /* table_entries * 16 bytes; entry = {uint64 key, uint32 pool index,
+                               uint32 stamp: last frame whose allocate touched the block} */
     float* tsdf;            /* pool_capacity * 512 floats each: per-voxel sums of the */
     float* weight;          /*   normalised signed distance (sdf / trunc), of the weight, */
     float* r;               /*   and of the colour channels (0..1).  Voxel v of block i is */
     float* g;               /*   element i * 512 + v, v = x + 8 y + 64 z within the block. */
     float* b;
     void* counters;         /* tsdf_counters_bytes() bytes */
+    void* scratch;          /* tsdf_scratch_bytes(config) bytes (the owner update's work
+                               list); may be NULL when that is 0 */
 } tsdf_buffers;
 
 /* One depth frame.  Pointers are device memory. */
@@ -90,24 +108,29 @@ typedef struct {
     int32_t width, height;  /* >= 0; an empty frame is a no-op */
     float fx, fy, cx, cy;   /* pinhole intrinsics, pixels; pixel (u, v) looks along
                                ((u - cx) / fx, (v - cy) / fy, 1) in camera coordinates */
-    float R[9];             /* camera-to-world rotation, row-major */
+    float R[9];             /* camera-to-world rotation, row-major; must be orthonormal to
+                               within 1e-4 (else TSDF_EINVAL) */
     float t[3];             /* camera position in the world, metres */
 } tsdf_frame;
 
-/* Counters accumulated since tsdf_create / tsdf_reset. */
+/* Counters accumulated since tsdf_create / tsdf_reset.  Point and voxel
+ * counts are taken by tsdf_allocate (every call counts its frame). */
 typedef struct {
     int64_t pool_used;       /* blocks holding a pool index (<= pool_capacity) */
     int64_t pool_overflow;   /* distinct keys inserted after the pool was full */
     int64_t table_full;      /* insertions that probed every table slot without room */
-    int64_t update_misses;   /* kept voxel contributions whose block has no pool index */
-    int64_t out_of_range;    /* update-pass points whose band leaves +-2^23 voxels */
-    int64_t near_skipped;    /* update-pass points with 0 < depth <= trunc */
-    int64_t points_valid;    /* update-pass points whose band was walked */
-    int64_t voxel_updates;   /* kept (point, voxel) pairs of the update pass */
+    int64_t update_misses;   /* kept voxel contributions lost: block without a pool index,
+                                or key not inserted because the table was full */
+    int64_t out_of_range;    /* points whose band leaves +-2^23 voxels */
+    int64_t near_skipped;    /* points with 0 < depth <= trunc */
+    int64_t points_valid;    /* points whose band was walked */
+    int64_t voxel_updates;   /* kept (point, voxel) pairs */
     int64_t walk_guard;      /* walks cut at TSDF_MAX_WALK (never expected: always 0) */
     int64_t probe_max;       /* longest probe sequence seen, slots */
+    int64_t fallback_blocks; /* owner update: blocks rescanned pixel by pixel because their
+                                run records did not fit the scratch buffer (slower, exact) */
     uint64_t probe_hist_alloc[TSDF_PROBE_BINS];   /* allocate: slots per table operation */
-    uint64_t probe_hist_update[TSDF_PROBE_BINS];  /* update: slots per lookup */
+    uint64_t probe_hist_update[TSDF_PROBE_BINS];  /* ray-parallel update: slots per lookup */
 } tsdf_stats;
 
 /* Default table size for a pool: the smallest power of two >= 2 * pool_capacity
@@ -116,6 +139,11 @@ int64_t tsdf_table_entries_for(int64_t pool_capacity);
 
 /* Size of the counters buffer. */
 size_t tsdf_counters_bytes(void);
+
+/* Size of the scratch buffer a configuration needs (0 for TSDF_UPDATE_RAYS):
+ * about 52 bytes per table entry plus 80 bytes per frame pixel (run records
+ * and their grouping by block).  0 for a NULL or invalid config. */
+size_t tsdf_scratch_bytes(const tsdf_config* config);
 
 /* Validate the configuration and buffers, then enqueue the initialisation of
  * the volume on `stream`: every table entry empty (all bits set), counters
@@ -130,16 +158,21 @@ tsdf_status tsdf_reset(tsdf_volume* volume, void* stream);
 /* The allocate kernel (paper, section 3): for every point, walk its
  * truncation band; for each kept voxel make sure its block is in the table,
  * inserting it with a single 64-bit compare-exchange of the packed key and
- * taking the next pool index.  The probe has no fixed bound: it stops at the
+ * taking the next pool index.  Block keys are de-duplicated within each
+ * wavefront before probing.  The probe has no fixed bound: it stops at the
  * key, at an empty slot it wins, or after trying every slot (table_full).  A
- * key inserted after the pool is full gets no index (pool_overflow). */
+ * key inserted after the pool is full gets no index (pool_overflow).  In
+ * owner mode it also records, once per block, the blocks this frame touches
+ * for the following tsdf_update. */
 tsdf_status tsdf_allocate(tsdf_volume* volume, const tsdf_frame* frame, void* stream);
 
 /* The update kernel (paper, section 3): the same walk and occlusion test;
- * for each kept voxel look its block up and add, with five float atomic
- * additions, sdf/trunc, 1, R/255, G/255, B/255 to the five pool arrays.
- * Blocks without an index count as update_misses.  Call after tsdf_allocate
- * of the same frame (stream order is the only ordering needed). */
+ * each kept voxel receives sdf/trunc, 1, R/255, G/255, B/255 in the five
+ * pool arrays (sums, not means).  Contributions to blocks without an index
+ * count as update_misses.  Call after tsdf_allocate of the same frame
+ * (stream order is the only ordering needed); in owner mode the call must
+ * directly follow tsdf_allocate of an identical tsdf_frame, else
+ * TSDF_EINVAL. */
 tsdf_status tsdf_update(tsdf_volume* volume, const tsdf_frame* frame, void* stream);
 
 /* tsdf_allocate then tsdf_update of one frame. */

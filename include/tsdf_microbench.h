@@ -27,14 +27,17 @@ enum {
     TSDF_MB_COALESCED = 0,  /* buf[i mod n]: a wave covers 64 consecutive floats */
     TSDF_MB_RANDOM = 1,     /* buf[hash(i) mod n]: every lane its own cache line */
     TSDF_MB_SAME_WAVE = 2,  /* buf[hash(i / 64) mod n]: a whole wave on one address */
-    TSDF_MB_BLOCK_ROW = 3   /* 64 consecutive floats at a random 512-float block and row */
+    TSDF_MB_BLOCK_ROW = 3,  /* 64 consecutive floats at a random 512-float block and row */
+    TSDF_MB_COUNTERS = 4    /* one lane per wave: counter (wave mod n/32), one 128-byte line each,
+                               i.e. n/32 shared counters (contention) */
 };
 
 /* dst[0 .. bytes) = src[0 .. bytes); bytes a multiple of 16, both 16-byte aligned. */
 tsdf_status tsdf_mb_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 /* n_ops no-return atomic additions of 1.0f into buf[0 .. n), n a power of two
- * (>= 512 for TSDF_MB_BLOCK_ROW). */
+ * (>= 512 for TSDF_MB_BLOCK_ROW, >= 32 for TSDF_MB_COUNTERS, where only one
+ * operation in 64 is performed). */
 tsdf_status tsdf_mb_atomic_add_f32(float* buf, size_t n, size_t n_ops, int pattern, uint32_t seed, void* stream);
 
 /* n_ops 64-bit compare-exchanges (expected 0, desired op id + 1) at random

@@ -30,11 +30,11 @@ def sort_blocks(coords: np.ndarray, arrays: Dict[str, np.ndarray]):
 
 
 def gpu_integrate(frames: Iterable, voxel_size, trunc, pool_capacity, table_entries=0, split=False,
-                  per_frame_stats=False):
-    """Integrate on the GPU; returns (volume, stats, coords, arrays[, per-frame stats])."""
+                  per_frame_stats=False, mode="owner"):
+    """Integrate on the GPU; returns (volume, stats, coords, arrays, per-frame stats)."""
     import torch
     from hash_table_amd import tsdf
-    vol = tsdf.Volume(voxel_size, trunc, pool_capacity, table_entries)
+    vol = tsdf.Volume(voxel_size, trunc, pool_capacity, table_entries, update_mode=mode)
     history = []
     for f in frames:
         df = tsdf.DeviceFrame(f)

@@ -38,7 +38,23 @@ def test_table_sizing_rule():
     assert tsdf.tsdf_table_entries_for(1 << 22) == 1 << 23
     assert tsdf.tsdf_table_entries_for(0) == -1
     assert tsdf.tsdf_table_entries_for(tsdf.TSDF_MAX_POOL_BLOCKS + 1) == -1
-    assert tsdf.tsdf_counters_bytes() == 640
+    assert tsdf.tsdf_counters_bytes() == 64 * 640
+
+
+def test_scratch_sizing():
+    def expect(entries, px):
+        seg_part, rec_part = -(-px // 64), -(-4 * px // 64)
+        item_part = max(64, entries // 32)
+        return (2 * 832 + 32 * entries + 16 * 64 * seg_part + 2 * 8 * 64 * rec_part + 4 * 64 * item_part
+                + 12 * entries)
+    owner = tsdf.tsdf_config(0.01, 0.04, 4096, 0, tsdf.TSDF_UPDATE_OWNER, 1000)
+    assert tsdf.tsdf_scratch_bytes(owner) == expect(8192, 1000)
+    default = tsdf.tsdf_config(0.01, 0.04, 4096, 0, tsdf.TSDF_UPDATE_OWNER, 0)
+    assert tsdf.tsdf_scratch_bytes(default) == expect(8192, 1 << 20)
+    rays = tsdf.tsdf_config(0.01, 0.04, 4096, 0, tsdf.TSDF_UPDATE_RAYS)
+    assert tsdf.tsdf_scratch_bytes(rays) == 0
+    bad = tsdf.tsdf_config(0.01, 0.04, 0, 0, tsdf.TSDF_UPDATE_OWNER)
+    assert tsdf.tsdf_scratch_bytes(bad) == 0
 
 
 def test_status_strings():
@@ -47,7 +63,7 @@ def test_status_strings():
 
 
 def _buffers(base=0x10000, step=0x100000):
-    return tsdf.tsdf_buffers(*(base + i * step for i in range(7)))
+    return tsdf.tsdf_buffers(*(base + i * step for i in range(8)))
 
 
 @pytest.mark.parametrize("cfg,code", [
@@ -57,6 +73,8 @@ def _buffers(base=0x10000, step=0x100000):
     ((0.01, 0.04, 4096, 6000), tsdf.TSDF_EINVAL),           # table not a power of two
     ((0.01, 0.04, 4096, 4096), tsdf.TSDF_EINVAL),           # table under twice the pool
     ((0.01, 0.04, 1 << 31, 0), tsdf.TSDF_EINVAL),           # pool too large
+    ((0.01, 0.04, 4096, 0, 7), tsdf.TSDF_EINVAL),           # unknown update mode
+    ((0.01, 0.04, 4096, 0, 0, -5), tsdf.TSDF_EINVAL),       # negative frame size
 ])
 def test_create_rejects_bad_config(cfg, code):
     with pytest.raises(tsdf.TsdfError) as e:
@@ -76,6 +94,11 @@ def test_create_rejects_bad_buffers():
     with pytest.raises(tsdf.TsdfError) as e:
         tsdf.tsdf_create(cfg, b)
     assert e.value.status == tsdf.TSDF_EALIGN
+    b = _buffers()
+    b.scratch = None                                  # the owner update needs its work list
+    with pytest.raises(tsdf.TsdfError) as e:
+        tsdf.tsdf_create(cfg, b)
+    assert e.value.status == tsdf.TSDF_EINVAL
 
 
 def test_null_handle_calls():
