@@ -2,8 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload room640x480]
 
-A step integrates the whole 100-frame, 640 x 480 room sequence (one
-tsdf_allocate and one tsdf_update per frame) into a freshly reset volume;
+A step integrates the whole 100-frame, 640 x 480 room sequence into a
+freshly reset volume, `--batch` frames per call (one allocate launch and one
+update over those frames; the result equals frame-by-frame integration);
 inputs are resident in device memory before timing starts.  Timing is gated
 on parity: the run first checks the volume against the oracle's stored
 counts for the same seeded frames.  Per-kernel durations come from HIP
@@ -135,7 +136,8 @@ def main():
     ap.add_argument("--no-microbench", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="time whole steps only")
     ap.add_argument("--mode", default="owner", choices=["owner", "rays"], help="update organisation")
-    ap.add_argument("--no-variant", action="store_true", help="skip timing the other update mode")
+    ap.add_argument("--batch", type=int, default=10, help="frames per integrate call (1..16)")
+    ap.add_argument("--no-variant", action="store_true", help="skip timing the per-frame variants")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -161,38 +163,42 @@ def main():
     pts = tot["points_valid"]
     vox = tot["voxel_updates"]
 
-    def measure(mode, steps, warmup, use_events):
+    def measure(mode, batch, steps, warmup, use_events):
         """Parity gate, then `steps` timed steps; returns (wall seconds,
-        per-launch allocate and update seconds and frame indices, stats, gate)."""
-        vol = tsdf.Volume(wl.voxel_size, wl.trunc, wl.pool_capacity, wl.table_entries, update_mode=mode)
+        per-call allocate and update seconds, frame lists per call, stats, gate)."""
+        vol = tsdf.Volume(wl.voxel_size, wl.trunc, wl.pool_capacity, wl.table_entries, update_mode=mode,
+                          max_batch_pixels=batch * wl.width * wl.height)
+        calls = [list(range(i, min(i + batch, len(frames)))) for i in range(0, len(frames), batch)]
+        arrays = [tsdf.frame_array([frames[i].desc for i in c]) for c in calls]
         torch.cuda.synchronize()
-        for f in frames:                       # parity gate: one full pass vs the oracle's counts
-            vol.integrate(f)
+        for arr, c in zip(arrays, calls):      # parity gate: one full pass vs the oracle's counts
+            tsdf.tsdf_integrate_batch(vol.handle, arr, sh, n=len(c))
         st = vol.stats()
         gate = {
             "blocks": st["pool_used"] == tot["blocks"],
             "voxel_updates": st["voxel_updates"] == tot["voxel_updates"],
             "points_valid": st["points_valid"] == tot["points_valid"],
             "no_loss": st["pool_overflow"] == st["table_full"] == st["update_misses"] == st["walk_guard"] == 0,
+            "no_rescans": st["fallback_blocks"] == 0,
         }
-        log(f"[{mode}] parity gate", gate)
+        log(f"[{mode} batch {batch}] parity gate", gate)
         if not all(gate.values()):
-            raise SystemExit(f"parity gate failed ({mode}): {gate}")
+            raise SystemExit(f"parity gate failed ({mode}, batch {batch}): {gate}")
         ev = []
 
         def step(record):
             vol.reset()
-            for i, f in enumerate(frames):
+            for arr, c in zip(arrays, calls):
                 if record:
                     e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
                     e[0].record(stream)
-                    tsdf.tsdf_allocate(vol.handle, f.desc, sh)
+                    tsdf.tsdf_allocate_batch(vol.handle, arr, sh, n=len(c))
                     e[1].record(stream)
-                    tsdf.tsdf_update(vol.handle, f.desc, sh)
+                    tsdf.tsdf_update_batch(vol.handle, arr, sh, n=len(c))
                     e[2].record(stream)
-                    ev.append((i, e))
+                    ev.append((c, e))
                 else:
-                    tsdf.tsdf_integrate(vol.handle, f.desc, sh)
+                    tsdf.tsdf_integrate_batch(vol.handle, arr, sh, n=len(c))
 
         for _ in range(warmup):
             step(False)
@@ -205,26 +211,31 @@ def main():
         st = vol.stats()
         t_alloc = [e[0].elapsed_time(e[1]) * 1e-3 for _, e in ev]
         t_upd = [e[1].elapsed_time(e[2]) * 1e-3 for _, e in ev]
-        idx = [i for i, _ in ev]
+        idx = [c for c, _ in ev]
         del vol
         torch.cuda.empty_cache()
         return wall, t_alloc, t_upd, idx, st, gate
 
     def kernel_report(t_alloc, t_upd, idx, steps):
-        b_alloc = [frame_bytes(counts["frames"][i])[0] for i in idx]
-        b_upd = [frame_bytes(counts["frames"][i])[1] for i in idx]
+        """Per-call durations -> throughput, algorithmic GB/s, per-frame latency."""
+        b_alloc = [sum(frame_bytes(counts["frames"][i])[0] for i in c) for c in idx]
+        b_upd = [sum(frame_bytes(counts["frames"][i])[1] for i in c) for c in idx]
+        per_frame_a = [t / len(c) for t, c in zip(t_alloc, idx)]
+        per_frame_u = [t / len(c) for t, c in zip(t_upd, idx)]
         ta, tu = sum(t_alloc), sum(t_upd)
         per = {
             "allocate": {"points_per_s": pts * steps / ta, "voxel_updates_per_s": vox * steps / ta,
-                         "GBps": sum(b_alloc) / ta / 1e9, "us_median": 1e6 * statistics.median(t_alloc),
-                         "us_p95": 1e6 * pct(t_alloc, 95), "us_p99": 1e6 * pct(t_alloc, 99)},
+                         "GBps": sum(b_alloc) / ta / 1e9, "us_per_frame_median": 1e6 * statistics.median(per_frame_a),
+                         "us_per_frame_p95": 1e6 * pct(per_frame_a, 95),
+                         "us_per_frame_p99": 1e6 * pct(per_frame_a, 99)},
             "update": {"points_per_s": pts * steps / tu, "voxel_updates_per_s": vox * steps / tu,
-                       "GBps": sum(b_upd) / tu / 1e9, "us_median": 1e6 * statistics.median(t_upd),
-                       "us_p95": 1e6 * pct(t_upd, 95), "us_p99": 1e6 * pct(t_upd, 99)},
+                       "GBps": sum(b_upd) / tu / 1e9, "us_per_frame_median": 1e6 * statistics.median(per_frame_u),
+                       "us_per_frame_p95": 1e6 * pct(per_frame_u, 95),
+                       "us_per_frame_p99": 1e6 * pct(per_frame_u, 99)},
             "integrate_kernels": {"points_per_s": pts * steps / (ta + tu),
                                   "voxel_updates_per_s": vox * steps / (ta + tu),
                                   "GBps": (sum(b_alloc) + sum(b_upd)) / (ta + tu) / 1e9},
-            "launches": len(t_alloc),
+            "calls": len(t_alloc),
         }
         for k in ("allocate", "update", "integrate_kernels"):
             per[k]["hbm_frac"] = per[k]["GBps"] / HBM_PEAK_GBS
@@ -232,7 +243,7 @@ def main():
         return per, ta, tu, sum(b_alloc), sum(b_upd)
 
     use_events = not args.no_events
-    wall, t_alloc, t_upd, idx, st, gate = measure(args.mode, args.steps, args.warmup, use_events)
+    wall, t_alloc, t_upd, idx, st, gate = measure(args.mode, args.batch, args.steps, args.warmup, use_events)
 
     n_frames = wl.n_frames
     ms_per_step = wall / args.steps * 1e3
@@ -252,15 +263,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "frames_per_step": n_frames, "width": wl.width, "height": wl.height,
                    "voxel_size": wl.voxel_size, "trunc": wl.trunc, "pool_capacity": wl.pool_capacity,
-                   "table_entries": wl.table_entries, "update_mode": args.mode, "points_per_step": pts,
-                   "voxel_updates_per_step": vox,
-                   "step": "reset used pool + table, then allocate+update for every frame"},
+                   "table_entries": wl.table_entries, "update_mode": args.mode, "frames_per_call": args.batch,
+                   "points_per_step": pts, "voxel_updates_per_step": vox,
+                   "step": "reset used pool + table, then allocate+update of all frames, batch frames per call"},
         "parity_gate": gate,
     }
     if use_events:
         per, ta, tu, ba, bu = kernel_report(t_alloc, t_upd, idx, args.steps)
         out["kernels"] = per
-        upd_name = "k_update_owner" if args.mode == "owner" else "k_update_rays"
+        # the update call is k_place_items + k_scatter_records + k_update_owner in
+        # owner mode; the roofline figure is for the whole call (the trace
+        # summary under profiles/ splits it)
+        upd_name = "update call (k_place_items+k_scatter_records+k_update_owner)" if args.mode == "owner" \
+            else "k_update_rays"
         dom, t_dom, b_dom = (upd_name, tu, bu) if tu >= ta else ("k_allocate", ta, ba)
         achieved = b_dom / t_dom / 1e9
         out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
@@ -269,12 +284,16 @@ def main():
                            "bytes_per_launch": round(b_dom / len(t_upd)),
                            "avg_launch_us": round(t_dom / len(t_upd) * 1e6, 3)}
     if not args.no_variant:
-        other = "rays" if args.mode == "owner" else "owner"
-        w2, a2, u2, i2, _, g2 = measure(other, max(1, args.steps // 2), 1, True)
-        per2, *_ = kernel_report(a2, u2, i2, max(1, args.steps // 2))
-        out["variants"] = {other: {"points_per_s": round(pts * max(1, args.steps // 2) / w2, 1),
-                                   "ms_per_step": round(w2 / max(1, args.steps // 2) * 1e3, 4),
-                                   "kernels": per2, "parity_gate": g2}}
+        out["variants"] = {}
+        for mode, batch in (("owner", 1), ("rays", 1)):
+            if (mode, batch) == (args.mode, args.batch):
+                continue
+            vs = max(1, args.steps // 2)
+            w2, a2, u2, i2, _, g2 = measure(mode, batch, vs, 1, True)
+            per2, *_ = kernel_report(a2, u2, i2, vs)
+            out["variants"][f"{mode}_batch{batch}"] = {"points_per_s": round(pts * vs / w2, 1),
+                                                       "ms_per_step": round(w2 / vs * 1e3, 4),
+                                                       "kernels": per2, "parity_gate": g2}
     out["loss_counters"] = {k: st[k] for k in ("pool_overflow", "table_full", "update_misses", "walk_guard")}
     if not args.no_microbench:
         log("microbenchmarks")

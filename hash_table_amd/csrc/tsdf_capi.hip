@@ -17,7 +17,7 @@ using namespace tsdf;
 namespace {
 
 constexpr int kOwnerGrid = 4096;                     // single-wavefront workgroups of the owner update
-constexpr int64_t kDefaultFramePixels = 1 << 20;    // owner-mode record buffers, per frame
+constexpr int64_t kDefaultFramePixels = 1 << 20;    // owner-mode record buffers, per call
 constexpr int64_t kRunsPerPixel = 4;                // record capacity per pixel (a room frame needs ~2.7)
 
 // Owner-mode scratch layout: per-frame counters, per-table-entry arrays,
@@ -64,7 +64,8 @@ struct tsdf_volume {
     unsigned int mask;
     unsigned int serial;        // allocate calls so far (frame stamp source)
     bool pending;               // an owner-mode allocate whose update has not run yet
-    tsdf_frame last;            // the frame of that allocate
+    int32_t n_last;             // the frames of that allocate
+    tsdf_frame last[TSDF_MAX_BATCH];
 };
 
 namespace {
@@ -104,7 +105,7 @@ OwnerArgs owner_args(const tsdf_volume* h, unsigned int serial) {
     o.parity = serial & 1u;
     o.stamp = serial;
     if (!o.build_items) return o;
-    const ScratchLayout L = scratch_layout(h->cfg.table_entries, h->cfg.max_frame_pixels);
+    const ScratchLayout L = scratch_layout(h->cfg.table_entries, h->cfg.max_batch_pixels);
     char* base = static_cast<char*>(h->buf.scratch);
     o.fc = reinterpret_cast<FrameCounters*>(base + L.fc);
     o.items = reinterpret_cast<unsigned int*>(base + L.items);
@@ -184,25 +185,35 @@ tsdf_status frame_args(const tsdf_volume* h, const tsdf_frame* fr, bool need_rgb
 
 bool same_frame(const tsdf_frame& a, const tsdf_frame& b) { return std::memcmp(&a, &b, sizeof(a)) == 0; }
 
-tsdf_status do_allocate(tsdf_volume* h, const tsdf_frame* frame, const FrameArgs& fa, hipStream_t s) {
-    if (h->pending && !launch_discard(volume_args(h), owner_args(h, h->serial), s)) return TSDF_EHIP;
-    h->pending = false;
-    const unsigned int serial = h->serial + 1 == 0xFFFFFFFFu ? 1u : h->serial + 1;
-    if (!launch_allocate(fa, volume_args(h), owner_args(h, serial), s)) return TSDF_EHIP;
-    h->serial = serial;
-    if (h->cfg.update_mode == TSDF_UPDATE_OWNER) {
-        h->pending = true;
-        h->last = *frame;
+// Validate n frames and gather the non-empty ones into a batch.
+tsdf_status batch_args(const tsdf_volume* h, const tsdf_frame* frames, int32_t n, bool need_rgb, BatchArgs* b) {
+    if (!frames || n < 0 || n > TSDF_MAX_BATCH) return TSDF_EINVAL;
+    b->n = 0;
+    b->tile_grid = 8;
+    for (int32_t i = 0; i < n; ++i) {
+        FrameArgs fa;
+        bool empty = false;
+        const tsdf_status st = frame_args(h, frames + i, need_rgb, &fa, &empty);
+        if (st != TSDF_OK) return st;
+        if (empty) continue;
+        b->f[b->n++] = fa;
+        b->tile_grid = std::max(b->tile_grid, tile_grid(fa));
     }
     return TSDF_OK;
 }
 
-tsdf_status do_update(tsdf_volume* h, const tsdf_frame* frame, const FrameArgs& fa, hipStream_t s) {
-    if (h->cfg.update_mode == TSDF_UPDATE_RAYS) return launch_update_rays(fa, volume_args(h), s) ? TSDF_OK : TSDF_EHIP;
-    if (!h->pending || !same_frame(h->last, *frame)) return TSDF_EINVAL;
-    if (!launch_update_owner(fa, volume_args(h), owner_args(h, h->serial), kOwnerGrid, s)) return TSDF_EHIP;
+tsdf_status do_allocate(tsdf_volume* h, const BatchArgs& b, hipStream_t s) {
+    if (h->pending && !launch_discard(volume_args(h), owner_args(h, h->serial), s)) return TSDF_EHIP;
     h->pending = false;
+    const unsigned int serial = h->serial + 1 == 0xFFFFFFFFu ? 1u : h->serial + 1;
+    if (!launch_allocate(b, volume_args(h), owner_args(h, serial), s)) return TSDF_EHIP;
+    h->serial = serial;
     return TSDF_OK;
+}
+
+tsdf_status do_update(tsdf_volume* h, const BatchArgs& b, hipStream_t s) {
+    if (h->cfg.update_mode == TSDF_UPDATE_RAYS) return launch_update_rays(b, volume_args(h), s) ? TSDF_OK : TSDF_EHIP;
+    return launch_update_owner(b, volume_args(h), owner_args(h, h->serial), kOwnerGrid, s) ? TSDF_OK : TSDF_EHIP;
 }
 
 }  // namespace
@@ -221,8 +232,8 @@ size_t tsdf_counters_bytes(void) { return sizeof(unsigned long long) * kReplicas
 size_t tsdf_scratch_bytes(const tsdf_config* config) {
     if (!config || config->update_mode != TSDF_UPDATE_OWNER) return 0;
     const int64_t entries = resolved_entries(config);
-    if (entries <= 0 || config->max_frame_pixels < 0 || config->max_frame_pixels > ((int64_t)1 << 28)) return 0;
-    return scratch_layout(entries, config->max_frame_pixels).bytes;
+    if (entries <= 0 || config->max_batch_pixels < 0 || config->max_batch_pixels > ((int64_t)1 << 28)) return 0;
+    return scratch_layout(entries, config->max_batch_pixels).bytes;
 }
 
 tsdf_status tsdf_create(const tsdf_config* config, const tsdf_buffers* buffers, void* stream, tsdf_volume** out) {
@@ -231,7 +242,7 @@ tsdf_status tsdf_create(const tsdf_config* config, const tsdf_buffers* buffers, 
     if (!finite_pos(config->voxel_size) || !finite_pos(config->trunc)) return TSDF_EINVAL;
     if (config->pool_capacity < 1 || config->pool_capacity > TSDF_MAX_POOL_BLOCKS) return TSDF_EINVAL;
     if (config->update_mode != TSDF_UPDATE_OWNER && config->update_mode != TSDF_UPDATE_RAYS) return TSDF_EINVAL;
-    if (config->max_frame_pixels < 0 || config->max_frame_pixels > ((int64_t)1 << 28)) return TSDF_EINVAL;
+    if (config->max_batch_pixels < 0 || config->max_batch_pixels > ((int64_t)1 << 28)) return TSDF_EINVAL;
     const int64_t entries = resolved_entries(config);
     if (!is_pow2(entries) || entries < 2 * config->pool_capacity || entries > TSDF_MAX_TABLE_ENTRIES)
         return TSDF_EINVAL;
@@ -263,34 +274,55 @@ tsdf_status tsdf_reset(tsdf_volume* h, void* stream) {
     return init_volume(h, false, static_cast<hipStream_t>(stream)) ? TSDF_OK : TSDF_EHIP;
 }
 
-tsdf_status tsdf_allocate(tsdf_volume* h, const tsdf_frame* frame, void* stream) {
+tsdf_status tsdf_allocate_batch(tsdf_volume* h, const tsdf_frame* frames, int32_t n_frames, void* stream) {
     if (!h) return TSDF_EINVAL;
-    FrameArgs fa;
-    bool empty = false;
-    const tsdf_status st = frame_args(h, frame, false, &fa, &empty);
-    if (st != TSDF_OK || empty) return st;
-    return do_allocate(h, frame, fa, static_cast<hipStream_t>(stream));
+    BatchArgs b;
+    const tsdf_status st = batch_args(h, frames, n_frames, false, &b);
+    if (st != TSDF_OK || b.n == 0) return st;
+    const tsdf_status a = do_allocate(h, b, static_cast<hipStream_t>(stream));
+    if (a == TSDF_OK && h->cfg.update_mode == TSDF_UPDATE_OWNER) {
+        h->pending = true;
+        h->n_last = n_frames;
+        std::memcpy(h->last, frames, sizeof(tsdf_frame) * (size_t)n_frames);
+    }
+    return a;
+}
+
+tsdf_status tsdf_update_batch(tsdf_volume* h, const tsdf_frame* frames, int32_t n_frames, void* stream) {
+    if (!h) return TSDF_EINVAL;
+    BatchArgs b;
+    const tsdf_status st = batch_args(h, frames, n_frames, true, &b);
+    if (st != TSDF_OK || b.n == 0) return st;
+    if (h->cfg.update_mode == TSDF_UPDATE_OWNER) {
+        if (!h->pending || h->n_last != n_frames) return TSDF_EINVAL;
+        for (int32_t i = 0; i < n_frames; ++i)
+            if (!same_frame(h->last[i], frames[i])) return TSDF_EINVAL;
+        h->pending = false;
+    }
+    return do_update(h, b, static_cast<hipStream_t>(stream));
+}
+
+tsdf_status tsdf_allocate(tsdf_volume* h, const tsdf_frame* frame, void* stream) {
+    return tsdf_allocate_batch(h, frame, 1, stream);
 }
 
 tsdf_status tsdf_update(tsdf_volume* h, const tsdf_frame* frame, void* stream) {
+    return tsdf_update_batch(h, frame, 1, stream);
+}
+
+tsdf_status tsdf_integrate_batch(tsdf_volume* h, const tsdf_frame* frames, int32_t n_frames, void* stream) {
     if (!h) return TSDF_EINVAL;
-    FrameArgs fa;
-    bool empty = false;
-    const tsdf_status st = frame_args(h, frame, true, &fa, &empty);
-    if (st != TSDF_OK || empty) return st;
-    return do_update(h, frame, fa, static_cast<hipStream_t>(stream));
+    BatchArgs b;
+    const tsdf_status st = batch_args(h, frames, n_frames, true, &b);
+    if (st != TSDF_OK || b.n == 0) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const tsdf_status a = do_allocate(h, b, s);
+    if (a != TSDF_OK) return a;
+    return do_update(h, b, s);
 }
 
 tsdf_status tsdf_integrate(tsdf_volume* h, const tsdf_frame* frame, void* stream) {
-    if (!h) return TSDF_EINVAL;
-    FrameArgs fa;
-    bool empty = false;
-    const tsdf_status st = frame_args(h, frame, true, &fa, &empty);
-    if (st != TSDF_OK || empty) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const tsdf_status a = do_allocate(h, frame, fa, s);
-    if (a != TSDF_OK) return a;
-    return do_update(h, frame, fa, s);
+    return tsdf_integrate_batch(h, frame, 1, stream);
 }
 
 tsdf_status tsdf_get_stats(tsdf_volume* h, tsdf_stats* out, void* stream) {

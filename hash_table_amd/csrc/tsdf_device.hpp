@@ -68,12 +68,16 @@ constexpr float kNearPlane = 1e-4f;                 // block corners closer than
 // One run of a walk inside one block: the pixel, the first cell the walk
 // visits in the block (voxel index), the cells it visits there and how many
 // of them pass the occlusion test.
-__device__ __forceinline__ unsigned int pack_run(int entry, int cells, int kept) {
-    return (unsigned int)entry | ((unsigned int)cells << 9) | ((unsigned int)kept << 15);
+// (A line crosses at most 22 cells of an 8^3 block, so 6 bits hold the
+// counts; 4 bits hold the frame of a batch.)
+__device__ __forceinline__ unsigned int pack_run(int entry, int cells, int kept, int frame) {
+    return (unsigned int)entry | ((unsigned int)cells << 9) | ((unsigned int)kept << 15) |
+           ((unsigned int)frame << 21);
 }
 __device__ __forceinline__ int run_entry(unsigned int info) { return (int)(info & 511u); }
 __device__ __forceinline__ int run_cells(unsigned int info) { return (int)((info >> 9) & 63u); }
 __device__ __forceinline__ int run_kept(unsigned int info) { return (int)((info >> 15) & 63u); }
+__device__ __forceinline__ int run_frame(unsigned int info) { return (int)((info >> 21) & 15u); }
 
 // A wavefront's runs through one block, as recorded by allocate.
 struct __align__(16) Segment {
@@ -135,6 +139,17 @@ struct FrameArgs {
     int tiles_x;         // 16 x 16 pixel tiles per row
     int n_tiles;
     int tiles_per_xcd;   // ceil(n_tiles / 8): workgroup -> tile remap
+};
+
+// The frames of one call (tsdf_integrate_batch, or one frame).  Frame i
+// uses workgroups [i * tile_grid, (i + 1) * tile_grid) of the per-pixel
+// kernels; tile_grid is a multiple of 8, so the workgroup -> XCD mapping is
+// the same for every frame.
+constexpr int kMaxBatch = 16;
+struct BatchArgs {
+    FrameArgs f[kMaxBatch];
+    int n;
+    int tile_grid;
 };
 
 struct VolumeArgs {

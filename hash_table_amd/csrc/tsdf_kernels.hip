@@ -41,9 +41,10 @@ constexpr int kListCap = 256;     // block runs a wavefront buffers before de-du
 constexpr int kSetCap = 256;      // per-wavefront LDS hash set (power of two, >= kListCap)
 constexpr float kInv255 = 1.0f / 255.0f;
 
-__device__ __forceinline__ bool workgroup_tile(const FrameArgs& f, int& tile_u0, int& tile_v0) {
-    const int wg = blockIdx.x;
-    const int tile = (wg % kXcds) * f.tiles_per_xcd + wg / kXcds;
+__device__ __forceinline__ bool workgroup_tile(const FrameArgs& f, int wg, int& tile_u0, int& tile_v0) {
+    const int rank = wg / kXcds;                   // position within the XCD's run of tiles
+    if (rank >= f.tiles_per_xcd) return false;     // a smaller frame of the batch
+    const int tile = (wg % kXcds) * f.tiles_per_xcd + rank;
     if (tile >= f.n_tiles) return false;
     tile_u0 = (tile % f.tiles_x) * kTile;
     tile_v0 = (tile / f.tiles_x) * kTile;
@@ -228,8 +229,10 @@ __device__ void flush_runs(AllocLds& L, int wave, int lane, int n, const VolumeA
     wave_lds_fence();
 }
 
-__global__ __launch_bounds__(kThreads) void k_allocate(FrameArgs f, VolumeArgs vol, OwnerArgs own) {
+__global__ __launch_bounds__(kThreads) void k_allocate(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ AllocLds L;
+    const int fi = blockIdx.x / B.tile_grid;                 // frame of this workgroup
+    const FrameArgs& f = B.f[fi];
     if (blockIdx.x == 0 && own.build_items) {
         // clear the next frame's counters (their last users finished before
         // this kernel started)
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void k_allocate(FrameArgs f, VolumeArgs v
         for (int i = threadIdx.x; i < (int)(sizeof(FrameCounters) / 8); i += kThreads) next[i] = 0;
     }
     int tu, tv;
-    if (!workgroup_tile(f, tu, tv)) return;
+    if (!workgroup_tile(f, blockIdx.x - fi * B.tile_grid, tu, tv)) return;
     if (threadIdx.x < kProbeBins) L.hist[threadIdx.x] = 0;
     if (threadIdx.x < 6) L.cnt[threadIdx.x] = 0;
     if (threadIdx.x == 0) L.pmax = 0;
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void k_allocate(FrameArgs f, VolumeArgs v
             if (key != cur) {                 // a new block: close the previous run
                 emit = kept > 0;
                 ekey = cur;
-                einfo = pack_run(entry, cells, kept);
+                einfo = pack_run(entry, cells, kept, fi);
                 cur = key;
                 entry = voxel_in_block(w.k0, w.k1, w.k2);
                 cells = 0;
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void k_allocate(FrameArgs f, VolumeArgs v
         } else if (!any_alive && cur != kEmptyKey) {   // after the last step: the last run
             emit = kept > 0;
             ekey = cur;
-            einfo = pack_run(entry, cells, kept);
+            einfo = pack_run(entry, cells, kept, fi);
             cur = kEmptyKey;
         }
         const unsigned long long m = __ballot(emit);
@@ -496,44 +499,51 @@ __device__ __forceinline__ void colour_words(const FrameArgs& f, size_t pix, uns
     c_gb = (unsigned long long)f.rgb[3 * pix + 1] | ((unsigned long long)f.rgb[3 * pix + 2] << 32);
 }
 
-// rescan: every pixel of the block's rectangle replays its walk through the block
-__device__ void rescan_block(UpdateLds& L, const FrameArgs& f, const VolumeArgs& vol, int bx, int by, int bz,
-                             unsigned int& n_kept) {
+// rescan: in every frame of the batch, every pixel of the block's rectangle
+// replays its walk through the block
+__device__ void rescan_block(UpdateLds& L, const FrameArgs* frames, int n_frames, const VolumeArgs& vol, int bx,
+                             int by, int bz, unsigned int& n_kept) {
     const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
-    const PixelRect r = block_rect(bx, by, bz, f, vol.vs);
-    if (r.u0 > r.u1 || r.v0 > r.v1) return;
-    const int rw = r.u1 - r.u0 + 1;
-    const long long area = (long long)rw * (r.v1 - r.v0 + 1);
-    const float zlo = r.zmin - vol.vs, zhi = r.zmax + vol.vs;
-    for (long long p = threadIdx.x; p < area; p += blockDim.x) {
-        const int u = r.u0 + (int)(p % rw);
-        const int v = r.v0 + (int)(p / rw);
-        const size_t pix = (size_t)v * f.width + u;
-        const float d = f.depth[pix];
-        if (!(d - vol.trunc <= zhi && d + vol.trunc >= zlo)) continue;      // band cannot reach the block
-        BandWalk w;
-        if (setup_walk(w, d, u, v, f, vol.trunc, vol.inv_vs) != kValid) continue;
-        if (w.span_hi0 < lo0 - 1 || w.span_lo0 > lo0 + 8 || w.span_hi1 < lo1 - 1 || w.span_lo1 > lo1 + 8 ||
-            w.span_hi2 < lo2 - 1 || w.span_lo2 > lo2 + 8)
-            continue;                                                        // cell span misses the block
-        unsigned long long c_wr, c_gb;
-        colour_words(f, pix, c_wr, c_gb);
-        bool inside = false;
-        for (int visits = 0;;) {
-            if ((unsigned)(w.k0 - lo0) < 8u && (unsigned)(w.k1 - lo1) < 8u && (unsigned)(w.k2 - lo2) < 8u) {
-                inside = true;
-                accumulate(L, w, f, vol, c_wr, c_gb, n_kept);
-            } else if (inside) {
-                break;                                                       // a walk crosses a block once
+    for (int fi = 0; fi < n_frames; ++fi) {
+        const FrameArgs& f = frames[fi];
+        const PixelRect r = block_rect(bx, by, bz, f, vol.vs);
+        if (r.u0 > r.u1 || r.v0 > r.v1) continue;
+        const int rw = r.u1 - r.u0 + 1;
+        const long long area = (long long)rw * (r.v1 - r.v0 + 1);
+        const float zlo = r.zmin - vol.vs, zhi = r.zmax + vol.vs;
+        for (long long p = threadIdx.x; p < area; p += blockDim.x) {
+            const int u = r.u0 + (int)(p % rw);
+            const int v = r.v0 + (int)(p / rw);
+            const size_t pix = (size_t)v * f.width + u;
+            const float d = f.depth[pix];
+            if (!(d - vol.trunc <= zhi && d + vol.trunc >= zlo)) continue;      // band cannot reach the block
+            BandWalk w;
+            if (setup_walk(w, d, u, v, f, vol.trunc, vol.inv_vs) != kValid) continue;
+            if (w.span_hi0 < lo0 - 1 || w.span_lo0 > lo0 + 8 || w.span_hi1 < lo1 - 1 || w.span_lo1 > lo1 + 8 ||
+                w.span_hi2 < lo2 - 1 || w.span_lo2 > lo2 + 8)
+                continue;                                                        // cell span misses the block
+            unsigned long long c_wr, c_gb;
+            colour_words(f, pix, c_wr, c_gb);
+            bool inside = false;
+            for (int visits = 0;;) {
+                if ((unsigned)(w.k0 - lo0) < 8u && (unsigned)(w.k1 - lo1) < 8u && (unsigned)(w.k2 - lo2) < 8u) {
+                    inside = true;
+                    accumulate(L, w, f, vol, c_wr, c_gb, n_kept);
+                } else if (inside) {
+                    break;                                                   // a walk crosses a block once
+                }
+                if (++visits >= f.max_visits || !advance(w)) break;
             }
-            if (++visits >= f.max_visits || !advance(w)) break;
         }
     }
 }
 
-__global__ __launch_bounds__(kOwnerThreads) void k_update_owner(FrameArgs f, VolumeArgs vol, OwnerArgs own) {
+__global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ UpdateLds L;
+    __shared__ FrameArgs s_frames[kMaxBatch];               // per-record frame lookups from LDS
     const int tid = threadIdx.x;
+    if (tid < B.n) s_frames[tid] = B.f[tid];
+    __syncthreads();
     const unsigned int n_items = own.fc[own.parity].items_total;
     unsigned int misses = 0, fallbacks = 0;
 
@@ -549,12 +559,13 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(FrameArgs f, Vol
         __syncthreads();
         unsigned int n_kept = 0;
         if (d.rec_count & kSegOverflow) {
-            rescan_block(L, f, vol, bx, by, bz, n_kept);
+            rescan_block(L, s_frames, B.n, vol, bx, by, bz, n_kept);
             fallbacks += tid == 0;
         } else {
             const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
             for (unsigned int r = tid; r < d.rec_count; r += kOwnerThreads) {
                 const uint2 rec = own.sorted[d.rec_first + r];
+                const FrameArgs& f = s_frames[run_frame(rec.y)];
                 const unsigned int pix = rec.x;
                 const int u = (int)(pix % (unsigned int)f.width), v = (int)(pix / (unsigned int)f.width);
                 BandWalk w;
@@ -602,12 +613,14 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(FrameArgs f, Vol
 // ray-parallel update: walk, test, look the block up once per block run of
 // the ray, add with five no-return f32 atomics into the SoA pool.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void k_update_rays(FrameArgs f, VolumeArgs vol) {
+__global__ __launch_bounds__(kThreads) void k_update_rays(BatchArgs B, VolumeArgs vol) {
+    const int fi = blockIdx.x / B.tile_grid;
+    const FrameArgs& f = B.f[fi];
     __shared__ unsigned int s_hist[kProbeBins];
     __shared__ unsigned int s_pmax;
     __shared__ unsigned int s_miss;
     int tu, tv;
-    if (!workgroup_tile(f, tu, tv)) return;
+    if (!workgroup_tile(f, blockIdx.x - fi * B.tile_grid, tu, tv)) return;
     if (threadIdx.x < kProbeBins) s_hist[threadIdx.x] = 0;
     if (threadIdx.x == 0) {
         s_pmax = 0;
@@ -738,15 +751,15 @@ bool launched() { return hipGetLastError() == hipSuccess; }
 // ---------------------------------------------------------------------------
 int tile_grid(const FrameArgs& f) { return f.tiles_per_xcd * kXcds; }
 
-bool launch_allocate(const FrameArgs& f, const VolumeArgs& v, const OwnerArgs& o, hipStream_t s) {
-    hipLaunchKernelGGL(k_allocate, dim3(tile_grid(f)), dim3(kThreads), 0, s, f, v, o);
+bool launch_allocate(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, hipStream_t s) {
+    hipLaunchKernelGGL(k_allocate, dim3(b.n * b.tile_grid), dim3(kThreads), 0, s, b, v, o);
     return launched();
 }
 
-bool launch_update_owner(const FrameArgs& f, const VolumeArgs& v, const OwnerArgs& o, int grid, hipStream_t s) {
+bool launch_update_owner(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, int grid, hipStream_t s) {
     hipLaunchKernelGGL(k_place_items, dim3(256), dim3(kThreads), 0, s, v, o);
     hipLaunchKernelGGL(k_scatter_records, dim3(2048), dim3(kThreads), 0, s, v, o);
-    hipLaunchKernelGGL(k_update_owner, dim3(grid), dim3(kOwnerThreads), 0, s, f, v, o);
+    hipLaunchKernelGGL(k_update_owner, dim3(grid), dim3(kOwnerThreads), 0, s, b, v, o);
     return launched();
 }
 
@@ -755,8 +768,8 @@ bool launch_discard(const VolumeArgs& v, const OwnerArgs& o, hipStream_t s) {
     return launched();
 }
 
-bool launch_update_rays(const FrameArgs& f, const VolumeArgs& v, hipStream_t s) {
-    hipLaunchKernelGGL(k_update_rays, dim3(tile_grid(f)), dim3(kThreads), 0, s, f, v);
+bool launch_update_rays(const BatchArgs& b, const VolumeArgs& v, hipStream_t s) {
+    hipLaunchKernelGGL(k_update_rays, dim3(b.n * b.tile_grid), dim3(kThreads), 0, s, b, v);
     return launched();
 }
 

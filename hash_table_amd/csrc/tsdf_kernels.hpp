@@ -9,15 +9,15 @@
 
 namespace tsdf {
 
-// workgroups of the per-point kernels for a frame
+// workgroups of the per-point kernels for a frame (a multiple of 8)
 int tile_grid(const FrameArgs& f);
 
-bool launch_allocate(const FrameArgs& f, const VolumeArgs& v, const OwnerArgs& o, hipStream_t s);
-// group the frame's run records by block, then update every touched block
-bool launch_update_owner(const FrameArgs& f, const VolumeArgs& v, const OwnerArgs& o, int grid, hipStream_t s);
+bool launch_allocate(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, hipStream_t s);
+// group the batch's run records by block, then update every touched block
+bool launch_update_owner(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, int grid, hipStream_t s);
 // forget an allocate's records (no update followed it)
 bool launch_discard(const VolumeArgs& v, const OwnerArgs& o, hipStream_t s);
-bool launch_update_rays(const FrameArgs& f, const VolumeArgs& v, hipStream_t s);
+bool launch_update_rays(const BatchArgs& b, const VolumeArgs& v, hipStream_t s);
 // zero the pool (whole, or the used part), empty the table, clear the counters
 // and (owner mode) the per-slot run counts and per-frame counters
 bool launch_init(const VolumeArgs& v, unsigned long long table_entries, bool whole_pool, const OwnerArgs* own,

@@ -22,6 +22,7 @@ TSDF_OK, TSDF_EINVAL, TSDF_EALIGN, TSDF_EHIP, TSDF_ESMALL = 0, -1, -2, -3, -4
 TSDF_UPDATE_OWNER, TSDF_UPDATE_RAYS = 0, 1
 UPDATE_MODES = {"owner": TSDF_UPDATE_OWNER, "rays": TSDF_UPDATE_RAYS}
 TSDF_PROBE_BINS = 32
+TSDF_MAX_BATCH = 16
 TSDF_MAX_POOL_BLOCKS = 1 << 30
 TSDF_MAX_TABLE_ENTRIES = 1 << 31
 BLOCK_VOXELS = 512
@@ -30,7 +31,8 @@ MB_COALESCED, MB_RANDOM, MB_SAME_WAVE, MB_BLOCK_ROW, MB_COUNTERS = 0, 1, 2, 3, 4
 # every symbol the headers declare
 EXPORTS = [
     "tsdf_table_entries_for", "tsdf_counters_bytes", "tsdf_scratch_bytes", "tsdf_create", "tsdf_reset", "tsdf_allocate",
-    "tsdf_update", "tsdf_integrate", "tsdf_export_blocks", "tsdf_get_stats", "tsdf_destroy",
+    "tsdf_update", "tsdf_integrate", "tsdf_integrate_batch", "tsdf_allocate_batch", "tsdf_update_batch",
+    "tsdf_export_blocks", "tsdf_get_stats", "tsdf_destroy",
     "tsdf_status_str", "tsdf_mb_copy", "tsdf_mb_atomic_add_f32", "tsdf_mb_cas_u64",
 ]
 
@@ -44,7 +46,7 @@ class TsdfError(RuntimeError):
 class tsdf_config(ctypes.Structure):
     _fields_ = [("voxel_size", ctypes.c_float), ("trunc", ctypes.c_float),
                 ("pool_capacity", ctypes.c_int64), ("table_entries", ctypes.c_int64),
-                ("update_mode", ctypes.c_int32), ("max_frame_pixels", ctypes.c_int64)]
+                ("update_mode", ctypes.c_int32), ("max_batch_pixels", ctypes.c_int64)]
 
 
 class tsdf_buffers(ctypes.Structure):
@@ -88,6 +90,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         "tsdf_allocate": (I32, [P, ctypes.POINTER(tsdf_frame), P]),
         "tsdf_update": (I32, [P, ctypes.POINTER(tsdf_frame), P]),
         "tsdf_integrate": (I32, [P, ctypes.POINTER(tsdf_frame), P]),
+        "tsdf_integrate_batch": (I32, [P, ctypes.POINTER(tsdf_frame), I32, P]),
+        "tsdf_allocate_batch": (I32, [P, ctypes.POINTER(tsdf_frame), I32, P]),
+        "tsdf_update_batch": (I32, [P, ctypes.POINTER(tsdf_frame), I32, P]),
         "tsdf_export_blocks": (I32, [P, P, P, P, P, P, P, I64, ctypes.POINTER(I64), P]),
         "tsdf_get_stats": (I32, [P, ctypes.POINTER(tsdf_stats), P]),
         "tsdf_destroy": (None, [P]),
@@ -156,6 +161,31 @@ def tsdf_update(volume, frame: tsdf_frame, stream: int = 0) -> None:
 
 def tsdf_integrate(volume, frame: tsdf_frame, stream: int = 0) -> None:
     _check(load().tsdf_integrate(volume, ctypes.byref(frame), ctypes.c_void_p(stream)), "tsdf_integrate")
+
+
+def frame_array(frames) -> ctypes.Array:
+    """A ctypes array of tsdf_frame from a sequence (or pass an array through)."""
+    if isinstance(frames, ctypes.Array):
+        return frames
+    return (tsdf_frame * max(len(frames), 1))(*frames)
+
+
+def tsdf_integrate_batch(volume, frames, stream: int = 0, n: Optional[int] = None) -> None:
+    arr = frame_array(frames)
+    _check(load().tsdf_integrate_batch(volume, arr, len(frames) if n is None else n, ctypes.c_void_p(stream)),
+           "tsdf_integrate_batch")
+
+
+def tsdf_allocate_batch(volume, frames, stream: int = 0, n: Optional[int] = None) -> None:
+    arr = frame_array(frames)
+    _check(load().tsdf_allocate_batch(volume, arr, len(frames) if n is None else n, ctypes.c_void_p(stream)),
+           "tsdf_allocate_batch")
+
+
+def tsdf_update_batch(volume, frames, stream: int = 0, n: Optional[int] = None) -> None:
+    arr = frame_array(frames)
+    _check(load().tsdf_update_batch(volume, arr, len(frames) if n is None else n, ctypes.c_void_p(stream)),
+           "tsdf_update_batch")
 
 
 def tsdf_export_blocks(volume, coords: int, tsdf: int, weight: int, r: int, g: int, b: int,
@@ -232,7 +262,7 @@ class Volume:
     tensors.  update_mode: "owner" (default) or "rays"."""
 
     def __init__(self, voxel_size: float, trunc: float, pool_capacity: int, table_entries: int = 0,
-                 update_mode: str = "owner", max_frame_pixels: int = 0, device="cuda", stream=None):
+                 update_mode: str = "owner", max_batch_pixels: int = 0, device="cuda", stream=None):
         import torch
         entries = table_entries or tsdf_table_entries_for(pool_capacity)
         if entries <= 0:
@@ -242,7 +272,7 @@ class Volume:
         self.update_mode = update_mode
         self.device = device
         self._cfg = tsdf_config(voxel_size, trunc, int(pool_capacity), int(table_entries), UPDATE_MODES[update_mode],
-                                int(max_frame_pixels))
+                                int(max_batch_pixels))
         n = int(pool_capacity) * BLOCK_VOXELS
         self.table = torch.empty(int(entries) * 2, dtype=torch.int64, device=device)
         self.pool = {k: torch.empty(n, dtype=torch.float32, device=device) for k in ("tsdf", "weight", "r", "g", "b")}
@@ -271,6 +301,9 @@ class Volume:
 
     def integrate(self, frame: DeviceFrame, stream=None):
         tsdf_integrate(self.handle, frame.desc, _stream_handle(stream))
+
+    def integrate_batch(self, frames, stream=None):
+        tsdf_integrate_batch(self.handle, [f.desc for f in frames], _stream_handle(stream))
 
     def stats(self, stream=None) -> Dict[str, object]:
         return tsdf_get_stats(self.handle, _stream_handle(stream))

@@ -55,6 +55,8 @@ typedef enum {
 /* Largest number of cells one point's band walk may visit (a frame whose
  * intrinsics allow more is rejected with TSDF_EINVAL). */
 #define TSDF_MAX_WALK 4096
+/* Most frames one tsdf_integrate_batch call takes. */
+#define TSDF_MAX_BATCH 16
 /* Bins of the probe-depth histograms: bin i counts probes of i+1 slots,
  * the last bin counts TSDF_PROBE_BINS slots or more. */
 #define TSDF_PROBE_BINS 32
@@ -80,9 +82,10 @@ typedef struct {
                                two >= 2 * pool_capacity (so the table is at most half full)
                                and <= TSDF_MAX_TABLE_ENTRIES */
     int32_t update_mode;    /* tsdf_update_mode */
-    int64_t max_frame_pixels; /* owner mode: frame size the per-frame record buffers are sized
-                               for (0: 2^20); larger frames still integrate exactly, but
-                               blocks whose records do not fit are rescanned (slower) */
+    int64_t max_batch_pixels; /* owner mode: total pixels of the frames one call integrates,
+                               which sizes the run-record buffers (0: 2^20); larger calls
+                               still integrate exactly, but blocks whose records do not fit
+                               are rescanned pixel by pixel (slower) */
 } tsdf_config;
 
 /* Device memory owned by the caller, all 16-byte aligned. */
@@ -141,8 +144,8 @@ int64_t tsdf_table_entries_for(int64_t pool_capacity);
 size_t tsdf_counters_bytes(void);
 
 /* Size of the scratch buffer a configuration needs (0 for TSDF_UPDATE_RAYS):
- * about 52 bytes per table entry plus 80 bytes per frame pixel (run records
- * and their grouping by block).  0 for a NULL or invalid config. */
+ * about 52 bytes per table entry plus 80 bytes per pixel of max_batch_pixels
+ * (run records and their grouping by block).  0 for a NULL or invalid config. */
 size_t tsdf_scratch_bytes(const tsdf_config* config);
 
 /* Validate the configuration and buffers, then enqueue the initialisation of
@@ -177,6 +180,19 @@ tsdf_status tsdf_update(tsdf_volume* volume, const tsdf_frame* frame, void* stre
 
 /* tsdf_allocate then tsdf_update of one frame. */
 tsdf_status tsdf_integrate(tsdf_volume* volume, const tsdf_frame* frame, void* stream);
+
+/* Integrate n_frames (0 .. TSDF_MAX_BATCH) frames with one allocate launch
+ * over all of them followed by one update: the result equals integrating
+ * them one by one (the block set is the union, sums commute; which keys an
+ * exhausted pool refuses may differ, their number does not), but each block
+ * the batch touches is read and written once.  Frames may differ in size. */
+tsdf_status tsdf_integrate_batch(tsdf_volume* volume, const tsdf_frame* frames, int32_t n_frames, void* stream);
+
+/* The two halves of tsdf_integrate_batch.  In owner mode tsdf_update_batch
+ * must directly follow tsdf_allocate_batch of identical frames, else
+ * TSDF_EINVAL; tsdf_allocate and tsdf_update are these with one frame. */
+tsdf_status tsdf_allocate_batch(tsdf_volume* volume, const tsdf_frame* frames, int32_t n_frames, void* stream);
+tsdf_status tsdf_update_batch(tsdf_volume* volume, const tsdf_frame* frames, int32_t n_frames, void* stream);
 
 /* Copy every block holding a pool index to caller device memory, in pool
  * index order: coords (n x 3 int32 block coordinates) and, for each non-null

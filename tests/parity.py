@@ -30,13 +30,23 @@ def sort_blocks(coords: np.ndarray, arrays: Dict[str, np.ndarray]):
 
 
 def gpu_integrate(frames: Iterable, voxel_size, trunc, pool_capacity, table_entries=0, split=False,
-                  per_frame_stats=False, mode="owner"):
-    """Integrate on the GPU; returns (volume, stats, coords, arrays, per-frame stats)."""
+                  per_frame_stats=False, mode="owner", batch=1, max_batch_pixels=0):
+    """Integrate on the GPU (one frame per call, or `batch` frames per
+    tsdf_integrate_batch call); returns (volume, stats, coords, arrays,
+    per-call stats)."""
     import torch
     from hash_table_amd import tsdf
-    vol = tsdf.Volume(voxel_size, trunc, pool_capacity, table_entries, update_mode=mode)
+    frames = list(frames)
+    vol = tsdf.Volume(voxel_size, trunc, pool_capacity, table_entries, update_mode=mode,
+                      max_batch_pixels=max_batch_pixels)
     history = []
-    for f in frames:
+    if batch > 1:
+        for i in range(0, len(frames), batch):
+            dfs = [tsdf.DeviceFrame(f) for f in frames[i:i + batch]]
+            vol.integrate_batch(dfs)
+            if per_frame_stats:
+                history.append(vol.stats())
+    for f in (frames if batch <= 1 else []):
         df = tsdf.DeviceFrame(f)
         if split:
             vol.allocate(df)

@@ -30,10 +30,12 @@ def golden(name):
         return json.load(fh)
 
 
-def run_both(frames, vs, tr, cap, table=0, split=False, mode="owner"):
+def run_both(frames, vs, tr, cap, table=0, split=False, mode="owner", batch=1, max_batch_pixels=0):
     frames = list(frames)
-    say(f"  gpu ({mode}): {len(frames)} frame(s) {frames[0].width}x{frames[0].height} vs={vs} trunc={tr} cap={cap}")
-    vol, st, coords, arrays, _ = parity.gpu_integrate(frames, vs, tr, cap, table, split=split, mode=mode)
+    say(f"  gpu ({mode}, batch {batch}): {len(frames)} frame(s) {frames[0].width}x{frames[0].height} "
+        f"vs={vs} trunc={tr} cap={cap}")
+    vol, st, coords, arrays, _ = parity.gpu_integrate(frames, vs, tr, cap, table, split=split, mode=mode,
+                                                      batch=batch, max_batch_pixels=max_batch_pixels)
     say(f"  oracle: {len(frames)} frame(s)")
     o = parity.oracle_integrate(frames, vs, tr, cap)
     return vol, st, coords, arrays, o
@@ -158,6 +160,55 @@ def test_load_factor_parity(target, mode):
 def tsdf_bins():
     from hash_table_amd import tsdf
     return tsdf.TSDF_PROBE_BINS
+
+
+# ---------------------------------------------------------------------------
+# batched integration (one allocate and one update for several frames)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("batch", [3, 16])
+def test_batched_room_parity(mode, batch):
+    wl = scenes.workload("room640x480")
+    frames = list(wl.frames(0, 20))
+    _, st, coords, arrays, o = run_both(frames, wl.voxel_size, wl.trunc, wl.pool_capacity, mode=mode,
+                                        batch=batch, max_batch_pixels=batch * 640 * 480)
+    assert_parity(st, coords, arrays, o)
+    assert st["fallback_blocks"] == 0
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_batch_of_mixed_frames(mode):
+    frames = [scenes.random_frame(s, W=W, H=H, invalid_frac=0.1, translation_scale=0.3)
+              for s, (W, H) in enumerate([(37, 23), (16, 16), (129, 65), (1, 33), (64, 48)])]
+    frames.append(scenes.workload("plane64x48").frame(0))
+    _, st, coords, arrays, o = run_both(frames, 0.01, 0.04, 1 << 16, mode=mode, batch=len(frames))
+    assert_parity(st, coords, arrays, o)
+
+
+def test_record_overflow_rescans_exactly():
+    # run records sized for 2,000 pixels per call: most blocks cannot keep
+    # their runs and are rescanned from their pixel rectangles instead
+    wl = scenes.workload("spherewall320x240")
+    frames = list(wl.frames(0, 4))
+    _, st, coords, arrays, o = run_both(frames, wl.voxel_size, wl.trunc, wl.pool_capacity, mode="owner",
+                                        batch=2, max_batch_pixels=2000)
+    assert st["fallback_blocks"] > 0
+    assert_parity(st, coords, arrays, o)
+
+
+def test_batch_limits():
+    from hash_table_amd import tsdf
+    wl = scenes.workload("plane64x48")
+    vol = tsdf.Volume(wl.voxel_size, wl.trunc, wl.pool_capacity)
+    f = tsdf.DeviceFrame(wl.frame(0))
+    with pytest.raises(tsdf.TsdfError):
+        vol.integrate_batch([f] * (tsdf.TSDF_MAX_BATCH + 1))
+    tsdf.tsdf_integrate_batch(vol.handle, [])          # nothing to do
+    vol.integrate_batch([f] * tsdf.TSDF_MAX_BATCH)
+    st = vol.stats()
+    assert st["pool_used"] == 234 and st["voxel_updates"] == 16 * 38688
+    c, a = vol.export()
+    assert float(a["weight"].sum()) == 16 * 38688
 
 
 # ---------------------------------------------------------------------------
