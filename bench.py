@@ -7,17 +7,20 @@ freshly reset volume, `--batch` frames per call (one allocate launch and one
 update over those frames; the result equals frame-by-frame integration);
 inputs are resident in device memory before timing starts.  Timing is gated
 on parity: the run first checks the volume against the oracle's stored
-counts for the same seeded frames.  Per-kernel durations come from HIP
-events recorded on the launch stream around every kernel of the timed
-steps.  Prints one JSON line.
+counts for the same seeded frames.  Per-call durations come from HIP events
+recorded on the launch stream around every allocate and update call; per
+kernel durations from the events the library records around each of its
+kernels on the same stream (tsdf_set_kernel_timing).  Prints one JSON line.
 
 Roofline: the path is HBM- and atomic-bound (no dense contraction).  The
 algorithmic bytes of a frame (per frame counts from the oracle) are
   allocate  4 P + 16 B_t + 16 B_n
   update    7 P + 16 B_t + 40 U
-with P valid... pixels (depth 4 B, colour 3 B per pixel), B_t blocks touched
-(one 16-byte table entry read), B_n new blocks (one entry written), U
-distinct voxels touched (five floats read and written).
+with P pixels (depth 4 B, colour 3 B per pixel), B_t blocks touched (one
+16-byte table entry read), B_n new blocks (one entry written), U distinct
+voxels touched (five floats read and written).  `roofline` is given for the
+kernel that takes the most time; `path_frac` is the whole path's fraction
+(allocate and update calls, every kernel in them).
 """
 from __future__ import annotations
 
@@ -53,6 +56,32 @@ def load_counts(name):
     path = os.path.join(ROOT, "tests", "golden", f"{name}_counts.json")
     with open(path) as fh:
         return json.load(fh)
+
+
+# HBM bytes per launch from hardware counters: rocprofv3 --pmc FETCH_SIZE,
+# then WRITE_SIZE, each scaled by what it reads for a copy kernel of known
+# size (the summaries under profiles/ give the commands and the factors).
+# A figure holds only for the kernel sources it was taken on, so each entry
+# carries their digest; after any change the field is null until re-measured.
+MEASURED_TRAFFIC = {
+    # (kernel, workload, frames per call, update mode): (bytes per launch, source digest)
+}
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("tsdf_kernels.hip", "tsdf_device.hpp"):
+        with open(os.path.join(ROOT, "hash_table_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload, batch, mode):
+    e = MEASURED_TRAFFIC.get((kernel, workload, batch, mode))
+    if e is None or e[1] != kernel_source_digest():
+        return None
+    return e[0]
 
 
 def frame_bytes(fr):
@@ -185,6 +214,9 @@ def main():
         if not all(gate.values()):
             raise SystemExit(f"parity gate failed ({mode}, batch {batch}): {gate}")
         ev = []
+        if use_events:
+            vol.set_kernel_timing(True)
+            vol.kernel_times()                       # drop the parity pass
 
         def step(record):
             vol.reset()
@@ -203,18 +235,21 @@ def main():
         for _ in range(warmup):
             step(False)
         torch.cuda.synchronize()
+        if use_events:
+            vol.kernel_times()                       # drop the warm-up
         t0 = time.perf_counter()
         for _ in range(steps):
             step(use_events)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         st = vol.stats()
+        kt = vol.kernel_times() if use_events else {}
         t_alloc = [e[0].elapsed_time(e[1]) * 1e-3 for _, e in ev]
         t_upd = [e[1].elapsed_time(e[2]) * 1e-3 for _, e in ev]
         idx = [c for c, _ in ev]
         del vol
         torch.cuda.empty_cache()
-        return wall, t_alloc, t_upd, idx, st, gate
+        return wall, t_alloc, t_upd, idx, st, gate, kt
 
     def kernel_report(t_alloc, t_upd, idx, steps):
         """Per-call durations -> throughput, algorithmic GB/s, per-frame latency."""
@@ -243,7 +278,7 @@ def main():
         return per, ta, tu, sum(b_alloc), sum(b_upd)
 
     use_events = not args.no_events
-    wall, t_alloc, t_upd, idx, st, gate = measure(args.mode, args.batch, args.steps, args.warmup, use_events)
+    wall, t_alloc, t_upd, idx, st, gate, ktimes = measure(args.mode, args.batch, args.steps, args.warmup, use_events)
 
     n_frames = wl.n_frames
     ms_per_step = wall / args.steps * 1e3
@@ -271,25 +306,36 @@ def main():
     if use_events:
         per, ta, tu, ba, bu = kernel_report(t_alloc, t_upd, idx, args.steps)
         out["kernels"] = per
-        # the update call is k_place_items + k_scatter_records + k_update_owner in
-        # owner mode; the roofline figure is for the whole call (the trace
-        # summary under profiles/ splits it)
-        upd_name = "update call (k_place_items+k_scatter_records+k_update_owner)" if args.mode == "owner" \
-            else "k_update_rays"
-        dom, t_dom, b_dom = (upd_name, tu, bu) if tu >= ta else ("k_allocate", ta, ba)
-        achieved = b_dom / t_dom / 1e9
+        # per-kernel durations: HIP events the library records on the launch
+        # stream around each of its kernels (tsdf_set_kernel_timing)
+        upd_kernel = "k_update_owner" if args.mode == "owner" else "k_update_rays"
+        alg = {"k_allocate": ba, upd_kernel: bu}          # algorithmic bytes over the timed steps
+        kt = {}
+        for name, v in sorted(ktimes.items(), key=lambda kv: -kv[1]["total_ms"]):
+            e = {"launches": v["launches"], "avg_us": round(v["total_ms"] * 1e3 / v["launches"], 3),
+                 "share_of_kernel_time": round(v["total_ms"] / sum(x["total_ms"] for x in ktimes.values()), 4)}
+            if name in alg:
+                e["algorithmic_GBps"] = round(alg[name] / (v["total_ms"] * 1e-3) / 1e9, 1)
+            kt[name] = e
+        out["kernel_times"] = kt
+        dom = max((k for k in alg if k in ktimes), key=lambda k: ktimes[k]["total_ms"])
+        launches = ktimes[dom]["launches"]
+        avg_s = ktimes[dom]["total_ms"] * 1e-3 / launches
+        per_launch = alg[dom] / launches
+        achieved = per_launch / avg_s / 1e9
         out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": None,
-                           "bytes_per_launch": round(b_dom / len(t_upd)),
-                           "avg_launch_us": round(t_dom / len(t_upd) * 1e6, 3)}
+                           "traffic": measured_traffic(dom, args.workload, args.batch, args.mode),
+                           "algorithmic_bytes_per_launch": round(per_launch),
+                           "avg_launch_us": round(avg_s * 1e6, 3),
+                           "path_frac": per["integrate_kernels"]["hbm_frac"]}
     if not args.no_variant:
         out["variants"] = {}
         for mode, batch in (("owner", 1), ("rays", 1)):
             if (mode, batch) == (args.mode, args.batch):
                 continue
             vs = max(1, args.steps // 2)
-            w2, a2, u2, i2, _, g2 = measure(mode, batch, vs, 1, True)
+            w2, a2, u2, i2, _, g2, _ = measure(mode, batch, vs, 1, True)
             per2, *_ = kernel_report(a2, u2, i2, vs)
             out["variants"][f"{mode}_batch{batch}"] = {"points_per_s": round(pts * vs / w2, 1),
                                                        "ms_per_step": round(w2 / vs * 1e3, 4),

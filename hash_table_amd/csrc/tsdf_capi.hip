@@ -6,8 +6,10 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "../../include/tsdf.h"
 #include "tsdf_kernels.hpp"
@@ -16,14 +18,14 @@ using namespace tsdf;
 
 namespace {
 
-constexpr int kOwnerGrid = 4096;                     // single-wavefront workgroups of the owner update
+constexpr int kOwnerGridDefault = 2048;              // owner-update workgroups if the occupancy query fails
 constexpr int64_t kDefaultFramePixels = 1 << 20;    // owner-mode record buffers, per call
 constexpr int64_t kRunsPerPixel = 4;                // record capacity per pixel (a room frame needs ~2.7)
 
 // Owner-mode scratch layout: per-frame counters, per-table-entry arrays,
 // then the per-frame segment and record buffers (kParts partitions each).
 struct ScratchLayout {
-    size_t fc, desc, segs, recs, sorted, items, items_spill, item_of, rec_count, bytes;
+    size_t fc, desc, segs, recs, sorted, items, items_spill, item_of, rec_count, rescan, bytes;
     unsigned int item_part_cap, seg_part_cap, rec_part_cap;
 };
 
@@ -52,9 +54,68 @@ ScratchLayout scratch_layout(int64_t entries, int64_t frame_pixels) {
     o += 4 * (size_t)entries;
     L.rec_count = o;
     o += 4 * (size_t)entries;
+    L.rescan = o;
+    o += 4 * (size_t)entries;
     L.bytes = o;
     return L;
 }
+
+}  // namespace
+
+namespace {
+
+// Kernel timing: an event pair per launch, summed when read.
+struct KernelClock {
+    struct Span {
+        int kernel;
+        hipEvent_t start, end;
+    };
+    std::vector<Span> spans;
+    std::vector<hipEvent_t> spare;
+    bool failed = false;
+
+    hipEvent_t take() {
+        hipEvent_t e = nullptr;
+        if (!spare.empty()) {
+            e = spare.back();
+            spare.pop_back();
+        } else if (hipEventCreate(&e) != hipSuccess) {
+            e = nullptr;
+        }
+        return e;
+    }
+    void give(hipEvent_t e) {
+        if (e) spare.push_back(e);
+    }
+    static void mark(void* ctx, int kernel, int phase, hipStream_t s) {
+        KernelClock* c = static_cast<KernelClock*>(ctx);
+        hipEvent_t e = c->take();
+        if (!e || hipEventRecord(e, s) != hipSuccess) {
+            c->give(e);
+            c->failed = true;
+            return;
+        }
+        if (phase == 0) {
+            c->spans.push_back(Span{kernel, e, nullptr});
+        } else if (!c->spans.empty() && c->spans.back().kernel == kernel && !c->spans.back().end) {
+            c->spans.back().end = e;
+        } else {
+            c->give(e);
+            c->failed = true;
+        }
+    }
+    void drop() {
+        for (Span& sp : spans) {
+            give(sp.start);
+            give(sp.end);
+        }
+        spans.clear();
+    }
+    ~KernelClock() {
+        drop();
+        for (hipEvent_t e : spare) (void)hipEventDestroy(e);
+    }
+};
 
 }  // namespace
 
@@ -63,12 +124,17 @@ struct tsdf_volume {
     tsdf_buffers buf;
     unsigned int mask;
     unsigned int serial;        // allocate calls so far (frame stamp source)
+    int owner_grid;             // owner-update workgroups: as many as the device holds at once
     bool pending;               // an owner-mode allocate whose update has not run yet
     int32_t n_last;             // the frames of that allocate
     tsdf_frame last[TSDF_MAX_BATCH];
+    KernelClock* clock;         // non-null while kernel timing is on
+    LaunchTimer timer;
 };
 
 namespace {
+
+const LaunchTimer* timer_of(const tsdf_volume* h) { return h->clock ? &h->timer : nullptr; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -112,6 +178,7 @@ OwnerArgs owner_args(const tsdf_volume* h, unsigned int serial) {
     o.items_spill = reinterpret_cast<unsigned int*>(base + L.items_spill);
     o.item_of = reinterpret_cast<unsigned int*>(base + L.item_of);
     o.rec_count = reinterpret_cast<unsigned int*>(base + L.rec_count);
+    o.rescan = reinterpret_cast<unsigned int*>(base + L.rescan);
     o.desc = reinterpret_cast<ItemDesc*>(base + L.desc);
     o.segs = reinterpret_cast<Segment*>(base + L.segs);
     o.recs = reinterpret_cast<uint2*>(base + L.recs);
@@ -133,7 +200,8 @@ bool init_volume(const tsdf_volume* h, bool whole_pool, hipStream_t s) {
 // without pixels (nothing to launch).
 tsdf_status frame_args(const tsdf_volume* h, const tsdf_frame* fr, bool need_rgb, FrameArgs* a, bool* empty) {
     if (!fr) return TSDF_EINVAL;
-    if (fr->width < 0 || fr->height < 0) return TSDF_EINVAL;
+    if (fr->width < 0 || fr->height < 0 || fr->width > TSDF_MAX_FRAME_SIDE || fr->height > TSDF_MAX_FRAME_SIDE)
+        return TSDF_EINVAL;
     const int64_t pixels = (int64_t)fr->width * fr->height;
     if (pixels > ((int64_t)1 << 31) - 1) return TSDF_EINVAL;
     *empty = pixels == 0;
@@ -203,17 +271,20 @@ tsdf_status batch_args(const tsdf_volume* h, const tsdf_frame* frames, int32_t n
 }
 
 tsdf_status do_allocate(tsdf_volume* h, const BatchArgs& b, hipStream_t s) {
-    if (h->pending && !launch_discard(volume_args(h), owner_args(h, h->serial), s)) return TSDF_EHIP;
+    if (h->pending && !launch_discard(volume_args(h), owner_args(h, h->serial), s, timer_of(h))) return TSDF_EHIP;
     h->pending = false;
     const unsigned int serial = h->serial + 1 == 0xFFFFFFFFu ? 1u : h->serial + 1;
-    if (!launch_allocate(b, volume_args(h), owner_args(h, serial), s)) return TSDF_EHIP;
+    if (!launch_allocate(b, volume_args(h), owner_args(h, serial), s, timer_of(h))) return TSDF_EHIP;
     h->serial = serial;
     return TSDF_OK;
 }
 
 tsdf_status do_update(tsdf_volume* h, const BatchArgs& b, hipStream_t s) {
-    if (h->cfg.update_mode == TSDF_UPDATE_RAYS) return launch_update_rays(b, volume_args(h), s) ? TSDF_OK : TSDF_EHIP;
-    return launch_update_owner(b, volume_args(h), owner_args(h, h->serial), kOwnerGrid, s) ? TSDF_OK : TSDF_EHIP;
+    if (h->cfg.update_mode == TSDF_UPDATE_RAYS)
+        return launch_update_rays(b, volume_args(h), s, timer_of(h)) ? TSDF_OK : TSDF_EHIP;
+    return launch_update_owner(b, volume_args(h), owner_args(h, h->serial), h->owner_grid, s, timer_of(h))
+               ? TSDF_OK
+               : TSDF_EHIP;
 }
 
 }  // namespace
@@ -260,6 +331,8 @@ tsdf_status tsdf_create(const tsdf_config* config, const tsdf_buffers* buffers, 
     h->cfg.table_entries = entries;
     h->buf = b;
     h->mask = (unsigned int)(entries - 1);
+    h->owner_grid = owner_grid();
+    if (h->owner_grid <= 0) h->owner_grid = kOwnerGridDefault;
     if (!init_volume(h, true, static_cast<hipStream_t>(stream))) {
         delete h;
         return TSDF_EHIP;
@@ -386,7 +459,62 @@ tsdf_status tsdf_export_blocks(tsdf_volume* h, int32_t* coords, float* tsdf, flo
     return TSDF_OK;
 }
 
-void tsdf_destroy(tsdf_volume* h) { delete h; }
+tsdf_status tsdf_set_kernel_timing(tsdf_volume* h, int32_t enable) {
+    if (!h) return TSDF_EINVAL;
+    if (enable && !h->clock) {
+        h->clock = new (std::nothrow) KernelClock;
+        if (!h->clock) return TSDF_EINVAL;
+        h->timer.ctx = h->clock;
+        h->timer.mark = &KernelClock::mark;
+    } else if (!enable && h->clock) {
+        delete h->clock;
+        h->clock = nullptr;
+    }
+    return TSDF_OK;
+}
+
+tsdf_status tsdf_kernel_times(tsdf_volume* h, tsdf_kernel_time* out, int32_t max_entries, int32_t* n_entries) {
+    if (!h || !n_entries || max_entries < 0 || (max_entries > 0 && !out)) return TSDF_EINVAL;
+    *n_entries = 0;
+    if (!h->clock) return TSDF_EINVAL;
+    KernelClock& c = *h->clock;
+    int64_t launches[kKernelIds] = {0};
+    double ms[kKernelIds] = {0.0};
+    bool ok = !c.failed;
+    for (const KernelClock::Span& sp : c.spans) {
+        float t = 0.0f;
+        if (!sp.end || hipEventSynchronize(sp.end) != hipSuccess ||
+            hipEventElapsedTime(&t, sp.start, sp.end) != hipSuccess) {
+            ok = false;
+            continue;
+        }
+        ++launches[sp.kernel];
+        ms[sp.kernel] += t;
+    }
+    c.drop();
+    c.failed = false;
+    if (!ok) return TSDF_EHIP;
+    int32_t n = 0;
+    for (int k = 0; k < kKernelIds; ++k) {
+        if (!launches[k]) continue;
+        if (n < max_entries) {
+            tsdf_kernel_time& e = out[n];
+            std::memset(&e, 0, sizeof(e));
+            std::snprintf(e.name, sizeof(e.name), "%s", kernel_name(k));
+            e.launches = launches[k];
+            e.total_ms = ms[k];
+        }
+        ++n;
+    }
+    *n_entries = n;
+    return n > max_entries ? TSDF_ESMALL : TSDF_OK;
+}
+
+void tsdf_destroy(tsdf_volume* h) {
+    if (!h) return;
+    delete h->clock;
+    delete h;
+}
 
 const char* tsdf_status_str(tsdf_status st) {
     switch (st) {

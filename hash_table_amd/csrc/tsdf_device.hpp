@@ -99,16 +99,22 @@ struct __align__(16) ItemDesc {
 // Per-frame counters of the owner update, in the caller's scratch buffer,
 // one set per frame parity.  Items and run records are reserved in
 // kParts partitions (wavefront w uses partition w mod kParts) so that no
-// single counter takes every wavefront's atomic.
+// single counter takes every wavefront's atomic.  The update hands blocks
+// out through one work counter per XCD, each in its own 128-byte line.
 constexpr int kParts = 64;
+constexpr int kXcds = 8;
+constexpr int kFetchStride = 32;        // words between the XCDs' work counters
 struct FrameCounters {
     unsigned long long segrec[kParts];  // segments << 32 | records reserved, per partition
     unsigned int items[kParts];         // blocks first touched, per partition
     unsigned int items_spill;           // blocks beyond their partition's share
     unsigned int items_total;           // all blocks (set when the blocks are placed)
     unsigned long long placed;          // records given to blocks
-    unsigned long long pad[6];
+    unsigned int n_rescan;              // blocks whose runs did not fit (rescanned)
+    unsigned int pad[27];
+    unsigned int fetch[kXcds * kFetchStride];   // next item of XCD x at fetch[x * kFetchStride]
 };
+static_assert(sizeof(FrameCounters) % 128 == 0, "FrameCounters keeps the work counters in their own lines");
 
 // Owner-update bookkeeping in the caller's scratch buffer.
 struct OwnerArgs {
@@ -117,9 +123,10 @@ struct OwnerArgs {
     unsigned int* items_spill; // [table entries] slots beyond a partition's share
     unsigned int* item_of;     // [table entries] slot -> its item this frame
     unsigned int* rec_count;   // [table entries] runs per slot this frame (| kSegOverflow)
+    unsigned int* rescan;      // [table entries] items whose runs did not fit
     ItemDesc* desc;            // [table entries] per item
     Segment* segs;             // [kParts * seg_part_cap]
-    uint2* recs;               // [kParts * rec_part_cap] (pixel, packed run), allocate order
+    uint2* recs;               // [kParts * rec_part_cap] (pixel u | v << 16, packed run), allocate order
     uint2* sorted;             // [kParts * rec_part_cap] the same records grouped by block
     unsigned int item_part_cap, seg_part_cap, rec_part_cap;
     unsigned int parity;       // frame serial & 1

@@ -9,14 +9,15 @@
 // occlusion test and produce the same per-voxel sums; how the update is
 // organised is this library's choice for the MI355X memory system:
 //
-//   * owner update (default): allocate hands every block its frame touched
-//     to the update exactly once (a per-frame stamp in the entry padding),
-//     with the pixel rectangle its band can be seen through.  One workgroup
-//     per block replays the exact walk of every candidate pixel, sums the
-//     block's contributions in LDS and then read-modify-writes the five pool
-//     arrays with plain coalesced loads and stores: a block has one writer
-//     per frame, so no device-scope float atomics are needed.  Blocks whose
-//     rectangle is split over several workgroups add with coalesced atomics.
+//   * owner update (default): allocate cuts every walk into runs, one per
+//     block it crosses, and records each run with a kept voxel (pixel, first
+//     cell, cells, kept, frame); the records are grouped by block, and one
+//     workgroup per block replays the exact walk of each of its runs, sums
+//     the block's contributions in LDS and then read-modify-writes the five
+//     pool arrays with plain coalesced loads and stores: a block has one
+//     writer per call, so no device-scope float atomics are needed.  A block
+//     whose runs did not fit the record buffers is rescanned from the pixel
+//     rectangle its band can be seen through.
 //   * ray-parallel update: the shape the paper describes (one thread per
 //     point, a lookup per block run, five no-return f32 atomic additions per
 //     voxel), kept as a variant.
@@ -28,6 +29,8 @@
 // gives each XCD a contiguous run of tiles so neighbouring tiles share an L2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "tsdf_kernels.hpp"
 
 namespace tsdf {
@@ -36,7 +39,6 @@ namespace {
 constexpr int kTile = 16;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kXcds = 8;
 constexpr int kListCap = 256;     // block runs a wavefront buffers before de-duplicating
 constexpr int kSetCap = 256;      // per-wavefront LDS hash set (power of two, >= kListCap)
 constexpr float kInv255 = 1.0f / 255.0f;
@@ -93,7 +95,7 @@ constexpr unsigned int kNoKeyBase = 0xFFFFFFFEu;  // runs of a key the full tabl
 
 struct AllocLds {
     unsigned long long lkey[kWaves][kListCap];    // run list: block key,
-    unsigned int lpix[kWaves][kListCap];          //   pixel index,
+    unsigned int lpix[kWaves][kListCap];          //   pixel (u | v << 16),
     unsigned int linfo[kWaves][kListCap];         //   packed run,
     unsigned short lset[kWaves][kListCap];        //   its set slot
     unsigned long long skey[kWaves][kSetCap];     // set: key,
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void k_allocate(BatchArgs B, VolumeArgs v
             if (emit) {
                 const int pos = base + __popcll(m & below);
                 L.lkey[wave][pos] = ekey;
-                L.lpix[wave][pos] = pix;
+                L.lpix[wave][pos] = (unsigned int)u | ((unsigned int)v << 16);
                 L.linfo[wave][pos] = einfo;
             }
             base += __popcll(m);
@@ -420,29 +422,64 @@ __global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerA
             d.pad[2] = 0;
             own.desc[i] = d;
             own.item_of[slot] = i;
+            if (rc & kSegOverflow) own.rescan[atomicAdd(&fc.n_rescan, 1u)] = i;
         }
         __syncthreads();
     }
 }
 
+// Each wavefront takes 64 segments, lays their runs end to end (a prefix
+// over the lanes) and copies the records with every lane busy: record p of
+// the group belongs to the first segment whose end lies beyond p.
 __global__ __launch_bounds__(kThreads) void k_scatter_records(VolumeArgs vol, OwnerArgs own) {
     __shared__ unsigned int s_cnt[kParts];
     __shared__ unsigned int s_pre[kParts + 2];
+    __shared__ unsigned int s_end[kWaves][64];
+    __shared__ unsigned int s_src[kWaves][64];
+    __shared__ unsigned int s_dst[kWaves][64];
     FrameCounters& fc = own.fc[own.parity];
     if (threadIdx.x < kParts) s_cnt[threadIdx.x] = (unsigned int)(fc.segrec[threadIdx.x] >> 32);
     __syncthreads();
     partition_prefix(s_cnt, own.seg_part_cap, 0, s_pre);
     const unsigned int n = s_pre[kParts];
-    const int lane = threadIdx.x & 63;
-    const unsigned int waves = gridDim.x * kWaves;
-    for (unsigned int j = blockIdx.x * kWaves + (threadIdx.x >> 6); j < n; j += waves) {
-        const int p = find_partition(s_pre, j);
-        const Segment sg = own.segs[(size_t)p * own.seg_part_cap + (j - s_pre[p])];
-        if (sg.slot == kNoSlot) continue;                       // refused for lack of space
-        const ItemDesc d = own.desc[own.item_of[sg.slot]];
-        if (d.rec_count & kSegOverflow) continue;               // the block is rescanned
-        for (unsigned int r = lane; r < sg.runs; r += 64)
-            own.sorted[d.rec_first + sg.block_off + r] = own.recs[sg.rec_base + r];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const unsigned int step = gridDim.x * kThreads;
+    for (unsigned int j0 = blockIdx.x * kThreads + wave * 64; j0 < n; j0 += step) {
+        const unsigned int j = j0 + lane;
+        unsigned int cnt = 0, src = 0, dst = 0;
+        if (j < n) {
+            const int p = find_partition(s_pre, j);
+            const Segment sg = own.segs[(size_t)p * own.seg_part_cap + (j - s_pre[p])];
+            if (sg.slot != kNoSlot) {                          // refused for lack of space: nothing
+                const ItemDesc& d = own.desc[own.item_of[sg.slot]];
+                const unsigned int rc = d.rec_count;
+                if (!(rc & kSegOverflow)) {                     // else the block is rescanned
+                    cnt = sg.runs;
+                    src = sg.rec_base;
+                    dst = d.rec_first + sg.block_off;
+                }
+            }
+        }
+        unsigned int x = cnt;                                  // inclusive prefix over the lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        const unsigned int total = __shfl(x, 63, 64);
+        s_end[wave][lane] = x;
+        s_src[wave][lane] = src - (x - cnt);                   // + p gives the record (mod 2^32)
+        s_dst[wave][lane] = dst - (x - cnt);
+        wave_lds_fence();
+        for (unsigned int p = lane; p < total; p += 64) {
+            int lo = 0, hi = 63;                               // first lane with end > p
+            while (lo < hi) {
+                const int m = (lo + hi) >> 1;
+                if (s_end[wave][m] > p) hi = m; else lo = m + 1;
+            }
+            own.sorted[s_dst[wave][lo] + p] = own.recs[s_src[wave][lo] + p];
+        }
+        wave_lds_fence();
     }
 }
 
@@ -462,129 +499,190 @@ __global__ __launch_bounds__(kThreads) void k_discard_items(VolumeArgs vol, Owne
 }
 
 // ---------------------------------------------------------------------------
-// owner update: one wavefront per touched block (blocks handed out
-// statically, no shared counter).  The block's runs are replayed from their
-// recorded first cell (the exact walk state there follows from the cell),
+// owner update: one workgroup per touched block at a time, blocks handed out
+// through one work counter per XCD.  The block's runs are replayed from their
+// recorded first cell (the exact walk state there follows from the cell);
 // kept voxels add into LDS (signed distance as f32, weight and colour bytes
-// as integer sums), and the block's touched voxels are then read, added to
-// and written with plain coalesced loads and stores: the block has no other
-// writer this frame.  A block whose runs did not fit the record buffers is
-// rescanned instead: every pixel of the rectangle its band can be seen
-// through replays its walk.
+// as one packed integer word), and the block's touched voxels are then read,
+// added to and written with plain coalesced loads and stores: the block has
+// no other writer in this call.  Blocks whose runs did not fit the record
+// buffers are left to k_update_rescan.
 // ---------------------------------------------------------------------------
-constexpr int kOwnerThreads = 64;
+constexpr int kOwnerThreads = 128;
+// A run adds at most once to each voxel, so a chunk of up to 1023 runs keeps
+// every per-voxel count below 2^10 and every colour sum below 255 * 1023 <
+// 2^18: weight | R << 10 | G << 28 | B << 46 then adds without carries.
+constexpr unsigned int kChunkRuns = 1023;
 
-struct UpdateLds {
+struct OwnerLds {
+    float tsdf[kBlockVoxels];
+    unsigned long long wrgb[kBlockVoxels];
+};
+
+__device__ __forceinline__ unsigned long long packed_colour(const FrameArgs& f, size_t pix) {
+    const uint8_t* c = f.rgb + 3 * pix;
+    return 1ull | ((unsigned long long)c[0] << 10) | ((unsigned long long)c[1] << 28) |
+           ((unsigned long long)c[2] << 46);
+}
+
+// Add the chunk's sums to the pool block and clear them for the next chunk.
+__device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, size_t base) {
+    for (int j = threadIdx.x; j < kBlockVoxels; j += kOwnerThreads) {
+        const unsigned long long s = L.wrgb[j];
+        const unsigned int cnt = (unsigned int)s & 1023u;
+        if (!cnt) continue;
+        const float ts = L.tsdf[j];
+        L.tsdf[j] = 0.0f;
+        L.wrgb[j] = 0;
+        const size_t off = base + j;
+        const float t0 = vol.tsdf[off], w0 = vol.weight[off], r0 = vol.r[off], g0 = vol.g[off], b0 = vol.b[off];
+        vol.tsdf[off] = t0 + ts;
+        vol.weight[off] = w0 + (float)cnt;
+        vol.r[off] = r0 + (float)((unsigned int)(s >> 10) & 0x3FFFFu) * kInv255;
+        vol.g[off] = g0 + (float)((unsigned int)(s >> 28) & 0x3FFFFu) * kInv255;
+        vol.b[off] = b0 + (float)((unsigned int)(s >> 46) & 0x3FFFFu) * kInv255;
+    }
+}
+
+__global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
+    __shared__ OwnerLds L;
+    __shared__ FrameArgs s_frames[kMaxBatch];               // per-record frame lookups from LDS
+    __shared__ unsigned int s_item[2];                      // alternates: read k while k + 1 is written
+    const int tid = threadIdx.x;
+    if (tid < B.n) s_frames[tid] = B.f[tid];
+    for (int j = tid; j < kBlockVoxels; j += kOwnerThreads) {
+        L.tsdf[j] = 0.0f;
+        L.wrgb[j] = 0;
+    }
+    FrameCounters& fc = own.fc[own.parity];
+    const unsigned int n_items = fc.items_total;
+    const unsigned int xcd = blockIdx.x % kXcds;
+    unsigned int* fetch = fc.fetch + xcd * kFetchStride;
+    unsigned int misses = 0;
+
+    for (unsigned int k = 0;; ++k) {
+        if (tid == 0) s_item[k & 1] = xcd + kXcds * atomicAdd(fetch, 1u);
+        __syncthreads();                                     // also: LDS sums clear, frames loaded
+        const unsigned int it = s_item[k & 1];
+        if (it >= n_items) break;
+        const ItemDesc d = own.desc[it];
+        if (d.rec_count & kSegOverflow) continue;            // rescanned (and its count cleared) later
+        if (tid == 0) own.rec_count[d.pad[0]] = 0;
+        if (d.idx >= vol.capacity) {                         // refused a pool index: count, not store
+            for (unsigned int r = tid; r < d.rec_count; r += kOwnerThreads)
+                misses += (unsigned int)run_kept(own.sorted[d.rec_first + r].y);
+            continue;
+        }
+        int bx, by, bz;
+        unpack_key(d.key, bx, by, bz);
+        const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
+        const size_t base = (size_t)d.idx * kBlockVoxels;
+        for (unsigned int c0 = 0; c0 < d.rec_count; c0 += kChunkRuns) {
+            const unsigned int c1 = min(d.rec_count, c0 + kChunkRuns);
+            for (unsigned int r = c0 + tid; r < c1; r += kOwnerThreads) {
+                const uint2 rec = own.sorted[d.rec_first + r];
+                const FrameArgs& f = s_frames[run_frame(rec.y)];
+                const int u = (int)(rec.x & 0xFFFFu), v = (int)(rec.x >> 16);
+                const size_t pix = (size_t)v * f.width + u;
+                BandWalk w;
+                if (setup_walk(w, f.depth[pix], u, v, f, vol.trunc, vol.inv_vs) != kValid) continue;  // cannot happen
+                const unsigned long long c = packed_colour(f, pix);
+                const int e = run_entry(rec.y);
+                resume_at(w, lo0 + (e & 7), lo1 + ((e >> 3) & 7), lo2 + (e >> 6));
+                const int cells = run_cells(rec.y);
+                for (int q = 0;;) {
+                    float sdf;
+                    if (centre_test(w, f, vol.vs, vol.trunc, sdf)) {
+                        const int j = voxel_in_block(w.k0, w.k1, w.k2);
+                        atomicAdd(L.tsdf + j, sdf * vol.inv_trunc);
+                        atomicAdd(L.wrgb + j, c);
+                    }
+                    if (++q >= cells || !advance(w)) break;
+                }
+            }
+            __syncthreads();
+            flush_owner(L, vol, base);
+            __syncthreads();
+        }
+    }
+    const unsigned int c_miss = wave_sum(misses);
+    if ((tid & 63) == 0 && c_miss) atomicAdd(replica(vol.counters) + kUpdateMisses, (unsigned long long)c_miss);
+}
+
+// ---------------------------------------------------------------------------
+// rescan of the blocks whose runs did not fit the record buffers: in every
+// frame of the batch, every pixel of the rectangle the block's band can be
+// seen through replays its walk through the block.  Counts can exceed the
+// packed word's range here, so weight and colour sums are kept as separate
+// 32-bit integer halves.
+// ---------------------------------------------------------------------------
+struct RescanLds {
     float tsdf[kBlockVoxels];
     unsigned long long wr[kBlockVoxels];          // weight | R sum << 32
     unsigned long long gb[kBlockVoxels];          // G sum | B sum << 32
 };
 
-__device__ __forceinline__ void accumulate(UpdateLds& L, const BandWalk& w, const FrameArgs& f,
-                                           const VolumeArgs& vol, unsigned long long c_wr, unsigned long long c_gb,
-                                           unsigned int& n_kept) {
-    float sdf;
-    if (centre_test(w, f, vol.vs, vol.trunc, sdf)) {
-        const int j = voxel_in_block(w.k0, w.k1, w.k2);
-        atomicAdd(L.tsdf + j, sdf * vol.inv_trunc);
-        atomicAdd(L.wr + j, c_wr);
-        atomicAdd(L.gb + j, c_gb);
-        ++n_kept;
-    }
-}
-
-__device__ __forceinline__ void colour_words(const FrameArgs& f, size_t pix, unsigned long long& c_wr,
-                                             unsigned long long& c_gb) {
-    c_wr = 1ull | ((unsigned long long)f.rgb[3 * pix + 0] << 32);
-    c_gb = (unsigned long long)f.rgb[3 * pix + 1] | ((unsigned long long)f.rgb[3 * pix + 2] << 32);
-}
-
-// rescan: in every frame of the batch, every pixel of the block's rectangle
-// replays its walk through the block
-__device__ void rescan_block(UpdateLds& L, const FrameArgs* frames, int n_frames, const VolumeArgs& vol, int bx,
-                             int by, int bz, unsigned int& n_kept) {
-    const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
-    for (int fi = 0; fi < n_frames; ++fi) {
-        const FrameArgs& f = frames[fi];
-        const PixelRect r = block_rect(bx, by, bz, f, vol.vs);
-        if (r.u0 > r.u1 || r.v0 > r.v1) continue;
-        const int rw = r.u1 - r.u0 + 1;
-        const long long area = (long long)rw * (r.v1 - r.v0 + 1);
-        const float zlo = r.zmin - vol.vs, zhi = r.zmax + vol.vs;
-        for (long long p = threadIdx.x; p < area; p += blockDim.x) {
-            const int u = r.u0 + (int)(p % rw);
-            const int v = r.v0 + (int)(p / rw);
-            const size_t pix = (size_t)v * f.width + u;
-            const float d = f.depth[pix];
-            if (!(d - vol.trunc <= zhi && d + vol.trunc >= zlo)) continue;      // band cannot reach the block
-            BandWalk w;
-            if (setup_walk(w, d, u, v, f, vol.trunc, vol.inv_vs) != kValid) continue;
-            if (w.span_hi0 < lo0 - 1 || w.span_lo0 > lo0 + 8 || w.span_hi1 < lo1 - 1 || w.span_lo1 > lo1 + 8 ||
-                w.span_hi2 < lo2 - 1 || w.span_lo2 > lo2 + 8)
-                continue;                                                        // cell span misses the block
-            unsigned long long c_wr, c_gb;
-            colour_words(f, pix, c_wr, c_gb);
-            bool inside = false;
-            for (int visits = 0;;) {
-                if ((unsigned)(w.k0 - lo0) < 8u && (unsigned)(w.k1 - lo1) < 8u && (unsigned)(w.k2 - lo2) < 8u) {
-                    inside = true;
-                    accumulate(L, w, f, vol, c_wr, c_gb, n_kept);
-                } else if (inside) {
-                    break;                                                   // a walk crosses a block once
-                }
-                if (++visits >= f.max_visits || !advance(w)) break;
-            }
-        }
-    }
-}
-
-__global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
-    __shared__ UpdateLds L;
-    __shared__ FrameArgs s_frames[kMaxBatch];               // per-record frame lookups from LDS
-    const int tid = threadIdx.x;
-    if (tid < B.n) s_frames[tid] = B.f[tid];
-    __syncthreads();
-    const unsigned int n_items = own.fc[own.parity].items_total;
-    unsigned int misses = 0, fallbacks = 0;
-
-    for (unsigned int it = blockIdx.x; it < n_items; it += gridDim.x) {
-        const ItemDesc d = own.desc[it];
+__global__ __launch_bounds__(kOwnerThreads) void k_update_rescan(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
+    __shared__ RescanLds L;
+    FrameCounters& fc = own.fc[own.parity];
+    const unsigned int n = fc.n_rescan;
+    unsigned int misses = 0, done = 0;
+    for (unsigned int q = blockIdx.x; q < n; q += gridDim.x) {
+        const ItemDesc d = own.desc[own.rescan[q]];
         int bx, by, bz;
         unpack_key(d.key, bx, by, bz);
-        for (int j = tid; j < kBlockVoxels; j += kOwnerThreads) {
+        for (int j = threadIdx.x; j < kBlockVoxels; j += kOwnerThreads) {
             L.tsdf[j] = 0.0f;
             L.wr[j] = 0;
             L.gb[j] = 0;
         }
         __syncthreads();
         unsigned int n_kept = 0;
-        if (d.rec_count & kSegOverflow) {
-            rescan_block(L, s_frames, B.n, vol, bx, by, bz, n_kept);
-            fallbacks += tid == 0;
-        } else {
-            const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
-            for (unsigned int r = tid; r < d.rec_count; r += kOwnerThreads) {
-                const uint2 rec = own.sorted[d.rec_first + r];
-                const FrameArgs& f = s_frames[run_frame(rec.y)];
-                const unsigned int pix = rec.x;
-                const int u = (int)(pix % (unsigned int)f.width), v = (int)(pix / (unsigned int)f.width);
+        const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
+        for (int fi = 0; fi < B.n; ++fi) {
+            const FrameArgs& f = B.f[fi];
+            const PixelRect rc = block_rect(bx, by, bz, f, vol.vs);
+            if (rc.u0 > rc.u1 || rc.v0 > rc.v1) continue;
+            const int rw = rc.u1 - rc.u0 + 1;
+            const long long area = (long long)rw * (rc.v1 - rc.v0 + 1);
+            const float zlo = rc.zmin - vol.vs, zhi = rc.zmax + vol.vs;
+            for (long long p = threadIdx.x; p < area; p += kOwnerThreads) {
+                const int u = rc.u0 + (int)(p % rw);
+                const int v = rc.v0 + (int)(p / rw);
+                const size_t pix = (size_t)v * f.width + u;
+                const float dep = f.depth[pix];
+                if (!(dep - vol.trunc <= zhi && dep + vol.trunc >= zlo)) continue;   // band cannot reach the block
                 BandWalk w;
-                if (setup_walk(w, f.depth[pix], u, v, f, vol.trunc, vol.inv_vs) != kValid) continue;  // cannot happen
-                unsigned long long c_wr, c_gb;
-                colour_words(f, pix, c_wr, c_gb);
-                const int e = run_entry(rec.y);
-                resume_at(w, lo0 + (e & 7), lo1 + ((e >> 3) & 7), lo2 + (e >> 6));
-                const int cells = run_cells(rec.y);
-                for (int q = 0;;) {
-                    accumulate(L, w, f, vol, c_wr, c_gb, n_kept);
-                    if (++q >= cells || !advance(w)) break;
+                if (setup_walk(w, dep, u, v, f, vol.trunc, vol.inv_vs) != kValid) continue;
+                if (w.span_hi0 < lo0 - 1 || w.span_lo0 > lo0 + 8 || w.span_hi1 < lo1 - 1 || w.span_lo1 > lo1 + 8 ||
+                    w.span_hi2 < lo2 - 1 || w.span_lo2 > lo2 + 8)
+                    continue;                                                     // cell span misses the block
+                const unsigned long long c_wr = 1ull | ((unsigned long long)f.rgb[3 * pix + 0] << 32);
+                const unsigned long long c_gb =
+                    (unsigned long long)f.rgb[3 * pix + 1] | ((unsigned long long)f.rgb[3 * pix + 2] << 32);
+                bool inside = false;
+                for (int visits = 0;;) {
+                    if ((unsigned)(w.k0 - lo0) < 8u && (unsigned)(w.k1 - lo1) < 8u && (unsigned)(w.k2 - lo2) < 8u) {
+                        inside = true;
+                        float sdf;
+                        if (centre_test(w, f, vol.vs, vol.trunc, sdf)) {
+                            const int j = voxel_in_block(w.k0, w.k1, w.k2);
+                            atomicAdd(L.tsdf + j, sdf * vol.inv_trunc);
+                            atomicAdd(L.wr + j, c_wr);
+                            atomicAdd(L.gb + j, c_gb);
+                            ++n_kept;
+                        }
+                    } else if (inside) {
+                        break;                                                // a walk crosses a block once
+                    }
+                    if (++visits >= f.max_visits || !advance(w)) break;
                 }
             }
         }
         __syncthreads();
         if (d.idx < vol.capacity) {
             const size_t base = (size_t)d.idx * kBlockVoxels;
-            for (int j = tid; j < kBlockVoxels; j += kOwnerThreads) {
+            for (int j = threadIdx.x; j < kBlockVoxels; j += kOwnerThreads) {
                 const unsigned long long wr = L.wr[j];
                 const unsigned int cnt = (unsigned int)wr;
                 if (!cnt) continue;
@@ -601,12 +699,15 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
         } else {
             misses += n_kept;               // block refused a pool index: counted, not stored
         }
-        if (tid == 0) own.rec_count[d.pad[0]] = 0;
+        if (threadIdx.x == 0) {
+            own.rec_count[d.pad[0]] = 0;
+            ++done;
+        }
         __syncthreads();
     }
     const unsigned int c_miss = wave_sum(misses);
-    if (tid == 0 && c_miss) atomicAdd(replica(vol.counters) + kUpdateMisses, (unsigned long long)c_miss);
-    if (tid == 0 && fallbacks) atomicAdd(replica(vol.counters) + kFallbackBlocks, (unsigned long long)fallbacks);
+    if ((threadIdx.x & 63) == 0 && c_miss) atomicAdd(replica(vol.counters) + kUpdateMisses, (unsigned long long)c_miss);
+    if (threadIdx.x == 0 && done) atomicAdd(replica(vol.counters) + kFallbackBlocks, (unsigned long long)done);
 }
 
 // ---------------------------------------------------------------------------
@@ -751,25 +852,52 @@ bool launched() { return hipGetLastError() == hipSuccess; }
 // ---------------------------------------------------------------------------
 int tile_grid(const FrameArgs& f) { return f.tiles_per_xcd * kXcds; }
 
-bool launch_allocate(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, hipStream_t s) {
-    hipLaunchKernelGGL(k_allocate, dim3(b.n * b.tile_grid), dim3(kThreads), 0, s, b, v, o);
+const char* kernel_name(int id) {
+    static const char* const names[kKernelIds] = {"k_allocate",      "k_place_items", "k_scatter_records",
+                                                  "k_update_owner",  "k_update_rescan", "k_discard_items",
+                                                  "k_update_rays"};
+    return id >= 0 && id < kKernelIds ? names[id] : "unknown";
+}
+
+#define TSDF_TIMED_LAUNCH(timer, id, kernel, grid, block, stream, ...)            \
+    do {                                                                          \
+        if (timer) (timer)->mark((timer)->ctx, (id), 0, (stream));                \
+        hipLaunchKernelGGL(kernel, (grid), (block), 0, (stream), __VA_ARGS__);    \
+        if (timer) (timer)->mark((timer)->ctx, (id), 1, (stream));                \
+    } while (0)
+
+bool launch_allocate(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, hipStream_t s,
+                     const LaunchTimer* t) {
+    TSDF_TIMED_LAUNCH(t, kKAllocate, k_allocate, dim3(b.n * b.tile_grid), dim3(kThreads), s, b, v, o);
     return launched();
 }
 
-bool launch_update_owner(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, int grid, hipStream_t s) {
-    hipLaunchKernelGGL(k_place_items, dim3(256), dim3(kThreads), 0, s, v, o);
-    hipLaunchKernelGGL(k_scatter_records, dim3(2048), dim3(kThreads), 0, s, v, o);
-    hipLaunchKernelGGL(k_update_owner, dim3(grid), dim3(kOwnerThreads), 0, s, b, v, o);
+bool launch_update_owner(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, int grid, hipStream_t s,
+                         const LaunchTimer* t) {
+    TSDF_TIMED_LAUNCH(t, kKPlaceItems, k_place_items, dim3(256), dim3(kThreads), s, v, o);
+    TSDF_TIMED_LAUNCH(t, kKScatterRecords, k_scatter_records, dim3(1024), dim3(kThreads), s, v, o);
+    TSDF_TIMED_LAUNCH(t, kKUpdateOwner, k_update_owner, dim3(grid), dim3(kOwnerThreads), s, b, v, o);
+    TSDF_TIMED_LAUNCH(t, kKUpdateRescan, k_update_rescan, dim3(256), dim3(kOwnerThreads), s, b, v, o);
     return launched();
 }
 
-bool launch_discard(const VolumeArgs& v, const OwnerArgs& o, hipStream_t s) {
-    hipLaunchKernelGGL(k_discard_items, dim3(64), dim3(kThreads), 0, s, v, o);
+int owner_grid() {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_update_owner),
+                                                     kOwnerThreads, 0) != hipSuccess)
+        return 0;
+    return std::max(1, cus) * std::max(1, per_cu);
+}
+
+bool launch_discard(const VolumeArgs& v, const OwnerArgs& o, hipStream_t s, const LaunchTimer* t) {
+    TSDF_TIMED_LAUNCH(t, kKDiscardItems, k_discard_items, dim3(64), dim3(kThreads), s, v, o);
     return launched();
 }
 
-bool launch_update_rays(const BatchArgs& b, const VolumeArgs& v, hipStream_t s) {
-    hipLaunchKernelGGL(k_update_rays, dim3(b.n * b.tile_grid), dim3(kThreads), 0, s, b, v);
+bool launch_update_rays(const BatchArgs& b, const VolumeArgs& v, hipStream_t s, const LaunchTimer* t) {
+    TSDF_TIMED_LAUNCH(t, kKUpdateRays, k_update_rays, dim3(b.n * b.tile_grid), dim3(kThreads), s, b, v);
     return launched();
 }
 

@@ -9,15 +9,39 @@
 
 namespace tsdf {
 
+// Kernels, as the optional launch timer sees them.
+enum KernelId {
+    kKAllocate = 0,
+    kKPlaceItems,
+    kKScatterRecords,
+    kKUpdateOwner,
+    kKUpdateRescan,
+    kKDiscardItems,
+    kKUpdateRays,
+    kKernelIds
+};
+const char* kernel_name(int id);
+
+// Called right before (phase 0) and after (phase 1) every launch of the
+// integrate path when the caller passes one.
+struct LaunchTimer {
+    void* ctx;
+    void (*mark)(void* ctx, int kernel, int phase, hipStream_t s);
+};
+
 // workgroups of the per-point kernels for a frame (a multiple of 8)
 int tile_grid(const FrameArgs& f);
 
-bool launch_allocate(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, hipStream_t s);
+bool launch_allocate(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, hipStream_t s,
+                     const LaunchTimer* t);
 // group the batch's run records by block, then update every touched block
-bool launch_update_owner(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, int grid, hipStream_t s);
+// (`grid` workgroups; owner_grid() is the number the device holds at once)
+bool launch_update_owner(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, int grid, hipStream_t s,
+                         const LaunchTimer* t);
+int owner_grid();
 // forget an allocate's records (no update followed it)
-bool launch_discard(const VolumeArgs& v, const OwnerArgs& o, hipStream_t s);
-bool launch_update_rays(const BatchArgs& b, const VolumeArgs& v, hipStream_t s);
+bool launch_discard(const VolumeArgs& v, const OwnerArgs& o, hipStream_t s, const LaunchTimer* t);
+bool launch_update_rays(const BatchArgs& b, const VolumeArgs& v, hipStream_t s, const LaunchTimer* t);
 // zero the pool (whole, or the used part), empty the table, clear the counters
 // and (owner mode) the per-slot run counts and per-frame counters
 bool launch_init(const VolumeArgs& v, unsigned long long table_entries, bool whole_pool, const OwnerArgs* own,

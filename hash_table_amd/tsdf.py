@@ -23,6 +23,7 @@ TSDF_UPDATE_OWNER, TSDF_UPDATE_RAYS = 0, 1
 UPDATE_MODES = {"owner": TSDF_UPDATE_OWNER, "rays": TSDF_UPDATE_RAYS}
 TSDF_PROBE_BINS = 32
 TSDF_MAX_BATCH = 16
+TSDF_MAX_FRAME_SIDE = 65535
 TSDF_MAX_POOL_BLOCKS = 1 << 30
 TSDF_MAX_TABLE_ENTRIES = 1 << 31
 BLOCK_VOXELS = 512
@@ -32,7 +33,7 @@ MB_COALESCED, MB_RANDOM, MB_SAME_WAVE, MB_BLOCK_ROW, MB_COUNTERS = 0, 1, 2, 3, 4
 EXPORTS = [
     "tsdf_table_entries_for", "tsdf_counters_bytes", "tsdf_scratch_bytes", "tsdf_create", "tsdf_reset", "tsdf_allocate",
     "tsdf_update", "tsdf_integrate", "tsdf_integrate_batch", "tsdf_allocate_batch", "tsdf_update_batch",
-    "tsdf_export_blocks", "tsdf_get_stats", "tsdf_destroy",
+    "tsdf_export_blocks", "tsdf_get_stats", "tsdf_set_kernel_timing", "tsdf_kernel_times", "tsdf_destroy",
     "tsdf_status_str", "tsdf_mb_copy", "tsdf_mb_atomic_add_f32", "tsdf_mb_cas_u64",
 ]
 
@@ -68,6 +69,10 @@ class tsdf_stats(ctypes.Structure):
         ("probe_hist_update", ctypes.c_uint64 * TSDF_PROBE_BINS)]
 
 
+class tsdf_kernel_time(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -95,6 +100,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         "tsdf_update_batch": (I32, [P, ctypes.POINTER(tsdf_frame), I32, P]),
         "tsdf_export_blocks": (I32, [P, P, P, P, P, P, P, I64, ctypes.POINTER(I64), P]),
         "tsdf_get_stats": (I32, [P, ctypes.POINTER(tsdf_stats), P]),
+        "tsdf_set_kernel_timing": (I32, [P, I32]),
+        "tsdf_kernel_times": (I32, [P, ctypes.POINTER(tsdf_kernel_time), I32, ctypes.POINTER(I32)]),
         "tsdf_destroy": (None, [P]),
         "tsdf_status_str": (ctypes.c_char_p, [I32]),
         "tsdf_mb_copy": (I32, [P, P, SZ, P]),
@@ -208,6 +215,20 @@ def tsdf_get_stats(volume, stream: int = 0) -> Dict[str, object]:
     return out
 
 
+def tsdf_set_kernel_timing(volume, enable: bool) -> None:
+    _check(load().tsdf_set_kernel_timing(volume, 1 if enable else 0), "tsdf_set_kernel_timing")
+
+
+def tsdf_kernel_times(volume) -> Dict[str, Dict[str, float]]:
+    """{kernel name: {"launches": n, "total_ms": ms}} since timing was enabled
+    or last read (waits for the recorded events)."""
+    out = (tsdf_kernel_time * 16)()
+    n = ctypes.c_int32(0)
+    _check(load().tsdf_kernel_times(volume, out, 16, ctypes.byref(n)), "tsdf_kernel_times")
+    return {out[i].name.decode(): {"launches": int(out[i].launches), "total_ms": float(out[i].total_ms)}
+            for i in range(n.value)}
+
+
 def tsdf_destroy(volume) -> None:
     if volume:
         load().tsdf_destroy(volume)
@@ -307,6 +328,12 @@ class Volume:
 
     def stats(self, stream=None) -> Dict[str, object]:
         return tsdf_get_stats(self.handle, _stream_handle(stream))
+
+    def set_kernel_timing(self, enable: bool = True) -> None:
+        tsdf_set_kernel_timing(self.handle, enable)
+
+    def kernel_times(self) -> Dict[str, Dict[str, float]]:
+        return tsdf_kernel_times(self.handle)
 
     def export(self, stream=None, arrays=("tsdf", "weight", "r", "g", "b")):
         """All pool blocks as host numpy arrays: coords (n, 3) int32 and

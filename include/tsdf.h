@@ -57,6 +57,9 @@ typedef enum {
 #define TSDF_MAX_WALK 4096
 /* Most frames one tsdf_integrate_batch call takes. */
 #define TSDF_MAX_BATCH 16
+/* Largest frame width and height, in pixels (a pixel position is recorded
+ * as two 16-bit halves). */
+#define TSDF_MAX_FRAME_SIDE 65535
 /* Bins of the probe-depth histograms: bin i counts probes of i+1 slots,
  * the last bin counts TSDF_PROBE_BINS slots or more. */
 #define TSDF_PROBE_BINS 32
@@ -67,8 +70,9 @@ typedef struct tsdf_volume tsdf_volume;     /* opaque host-side handle */
  *   TSDF_UPDATE_OWNER  each block the frame touched is handed to one
  *                      workgroup, which replays the band walks that reach it,
  *                      sums them in LDS and read-modify-writes the block's
- *                      voxels with plain coalesced loads and stores (blocks
- *                      split over several workgroups add atomically);
+ *                      voxels with plain coalesced loads and stores (a block
+ *                      whose runs overflow the scratch record buffers is
+ *                      rescanned from the pixels its band can be seen through);
  *   TSDF_UPDATE_RAYS   one thread per point walks its band, looks each block
  *                      run up and adds with five f32 atomics per voxel (the
  *                      paper's section 3 shape). */
@@ -108,7 +112,7 @@ typedef struct {
                                0, negative or non-finite = no measurement */
     const uint8_t* rgb;     /* height * width * 3 bytes, row-major, R G B interleaved;
                                needed by update and integrate, ignored by allocate */
-    int32_t width, height;  /* >= 0; an empty frame is a no-op */
+    int32_t width, height;  /* 0 .. TSDF_MAX_FRAME_SIDE; an empty frame is a no-op */
     float fx, fy, cx, cy;   /* pinhole intrinsics, pixels; pixel (u, v) looks along
                                ((u - cx) / fx, (v - cy) / fy, 1) in camera coordinates */
     float R[9];             /* camera-to-world rotation, row-major; must be orthonormal to
@@ -206,7 +210,26 @@ tsdf_status tsdf_export_blocks(tsdf_volume* volume, int32_t* coords, float* tsdf
 /* Read the counters into *stats (host memory).  Waits for the stream. */
 tsdf_status tsdf_get_stats(tsdf_volume* volume, tsdf_stats* stats, void* stream);
 
-/* Free the handle.  Never frees caller memory. */
+/* Per-kernel timing, for measurement (the paper's section 4 times each
+ * stage on its own).  While enabled, every kernel the volume launches is
+ * bracketed by two HIP events recorded on its launch stream.
+ * tsdf_kernel_times waits for the events recorded so far, and writes one
+ * entry per kernel that ran since timing was enabled or last read: its
+ * name, launches and summed event-to-event milliseconds; then it clears the
+ * sums.  *n_entries receives the number of entries (host memory); at most
+ * max_entries are written, TSDF_ESMALL if more exist.  Disabling drops
+ * unread records.  Timing costs two event records per launch. */
+typedef struct {
+    char name[32];          /* kernel name, e.g. "k_update_owner" */
+    int64_t launches;
+    double total_ms;
+} tsdf_kernel_time;
+
+tsdf_status tsdf_set_kernel_timing(tsdf_volume* volume, int32_t enable);
+tsdf_status tsdf_kernel_times(tsdf_volume* volume, tsdf_kernel_time* out, int32_t max_entries,
+                              int32_t* n_entries);
+
+/* Free the handle (and its timing events).  Never frees caller memory. */
 void tsdf_destroy(tsdf_volume* volume);
 
 /* Name of a status code. */

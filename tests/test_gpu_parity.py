@@ -377,3 +377,35 @@ def test_export_too_small_and_invalid_frames():
     bad.desc.R[0] = 2.0                              # not a rotation
     with pytest.raises(tsdf.TsdfError):
         vol.allocate(bad)
+    # wider than TSDF_MAX_FRAME_SIDE: refused before any launch (the buffers
+    # are sized for the frame anyway, all depths 0, so nothing can read past them)
+    wide = scenes.Frame(np.zeros((1, tsdf.TSDF_MAX_FRAME_SIDE + 1), np.float32),
+                        np.zeros((1, tsdf.TSDF_MAX_FRAME_SIDE + 1, 3), np.uint8),
+                        1000.0, 1000.0, 0.0, 0.0, np.eye(3, dtype=np.float32), np.zeros(3, np.float32))
+    with pytest.raises(tsdf.TsdfError) as e:
+        vol.allocate(tsdf.DeviceFrame(wide))
+    assert e.value.status == tsdf.TSDF_EINVAL
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_kernel_timing(mode):
+    import torch
+    from hash_table_amd import tsdf
+    wl = scenes.workload("spherewall320x240")
+    frames = [tsdf.DeviceFrame(wl.frame(i)) for i in range(3)]
+    vol = tsdf.Volume(wl.voxel_size, wl.trunc, wl.pool_capacity, update_mode=mode)
+    with pytest.raises(tsdf.TsdfError):
+        vol.kernel_times()                            # timing is off
+    vol.set_kernel_timing(True)
+    vol.integrate_batch(frames)
+    vol.integrate(frames[0])
+    kt = vol.kernel_times()
+    say(f"  kernel times ({mode}): {kt}")
+    expect = {"k_allocate", "k_place_items", "k_scatter_records", "k_update_owner", "k_update_rescan"} \
+        if mode == "owner" else {"k_allocate", "k_update_rays"}
+    assert set(kt) == expect
+    for v in kt.values():
+        assert v["launches"] == 2 and v["total_ms"] > 0.0
+    assert vol.kernel_times() == {}                   # read sums are cleared
+    vol.set_kernel_timing(False)
+    torch.cuda.synchronize()
