@@ -40,7 +40,7 @@ constexpr int kTile = 16;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kListCap = 256;     // block runs a wavefront buffers before de-duplicating
-constexpr int kSetCap = 256;      // per-wavefront LDS hash set (power of two, >= kListCap)
+constexpr int kSetCap = 256;      // per-wavefront LDS hash set (power of two, >= kListCap, <= 256)
 constexpr float kInv255 = 1.0f / 255.0f;
 
 __device__ __forceinline__ bool workgroup_tile(const FrameArgs& f, int wg, int& tile_u0, int& tile_v0) {
@@ -97,12 +97,10 @@ struct AllocLds {
     unsigned long long lkey[kWaves][kListCap];    // run list: block key,
     unsigned int lpix[kWaves][kListCap];          //   pixel (u | v << 16),
     unsigned int linfo[kWaves][kListCap];         //   packed run,
-    unsigned short lset[kWaves][kListCap];        //   its set slot
+    unsigned char lset[kWaves][kListCap];         //   its set slot
     unsigned long long skey[kWaves][kSetCap];     // set: key,
-    unsigned int sruns[kWaves][kSetCap];          //   runs,
-    unsigned int sbase[kWaves][kSetCap];          //   first record,
-    unsigned int sfill[kWaves][kSetCap];          //   records written
-    unsigned short suniq[kWaves][kSetCap];        // occupied set slots, compacted
+    unsigned int sruns[kWaves][kSetCap];          //   runs; after the reservation, the next record
+    unsigned char suniq[kWaves][kSetCap];         // occupied set slots, compacted
     unsigned int nuniq[kWaves];
     unsigned int hist[kProbeBins];
     unsigned int pmax;
@@ -114,7 +112,6 @@ __device__ void flush_runs(AllocLds& L, int wave, int lane, int n, const VolumeA
     for (int i = lane; i < kSetCap; i += 64) {
         L.skey[wave][i] = kEmptyKey;
         L.sruns[wave][i] = 0;
-        L.sfill[wave][i] = 0;
     }
     if (lane == 0) L.nuniq[wave] = 0;
     wave_lds_fence();
@@ -124,13 +121,13 @@ __device__ void flush_runs(AllocLds& L, int wave, int lane, int n, const VolumeA
         for (;;) {     // n <= kSetCap distinct keys at most: the probe always finds room
             const unsigned long long prev = atomicCAS(&L.skey[wave][h], kEmptyKey, key);
             if (prev == kEmptyKey) {
-                L.suniq[wave][atomicAdd(&L.nuniq[wave], 1u)] = (unsigned short)h;
+                L.suniq[wave][atomicAdd(&L.nuniq[wave], 1u)] = (unsigned char)h;
                 break;
             }
             if (prev == key) break;
             h = (h + 1) & (kSetCap - 1);
         }
-        L.lset[wave][i] = (unsigned short)h;
+        L.lset[wave][i] = (unsigned char)h;
         atomicAdd(&L.sruns[wave][h], 1u);
     }
     wave_lds_fence();
@@ -198,7 +195,7 @@ __device__ void flush_runs(AllocLds& L, int wave, int lane, int n, const VolumeA
                 sg.runs = runs;
                 sg.block_off = atomicAdd(own.rec_count + slot, runs) & ~kSegOverflow;
                 segs[seg] = sg;
-                L.sbase[wave][h] = sg.rec_base;
+                L.sruns[wave][h] = sg.rec_base;
             } else {                                 // out of space: the update rescans the block
                 if (seg < own.seg_part_cap) {        // the scatter reads every reserved segment
                     Segment sg;
@@ -209,22 +206,22 @@ __device__ void flush_runs(AllocLds& L, int wave, int lane, int n, const VolumeA
                     segs[seg] = sg;
                 }
                 atomicOr(own.rec_count + slot, kSegOverflow);
-                L.sbase[wave][h] = kNoBase;
+                L.sruns[wave][h] = kNoBase;
             }
         } else if (has) {                            // the full table refused the key: its
-            L.sbase[wave][h] = kNoKeyBase;           // kept visits are lost, counted below
+            L.sruns[wave][h] = kNoKeyBase;           // kept visits are lost, counted below
         }
     }
     wave_lds_fence();
     if (own.build_items) {
         for (int i = lane; i < n; i += 64) {
             const int h = L.lset[wave][i];
-            const unsigned int base = L.sbase[wave][h];
+            const unsigned int base = L.sruns[wave][h];
             if (base == kNoKeyBase) {
                 misses += (unsigned int)run_kept(L.linfo[wave][i]);
             } else if (base != kNoBase) {
-                const unsigned int pos = atomicAdd(&L.sfill[wave][h], 1u);
-                own.recs[base + pos] = make_uint2(L.lpix[wave][i], L.linfo[wave][i]);
+                const unsigned int rec = atomicAdd(&L.sruns[wave][h], 1u);
+                own.recs[rec] = make_uint2(L.lpix[wave][i], L.linfo[wave][i]);
             }
         }
     }
@@ -258,45 +255,42 @@ __global__ __launch_bounds__(kThreads) void k_allocate(BatchArgs B, VolumeArgs v
     int cls = kInvalid;
     if (u < f.width && v < f.height) cls = setup_walk(w, f.depth[pix], u, v, f, vol.trunc, vol.inv_vs);
     bool alive = cls == kValid;
-    unsigned long long cur = kEmptyKey;       // block of the current run
-    int entry = 0, cells = 0, kept = 0;       // the current run
+    // the current run: its block, first cell, cells visited and kept
+    unsigned long long cur = alive ? block_key(w.k0, w.k1, w.k2) : kEmptyKey;
+    int entry = alive ? voxel_in_block(w.k0, w.k1, w.k2) : 0;
+    int cells = 0, kept = 0;
     unsigned int n_upd = 0, n_guard = 0, misses = 0;
     int visits = 0;
     int base = 0;                             // wavefront-uniform fill of the run list
+    const unsigned int xy = (unsigned int)u | ((unsigned int)v << 16);
 
-    for (;;) {
-        const bool any_alive = __any(alive);
+    // one cell per lane per iteration; a run is emitted by the step that
+    // leaves its block or ends the walk
+    while (__any(alive)) {
         bool emit = false;
-        unsigned long long ekey = kEmptyKey;
+        unsigned long long ekey = cur;
         unsigned int einfo = 0;
         if (alive) {
-            const unsigned long long key = block_key(w.k0, w.k1, w.k2);
-            if (key != cur) {                 // a new block: close the previous run
+            float sdf;
+            const bool keep = centre_test(w, f, vol.vs, vol.trunc, sdf);
+            ++cells;
+            kept += keep ? 1 : 0;
+            bool crossed;
+            bool more = advance_select(w, crossed);
+            if (++visits >= f.max_visits && more) {   // cut by the safety bound (never expected)
+                ++n_guard;
+                more = false;
+            }
+            if (!more || crossed) {
                 emit = kept > 0;
-                ekey = cur;
                 einfo = pack_run(entry, cells, kept, fi);
-                cur = key;
+                n_upd += (unsigned int)kept;
+                cur = block_key(w.k0, w.k1, w.k2);
                 entry = voxel_in_block(w.k0, w.k1, w.k2);
                 cells = 0;
                 kept = 0;
             }
-            ++cells;
-            float sdf;
-            if (centre_test(w, f, vol.vs, vol.trunc, sdf)) {
-                ++kept;
-                ++n_upd;
-            }
-            if (++visits >= f.max_visits) {
-                n_guard += advance(w) ? 1u : 0u;
-                alive = false;
-            } else {
-                alive = advance(w);
-            }
-        } else if (!any_alive && cur != kEmptyKey) {   // after the last step: the last run
-            emit = kept > 0;
-            ekey = cur;
-            einfo = pack_run(entry, cells, kept, fi);
-            cur = kEmptyKey;
+            alive = more;
         }
         const unsigned long long m = __ballot(emit);
         if (m) {
@@ -307,12 +301,11 @@ __global__ __launch_bounds__(kThreads) void k_allocate(BatchArgs B, VolumeArgs v
             if (emit) {
                 const int pos = base + __popcll(m & below);
                 L.lkey[wave][pos] = ekey;
-                L.lpix[wave][pos] = (unsigned int)u | ((unsigned int)v << 16);
+                L.lpix[wave][pos] = xy;
                 L.linfo[wave][pos] = einfo;
             }
             base += __popcll(m);
         }
-        if (!any_alive) break;
     }
     if (base > 0) flush_runs(L, wave, lane, base, vol, own, misses);
 
@@ -597,7 +590,8 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
                         atomicAdd(L.tsdf + j, sdf * vol.inv_trunc);
                         atomicAdd(L.wrgb + j, c);
                     }
-                    if (++q >= cells || !advance(w)) break;
+                    bool crossed;
+                    if (++q >= cells || !advance_select(w, crossed)) break;
                 }
             }
             __syncthreads();
@@ -769,7 +763,8 @@ __global__ __launch_bounds__(kThreads) void k_update_rays(BatchArgs B, VolumeArg
                     ++n_miss;
                 }
             }
-            if (++visits >= f.max_visits || !advance(w)) break;
+            bool crossed;
+            if (++visits >= f.max_visits || !advance_select(w, crossed)) break;
         }
     }
     const unsigned int c_miss = wave_sum(n_miss);
