@@ -43,9 +43,9 @@ ScratchLayout scratch_layout(int64_t entries, int64_t frame_pixels) {
     L.segs = o;
     o += sizeof(Segment) * (size_t)kParts * L.seg_part_cap;
     L.recs = o;
-    o += sizeof(uint2) * (size_t)kParts * L.rec_part_cap;
+    o += sizeof(RunRecord) * (size_t)kParts * L.rec_part_cap;
     L.sorted = o;
-    o += sizeof(uint2) * (size_t)kParts * L.rec_part_cap;
+    o += sizeof(RunRecord) * (size_t)kParts * L.rec_part_cap;
     L.items = o;
     o += 4 * (size_t)kParts * L.item_part_cap;
     L.items_spill = o;
@@ -181,8 +181,8 @@ OwnerArgs owner_args(const tsdf_volume* h, unsigned int serial) {
     o.rescan = reinterpret_cast<unsigned int*>(base + L.rescan);
     o.desc = reinterpret_cast<ItemDesc*>(base + L.desc);
     o.segs = reinterpret_cast<Segment*>(base + L.segs);
-    o.recs = reinterpret_cast<uint2*>(base + L.recs);
-    o.sorted = reinterpret_cast<uint2*>(base + L.sorted);
+    o.recs = reinterpret_cast<RunRecord*>(base + L.recs);
+    o.sorted = reinterpret_cast<RunRecord*>(base + L.sorted);
     o.item_part_cap = L.item_part_cap;
     o.seg_part_cap = L.seg_part_cap;
     o.rec_part_cap = L.rec_part_cap;

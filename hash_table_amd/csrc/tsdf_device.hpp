@@ -65,19 +65,38 @@ constexpr unsigned int kNoSlot = 0xFFFFFFFFu;
 constexpr unsigned int kSegOverflow = 0x80000000u;   // block's runs did not all fit: rescan it
 constexpr float kNearPlane = 1e-4f;                 // block corners closer than this: whole image
 
-// One run of a walk inside one block: the pixel, the first cell the walk
-// visits in the block (voxel index), the cells it visits there and how many
-// of them pass the occlusion test.
-// (A line crosses at most 22 cells of an 8^3 block, so 6 bits hold the
-// counts; 4 bits hold the frame of a batch.)
-__device__ __forceinline__ unsigned int pack_run(int entry, int cells, int kept, int frame) {
-    return (unsigned int)entry | ((unsigned int)cells << 9) | ((unsigned int)kept << 15) |
-           ((unsigned int)frame << 21);
+// One run of a walk inside one block, as allocate records it for the
+// update (16 bytes):
+//   depth     the point's depth (f32 bits)
+//   meta      colour R | G << 8 | B << 16, frame of the batch << 24 (4 bits),
+//             axis direction bits << 28 (bit set: that axis steps by -1)
+//   code      first cell (voxel index in the block, 9 bits) | cells - 1 << 9
+//             (5 bits) | the axis of each step inside the block, 2 bits per
+//             step, << 14 (up to 21 steps) | kept cells << 56 (6 bits)
+// A line crosses at most 8 + 8 + 8 - 2 = 22 cells of an 8^3 block, so 21
+// steps and 5 bits of cell count always suffice.  The update enumerates the
+// run's cells from the code alone: it never repeats the walk's arithmetic.
+struct __align__(16) RunRecord {
+    unsigned int depth;
+    unsigned int meta;
+    unsigned int code_lo;
+    unsigned int code_hi;
+};
+
+constexpr int kStepShift = 14;
+constexpr int kKeptShift = 56;
+
+__device__ __forceinline__ unsigned long long run_code(int entry, int cells, unsigned long long steps, int kept) {
+    return (unsigned long long)entry | ((unsigned long long)(cells - 1) << 9) | (steps << kStepShift) |
+           ((unsigned long long)kept << kKeptShift);
 }
-__device__ __forceinline__ int run_entry(unsigned int info) { return (int)(info & 511u); }
-__device__ __forceinline__ int run_cells(unsigned int info) { return (int)((info >> 9) & 63u); }
-__device__ __forceinline__ int run_kept(unsigned int info) { return (int)((info >> 15) & 63u); }
-__device__ __forceinline__ int run_frame(unsigned int info) { return (int)((info >> 21) & 15u); }
+__device__ __forceinline__ unsigned long long record_code(const RunRecord& r) {
+    return (unsigned long long)r.code_lo | ((unsigned long long)r.code_hi << 32);
+}
+__device__ __forceinline__ int code_entry(unsigned long long c) { return (int)(c & 511u); }
+__device__ __forceinline__ int code_cells(unsigned long long c) { return (int)((c >> 9) & 31u) + 1; }
+__device__ __forceinline__ int code_kept(unsigned long long c) { return (int)((c >> kKeptShift) & 63u); }
+__device__ __forceinline__ int meta_frame(unsigned int m) { return (int)((m >> 24) & 15u); }
 
 // A wavefront's runs through one block, as recorded by allocate.
 struct __align__(16) Segment {
@@ -126,8 +145,8 @@ struct OwnerArgs {
     unsigned int* rescan;      // [table entries] items whose runs did not fit
     ItemDesc* desc;            // [table entries] per item
     Segment* segs;             // [kParts * seg_part_cap]
-    uint2* recs;               // [kParts * rec_part_cap] (pixel u | v << 16, packed run), allocate order
-    uint2* sorted;             // [kParts * rec_part_cap] the same records grouped by block
+    RunRecord* recs;           // [kParts * rec_part_cap] allocate order
+    RunRecord* sorted;         // [kParts * rec_part_cap] the same records grouped by block
     unsigned int item_part_cap, seg_part_cap, rec_part_cap;
     unsigned int parity;       // frame serial & 1
     unsigned int stamp;        // frame serial, never 0xFFFFFFFF
@@ -261,6 +280,44 @@ __device__ __forceinline__ bool centre_test(const BandWalk& w, const FrameArgs& 
     return sdf >= -trunc && sdf <= trunc;
 }
 
+// The same test with the pose's third column and the translation held in
+// registers (callers whose frame lives in LDS load them once per walk).
+struct DepthAxis {
+    float r2, r5, r8, t0, t1, t2;
+};
+
+__device__ __forceinline__ DepthAxis depth_axis(const FrameArgs& f) {
+    DepthAxis a;
+    a.r2 = f.R[2];
+    a.r5 = f.R[5];
+    a.r8 = f.R[8];
+    a.t0 = f.t[0];
+    a.t1 = f.t[1];
+    a.t2 = f.t[2];
+    return a;
+}
+
+__device__ __forceinline__ bool centre_test(const BandWalk& w, const DepthAxis& a, float vs, float trunc,
+                                            float& sdf) {
+    const float c0 = ((float)w.k0 + 0.5f) * vs;
+    const float c1 = ((float)w.k1 + 0.5f) * vs;
+    const float c2 = ((float)w.k2 + 0.5f) * vs;
+    const float zc = (a.r2 * (c0 - a.t0) + a.r5 * (c1 - a.t1)) + a.r8 * (c2 - a.t2);
+    sdf = w.d - zc;
+    return sdf >= -trunc && sdf <= trunc;
+}
+
+// The same test for cell (k0, k1, k2) of a point with depth d.
+__device__ __forceinline__ bool centre_test(int k0, int k1, int k2, float d, const DepthAxis& a, float vs,
+                                            float trunc, float& sdf) {
+    const float c0 = ((float)k0 + 0.5f) * vs;
+    const float c1 = ((float)k1 + 0.5f) * vs;
+    const float c2 = ((float)k2 + 0.5f) * vs;
+    const float zc = (a.r2 * (c0 - a.t0) + a.r5 * (c1 - a.t1)) + a.r8 * (c2 - a.t2);
+    sdf = d - zc;
+    return sdf >= -trunc && sdf <= trunc;
+}
+
 // Step to the next cell: the axis with the smallest boundary parameter (ties
 // to x, then y), until that parameter passes the segment end (1).
 __device__ __forceinline__ bool advance(BandWalk& w) {
@@ -292,7 +349,8 @@ __device__ __forceinline__ bool advance(BandWalk& w) {
 // parameter, ties to x, then y) and the same recomputation, done with
 // selects so the lanes of a wavefront never split on the axis.  Returns
 // false, leaving the walk unchanged, when the walk ends; otherwise sets
-// `crossed` if the step left the 8^3 block of the previous cell.
+// `crossed` if the step left the 8^3 block of the previous cell, and `axis`
+// to the axis stepped.
 // (The walk's fields pass through an empty asm statement before they are
 // selected: a select between two fields of one struct would otherwise be
 // folded into a load through a selected address, which keeps the whole
@@ -303,7 +361,7 @@ __device__ __forceinline__ T in_register(T x) {
     return x;
 }
 
-__device__ __forceinline__ bool advance_select(BandWalk& w, bool& crossed) {
+__device__ __forceinline__ bool advance_select(BandWalk& w, bool& crossed, int& axis) {
     const float tm0 = in_register(w.tm0), tm1 = in_register(w.tm1), tm2 = in_register(w.tm2);
     const int k0 = in_register(w.k0), k1 = in_register(w.k1), k2 = in_register(w.k2);
     const int s0 = in_register(w.s0), s1 = in_register(w.s1), s2 = in_register(w.s2);
@@ -330,6 +388,7 @@ __device__ __forceinline__ bool advance_select(BandWalk& w, bool& crossed) {
     w.tm1 = a1 ? t : tm1;
     w.tm2 = a2 ? t : tm2;
     crossed = more && (k >> 3) != (k_old >> 3);
+    axis = c2 ? 2 : (c1 ? 1 : 0);
     return more;
 }
 

@@ -95,8 +95,8 @@ constexpr unsigned int kNoKeyBase = 0xFFFFFFFEu;  // runs of a key the full tabl
 
 struct AllocLds {
     unsigned long long lkey[kWaves][kListCap];    // run list: block key,
-    unsigned int lpix[kWaves][kListCap];          //   pixel (u | v << 16),
-    unsigned int linfo[kWaves][kListCap];         //   packed run,
+    unsigned long long lcode[kWaves][kListCap];   //   run code (first cell, cells, steps, kept),
+    unsigned char llane[kWaves][kListCap];        //   the lane (pixel) that walked it,
     unsigned char lset[kWaves][kListCap];         //   its set slot
     unsigned long long skey[kWaves][kSetCap];     // set: key,
     unsigned int sruns[kWaves][kSetCap];          //   runs; after the reservation, the next record
@@ -107,8 +107,9 @@ struct AllocLds {
     unsigned int cnt[6];
 };
 
+// depth and meta: this lane's point, for the records of the runs it walked
 __device__ void flush_runs(AllocLds& L, int wave, int lane, int n, const VolumeArgs& vol, const OwnerArgs& own,
-                           unsigned int& misses) {
+                           unsigned int depth, unsigned int meta, unsigned int& misses) {
     for (int i = lane; i < kSetCap; i += 64) {
         L.skey[wave][i] = kEmptyKey;
         L.sruns[wave][i] = 0;
@@ -214,14 +215,24 @@ __device__ void flush_runs(AllocLds& L, int wave, int lane, int n, const VolumeA
     }
     wave_lds_fence();
     if (own.build_items) {
-        for (int i = lane; i < n; i += 64) {
+        for (int i0 = 0; i0 < n; i0 += 64) {          // wavefront-uniform: every lane shuffles
+            const int i = i0 + lane;
+            const int src = i < n ? (int)L.llane[wave][i] : 0;
+            const unsigned int d = __shfl(depth, src, 64), m = __shfl(meta, src, 64);
+            if (i >= n) continue;
             const int h = L.lset[wave][i];
             const unsigned int base = L.sruns[wave][h];
+            const unsigned long long code = L.lcode[wave][i];
             if (base == kNoKeyBase) {
-                misses += (unsigned int)run_kept(L.linfo[wave][i]);
+                misses += (unsigned int)code_kept(code);
             } else if (base != kNoBase) {
                 const unsigned int rec = atomicAdd(&L.sruns[wave][h], 1u);
-                own.recs[rec] = make_uint2(L.lpix[wave][i], L.linfo[wave][i]);
+                RunRecord r;
+                r.depth = d;
+                r.meta = m;
+                r.code_lo = (unsigned int)code;
+                r.code_hi = (unsigned int)(code >> 32);
+                own.recs[rec] = r;
             }
         }
     }
@@ -253,61 +264,82 @@ __global__ __launch_bounds__(kThreads) void k_allocate(BatchArgs B, VolumeArgs v
     const unsigned int pix = (unsigned int)v * (unsigned int)f.width + (unsigned int)u;
     BandWalk w;
     int cls = kInvalid;
-    if (u < f.width && v < f.height) cls = setup_walk(w, f.depth[pix], u, v, f, vol.trunc, vol.inv_vs);
+    float depth = 0.0f;
+    if (u < f.width && v < f.height) {
+        depth = f.depth[pix];
+        cls = setup_walk(w, depth, u, v, f, vol.trunc, vol.inv_vs);
+    }
     bool alive = cls == kValid;
-    // the current run: its block, first cell, cells visited and kept
+    // what the update needs of this point besides the run codes: depth,
+    // colour (when the frame has it: an update needs the same frame, colour
+    // included), frame of the batch and the directions of the stepping axes
+    unsigned int meta = 0;
+    if (alive && own.build_items) {
+        if (f.rgb) {
+            const uint8_t* c = f.rgb + 3 * (size_t)pix;
+            meta = (unsigned int)c[0] | ((unsigned int)c[1] << 8) | ((unsigned int)c[2] << 16);
+        }
+        meta |= ((unsigned int)fi << 24) | (w.s0 < 0 ? 1u << 28 : 0u) | (w.s1 < 0 ? 1u << 29 : 0u) |
+                (w.s2 < 0 ? 1u << 30 : 0u);
+    }
+    const unsigned int depth_bits = __float_as_uint(depth);
+    // the current run: its block, first cell, cells visited and kept, and
+    // the axis of each step taken inside the block
     unsigned long long cur = alive ? block_key(w.k0, w.k1, w.k2) : kEmptyKey;
     int entry = alive ? voxel_in_block(w.k0, w.k1, w.k2) : 0;
     int cells = 0, kept = 0;
+    unsigned long long steps = 0;
     unsigned int n_upd = 0, n_guard = 0, misses = 0;
     int visits = 0;
     int base = 0;                             // wavefront-uniform fill of the run list
-    const unsigned int xy = (unsigned int)u | ((unsigned int)v << 16);
 
     // one cell per lane per iteration; a run is emitted by the step that
     // leaves its block or ends the walk
     while (__any(alive)) {
         bool emit = false;
-        unsigned long long ekey = cur;
-        unsigned int einfo = 0;
+        unsigned long long ekey = cur, ecode = 0;
         if (alive) {
             float sdf;
             const bool keep = centre_test(w, f, vol.vs, vol.trunc, sdf);
             ++cells;
             kept += keep ? 1 : 0;
             bool crossed;
-            bool more = advance_select(w, crossed);
+            int axis;
+            bool more = advance_select(w, crossed, axis);
             if (++visits >= f.max_visits && more) {   // cut by the safety bound (never expected)
                 ++n_guard;
                 more = false;
             }
             if (!more || crossed) {
                 emit = kept > 0;
-                einfo = pack_run(entry, cells, kept, fi);
+                ecode = run_code(entry, cells, steps, kept);
                 n_upd += (unsigned int)kept;
                 cur = block_key(w.k0, w.k1, w.k2);
                 entry = voxel_in_block(w.k0, w.k1, w.k2);
                 cells = 0;
                 kept = 0;
+                steps = 0;
+            } else {
+                steps |= (unsigned long long)axis << (2 * (cells - 1));
             }
             alive = more;
         }
         const unsigned long long m = __ballot(emit);
         if (m) {
             if (base + 64 > kListCap) {
-                flush_runs(L, wave, lane, base, vol, own, misses);
+                flush_runs(L, wave, lane, base, vol, own, depth_bits, meta, misses);
                 base = 0;
             }
             if (emit) {
                 const int pos = base + __popcll(m & below);
                 L.lkey[wave][pos] = ekey;
-                L.lpix[wave][pos] = xy;
-                L.linfo[wave][pos] = einfo;
+                L.lcode[wave][pos] = ecode;
+                L.llane[wave][pos] = (unsigned char)lane;
             }
             base += __popcll(m);
         }
     }
-    if (base > 0) flush_runs(L, wave, lane, base, vol, own, misses);
+    if (base > 0) flush_runs(L, wave, lane, base, vol, own, depth_bits, meta, misses);
 
     const unsigned int c_valid = wave_sum(cls == kValid);
     const unsigned int c_near = wave_sum(cls == kNear);
@@ -470,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter_records(VolumeArgs vol, Ow
                 const int m = (lo + hi) >> 1;
                 if (s_end[wave][m] > p) hi = m; else lo = m + 1;
             }
-            own.sorted[s_dst[wave][lo] + p] = own.recs[s_src[wave][lo] + p];
+            own.sorted[s_dst[wave][lo] + p] = own.recs[s_src[wave][lo] + p];   // 16-byte records
         }
         wave_lds_fence();
     }
@@ -505,10 +537,16 @@ constexpr int kOwnerThreads = 128;
 // A run adds at most once to each voxel, so a chunk of up to 1023 runs keeps
 // every per-voxel count below 2^10 and every colour sum below 255 * 1023 <
 // 2^18: weight | R << 10 | G << 28 | B << 46 then adds without carries.
+// The normalised signed distance (in [-1, 1]) is summed in LDS as a 32-bit
+// integer in units of 2^-20: LDS float atomics issue far slower than integer
+// ones on this chip, and |sum| <= 1023 < 2^11 fits.  Rounding each term to
+// the nearest 2^-20 moves a mean by at most 2^-21.
 constexpr unsigned int kChunkRuns = 1023;
+constexpr float kTsdfScale = 1048576.0f;           // 2^20
+constexpr float kTsdfUnit = 1.0f / 1048576.0f;
 
 struct OwnerLds {
-    float tsdf[kBlockVoxels];
+    int tsdf[kBlockVoxels];
     unsigned long long wrgb[kBlockVoxels];
 };
 
@@ -524,8 +562,8 @@ __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, 
         const unsigned long long s = L.wrgb[j];
         const unsigned int cnt = (unsigned int)s & 1023u;
         if (!cnt) continue;
-        const float ts = L.tsdf[j];
-        L.tsdf[j] = 0.0f;
+        const float ts = (float)L.tsdf[j] * kTsdfUnit;
+        L.tsdf[j] = 0;
         L.wrgb[j] = 0;
         const size_t off = base + j;
         const float t0 = vol.tsdf[off], w0 = vol.weight[off], r0 = vol.r[off], g0 = vol.g[off], b0 = vol.b[off];
@@ -539,12 +577,12 @@ __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, 
 
 __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ OwnerLds L;
-    __shared__ FrameArgs s_frames[kMaxBatch];               // per-record frame lookups from LDS
+    __shared__ DepthAxis s_axis[kMaxBatch];                 // per-record frame lookups from LDS
     __shared__ unsigned int s_item[2];                      // alternates: read k while k + 1 is written
     const int tid = threadIdx.x;
-    if (tid < B.n) s_frames[tid] = B.f[tid];
+    if (tid < B.n) s_axis[tid] = depth_axis(B.f[tid]);
     for (int j = tid; j < kBlockVoxels; j += kOwnerThreads) {
-        L.tsdf[j] = 0.0f;
+        L.tsdf[j] = 0;
         L.wrgb[j] = 0;
     }
     FrameCounters& fc = own.fc[own.parity];
@@ -563,7 +601,7 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
         if (tid == 0) own.rec_count[d.pad[0]] = 0;
         if (d.idx >= vol.capacity) {                         // refused a pool index: count, not store
             for (unsigned int r = tid; r < d.rec_count; r += kOwnerThreads)
-                misses += (unsigned int)run_kept(own.sorted[d.rec_first + r].y);
+                misses += (unsigned int)code_kept(record_code(own.sorted[d.rec_first + r]));
             continue;
         }
         int bx, by, bz;
@@ -572,26 +610,38 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
         const size_t base = (size_t)d.idx * kBlockVoxels;
         for (unsigned int c0 = 0; c0 < d.rec_count; c0 += kChunkRuns) {
             const unsigned int c1 = min(d.rec_count, c0 + kChunkRuns);
-            for (unsigned int r = c0 + tid; r < c1; r += kOwnerThreads) {
-                const uint2 rec = own.sorted[d.rec_first + r];
-                const FrameArgs& f = s_frames[run_frame(rec.y)];
-                const int u = (int)(rec.x & 0xFFFFu), v = (int)(rec.x >> 16);
-                const size_t pix = (size_t)v * f.width + u;
-                BandWalk w;
-                if (setup_walk(w, f.depth[pix], u, v, f, vol.trunc, vol.inv_vs) != kValid) continue;  // cannot happen
-                const unsigned long long c = packed_colour(f, pix);
-                const int e = run_entry(rec.y);
-                resume_at(w, lo0 + (e & 7), lo1 + ((e >> 3) & 7), lo2 + (e >> 6));
-                const int cells = run_cells(rec.y);
+            // each thread takes a contiguous share of the chunk: runs next to
+            // each other come from neighbouring pixels and hit the same
+            // voxels, so spreading the lanes apart spreads their LDS atomics
+            const unsigned int share = (c1 - c0 + kOwnerThreads - 1) / kOwnerThreads;
+            const unsigned int r0 = c0 + tid * share, r1 = min(c1, r0 + share);
+            for (unsigned int r = r0; r < r1; ++r) {
+                const RunRecord rec = own.sorted[d.rec_first + r];
+                const float dep = __uint_as_float(rec.depth);
+                const DepthAxis ax = s_axis[meta_frame(rec.meta)];
+                const unsigned long long c = 1ull | ((unsigned long long)(rec.meta & 0xFFu) << 10) |
+                                             ((unsigned long long)((rec.meta >> 8) & 0xFFu) << 28) |
+                                             ((unsigned long long)((rec.meta >> 16) & 0xFFu) << 46);
+                const int d0 = (rec.meta >> 28) & 1u ? -1 : 1;
+                const int d1 = (rec.meta >> 29) & 1u ? -1 : 1;
+                const int d2 = (rec.meta >> 30) & 1u ? -1 : 1;
+                const unsigned long long code = record_code(rec);
+                const int e = code_entry(code), cells = code_cells(code);
+                int k0 = lo0 + (e & 7), k1 = lo1 + ((e >> 3) & 7), k2 = lo2 + (e >> 6);
+                unsigned long long st = code >> kStepShift;
                 for (int q = 0;;) {
                     float sdf;
-                    if (centre_test(w, f, vol.vs, vol.trunc, sdf)) {
-                        const int j = voxel_in_block(w.k0, w.k1, w.k2);
-                        atomicAdd(L.tsdf + j, sdf * vol.inv_trunc);
+                    if (centre_test(k0, k1, k2, dep, ax, vol.vs, vol.trunc, sdf)) {
+                        const int j = (k0 & 7) | ((k1 & 7) << 3) | ((k2 & 7) << 6);
+                        atomicAdd(L.tsdf + j, __float2int_rn(sdf * vol.inv_trunc * kTsdfScale));
                         atomicAdd(L.wrgb + j, c);
                     }
-                    bool crossed;
-                    if (++q >= cells || !advance_select(w, crossed)) break;
+                    if (++q >= cells) break;
+                    const int axis = (int)(st & 3u);
+                    st >>= 2;
+                    k0 += axis == 0 ? d0 : 0;
+                    k1 += axis == 1 ? d1 : 0;
+                    k2 += axis == 2 ? d2 : 0;
                 }
             }
             __syncthreads();
@@ -764,7 +814,8 @@ __global__ __launch_bounds__(kThreads) void k_update_rays(BatchArgs B, VolumeArg
                 }
             }
             bool crossed;
-            if (++visits >= f.max_visits || !advance_select(w, crossed)) break;
+            int axis;
+            if (++visits >= f.max_visits || !advance_select(w, crossed, axis)) break;
         }
     }
     const unsigned int c_miss = wave_sum(n_miss);
