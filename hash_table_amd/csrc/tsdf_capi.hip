@@ -25,7 +25,7 @@ constexpr int64_t kRunsPerPixel = 4;                // record capacity per pixel
 // Owner-mode scratch layout: per-frame counters, per-table-entry arrays,
 // then the per-frame segment and record buffers (kParts partitions each).
 struct ScratchLayout {
-    size_t fc, desc, segs, recs, sorted, items, items_spill, item_of, rec_count, rescan, bytes;
+    size_t fc, desc, segs, recs, seg_list, blk_count, items, items_spill, item_of, rescan, bytes;
     unsigned int item_part_cap, seg_part_cap, rec_part_cap;
 };
 
@@ -44,15 +44,15 @@ ScratchLayout scratch_layout(int64_t entries, int64_t frame_pixels) {
     o += sizeof(Segment) * (size_t)kParts * L.seg_part_cap;
     L.recs = o;
     o += sizeof(RunRecord) * (size_t)kParts * L.rec_part_cap;
-    L.sorted = o;
-    o += sizeof(RunRecord) * (size_t)kParts * L.rec_part_cap;
+    L.seg_list = o;                   // 8-byte pieces
+    o += sizeof(uint2) * (size_t)kParts * L.seg_part_cap;
+    L.blk_count = o;
+    o += 8 * (size_t)entries;
     L.items = o;
     o += 4 * (size_t)kParts * L.item_part_cap;
     L.items_spill = o;
     o += 4 * (size_t)entries;
     L.item_of = o;
-    o += 4 * (size_t)entries;
-    L.rec_count = o;
     o += 4 * (size_t)entries;
     L.rescan = o;
     o += 4 * (size_t)entries;
@@ -177,12 +177,12 @@ OwnerArgs owner_args(const tsdf_volume* h, unsigned int serial) {
     o.items = reinterpret_cast<unsigned int*>(base + L.items);
     o.items_spill = reinterpret_cast<unsigned int*>(base + L.items_spill);
     o.item_of = reinterpret_cast<unsigned int*>(base + L.item_of);
-    o.rec_count = reinterpret_cast<unsigned int*>(base + L.rec_count);
+    o.blk_count = reinterpret_cast<unsigned long long*>(base + L.blk_count);
     o.rescan = reinterpret_cast<unsigned int*>(base + L.rescan);
     o.desc = reinterpret_cast<ItemDesc*>(base + L.desc);
     o.segs = reinterpret_cast<Segment*>(base + L.segs);
     o.recs = reinterpret_cast<RunRecord*>(base + L.recs);
-    o.sorted = reinterpret_cast<RunRecord*>(base + L.sorted);
+    o.seg_list = reinterpret_cast<uint2*>(base + L.seg_list);
     o.item_part_cap = L.item_part_cap;
     o.seg_part_cap = L.seg_part_cap;
     o.rec_part_cap = L.rec_part_cap;

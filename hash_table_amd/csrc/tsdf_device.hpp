@@ -98,21 +98,27 @@ __device__ __forceinline__ int code_cells(unsigned long long c) { return (int)((
 __device__ __forceinline__ int code_kept(unsigned long long c) { return (int)((c >> kKeptShift) & 63u); }
 __device__ __forceinline__ int meta_frame(unsigned int m) { return (int)((m >> 24) & 15u); }
 
-// A wavefront's runs through one block, as recorded by allocate.
+// A wavefront's runs through one block, as recorded by allocate.  One
+// 64-bit atomic on the block's counter (segments << 32 | runs) gives both
+// the segment's position among the block's segments and its first run's
+// position among the block's runs, so in segment order block_off is the
+// running total of the runs before it.
 struct __align__(16) Segment {
-    unsigned int slot;        // table slot of the block
-    unsigned int rec_base;    // its first record in the unsorted record buffer
-    unsigned int runs;        // records
-    unsigned int block_off;   // where its records start among the block's records
+    unsigned int slot;        // table slot of the block (kNoSlot: refused for lack of space)
+    unsigned int rec_base;    // its first record in the record buffer
+    unsigned int block_off;   // runs of the block's earlier segments
+    unsigned int seg_pos;     // its position among the block's segments
 };
 
-// A block touched by the frame, as the owner update reads it.
+// A block touched by the call, as the owner update reads it.
 struct __align__(16) ItemDesc {
     unsigned long long key;
     unsigned int idx;         // pool index (>= capacity: none)
-    unsigned int rec_first;   // first record in the block-ordered buffer
-    unsigned int rec_count;   // | kSegOverflow: records did not fit, rescan
-    unsigned int pad[3];
+    unsigned int rec_count;   // runs | kSegOverflow: runs did not fit, rescan
+    unsigned int seg_first;   // its first segment in the block-ordered segment list
+    unsigned int seg_count;
+    unsigned int slot;
+    unsigned int pad;
 };
 
 // Per-frame counters of the owner update, in the caller's scratch buffer,
@@ -128,7 +134,7 @@ struct FrameCounters {
     unsigned int items[kParts];         // blocks first touched, per partition
     unsigned int items_spill;           // blocks beyond their partition's share
     unsigned int items_total;           // all blocks (set when the blocks are placed)
-    unsigned long long placed;          // records given to blocks
+    unsigned long long placed;          // segments given to blocks
     unsigned int n_rescan;              // blocks whose runs did not fit (rescanned)
     unsigned int pad[27];
     unsigned int fetch[kXcds * kFetchStride];   // next item of XCD x at fetch[x * kFetchStride]
@@ -141,12 +147,12 @@ struct OwnerArgs {
     unsigned int* items;       // [kParts * item_part_cap] first-touched slots, by partition
     unsigned int* items_spill; // [table entries] slots beyond a partition's share
     unsigned int* item_of;     // [table entries] slot -> its item this frame
-    unsigned int* rec_count;   // [table entries] runs per slot this frame (| kSegOverflow)
+    unsigned long long* blk_count;  // [table entries] segments << 32 | runs (| kSegOverflow) per slot
     unsigned int* rescan;      // [table entries] items whose runs did not fit
     ItemDesc* desc;            // [table entries] per item
-    Segment* segs;             // [kParts * seg_part_cap]
-    RunRecord* recs;           // [kParts * rec_part_cap] allocate order
-    RunRecord* sorted;         // [kParts * rec_part_cap] the same records grouped by block
+    Segment* segs;             // [kParts * seg_part_cap] allocate order
+    uint2* seg_list;           // [kParts * seg_part_cap] (rec_base, block_off), grouped by block
+    RunRecord* recs;           // [kParts * rec_part_cap] allocate order (read in place)
     unsigned int item_part_cap, seg_part_cap, rec_part_cap;
     unsigned int parity;       // frame serial & 1
     unsigned int stamp;        // frame serial, never 0xFFFFFFFF

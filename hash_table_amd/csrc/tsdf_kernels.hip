@@ -190,23 +190,24 @@ __device__ void flush_runs(AllocLds& L, int wave, int lane, int n, const VolumeA
             const unsigned int rec = (unsigned int)r0 + (x - runs);
             Segment* segs = own.segs + (size_t)part * own.seg_part_cap;
             if (seg < own.seg_part_cap && (unsigned long long)rec + runs <= own.rec_part_cap) {
+                const unsigned long long bc = atomicAdd(own.blk_count + slot, (1ull << 32) | runs);
                 Segment sg;
                 sg.slot = slot;
                 sg.rec_base = part * own.rec_part_cap + rec;
-                sg.runs = runs;
-                sg.block_off = atomicAdd(own.rec_count + slot, runs) & ~kSegOverflow;
+                sg.block_off = (unsigned int)bc & ~kSegOverflow;
+                sg.seg_pos = (unsigned int)(bc >> 32);
                 segs[seg] = sg;
                 L.sruns[wave][h] = sg.rec_base;
             } else {                                 // out of space: the update rescans the block
-                if (seg < own.seg_part_cap) {        // the scatter reads every reserved segment
+                if (seg < own.seg_part_cap) {        // the placing pass reads every reserved segment
                     Segment sg;
                     sg.slot = kNoSlot;
                     sg.rec_base = 0;
-                    sg.runs = 0;
                     sg.block_off = 0;
+                    sg.seg_pos = 0;
                     segs[seg] = sg;
                 }
-                atomicOr(own.rec_count + slot, kSegOverflow);
+                atomicOr(own.blk_count + slot, (unsigned long long)kSegOverflow);
                 L.sruns[wave][h] = kNoBase;
             }
         } else if (has) {                            // the full table refused the key: its
@@ -369,10 +370,11 @@ __global__ __launch_bounds__(kThreads) void k_allocate(BatchArgs B, VolumeArgs v
 }
 
 // ---------------------------------------------------------------------------
-// grouping the frame's run records by block.  k_place_items gives every
-// touched block a descriptor and a contiguous record range (one atomic per
-// 256 blocks); k_scatter_records copies each segment's records into its
-// block's range (the segment knows its offset there).
+// grouping the call's run records by block.  k_place_items gives every
+// touched block a descriptor and a contiguous range of the block-ordered
+// segment list (one atomic per 256 blocks); k_place_segments puts each
+// segment's (first record, runs before it) at its position in that range.
+// The records themselves stay where allocate wrote them.
 // ---------------------------------------------------------------------------
 // prefix over the partitions' counts (+ the spill list): pre[p] = first
 // global index of partition p, pre[kParts + 1] = total
@@ -409,13 +411,15 @@ __global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerA
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (unsigned int b = blockIdx.x * kThreads; b < n; b += gridDim.x * kThreads) {
         const unsigned int i = b + tid;
-        unsigned int slot = 0, rc = 0, cnt = 0;
+        unsigned int slot = 0, rc = 0, nseg = 0, cnt = 0;
         if (i < n) {
             const int p = find_partition(s_pre, i);
             slot = p < kParts ? own.items[(size_t)p * own.item_part_cap + (i - s_pre[p])]
                               : own.items_spill[i - s_pre[kParts]];
-            rc = own.rec_count[slot];
-            cnt = (rc & kSegOverflow) ? 0u : rc;
+            const unsigned long long bc = own.blk_count[slot];
+            rc = (unsigned int)bc;
+            nseg = (unsigned int)(bc >> 32);
+            cnt = (rc & kSegOverflow) ? 0u : nseg;
         }
         unsigned int x = cnt;
 #pragma unroll
@@ -440,11 +444,11 @@ __global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerA
             ItemDesc d;
             d.key = e.x;
             d.idx = (unsigned int)e.y;
-            d.rec_first = s_base + s_wave[wave] + x - cnt;
             d.rec_count = rc;
-            d.pad[0] = slot;
-            d.pad[1] = 0;
-            d.pad[2] = 0;
+            d.seg_first = s_base + s_wave[wave] + x - cnt;
+            d.seg_count = cnt;
+            d.slot = slot;
+            d.pad = 0;
             own.desc[i] = d;
             own.item_of[slot] = i;
             if (rc & kSegOverflow) own.rescan[atomicAdd(&fc.n_rescan, 1u)] = i;
@@ -453,58 +457,21 @@ __global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerA
     }
 }
 
-// Each wavefront takes 64 segments, lays their runs end to end (a prefix
-// over the lanes) and copies the records with every lane busy: record p of
-// the group belongs to the first segment whose end lies beyond p.
-__global__ __launch_bounds__(kThreads) void k_scatter_records(VolumeArgs vol, OwnerArgs own) {
+__global__ __launch_bounds__(kThreads) void k_place_segments(VolumeArgs vol, OwnerArgs own) {
     __shared__ unsigned int s_cnt[kParts];
     __shared__ unsigned int s_pre[kParts + 2];
-    __shared__ unsigned int s_end[kWaves][64];
-    __shared__ unsigned int s_src[kWaves][64];
-    __shared__ unsigned int s_dst[kWaves][64];
     FrameCounters& fc = own.fc[own.parity];
     if (threadIdx.x < kParts) s_cnt[threadIdx.x] = (unsigned int)(fc.segrec[threadIdx.x] >> 32);
     __syncthreads();
     partition_prefix(s_cnt, own.seg_part_cap, 0, s_pre);
     const unsigned int n = s_pre[kParts];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const unsigned int step = gridDim.x * kThreads;
-    for (unsigned int j0 = blockIdx.x * kThreads + wave * 64; j0 < n; j0 += step) {
-        const unsigned int j = j0 + lane;
-        unsigned int cnt = 0, src = 0, dst = 0;
-        if (j < n) {
-            const int p = find_partition(s_pre, j);
-            const Segment sg = own.segs[(size_t)p * own.seg_part_cap + (j - s_pre[p])];
-            if (sg.slot != kNoSlot) {                          // refused for lack of space: nothing
-                const ItemDesc& d = own.desc[own.item_of[sg.slot]];
-                const unsigned int rc = d.rec_count;
-                if (!(rc & kSegOverflow)) {                     // else the block is rescanned
-                    cnt = sg.runs;
-                    src = sg.rec_base;
-                    dst = d.rec_first + sg.block_off;
-                }
-            }
-        }
-        unsigned int x = cnt;                                  // inclusive prefix over the lanes
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const unsigned int y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
-        }
-        const unsigned int total = __shfl(x, 63, 64);
-        s_end[wave][lane] = x;
-        s_src[wave][lane] = src - (x - cnt);                   // + p gives the record (mod 2^32)
-        s_dst[wave][lane] = dst - (x - cnt);
-        wave_lds_fence();
-        for (unsigned int p = lane; p < total; p += 64) {
-            int lo = 0, hi = 63;                               // first lane with end > p
-            while (lo < hi) {
-                const int m = (lo + hi) >> 1;
-                if (s_end[wave][m] > p) hi = m; else lo = m + 1;
-            }
-            own.sorted[s_dst[wave][lo] + p] = own.recs[s_src[wave][lo] + p];   // 16-byte records
-        }
-        wave_lds_fence();
+    for (unsigned int j = blockIdx.x * kThreads + threadIdx.x; j < n; j += gridDim.x * kThreads) {
+        const int p = find_partition(s_pre, j);
+        const Segment sg = own.segs[(size_t)p * own.seg_part_cap + (j - s_pre[p])];
+        if (sg.slot == kNoSlot) continue;                       // refused for lack of space
+        const ItemDesc& d = own.desc[own.item_of[sg.slot]];
+        if (d.rec_count & kSegOverflow) continue;               // the block is rescanned
+        own.seg_list[d.seg_first + sg.seg_pos] = make_uint2(sg.rec_base, sg.block_off);
     }
 }
 
@@ -519,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void k_discard_items(VolumeArgs vol, Owne
         const int p = find_partition(s_pre, i);
         const unsigned int slot = p < kParts ? own.items[(size_t)p * own.item_part_cap + (i - s_pre[p])]
                                              : own.items_spill[i - s_pre[kParts]];
-        own.rec_count[slot] = 0;
+        own.blk_count[slot] = 0;
     }
 }
 
@@ -542,6 +509,7 @@ constexpr int kOwnerThreads = 128;
 // ones on this chip, and |sum| <= 1023 < 2^11 fits.  Rounding each term to
 // the nearest 2^-20 moves a mean by at most 2^-21.
 constexpr unsigned int kChunkRuns = 1023;
+constexpr int kSegWindow = 512;                      // segments of a block held in LDS at once
 constexpr float kTsdfScale = 1048576.0f;           // 2^20
 constexpr float kTsdfUnit = 1.0f / 1048576.0f;
 
@@ -579,6 +547,8 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
     __shared__ OwnerLds L;
     __shared__ DepthAxis s_axis[kMaxBatch];                 // per-record frame lookups from LDS
     __shared__ unsigned int s_item[2];                      // alternates: read k while k + 1 is written
+    __shared__ unsigned int s_rec[kSegWindow];
+    __shared__ unsigned int s_off[kSegWindow + 1];
     const int tid = threadIdx.x;
     if (tid < B.n) s_axis[tid] = depth_axis(B.f[tid]);
     for (int j = tid; j < kBlockVoxels; j += kOwnerThreads) {
@@ -598,55 +568,81 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
         if (it >= n_items) break;
         const ItemDesc d = own.desc[it];
         if (d.rec_count & kSegOverflow) continue;            // rescanned (and its count cleared) later
-        if (tid == 0) own.rec_count[d.pad[0]] = 0;
-        if (d.idx >= vol.capacity) {                         // refused a pool index: count, not store
-            for (unsigned int r = tid; r < d.rec_count; r += kOwnerThreads)
-                misses += (unsigned int)code_kept(record_code(own.sorted[d.rec_first + r]));
-            continue;
-        }
+        if (tid == 0) own.blk_count[d.slot] = 0;
+        const bool store = d.idx < vol.capacity;             // else refused a pool index: count, not store
         int bx, by, bz;
         unpack_key(d.key, bx, by, bz);
         const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
         const size_t base = (size_t)d.idx * kBlockVoxels;
-        for (unsigned int c0 = 0; c0 < d.rec_count; c0 += kChunkRuns) {
-            const unsigned int c1 = min(d.rec_count, c0 + kChunkRuns);
-            // each thread takes a contiguous share of the chunk: runs next to
-            // each other come from neighbouring pixels and hit the same
-            // voxels, so spreading the lanes apart spreads their LDS atomics
-            const unsigned int share = (c1 - c0 + kOwnerThreads - 1) / kOwnerThreads;
-            const unsigned int r0 = c0 + tid * share, r1 = min(c1, r0 + share);
-            for (unsigned int r = r0; r < r1; ++r) {
-                const RunRecord rec = own.sorted[d.rec_first + r];
-                const float dep = __uint_as_float(rec.depth);
-                const DepthAxis ax = s_axis[meta_frame(rec.meta)];
-                const unsigned long long c = 1ull | ((unsigned long long)(rec.meta & 0xFFu) << 10) |
-                                             ((unsigned long long)((rec.meta >> 8) & 0xFFu) << 28) |
-                                             ((unsigned long long)((rec.meta >> 16) & 0xFFu) << 46);
-                const int d0 = (rec.meta >> 28) & 1u ? -1 : 1;
-                const int d1 = (rec.meta >> 29) & 1u ? -1 : 1;
-                const int d2 = (rec.meta >> 30) & 1u ? -1 : 1;
-                const unsigned long long code = record_code(rec);
-                const int e = code_entry(code), cells = code_cells(code);
-                int k0 = lo0 + (e & 7), k1 = lo1 + ((e >> 3) & 7), k2 = lo2 + (e >> 6);
-                unsigned long long st = code >> kStepShift;
-                for (int q = 0;;) {
-                    float sdf;
-                    if (centre_test(k0, k1, k2, dep, ax, vol.vs, vol.trunc, sdf)) {
-                        const int j = (k0 & 7) | ((k1 & 7) << 3) | ((k2 & 7) << 6);
-                        atomicAdd(L.tsdf + j, __float2int_rn(sdf * vol.inv_trunc * kTsdfScale));
-                        atomicAdd(L.wrgb + j, c);
-                    }
-                    if (++q >= cells) break;
-                    const int axis = (int)(st & 3u);
-                    st >>= 2;
-                    k0 += axis == 0 ? d0 : 0;
-                    k1 += axis == 1 ? d1 : 0;
-                    k2 += axis == 2 ? d2 : 0;
+        // the block's segments, a window at a time: segment i holds runs
+        // [s_off[i], s_off[i + 1]) of the block, stored from s_rec[i] on
+        for (unsigned int w0 = 0; w0 < d.seg_count; w0 += kSegWindow) {
+            const unsigned int wn = min(d.seg_count - w0, (unsigned int)kSegWindow);
+            for (unsigned int i = tid; i <= wn; i += kOwnerThreads) {
+                if (i < wn) {
+                    const uint2 e = own.seg_list[d.seg_first + w0 + i];
+                    s_rec[i] = e.x;
+                    s_off[i] = e.y;
+                } else {
+                    s_off[i] = w0 + wn < d.seg_count ? own.seg_list[d.seg_first + w0 + wn].y : d.rec_count;
                 }
             }
             __syncthreads();
-            flush_owner(L, vol, base);
-            __syncthreads();
+            const unsigned int wr0 = s_off[0], wr1 = s_off[wn];
+            for (unsigned int c0 = wr0; c0 < wr1; c0 += kChunkRuns) {
+                const unsigned int c1 = min(wr1, c0 + kChunkRuns);
+                // each thread takes a contiguous share of the chunk: runs next
+                // to each other come from neighbouring pixels and hit the same
+                // voxels, so spreading the lanes apart spreads their LDS atomics
+                const unsigned int share = (c1 - c0 + kOwnerThreads - 1) / kOwnerThreads;
+                const unsigned int r0 = c0 + tid * share, r1 = min(c1, r0 + share);
+                unsigned int si = 0;
+                if (r0 < r1) {                               // last segment starting at or before r0
+                    unsigned int lo = 0, hi = wn - 1;
+                    while (lo < hi) {
+                        const unsigned int m = (lo + hi + 1) >> 1;
+                        if (s_off[m] <= r0) lo = m; else hi = m - 1;
+                    }
+                    si = lo;
+                }
+                for (unsigned int r = r0; r < r1; ++r) {
+                    while (r >= s_off[si + 1]) ++si;         // s_off[wn] = wr1 > r ends it
+                    const RunRecord rec = own.recs[s_rec[si] + (r - s_off[si])];
+                    const unsigned long long code = record_code(rec);
+                    if (!store) {
+                        misses += (unsigned int)code_kept(code);
+                        continue;
+                    }
+                    const float dep = __uint_as_float(rec.depth);
+                    const DepthAxis ax = s_axis[meta_frame(rec.meta)];
+                    const unsigned long long c = 1ull | ((unsigned long long)(rec.meta & 0xFFu) << 10) |
+                                                 ((unsigned long long)((rec.meta >> 8) & 0xFFu) << 28) |
+                                                 ((unsigned long long)((rec.meta >> 16) & 0xFFu) << 46);
+                    const int d0 = (rec.meta >> 28) & 1u ? -1 : 1;
+                    const int d1 = (rec.meta >> 29) & 1u ? -1 : 1;
+                    const int d2 = (rec.meta >> 30) & 1u ? -1 : 1;
+                    const int e = code_entry(code), cells = code_cells(code);
+                    int k0 = lo0 + (e & 7), k1 = lo1 + ((e >> 3) & 7), k2 = lo2 + (e >> 6);
+                    unsigned long long st = code >> kStepShift;
+                    for (int q = 0;;) {
+                        float sdf;
+                        if (centre_test(k0, k1, k2, dep, ax, vol.vs, vol.trunc, sdf)) {
+                            const int j = (k0 & 7) | ((k1 & 7) << 3) | ((k2 & 7) << 6);
+                            atomicAdd(L.tsdf + j, __float2int_rn(sdf * vol.inv_trunc * kTsdfScale));
+                            atomicAdd(L.wrgb + j, c);
+                        }
+                        if (++q >= cells) break;
+                        const int axis = (int)(st & 3u);
+                        st >>= 2;
+                        k0 += axis == 0 ? d0 : 0;
+                        k1 += axis == 1 ? d1 : 0;
+                        k2 += axis == 2 ? d2 : 0;
+                    }
+                }
+                __syncthreads();
+                if (store) flush_owner(L, vol, base);
+                __syncthreads();                             // also: the window may be reloaded
+            }
         }
     }
     const unsigned int c_miss = wave_sum(misses);
@@ -744,7 +740,7 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_rescan(BatchArgs B, Vo
             misses += n_kept;               // block refused a pool index: counted, not stored
         }
         if (threadIdx.x == 0) {
-            own.rec_count[d.pad[0]] = 0;
+            own.blk_count[d.slot] = 0;
             ++done;
         }
         __syncthreads();
@@ -899,7 +895,7 @@ bool launched() { return hipGetLastError() == hipSuccess; }
 int tile_grid(const FrameArgs& f) { return f.tiles_per_xcd * kXcds; }
 
 const char* kernel_name(int id) {
-    static const char* const names[kKernelIds] = {"k_allocate",      "k_place_items", "k_scatter_records",
+    static const char* const names[kKernelIds] = {"k_allocate",      "k_place_items", "k_place_segments",
                                                   "k_update_owner",  "k_update_rescan", "k_discard_items",
                                                   "k_update_rays"};
     return id >= 0 && id < kKernelIds ? names[id] : "unknown";
@@ -921,7 +917,7 @@ bool launch_allocate(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o
 bool launch_update_owner(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, int grid, hipStream_t s,
                          const LaunchTimer* t) {
     TSDF_TIMED_LAUNCH(t, kKPlaceItems, k_place_items, dim3(256), dim3(kThreads), s, v, o);
-    TSDF_TIMED_LAUNCH(t, kKScatterRecords, k_scatter_records, dim3(1024), dim3(kThreads), s, v, o);
+    TSDF_TIMED_LAUNCH(t, kKPlaceSegments, k_place_segments, dim3(1024), dim3(kThreads), s, v, o);
     TSDF_TIMED_LAUNCH(t, kKUpdateOwner, k_update_owner, dim3(grid), dim3(kOwnerThreads), s, b, v, o);
     TSDF_TIMED_LAUNCH(t, kKUpdateRescan, k_update_rescan, dim3(256), dim3(kOwnerThreads), s, b, v, o);
     return launched();
@@ -950,8 +946,8 @@ bool launch_update_rays(const BatchArgs& b, const VolumeArgs& v, hipStream_t s, 
 bool launch_init(const VolumeArgs& v, unsigned long long table_entries, bool whole_pool, const OwnerArgs* own,
                  hipStream_t s) {
     if (own) {
-        hipLaunchKernelGGL(k_zero_words, dim3(grid_for(table_entries)), dim3(kThreads), 0, s, own->rec_count,
-                           table_entries);
+        hipLaunchKernelGGL(k_zero_words, dim3(grid_for(2 * table_entries)), dim3(kThreads), 0, s,
+                           reinterpret_cast<unsigned int*>(own->blk_count), 2 * table_entries);
         hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(kThreads), 0, s, reinterpret_cast<unsigned int*>(own->fc),
                            (unsigned long long)(2 * sizeof(FrameCounters) / 4));
     }

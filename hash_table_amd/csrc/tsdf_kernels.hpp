@@ -13,7 +13,7 @@ namespace tsdf {
 enum KernelId {
     kKAllocate = 0,
     kKPlaceItems,
-    kKScatterRecords,
+    kKPlaceSegments,
     kKUpdateOwner,
     kKUpdateRescan,
     kKDiscardItems,

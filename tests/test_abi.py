@@ -45,8 +45,8 @@ def test_scratch_sizing():
     def expect(entries, px):
         seg_part, rec_part = -(-px // 64), -(-4 * px // 64)
         item_part = max(64, entries // 32)
-        return (2 * 1920 + 32 * entries + 16 * 64 * seg_part + 2 * 16 * 64 * rec_part + 4 * 64 * item_part
-                + 16 * entries)
+        return (2 * 1920 + 32 * entries + 16 * 64 * seg_part + 16 * 64 * rec_part + 8 * 64 * seg_part
+                + 8 * entries + 4 * 64 * item_part + 12 * entries)
     owner = tsdf.tsdf_config(0.01, 0.04, 4096, 0, tsdf.TSDF_UPDATE_OWNER, 1000)
     assert tsdf.tsdf_scratch_bytes(owner) == expect(8192, 1000)
     default = tsdf.tsdf_config(0.01, 0.04, 4096, 0, tsdf.TSDF_UPDATE_OWNER, 0)

@@ -196,6 +196,19 @@ def test_record_overflow_rescans_exactly():
     assert_parity(st, coords, arrays, o)
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_dense_blocks_span_several_segment_windows(mode):
+    # planes 0.1 m in front of a 640 x 480 camera: a 4 cm block covers about
+    # 210 x 210 pixels, so one block gathers ~44,000 runs from ~700 wavefront
+    # segments per frame -- more than one LDS window of segments and more
+    # than one 1023-run chunk of packed sums in the owner update
+    frames = [scenes.plane_frame(seed=s, W=640, H=480, depth=d, fx=525.0, fy=525.0, cx=319.5, cy=239.5)
+              for s, d in ((3, 0.1), (4, 0.1037))]
+    _, st, coords, arrays, o = run_both(frames, 0.005, 0.02, 4096, mode=mode, batch=2)
+    assert st["fallback_blocks"] == 0
+    assert_parity(st, coords, arrays, o)
+
+
 def test_batch_limits():
     from hash_table_amd import tsdf
     wl = scenes.workload("plane64x48")
@@ -401,7 +414,7 @@ def test_kernel_timing(mode):
     vol.integrate(frames[0])
     kt = vol.kernel_times()
     say(f"  kernel times ({mode}): {kt}")
-    expect = {"k_allocate", "k_place_items", "k_scatter_records", "k_update_owner", "k_update_rescan"} \
+    expect = {"k_allocate", "k_place_items", "k_place_segments", "k_update_owner", "k_update_rescan"} \
         if mode == "owner" else {"k_allocate", "k_update_rays"}
     assert set(kt) == expect
     for v in kt.values():
