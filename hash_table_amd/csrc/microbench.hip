@@ -2,7 +2,7 @@
 // float atomic-add rate by access pattern, 64-bit compare-exchange rate.
 #include <hip/hip_runtime.h>
 
-#include "../../include/tsdf_microbench.h"
+#include "tsdf_microbench.h"
 
 namespace {
 

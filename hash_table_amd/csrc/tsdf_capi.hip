@@ -11,7 +11,7 @@
 #include <new>
 #include <vector>
 
-#include "../../include/tsdf.h"
+#include "tsdf.h"
 #include "tsdf_kernels.hpp"
 
 using namespace tsdf;

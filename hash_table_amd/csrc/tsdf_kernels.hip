@@ -240,7 +240,8 @@ __device__ void flush_runs(AllocLds& L, int wave, int lane, int n, const VolumeA
     wave_lds_fence();
 }
 
-__global__ __launch_bounds__(kThreads) void k_allocate(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
+// (at least 5 wavefronts per SIMD: the LDS of five workgroups fits a CU)
+__global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ AllocLds L;
     const int fi = blockIdx.x / B.tile_grid;                 // frame of this workgroup
     const FrameArgs& f = B.f[fi];
