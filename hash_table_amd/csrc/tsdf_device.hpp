@@ -357,34 +357,32 @@ __device__ __forceinline__ bool advance(BandWalk& w) {
 // false, leaving the walk unchanged, when the walk ends; otherwise sets
 // `crossed` if the step left the 8^3 block of the previous cell, and `axis`
 // to the axis stepped.
-// (The walk's fields pass through an empty asm statement before they are
-// selected: a select between two fields of one struct would otherwise be
-// folded into a load through a selected address, which keeps the whole
-// walk in scratch memory.)
+// (Every operand of the selects below is a prvalue: a conditional between
+// two lvalue fields of the walk would select between their addresses and
+// keep the whole walk in scratch memory.)
 template <typename T>
-__device__ __forceinline__ T in_register(T x) {
-    asm("" : "+v"(x));
+__device__ __forceinline__ T value_of(const T& x) {
     return x;
 }
 
 __device__ __forceinline__ bool advance_select(BandWalk& w, bool& crossed, int& axis) {
-    const float tm0 = in_register(w.tm0), tm1 = in_register(w.tm1), tm2 = in_register(w.tm2);
-    const int k0 = in_register(w.k0), k1 = in_register(w.k1), k2 = in_register(w.k2);
-    const int s0 = in_register(w.s0), s1 = in_register(w.s1), s2 = in_register(w.s2);
-    const float g0 = in_register(w.gA0), g1 = in_register(w.gA1), g2 = in_register(w.gA2);
-    const float i0 = in_register(w.inv0), i1 = in_register(w.inv1), i2 = in_register(w.inv2);
+    const float tm0 = value_of(w.tm0), tm1 = value_of(w.tm1), tm2 = value_of(w.tm2);
+    const int k0 = value_of(w.k0), k1 = value_of(w.k1), k2 = value_of(w.k2);
     const bool c1 = tm1 < tm0;
-    const float t01 = c1 ? tm1 : tm0;
+    const float t01 = c1 ? (float)tm1 : (float)tm0;
     const bool c2 = tm2 < t01;
-    const float tmin = c2 ? tm2 : t01;
+    const float tmin = c2 ? (float)tm2 : (float)t01;
     const bool more = tmin <= 1.0f;
     const bool a2 = more && c2;
     const bool a1 = more && !c2 && c1;
     const bool a0 = more && !c2 && !c1;
-    const int k_old = c2 ? k2 : (c1 ? k1 : k0);
-    const int s = c2 ? s2 : (c1 ? s1 : s0);
-    const float gA = c2 ? g2 : (c1 ? g1 : g0);
-    const float inv = c2 ? i2 : (c1 ? i1 : i0);
+    const int s0 = value_of(w.s0), s1 = value_of(w.s1), s2 = value_of(w.s2);
+    const float g0 = value_of(w.gA0), g1 = value_of(w.gA1), g2 = value_of(w.gA2);
+    const float i0 = value_of(w.inv0), i1 = value_of(w.inv1), i2 = value_of(w.inv2);
+    const int k_old = c2 ? (int)k2 : (c1 ? (int)k1 : (int)k0);
+    const int s = c2 ? (int)s2 : (c1 ? (int)s1 : (int)s0);
+    const float gA = c2 ? (float)g2 : (c1 ? (float)g1 : (float)g0);
+    const float inv = c2 ? (float)i2 : (c1 ? (float)i1 : (float)i0);
     const int k = k_old + s;
     const float t = ((float)(s > 0 ? k + 1 : k) - gA) * inv;
     w.k0 = a0 ? k : k0;

@@ -294,6 +294,14 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
     unsigned int n_upd = 0, n_guard = 0, misses = 0;
     int visits = 0;
     int base = 0;                             // wavefront-uniform fill of the run list
+    // a step that leaves a block moves the key by one block along its axis
+    // (biased fields stay inside [0, 2^21): no carries between them)
+    const unsigned long long dk0 = (unsigned long long)(long long)w.s0;
+    const unsigned long long dk1 = (unsigned long long)((long long)w.s1 * (1ll << 21));
+    const unsigned long long dk2 = (unsigned long long)((long long)w.s2 * (1ll << 42));
+    const DepthAxis ax = depth_axis(f);
+    const int max_visits = f.max_visits;
+    const float vs = vol.vs, trunc = vol.trunc;
 
     // one cell per lane per iteration; a run is emitted by the step that
     // leaves its block or ends the walk
@@ -302,28 +310,26 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
         unsigned long long ekey = cur, ecode = 0;
         if (alive) {
             float sdf;
-            const bool keep = centre_test(w, f, vol.vs, vol.trunc, sdf);
+            const bool keep = centre_test(w.k0, w.k1, w.k2, w.d, ax, vs, trunc, sdf);
             ++cells;
             kept += keep ? 1 : 0;
             bool crossed;
             int axis;
             bool more = advance_select(w, crossed, axis);
-            if (++visits >= f.max_visits && more) {   // cut by the safety bound (never expected)
+            if (++visits >= max_visits && more) {     // cut by the safety bound (never expected)
                 ++n_guard;
                 more = false;
             }
-            if (!more || crossed) {
-                emit = kept > 0;
-                ecode = run_code(entry, cells, steps, kept);
-                n_upd += (unsigned int)kept;
-                cur = block_key(w.k0, w.k1, w.k2);
-                entry = voxel_in_block(w.k0, w.k1, w.k2);
-                cells = 0;
-                kept = 0;
-                steps = 0;
-            } else {
-                steps |= (unsigned long long)axis << (2 * (cells - 1));
-            }
+            const bool close = !more || crossed;
+            emit = close && kept > 0;
+            ecode = run_code(entry, cells, steps, kept);
+            n_upd += close ? (unsigned int)kept : 0u;
+            const unsigned long long dk = axis == 2 ? dk2 : (axis == 1 ? dk1 : dk0);
+            cur = crossed ? cur + dk : cur;
+            entry = close ? voxel_in_block(w.k0, w.k1, w.k2) : entry;
+            steps = close ? 0ull : steps | ((unsigned long long)axis << (2 * (cells - 1)));
+            cells = close ? 0 : cells;
+            kept = close ? 0 : kept;
             alive = more;
         }
         const unsigned long long m = __ballot(emit);
