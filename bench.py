@@ -82,6 +82,9 @@ def load_counts(name):
 # carries their digest; after any change the field is null until re-measured.
 MEASURED_TRAFFIC = {
     # (kernel, workload, frames per call, update mode): (bytes per launch, source digest)
+    # profiles/integrate_room640x480_batch16.md
+    ("k_allocate", "room640x480", 16, "owner"): (241853658, "4fd5e94bd97e05cc"),
+    ("k_update_owner", "room640x480", 16, "owner"): (753449867, "4fd5e94bd97e05cc"),
 }
 
 
@@ -153,6 +156,17 @@ def microbench(torch, tsdf, stream):
     return out
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(wl, n_frames):
     """The oracle, single-threaded, on the first n_frames of the workload."""
     import oracle
@@ -170,7 +184,7 @@ def cpu_baseline(wl, n_frames):
         "voxel_updates_per_s": round(tot["voxel_updates"] / dt, 1),
         "cores": 1,
         "host_cores": os.cpu_count(),
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
         "kind": "oracle",
         "sample": f"first {n_frames} of {wl.n_frames} frames ({tot['points_valid']} points), {dt:.1f} s",
     }
@@ -182,7 +196,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="room640x480")
-    ap.add_argument("--cpu-frames", type=int, default=40)
+    ap.add_argument("--cpu-frames", type=int, default=100, help="frames of the workload the oracle integrates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-microbench", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="time whole steps only")
