@@ -153,6 +153,15 @@ def microbench(torch, tsdf, stream):
     t = timed(lambda: tsdf.tsdf_mb_cas_u64(cbuf.data_ptr(), n, ops, 3, s))
     out["cas_u64_random_Gops"] = round(ops / t / 1e9, 2)
     del cbuf
+    # LDS atomics, lane operations per clock per CU (256 CUs at 2.4 GHz)
+    grid, iters = 256 * 8, 4096
+    sink = torch.zeros(grid, dtype=torch.float32, device="cuda")
+    for tname, ty in (("u32", tsdf.MB_LDS_U32), ("f32", tsdf.MB_LDS_F32), ("u64", tsdf.MB_LDS_U64)):
+        for pname, pat in (("distinct", tsdf.MB_LDS_DISTINCT), ("random", tsdf.MB_LDS_RANDOM),
+                           ("groups8", tsdf.MB_LDS_GROUPS)):
+            t = timed(lambda: tsdf.tsdf_mb_lds_atomic(ty, pat, grid, iters, sink.data_ptr(), s), reps=3)
+            out[f"lds_add_{tname}_{pname}_per_clk_per_cu"] = round(grid * 256 * iters / t / 2.4e9 / 256, 2)
+    del sink
     return out
 
 

@@ -1,5 +1,6 @@
 // microbench.hip -- ceilings for the integrate kernels: copy bandwidth,
-// float atomic-add rate by access pattern, 64-bit compare-exchange rate.
+// float atomic-add rate by access pattern, 64-bit compare-exchange rate,
+// LDS atomic-add rate by operand type and pattern.
 #include <hip/hip_runtime.h>
 
 #include "tsdf_microbench.h"
@@ -54,6 +55,49 @@ __global__ __launch_bounds__(kThreads) void k_cas(unsigned long long* buf, unsig
         atomicCAS(buf + (mix32((unsigned int)i ^ seed) & mask), 0ull, i + 1);
 }
 
+template <int TYPE, int PAT>
+__global__ __launch_bounds__(kThreads) void k_lds_atomic(unsigned int iters, float* sink) {
+    __shared__ unsigned int au[512];
+    __shared__ float af[512];
+    __shared__ unsigned long long a64[512];
+    for (int i = threadIdx.x; i < 512; i += kThreads) {
+        au[i] = 0;
+        af[i] = 0.0f;
+        a64[i] = 0;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    unsigned int x = mix32(threadIdx.x * 2654435761u ^ blockIdx.x);
+    for (unsigned int it = 0; it < iters; ++it) {
+        int j;
+        if (PAT == 0) {
+            j = (lane + 64 * wave + (int)it) & 511;
+        } else if (PAT == 1) {
+            x = x * 1664525u + 1013904223u;
+            j = (int)((x >> 8) & 511u);
+        } else if (PAT == 2) {
+            j = ((int)it * 7 + wave) & 511;
+        } else {
+            j = ((lane >> 3) * 9 + (int)it + 64 * wave) & 511;
+        }
+        if (TYPE == 0) atomicAdd(&au[j], 1u);
+        else if (TYPE == 1) atomicAdd(&af[j], 1.0f);
+        else atomicAdd(&a64[j], 1ull);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = (float)au[5] + af[7] + (float)a64[9];
+}
+
+template <int TYPE>
+void launch_lds(int pattern, unsigned int grid, unsigned int iters, float* sink, hipStream_t s) {
+    switch (pattern) {
+        case 0: hipLaunchKernelGGL((k_lds_atomic<TYPE, 0>), dim3(grid), dim3(kThreads), 0, s, iters, sink); break;
+        case 1: hipLaunchKernelGGL((k_lds_atomic<TYPE, 1>), dim3(grid), dim3(kThreads), 0, s, iters, sink); break;
+        case 2: hipLaunchKernelGGL((k_lds_atomic<TYPE, 2>), dim3(grid), dim3(kThreads), 0, s, iters, sink); break;
+        default: hipLaunchKernelGGL((k_lds_atomic<TYPE, 3>), dim3(grid), dim3(kThreads), 0, s, iters, sink);
+    }
+}
+
 unsigned int grid_for(unsigned long long n) {
     unsigned long long g = (n + kThreads - 1) / kThreads;
     return (unsigned int)(g < 1 ? 1 : (g > kMaxGrid ? kMaxGrid : g));
@@ -91,6 +135,17 @@ tsdf_status tsdf_mb_cas_u64(uint64_t* buf, size_t n, size_t n_ops, uint32_t seed
     hipLaunchKernelGGL(k_cas, dim3(grid_for(n_ops)), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                        reinterpret_cast<unsigned long long*>(buf), (unsigned long long)(n - 1),
                        (unsigned long long)n_ops, seed);
+    return launched();
+}
+
+tsdf_status tsdf_mb_lds_atomic(int type, int pattern, uint32_t n_workgroups, uint32_t iters, float* sink,
+                               void* stream) {
+    if (!sink || type < 0 || type > 2 || pattern < 0 || pattern > 3 || n_workgroups < 1 || n_workgroups > kMaxGrid)
+        return TSDF_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (type == 0) launch_lds<0>(pattern, n_workgroups, iters, sink, s);
+    else if (type == 1) launch_lds<1>(pattern, n_workgroups, iters, sink, s);
+    else launch_lds<2>(pattern, n_workgroups, iters, sink, s);
     return launched();
 }
 

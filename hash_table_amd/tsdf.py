@@ -28,13 +28,15 @@ TSDF_MAX_POOL_BLOCKS = 1 << 30
 TSDF_MAX_TABLE_ENTRIES = 1 << 31
 BLOCK_VOXELS = 512
 MB_COALESCED, MB_RANDOM, MB_SAME_WAVE, MB_BLOCK_ROW, MB_COUNTERS = 0, 1, 2, 3, 4
+MB_LDS_U32, MB_LDS_F32, MB_LDS_U64 = 0, 1, 2
+MB_LDS_DISTINCT, MB_LDS_RANDOM, MB_LDS_SAME, MB_LDS_GROUPS = 0, 1, 2, 3
 
 # every symbol the headers declare
 EXPORTS = [
     "tsdf_table_entries_for", "tsdf_counters_bytes", "tsdf_scratch_bytes", "tsdf_create", "tsdf_reset", "tsdf_allocate",
     "tsdf_update", "tsdf_integrate", "tsdf_integrate_batch", "tsdf_allocate_batch", "tsdf_update_batch",
     "tsdf_export_blocks", "tsdf_get_stats", "tsdf_set_kernel_timing", "tsdf_kernel_times", "tsdf_destroy",
-    "tsdf_status_str", "tsdf_mb_copy", "tsdf_mb_atomic_add_f32", "tsdf_mb_cas_u64",
+    "tsdf_status_str", "tsdf_mb_copy", "tsdf_mb_atomic_add_f32", "tsdf_mb_cas_u64", "tsdf_mb_lds_atomic",
 ]
 
 
@@ -107,6 +109,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         "tsdf_mb_copy": (I32, [P, P, SZ, P]),
         "tsdf_mb_atomic_add_f32": (I32, [P, SZ, SZ, ctypes.c_int, ctypes.c_uint32, P]),
         "tsdf_mb_cas_u64": (I32, [P, SZ, SZ, ctypes.c_uint32, P]),
+        "tsdf_mb_lds_atomic": (I32, [ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -245,6 +248,11 @@ def tsdf_mb_atomic_add_f32(buf: int, n: int, n_ops: int, pattern: int, seed: int
 
 def tsdf_mb_cas_u64(buf: int, n: int, n_ops: int, seed: int = 1, stream: int = 0) -> None:
     _check(load().tsdf_mb_cas_u64(buf, n, n_ops, seed, ctypes.c_void_p(stream)), "tsdf_mb_cas_u64")
+
+
+def tsdf_mb_lds_atomic(type_: int, pattern: int, n_workgroups: int, iters: int, sink: int, stream: int = 0) -> None:
+    _check(load().tsdf_mb_lds_atomic(type_, pattern, n_workgroups, iters, ctypes.c_void_p(sink),
+                                     ctypes.c_void_p(stream)), "tsdf_mb_lds_atomic")
 
 
 # ---------------------------------------------------------------------------

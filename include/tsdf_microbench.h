@@ -44,6 +44,26 @@ tsdf_status tsdf_mb_atomic_add_f32(float* buf, size_t n, size_t n_ops, int patte
  * slots of buf[0 .. n), n a power of two. */
 tsdf_status tsdf_mb_cas_u64(uint64_t* buf, size_t n, size_t n_ops, uint32_t seed, void* stream);
 
+/* LDS atomic additions (the owner update sums a block in LDS): operand
+ * types and LDS address patterns of tsdf_mb_lds_atomic. */
+enum {
+    TSDF_MB_LDS_U32 = 0,
+    TSDF_MB_LDS_F32 = 1,
+    TSDF_MB_LDS_U64 = 2
+};
+enum {
+    TSDF_MB_LDS_DISTINCT = 0,   /* the 64 lanes of a wave on 64 consecutive words */
+    TSDF_MB_LDS_RANDOM = 1,     /* every lane a random word of 512 */
+    TSDF_MB_LDS_SAME = 2,       /* a whole wave on one word */
+    TSDF_MB_LDS_GROUPS = 3      /* groups of 8 lanes on one word */
+};
+
+/* n_workgroups workgroups of 256 threads, each thread adding `iters` times
+ * into a 512-entry LDS array of the given type with the given pattern.
+ * Rate = n_workgroups * 256 * iters lane operations over the kernel time. */
+tsdf_status tsdf_mb_lds_atomic(int type, int pattern, uint32_t n_workgroups, uint32_t iters, float* sink,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

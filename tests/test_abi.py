@@ -120,3 +120,9 @@ def test_microbench_rejects_bad_arguments():
         tsdf.tsdf_mb_atomic_add_f32(0x1000, 256, 10, tsdf.MB_BLOCK_ROW)    # under one block
     with pytest.raises(tsdf.TsdfError):
         tsdf.tsdf_mb_cas_u64(0, 1024, 10)
+    with pytest.raises(tsdf.TsdfError):
+        tsdf.tsdf_mb_lds_atomic(3, tsdf.MB_LDS_RANDOM, 8, 16, 0x1000)       # no such operand type
+    with pytest.raises(tsdf.TsdfError):
+        tsdf.tsdf_mb_lds_atomic(tsdf.MB_LDS_U32, 4, 8, 16, 0x1000)          # no such pattern
+    with pytest.raises(tsdf.TsdfError):
+        tsdf.tsdf_mb_lds_atomic(tsdf.MB_LDS_U32, tsdf.MB_LDS_SAME, 8, 16, 0)  # no sink
