@@ -161,6 +161,7 @@ VolumeArgs volume_args(const tsdf_volume* h) {
     a.inv_vs = 1.0f / h->cfg.voxel_size;
     a.trunc = h->cfg.trunc;
     a.inv_trunc = 1.0f / h->cfg.trunc;
+    a.probe_limit = h->cfg.probe_limit > 0 ? (unsigned int)h->cfg.probe_limit : 0xFFFFFFFFu;
     return a;
 }
 
@@ -314,6 +315,7 @@ tsdf_status tsdf_create(const tsdf_config* config, const tsdf_buffers* buffers, 
     if (config->pool_capacity < 1 || config->pool_capacity > TSDF_MAX_POOL_BLOCKS) return TSDF_EINVAL;
     if (config->update_mode != TSDF_UPDATE_OWNER && config->update_mode != TSDF_UPDATE_RAYS) return TSDF_EINVAL;
     if (config->max_batch_pixels < 0 || config->max_batch_pixels > ((int64_t)1 << 28)) return TSDF_EINVAL;
+    if (config->probe_limit < 0) return TSDF_EINVAL;
     const int64_t entries = resolved_entries(config);
     if (!is_pow2(entries) || entries < 2 * config->pool_capacity || entries > TSDF_MAX_TABLE_ENTRIES)
         return TSDF_EINVAL;
@@ -424,6 +426,7 @@ tsdf_status tsdf_get_stats(tsdf_volume* h, tsdf_stats* out, void* stream) {
     out->walk_guard = (int64_t)sum[kWalkGuard];
     out->probe_max = (int64_t)sum[kProbeMax];
     out->fallback_blocks = (int64_t)sum[kFallbackBlocks];
+    out->probe_exhausted = (int64_t)sum[kProbeExhausted];
     for (int i = 0; i < kProbeBins; ++i) {
         out->probe_hist_alloc[i] = sum[kHistAlloc + i];
         out->probe_hist_update[i] = sum[kHistUpdate + i];

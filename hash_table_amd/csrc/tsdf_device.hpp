@@ -41,6 +41,7 @@ enum CounterWord {
     kWalkGuard,
     kProbeMax,
     kFallbackBlocks,     // owner update: blocks rescanned because their runs did not fit
+    kProbeExhausted,     // table operations that stopped at the configured probe limit
     kHistAlloc = 16,
     kHistUpdate = kHistAlloc + kProbeBins,
     kCounterWords = kHistUpdate + kProbeBins,
@@ -195,6 +196,7 @@ struct VolumeArgs {
     float* b;
     unsigned long long* counters;
     float vs, inv_vs, trunc, inv_trunc;
+    unsigned int probe_limit;        // slots a table operation may probe (0xFFFFFFFF: no limit)
 };
 
 enum PointClass { kInvalid = 0, kNear = 1, kOutside = 2, kValid = 3 };
@@ -464,6 +466,10 @@ __device__ __forceinline__ unsigned int insert_key(const VolumeArgs& vol, unsign
             atomicAdd(replica(vol.counters) + kTableFull, 1ull);
             return kNoSlot;
         }
+        if (probes >= vol.probe_limit) {   // the bounded-probe control gives up here
+            atomicAdd(replica(vol.counters) + kProbeExhausted, 1ull);
+            return kNoSlot;
+        }
         slot = (slot + 1) & vol.mask;
         ++probes;
     }
@@ -500,6 +506,10 @@ __device__ __forceinline__ unsigned int lookup_key(const VolumeArgs& vol, unsign
             return idx < vol.capacity ? idx : kNoIndex;
         }
         if (e.x == kEmptyKey || probes > vol.mask) return kNoIndex;
+        if (probes >= vol.probe_limit) {
+            atomicAdd(replica(vol.counters) + kProbeExhausted, 1ull);
+            return kNoIndex;
+        }
         slot = (slot + 1) & vol.mask;
         ++probes;
     }

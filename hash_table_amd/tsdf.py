@@ -49,7 +49,8 @@ class TsdfError(RuntimeError):
 class tsdf_config(ctypes.Structure):
     _fields_ = [("voxel_size", ctypes.c_float), ("trunc", ctypes.c_float),
                 ("pool_capacity", ctypes.c_int64), ("table_entries", ctypes.c_int64),
-                ("update_mode", ctypes.c_int32), ("max_batch_pixels", ctypes.c_int64)]
+                ("update_mode", ctypes.c_int32), ("max_batch_pixels", ctypes.c_int64),
+                ("probe_limit", ctypes.c_int32)]
 
 
 class tsdf_buffers(ctypes.Structure):
@@ -66,7 +67,7 @@ class tsdf_frame(ctypes.Structure):
 class tsdf_stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "pool_used", "pool_overflow", "table_full", "update_misses", "out_of_range", "near_skipped",
-        "points_valid", "voxel_updates", "walk_guard", "probe_max", "fallback_blocks")] + [
+        "points_valid", "voxel_updates", "walk_guard", "probe_max", "fallback_blocks", "probe_exhausted")] + [
         ("probe_hist_alloc", ctypes.c_uint64 * TSDF_PROBE_BINS),
         ("probe_hist_update", ctypes.c_uint64 * TSDF_PROBE_BINS)]
 
@@ -212,7 +213,7 @@ def tsdf_export_blocks(volume, coords: int, tsdf: int, weight: int, r: int, g: i
 def tsdf_get_stats(volume, stream: int = 0) -> Dict[str, object]:
     s = tsdf_stats()
     _check(load().tsdf_get_stats(volume, ctypes.byref(s), ctypes.c_void_p(stream)), "tsdf_get_stats")
-    out: Dict[str, object] = {n: int(getattr(s, n)) for n, _ in tsdf_stats._fields_[:11]}
+    out: Dict[str, object] = {n: int(getattr(s, n)) for n, _ in tsdf_stats._fields_[:12]}
     out["probe_hist_alloc"] = np.array(s.probe_hist_alloc[:], np.int64)
     out["probe_hist_update"] = np.array(s.probe_hist_update[:], np.int64)
     return out
@@ -291,7 +292,8 @@ class Volume:
     tensors.  update_mode: "owner" (default) or "rays"."""
 
     def __init__(self, voxel_size: float, trunc: float, pool_capacity: int, table_entries: int = 0,
-                 update_mode: str = "owner", max_batch_pixels: int = 0, device="cuda", stream=None):
+                 update_mode: str = "owner", max_batch_pixels: int = 0, device="cuda", stream=None,
+                 probe_limit: int = 0):
         import torch
         entries = table_entries or tsdf_table_entries_for(pool_capacity)
         if entries <= 0:
@@ -301,7 +303,7 @@ class Volume:
         self.update_mode = update_mode
         self.device = device
         self._cfg = tsdf_config(voxel_size, trunc, int(pool_capacity), int(table_entries), UPDATE_MODES[update_mode],
-                                int(max_batch_pixels))
+                                int(max_batch_pixels), int(probe_limit))
         n = int(pool_capacity) * BLOCK_VOXELS
         self.table = torch.empty(int(entries) * 2, dtype=torch.int64, device=device)
         self.pool = {k: torch.empty(n, dtype=torch.float32, device=device) for k in ("tsdf", "weight", "r", "g", "b")}
@@ -316,7 +318,10 @@ class Volume:
     def __del__(self):
         h = getattr(self, "handle", None)
         if h:
-            tsdf_destroy(h)
+            try:
+                tsdf_destroy(h)
+            except TypeError:               # interpreter shutdown: module globals already gone
+                pass
             self.handle = None
 
     def reset(self, stream=None):

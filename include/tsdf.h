@@ -90,6 +90,12 @@ typedef struct {
                                which sizes the run-record buffers (0: 2^20); larger calls
                                still integrate exactly, but blocks whose records do not fit
                                are rescanned pixel by pixel (slower) */
+    int32_t probe_limit;    /* 0: probes run until they find the key or a free slot (the
+                               paper's CUDA C++ and Rust probes, section 7).  n > 0: a
+                               negative control reproducing the bounded probe of the
+                               paper's Triton arm (section 7): a table operation gives up
+                               after n slots; such keys are counted in probe_exhausted and
+                               their contributions in update_misses.  Not for production. */
 } tsdf_config;
 
 /* Device memory owned by the caller, all 16-byte aligned. */
@@ -127,7 +133,7 @@ typedef struct {
     int64_t pool_overflow;   /* distinct keys inserted after the pool was full */
     int64_t table_full;      /* insertions that probed every table slot without room */
     int64_t update_misses;   /* kept voxel contributions lost: block without a pool index,
-                                or key not inserted because the table was full */
+                                or key not inserted (full table, or probe_limit reached) */
     int64_t out_of_range;    /* points whose band leaves +-2^23 voxels */
     int64_t near_skipped;    /* points with 0 < depth <= trunc */
     int64_t points_valid;    /* points whose band was walked */
@@ -136,6 +142,8 @@ typedef struct {
     int64_t probe_max;       /* longest probe sequence seen, slots */
     int64_t fallback_blocks; /* owner update: blocks rescanned pixel by pixel because their
                                 run records did not fit the scratch buffer (slower, exact) */
+    int64_t probe_exhausted; /* table operations that gave up at probe_limit slots (0
+                                unless the config sets a limit) */
     uint64_t probe_hist_alloc[TSDF_PROBE_BINS];   /* allocate: slots per table operation */
     uint64_t probe_hist_update[TSDF_PROBE_BINS];  /* ray-parallel update: slots per lookup */
 } tsdf_stats;

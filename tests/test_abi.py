@@ -75,6 +75,7 @@ def _buffers(base=0x10000, step=0x100000):
     ((0.01, 0.04, 1 << 31, 0), tsdf.TSDF_EINVAL),           # pool too large
     ((0.01, 0.04, 4096, 0, 7), tsdf.TSDF_EINVAL),           # unknown update mode
     ((0.01, 0.04, 4096, 0, 0, -5), tsdf.TSDF_EINVAL),       # negative frame size
+    ((0.01, 0.04, 4096, 0, 0, 0, -1), tsdf.TSDF_EINVAL),    # negative probe limit
 ])
 def test_create_rejects_bad_config(cfg, code):
     with pytest.raises(tsdf.TsdfError) as e:

@@ -3,8 +3,10 @@
 Bit-exact: block set, block count, per-voxel weights, point / update / loss
 counts.  Within 1e-4: mean TSDF and mean colour.  Workloads: the plane, the
 sphere-and-wall arc, the 640 x 480 room (a prefix element by element, and
-all 100 frames), the 0.2 m contention cube, the load-factor sweep, tiny
-random frames with ragged sizes, and the edge cases.
+all 100 frames in the benchmark's launch configuration), the 1280 x 720 room
+at its full sizes, the 0.2 m contention cube, the load-factor sweep and the
+bounded-probe control on it, tiny random frames with ragged sizes, dense
+blocks spanning several LDS windows, batches, and the edge cases.
 """
 from __future__ import annotations
 
@@ -87,34 +89,72 @@ def test_room_prefix_parity_split_calls(mode):
     assert_parity(st, coords, arrays, o)
 
 
+def _check_history(label, hist, g, calls):
+    """Per-call counters against the oracle's stored per-frame counts."""
+    for h, c in zip(hist, calls):
+        last = c[-1]
+        assert h["pool_used"] == g["frames"][last]["blocks_total"], f"{label} after frame {last}: blocks"
+        assert h["voxel_updates"] == sum(f["voxel_updates"] for f in g["frames"][:last + 1]), \
+            f"{label} after frame {last}: voxel updates"
+        assert h["points_valid"] == sum(f["points_valid"] for f in g["frames"][:last + 1]), \
+            f"{label} after frame {last}: valid points"
+
+
 @pytest.mark.timeout(600)
 def test_room_full_parity():
-    """All 100 frames of the 640 x 480 room, in the launch configuration the
-    benchmark times (tsdf_integrate per frame), with both update modes:
-    per-frame counts against the stored oracle counts, then every voxel
-    against a live oracle run."""
+    """All 100 frames of the 640 x 480 room: in the launch configuration the
+    benchmark times (owner update, 16 frames per call) and one frame per call
+    with both update modes; counts after every call against the stored
+    oracle counts, then every voxel against a live oracle run."""
     wl = scenes.workload("room640x480")
     g = golden("room640x480")
     frames = list(wl.frames())
     for i, f in enumerate(frames[:3]):
         assert scenes.frame_digest([f]) == g["frames"][i]["sha256"], "generator drifted from the stored counts"
     results = {}
-    for mode in MODES:
-        say(f"  gpu ({mode}): 100 frames 640x480")
+    for mode, batch in (("owner", 16), ("owner", 1), ("rays", 1)):
+        say(f"  gpu ({mode}, {batch} frames per call): 100 frames 640x480")
         _, st, coords, arrays, hist = parity.gpu_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity,
-                                                           per_frame_stats=True, mode=mode)
-        prev_v = prev_p = 0
-        for i, (h, gf) in enumerate(zip(hist, g["frames"])):
-            assert h["pool_used"] == gf["blocks_total"], f"{mode} frame {i}: blocks {h['pool_used']}"
-            assert h["voxel_updates"] - prev_v == gf["voxel_updates"], f"{mode} frame {i}: voxel updates"
-            assert h["points_valid"] - prev_p == gf["points_valid"], f"{mode} frame {i}: valid points"
-            prev_v, prev_p = h["voxel_updates"], h["points_valid"]
-        results[mode] = (st, coords, arrays)
+                                                           per_frame_stats=True, mode=mode, batch=batch,
+                                                           max_batch_pixels=batch * 640 * 480)
+        calls = [list(range(i, min(i + batch, 100))) for i in range(0, 100, batch)]
+        _check_history(f"{mode}/{batch}", hist, g, calls)
+        assert st["fallback_blocks"] == 0
+        results[(mode, batch)] = (st, coords, arrays)
     say("  oracle: 100 frames")
     o = parity.oracle_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity)
-    for mode, (st, coords, arrays) in results.items():
-        say(f"  compare {mode}")
+    for key, (st, coords, arrays) in results.items():
+        say(f"  compare {key}")
         assert_parity(st, coords, arrays, o)
+
+
+@pytest.mark.timeout(900)
+def test_room1280x720_full_size_prefix():
+    """The 1280 x 720 room at its full sizes -- 921,600-pixel frames, a pool
+    of 2^22 blocks (40 GiB of sums), a 2^24-entry table -- in the benchmark's
+    launch configuration (owner update, 16 frames per call): counts after
+    every call against the stored oracle counts of all 300 frames' run, then
+    the block set in full and 64 sampled blocks voxel by voxel against a live
+    oracle run of the same 48 frames."""
+    wl = scenes.workload("room1280x720")
+    g = golden("room1280x720")
+    n, batch = 48, 16
+    frames = list(wl.frames(0, n))
+    for i in (0, n - 1):
+        assert scenes.frame_digest([frames[i]]) == g["frames"][i]["sha256"], "generator drifted"
+    say(f"  gpu: {n} frames 1280x720, pool {wl.pool_capacity}, table {wl.table_entries}")
+    _, st, coords, arrays, hist = parity.gpu_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity,
+                                                       wl.table_entries, per_frame_stats=True, batch=batch,
+                                                       max_batch_pixels=batch * wl.width * wl.height)
+    _check_history("1280x720", hist, g, [list(range(i, i + batch)) for i in range(0, n, batch)])
+    assert st["fallback_blocks"] == 0
+    say(f"  oracle: {n} frames")
+    o = parity.oracle_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity)
+    rng = np.random.default_rng(1280)
+    oc = o.block_coords()
+    sample = oc[rng.choice(len(oc), size=64, replace=False)]
+    f = parity.compare_stats(st, o) + parity.compare_blocks(coords, arrays, o, sample=sample)
+    assert f == [], f
 
 
 def _lf_case(target):
@@ -155,6 +195,60 @@ def test_load_factor_parity(target, mode):
         knuth = 0.5 * (1 + 1 / (1 - lf))
         say(f"  update probes: mean {mean:.3f}, Knuth {knuth:.3f}")
         assert abs(mean - knuth) < 0.35 * knuth
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_bounded_probe_control_counts_every_loss(mode):
+    # The paper's section 7: a probe bounded at 8 slots (its Triton arm) loses
+    # blocks once the table fills, silently there.  The same bound here (a
+    # negative control, never the default) must lose only whole keys -- every
+    # surviving block exact -- and count every lost contribution.
+    from hash_table_amd import tsdf
+    wl = scenes.workload("room640x480")
+    lost_any = False
+    for target in (0.1, 0.25, 0.5):
+        cap, n, lf = _lf_case(target)
+        frames = list(wl.frames(0, n))
+        vol = tsdf.Volume(wl.voxel_size, wl.trunc, cap, 2 * cap, update_mode=mode, probe_limit=8)
+        for i in range(0, n, 16):
+            vol.integrate_batch([tsdf.DeviceFrame(f) for f in frames[i:i + 16]])
+        st = vol.stats()
+        coords, arrays = vol.export()
+        o = parity.oracle_integrate(frames, wl.voxel_size, wl.trunc, cap)
+        tot = o.totals()
+        oc = {tuple(c) for c in o.block_coords().tolist()}
+        gc = {tuple(c) for c in coords.tolist()}
+        lost = oc - gc
+        say(f"  {mode} load factor {lf:.3f} ({n} frames): blocks {len(gc)} of {len(oc)}, "
+            f"probe_exhausted {st['probe_exhausted']}, update_misses {st['update_misses']}, probe_max {st['probe_max']}")
+        assert gc <= oc and st["probe_max"] <= 8
+        assert st["voxel_updates"] == tot["voxel_updates"] and st["table_full"] == 0
+        if lost:
+            lost_any = True
+            assert st["probe_exhausted"] >= len(lost)
+        w_lost = float(o.block_sums(np.array(sorted(lost), np.int32).reshape(-1, 3))["weight"].sum()) if lost else 0.0
+        assert st["update_misses"] == w_lost                     # every lost contribution counted
+        assert float(arrays["weight"].astype(np.float64).sum()) + st["update_misses"] == tot["voxel_updates"]
+        f = parity.compare_blocks(coords, arrays, _OracleSubset(o, gc))
+        assert f == [], f                                        # surviving blocks are exact
+        del vol
+    assert lost_any, "the bounded probe never ran out: the control did not exercise the loss"
+
+
+class _OracleSubset:
+    """An oracle view restricted to the blocks the GPU kept (for comparing
+    the survivors of the bounded-probe control)."""
+
+    def __init__(self, o, keep):
+        self.o, self.keep = o, keep
+
+    def block_coords(self):
+        c = self.o.block_coords()
+        m = np.array([tuple(x) in self.keep for x in c.tolist()], bool)
+        return c[m]
+
+    def block_sums(self, coords):
+        return self.o.block_sums(coords)
 
 
 def tsdf_bins():
