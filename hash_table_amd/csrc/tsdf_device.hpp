@@ -72,11 +72,15 @@ constexpr float kNearPlane = 1e-4f;                 // block corners closer than
 //   meta      colour R | G << 8 | B << 16, frame of the batch << 24 (4 bits),
 //             axis direction bits << 28 (bit set: that axis steps by -1)
 //   code      first cell (voxel index in the block, 9 bits) | cells - 1 << 9
-//             (5 bits) | the axis of each step inside the block, 2 bits per
-//             step, << 14 (up to 21 steps) | kept cells << 56 (6 bits)
-// A line crosses at most 8 + 8 + 8 - 2 = 22 cells of an 8^3 block, so 21
-// steps and 5 bits of cell count always suffice.  The update enumerates the
-// run's cells from the code alone: it never repeats the walk's arithmetic.
+//             (5 bits) | y-step plane << 14 (21 bits) | z-step plane << 35
+//             (21 bits) | kept cells << 56 (6 bits)
+// Bit q of the y-step (z-step) plane is set when the run's step q, the one
+// from its cell q to cell q + 1, moves along y (z); a step with neither bit
+// moves along x.  The walk is monotonic on every axis and a block spans 8
+// cells per axis, so a run takes at most 7 + 7 + 7 = 21 steps (22 cells):
+// 21-bit planes and 5 bits of cell count always suffice.  The update
+// enumerates the run's cells from the code alone: it never repeats the
+// walk's arithmetic.
 struct __align__(16) RunRecord {
     unsigned int depth;
     unsigned int meta;
@@ -85,17 +89,25 @@ struct __align__(16) RunRecord {
 };
 
 constexpr int kStepShift = 14;
+constexpr int kPlaneBits = 21;
 constexpr int kKeptShift = 56;
 
-__device__ __forceinline__ unsigned long long run_code(int entry, int cells, unsigned long long steps, int kept) {
-    return (unsigned long long)entry | ((unsigned long long)(cells - 1) << 9) | (steps << kStepShift) |
-           ((unsigned long long)kept << kKeptShift);
+__device__ __forceinline__ unsigned long long run_code(unsigned int entry, unsigned int cells, unsigned int ysteps,
+                                                       unsigned int zsteps, unsigned int kept) {
+    return (unsigned long long)(entry | ((cells - 1) << 9)) | ((unsigned long long)ysteps << kStepShift) |
+           ((unsigned long long)zsteps << (kStepShift + kPlaneBits)) | ((unsigned long long)kept << kKeptShift);
 }
 __device__ __forceinline__ unsigned long long record_code(const RunRecord& r) {
     return (unsigned long long)r.code_lo | ((unsigned long long)r.code_hi << 32);
 }
 __device__ __forceinline__ int code_entry(unsigned long long c) { return (int)(c & 511u); }
 __device__ __forceinline__ int code_cells(unsigned long long c) { return (int)((c >> 9) & 31u) + 1; }
+__device__ __forceinline__ unsigned int code_ysteps(unsigned long long c) {
+    return (unsigned int)(c >> kStepShift) & ((1u << kPlaneBits) - 1u);
+}
+__device__ __forceinline__ unsigned int code_zsteps(unsigned long long c) {
+    return (unsigned int)(c >> (kStepShift + kPlaneBits)) & ((1u << kPlaneBits) - 1u);
+}
 __device__ __forceinline__ int code_kept(unsigned long long c) { return (int)((c >> kKeptShift) & 63u); }
 __device__ __forceinline__ int meta_frame(unsigned int m) { return (int)((m >> 24) & 15u); }
 

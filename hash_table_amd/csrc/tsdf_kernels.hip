@@ -42,6 +42,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kListCap = 256;     // block runs a wavefront buffers before de-duplicating
 constexpr int kSetCap = 256;      // per-wavefront LDS hash set (power of two, >= kListCap, <= 256)
 constexpr float kInv255 = 1.0f / 255.0f;
+constexpr int kChunkCells = 31;   // cells of a walk per pass of the allocate loop (plus a sentinel bit)
 
 __device__ __forceinline__ bool workgroup_tile(const FrameArgs& f, int wg, int& tile_u0, int& tile_v0) {
     const int rank = wg / kXcds;                   // position within the XCD's run of tiles
@@ -285,66 +286,147 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
                 (w.s2 < 0 ? 1u << 30 : 0u);
     }
     const unsigned int depth_bits = __float_as_uint(depth);
-    // the current run: its block, first cell, cells visited and kept, and
-    // the axis of each step taken inside the block
-    unsigned long long cur = alive ? block_key(w.k0, w.k1, w.k2) : kEmptyKey;
-    int entry = alive ? voxel_in_block(w.k0, w.k1, w.k2) : 0;
-    int cells = 0, kept = 0;
-    unsigned long long steps = 0;
     unsigned int n_upd = 0, n_guard = 0, misses = 0;
-    int visits = 0;
     int base = 0;                             // wavefront-uniform fill of the run list
-    // a step that leaves a block moves the key by one block along its axis
-    // (biased fields stay inside [0, 2^21): no carries between them)
-    const unsigned long long dk0 = (unsigned long long)(long long)w.s0;
-    const unsigned long long dk1 = (unsigned long long)((long long)w.s1 * (1ll << 21));
-    const unsigned long long dk2 = (unsigned long long)((long long)w.s2 * (1ll << 42));
-    const DepthAxis ax = depth_axis(f);
     const int max_visits = f.max_visits;
     const float vs = vol.vs, trunc = vol.trunc;
+    const DepthAxis ax = depth_axis(f);
 
-    // one cell per lane per iteration; a run is emitted by the step that
-    // leaves its block or ends the walk
-    while (__any(alive)) {
-        bool emit = false;
-        unsigned long long ekey = cur, ecode = 0;
-        if (alive) {
-            float sdf;
-            const bool keep = centre_test(w.k0, w.k1, w.k2, w.d, ax, vs, trunc, sdf);
-            ++cells;
-            kept += keep ? 1 : 0;
-            bool crossed;
-            int axis;
-            bool more = advance_select(w, crossed, axis);
-            if (++visits >= max_visits && more) {     // cut by the safety bound (never expected)
-                ++n_guard;
-                more = false;
+    // Walk state in registers, per axis: cell, next boundary parameter,
+    // start and reciprocal of the direction (both in voxel units), step,
+    // the offset of the next boundary's cell (1 when stepping up), and the
+    // centre's term of the camera depth, axis_r * (centre - t), recomputed
+    // from the cell whenever the cell changes (same operations as a full
+    // evaluation, so the depth sum below is the one the written rule gives).
+    int k0 = 0, k1 = 0, k2 = 0, s0 = 0, s1 = 0, s2 = 0;
+    float tm0 = 0.f, tm1 = 0.f, tm2 = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, i0 = 0.f, i1 = 0.f, i2 = 0.f;
+    if (alive) {
+        k0 = w.k0; k1 = w.k1; k2 = w.k2;
+        s0 = w.s0; s1 = w.s1; s2 = w.s2;
+        tm0 = w.tm0; tm1 = w.tm1; tm2 = w.tm2;
+        g0 = w.gA0; g1 = w.gA1; g2 = w.gA2;
+        i0 = w.inv0; i1 = w.inv1; i2 = w.inv2;
+    }
+    const int o0 = s0 > 0, o1 = s1 > 0, o2 = s2 > 0;
+    float p0 = ax.r2 * ((((float)k0 + 0.5f) * vs) - ax.t0);
+    float p1 = ax.r5 * ((((float)k1 + 0.5f) * vs) - ax.t1);
+    float p2 = ax.r8 * ((((float)k2 + 0.5f) * vs) - ax.t2);
+    const float dd = depth;
+    // the centre test of the walk's current cell (evaluated on entering it)
+    bool keep;
+    {
+        const float sdf = dd - ((p0 + p1) + p2);
+        keep = sdf >= -trunc && sdf <= trunc;
+    }
+
+    // The walk goes in chunks of up to kChunkCells cells.  All lanes start
+    // together, so a lane's cell index within the chunk is the (uniform)
+    // iteration count; each iteration shifts one bit into four per-lane
+    // planes: the cell was kept, the step after it moved along y, along z,
+    // left the block.  After the chunk the planes are cut into runs (one
+    // per block the chunk's part of the walk crosses), which go to the
+    // wavefront's run list.  A walk longer than a chunk has its run at the
+    // chunk boundary split in two records of the same block: the update
+    // adds both.
+    for (int done = 0; __any(alive); done += kChunkCells) {
+        int x = k0, y = k1, z = k2;           // the chunk's first cell
+        unsigned int kp = 1u, yp = 0u, zp = 0u, cp = 0u;   // kept plane starts with a sentinel bit
+        // the safety bound on cells per walk limits the chunk (uniform)
+        const int lim = min(kChunkCells, max_visits - done);
+        for (int it = 0; it < lim; ++it) {
+            if (!__any(alive)) break;
+            if (alive) {
+                kp = kp + kp + (keep ? 1u : 0u);
+                const float tmin = fminf(fminf(tm0, tm1), tm2);
+                const bool more = tmin <= 1.0f;
+                // smallest boundary parameter, ties to x, then y
+                const bool e0 = tm0 == tmin, e1 = tm1 == tmin;
+                const bool a0 = more && e0, a1 = more && !e0 && e1, a2 = more && !e0 && !e1;
+                yp = yp + yp + (a1 ? 1u : 0u);
+                zp = zp + zp + (a2 ? 1u : 0u);
+                bool cr = false;
+                if (a0) {
+                    const int prev = k0;
+                    k0 += s0;
+                    tm0 = ((float)(k0 + o0) - g0) * i0;
+                    p0 = ax.r2 * ((((float)k0 + 0.5f) * vs) - ax.t0);
+                    cr = (unsigned int)(k0 ^ prev) > 7u;   // the block index (k >> 3) changed
+                }
+                if (a1) {
+                    const int prev = k1;
+                    k1 += s1;
+                    tm1 = ((float)(k1 + o1) - g1) * i1;
+                    p1 = ax.r5 * ((((float)k1 + 0.5f) * vs) - ax.t1);
+                    cr = (unsigned int)(k1 ^ prev) > 7u;   // the block index (k >> 3) changed
+                }
+                if (a2) {
+                    const int prev = k2;
+                    k2 += s2;
+                    tm2 = ((float)(k2 + o2) - g2) * i2;
+                    p2 = ax.r8 * ((((float)k2 + 0.5f) * vs) - ax.t2);
+                    cr = (unsigned int)(k2 ^ prev) > 7u;   // the block index (k >> 3) changed
+                }
+                cp = cp + cp + (cr ? 1u : 0u);
+                const float sdf = dd - ((p0 + p1) + p2);       // the cell just entered
+                keep = sdf >= -trunc && sdf <= trunc;
+                alive = more;
             }
-            const bool close = !more || crossed;
-            emit = close && kept > 0;
-            ecode = run_code(entry, cells, steps, kept);
-            n_upd += close ? (unsigned int)kept : 0u;
-            const unsigned long long dk = axis == 2 ? dk2 : (axis == 1 ? dk1 : dk0);
-            cur = crossed ? cur + dk : cur;
-            entry = close ? voxel_in_block(w.k0, w.k1, w.k2) : entry;
-            steps = close ? 0ull : steps | ((unsigned long long)axis << (2 * (cells - 1)));
-            cells = close ? 0 : cells;
-            kept = close ? 0 : kept;
-            alive = more;
         }
-        const unsigned long long m = __ballot(emit);
-        if (m) {
-            if (base + 64 > kListCap) {
-                flush_runs(L, wave, lane, base, vol, own, depth_bits, meta, misses);
-                base = 0;
+        // A walk still going after max_visits cells is cut there (counted).
+        // Its last iteration took one more step; that step's bits sit after
+        // the lane's last cell and no run reads them.
+        if (done + lim >= max_visits && alive) {
+            ++n_guard;
+            alive = false;
+        }
+        // planes in walk order: bit j = the chunk's cell j (the sentinel marks
+        // how many cells this lane walked in the chunk)
+        const int n = 31 - __clz(kp);
+        const unsigned int sh = (unsigned int)(32 - n) & 31u;
+        const unsigned int kf = n ? __builtin_bitreverse32(kp) >> sh : 0u;
+        const unsigned int yf = n ? __builtin_bitreverse32(yp) >> sh : 0u;
+        const unsigned int zf = n ? __builtin_bitreverse32(zp) >> sh : 0u;
+        const unsigned int cf = n ? __builtin_bitreverse32(cp) >> sh : 0u;
+        // cut into runs: a run ends at a cell whose step leaves the block, or
+        // at the lane's last cell of the chunk
+        for (int j0 = 0; __any(j0 < n);) {
+            bool emit = false;
+            unsigned long long ekey = 0, ecode = 0;
+            if (j0 < n) {
+                const unsigned int rest = cf >> j0;
+                const unsigned int tz = rest ? (unsigned int)__builtin_ctz(rest) : 32u;
+                const unsigned int e = min(tz, (unsigned int)(n - 1 - j0));   // steps inside the run
+                const unsigned int len = e + 1;                                 // its cells
+                const unsigned int kept = __popc(__builtin_amdgcn_ubfe(kf, j0, len));
+                const unsigned int ys = __builtin_amdgcn_ubfe(yf, j0, e);
+                const unsigned int zs = __builtin_amdgcn_ubfe(zf, j0, e);
+                const unsigned int entry = (unsigned int)voxel_in_block(x, y, z);
+                ekey = block_key(x, y, z);
+                ecode = run_code(entry, len, ys, zs, kept);
+                emit = kept > 0;
+                n_upd += kept;
+                // the next run's first cell: the run's steps and the one leaving it
+                const int cy = __popc(__builtin_amdgcn_ubfe(yf, j0, len));
+                const int cz = __popc(__builtin_amdgcn_ubfe(zf, j0, len));
+                x += __mul24(s0, (int)len - cy - cz);
+                y += __mul24(s1, cy);
+                z += __mul24(s2, cz);
+                j0 += (int)len;
             }
-            if (emit) {
-                const int pos = base + __popcll(m & below);
-                L.lkey[wave][pos] = ekey;
-                L.lcode[wave][pos] = ecode;
-                L.llane[wave][pos] = (unsigned char)lane;
+            const unsigned long long m = __ballot(emit);
+            if (m) {
+                if (base + 64 > kListCap) {
+                    flush_runs(L, wave, lane, base, vol, own, depth_bits, meta, misses);
+                    base = 0;
+                }
+                if (emit) {
+                    const int pos = base + __popcll(m & below);
+                    L.lkey[wave][pos] = ekey;
+                    L.lcode[wave][pos] = ecode;
+                    L.llane[wave][pos] = (unsigned char)lane;
+                }
+                base += __popcll(m);
             }
-            base += __popcll(m);
         }
     }
     if (base > 0) flush_runs(L, wave, lane, base, vol, own, depth_bits, meta, misses);
@@ -630,7 +712,7 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
                     const int d2 = (rec.meta >> 30) & 1u ? -1 : 1;
                     const int e = code_entry(code), cells = code_cells(code);
                     int k0 = lo0 + (e & 7), k1 = lo1 + ((e >> 3) & 7), k2 = lo2 + (e >> 6);
-                    unsigned long long st = code >> kStepShift;
+                    unsigned int ys = code_ysteps(code), zs = code_zsteps(code);
                     for (int q = 0;;) {
                         float sdf;
                         if (centre_test(k0, k1, k2, dep, ax, vol.vs, vol.trunc, sdf)) {
@@ -639,11 +721,12 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
                             atomicAdd(L.wrgb + j, c);
                         }
                         if (++q >= cells) break;
-                        const int axis = (int)(st & 3u);
-                        st >>= 2;
-                        k0 += axis == 0 ? d0 : 0;
-                        k1 += axis == 1 ? d1 : 0;
-                        k2 += axis == 2 ? d2 : 0;
+                        const bool sy = ys & 1u, sz = zs & 1u;
+                        ys >>= 1;
+                        zs >>= 1;
+                        k0 += (sy || sz) ? 0 : d0;
+                        k1 += sy ? d1 : 0;
+                        k2 += sz ? d2 : 0;
                     }
                 }
                 __syncthreads();
