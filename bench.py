@@ -10,7 +10,8 @@ on parity: the run first checks the volume against the oracle's stored
 counts for the same seeded frames.  Per-call durations come from HIP events
 recorded on the launch stream around every allocate and update call; per
 kernel durations from the events the library records around each of its
-kernels on the same stream (tsdf_set_kernel_timing).  Prints one JSON line.
+kernels on the same stream (tsdf_set_kernel_timing), in separate steps of
+the same work after the timed ones.  Prints one JSON line.
 
 Rooflines.  The update kernel is HBM-bound; its algorithmic bytes per
 frame (per frame counts from the oracle) are
@@ -259,9 +260,6 @@ def main():
         if not all(gate.values()):
             raise SystemExit(f"parity gate failed ({mode}, batch {batch}): {gate}")
         ev = []
-        if use_events:
-            vol.set_kernel_timing(True)
-            vol.kernel_times()                       # drop the parity pass
 
         def step(record):
             vol.reset()
@@ -280,15 +278,24 @@ def main():
         for _ in range(warmup):
             step(False)
         torch.cuda.synchronize()
-        if use_events:
-            vol.kernel_times()                       # drop the warm-up
         t0 = time.perf_counter()
         for _ in range(steps):
             step(use_events)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         st = vol.stats()
-        kt = vol.kernel_times() if use_events else {}
+        kt = {}
+        if use_events:
+            # per-kernel durations from further steps of the same work with the
+            # library's kernel events on (kept out of the timed steps above,
+            # whose windows then hold only the kernels and their launch gaps)
+            vol.set_kernel_timing(True)
+            vol.kernel_times()
+            for _ in range(max(2, steps // 2)):
+                step(False)
+            torch.cuda.synchronize()
+            kt = vol.kernel_times()
+            vol.set_kernel_timing(False)
         t_alloc = [e[0].elapsed_time(e[1]) * 1e-3 for _, e in ev]
         t_upd = [e[1].elapsed_time(e[2]) * 1e-3 for _, e in ev]
         idx = [c for c, _ in ev]

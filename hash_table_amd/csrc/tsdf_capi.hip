@@ -123,7 +123,7 @@ struct tsdf_volume {
     tsdf_config cfg;
     tsdf_buffers buf;
     unsigned int mask;
-    unsigned int serial;        // allocate calls so far (frame stamp source)
+    unsigned int serial;        // allocate calls so far (selects the per-call counter set)
     int owner_grid;             // owner-update workgroups: as many as the device holds at once
     bool pending;               // an owner-mode allocate whose update has not run yet
     int32_t n_last;             // the frames of that allocate
@@ -170,7 +170,6 @@ OwnerArgs owner_args(const tsdf_volume* h, unsigned int serial) {
     std::memset(&o, 0, sizeof(o));
     o.build_items = h->cfg.update_mode == TSDF_UPDATE_OWNER;
     o.parity = serial & 1u;
-    o.stamp = serial;
     if (!o.build_items) return o;
     const ScratchLayout L = scratch_layout(h->cfg.table_entries, h->cfg.max_batch_pixels);
     char* base = static_cast<char*>(h->buf.scratch);

@@ -52,14 +52,11 @@ __device__ __forceinline__ unsigned long long* replica(unsigned long long* count
     return counters + (size_t)(blockIdx.x % kReplicas) * kCounterWords;
 }
 
-// 16-byte table entry: packed key, pool index, and (in the 4 bytes the
-// paper's entry leaves as padding) the serial of the last frame whose
-// allocate pass touched the block, so each touched block is handed to the
-// update pass exactly once per frame.
+// 16-byte table entry: packed key, pool index, 4 bytes of padding.
 struct __align__(16) Entry {
     unsigned long long key;
     unsigned int idx;
-    unsigned int stamp;
+    unsigned int pad;
 };
 
 constexpr unsigned int kNoSlot = 0xFFFFFFFFu;
@@ -167,8 +164,7 @@ struct OwnerArgs {
     uint2* seg_list;           // [kParts * seg_part_cap] (rec_base, block_off), grouped by block
     RunRecord* recs;           // [kParts * rec_part_cap] allocate order (read in place)
     unsigned int item_part_cap, seg_part_cap, rec_part_cap;
-    unsigned int parity;       // frame serial & 1
-    unsigned int stamp;        // frame serial, never 0xFFFFFFFF
+    unsigned int parity;       // call serial & 1
     int build_items;           // 0: ray-parallel update, nothing recorded
 };
 

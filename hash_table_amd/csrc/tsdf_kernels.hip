@@ -39,8 +39,6 @@ namespace {
 constexpr int kTile = 16;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kListCap = 256;     // block runs a wavefront buffers before de-duplicating
-constexpr int kSetCap = 256;      // per-wavefront LDS hash set (power of two, >= kListCap, <= 256)
 constexpr float kInv255 = 1.0f / 255.0f;
 constexpr int kChunkCells = 31;   // cells of a walk per pass of the allocate loop (plus a sentinel bit)
 
@@ -82,81 +80,129 @@ __device__ __forceinline__ void wave_lds_fence() {
 }
 
 // ---------------------------------------------------------------------------
-// allocate.  Each lane walks its ray and cuts it into runs, one per block it
-// crosses (a ray enters a block once); runs with at least one kept voxel are
-// compacted by ballot into a per-wavefront LDS list.  A full list is
-// de-duplicated by block key in a per-wavefront LDS hash set, and one lane
-// per distinct key probes the global table, all of the wavefront's distinct
-// keys in flight together.  For the owner update each (wavefront, block)
-// group of runs is then stored as a segment of run records.  Also counts
-// the point classes and the kept (point, voxel) pairs.
+// allocate.  Each lane walks its ray in chunks of up to kChunkCells cells and
+// cuts each chunk into runs, one per block the walk crosses; a lane holds
+// its runs with a kept voxel in kSlots register slots.  Full slots (or the
+// end of the chunk) are filed for the whole wavefront at once: the run keys
+// go into a per-wavefront LDS hash set, whose per-key run counter hands each
+// run its rank among the key's runs; one lane per distinct key probes the
+// global table and reserves the key's segment of run records; every lane
+// then writes the records of its own runs at the key's base + rank.  Also
+// counts the point classes and the kept (point, voxel) pairs.
 // ---------------------------------------------------------------------------
+constexpr int kSlots = 4;                         // runs a lane holds between filings
+constexpr int kSetCap = kSlots * 64;              // per-wavefront LDS set: room for every run of a filing
 constexpr unsigned int kNoBase = 0xFFFFFFFFu;     // runs not recorded (block rescanned)
 constexpr unsigned int kNoKeyBase = 0xFFFFFFFEu;  // runs of a key the full table refused
 
 struct AllocLds {
-    unsigned long long lkey[kWaves][kListCap];    // run list: block key,
-    unsigned long long lcode[kWaves][kListCap];   //   run code (first cell, cells, steps, kept),
-    unsigned char llane[kWaves][kListCap];        //   the lane (pixel) that walked it,
-    unsigned char lset[kWaves][kListCap];         //   its set slot
-    unsigned long long skey[kWaves][kSetCap];     // set: key,
-    unsigned int sruns[kWaves][kSetCap];          //   runs; after the reservation, the next record
-    unsigned char suniq[kWaves][kSetCap];         // occupied set slots, compacted
+    unsigned long long skey[kWaves][kSetCap];     // set: key (empty: all ones),
+    unsigned int scnt[kWaves][kSetCap];           //   its runs; after the reservation, its first record
+    unsigned char sslot[kWaves][kSetCap];         // set slots of the distinct keys, in insertion order
     unsigned int nuniq[kWaves];
     unsigned int hist[kProbeBins];
     unsigned int pmax;
     unsigned int cnt[6];
 };
 
-// depth and meta: this lane's point, for the records of the runs it walked
-__device__ void flush_runs(AllocLds& L, int wave, int lane, int n, const VolumeArgs& vol, const OwnerArgs& own,
-                           unsigned int depth, unsigned int meta, unsigned int& misses) {
+// A lane's runs since the last filing: slot q holds its q-th run (pend: a
+// run with a kept voxel waiting to be filed).
+struct RunSlots {
+    unsigned long long key[kSlots];
+    unsigned long long code[kSlots];
+    bool pend[kSlots];
+};
+
+// Home slot of a block key in the LDS set (multiply-xor of the key's halves).
+__device__ __forceinline__ unsigned int set_slot(unsigned long long key) {
+    const unsigned int lo = (unsigned int)key, hi = (unsigned int)(key >> 32);
+    return ((lo * 0x9E3779B1u) ^ (hi * 0x85EBCA77u)) >> 24;
+}
+static_assert(kSetCap == 256, "set_slot yields 8 bits");
+
+// File the wavefront's pending runs (see above).  depth and meta: this
+// lane's point, for the records of its runs.  Must be called by the whole
+// wavefront.
+__device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, int lane, unsigned int part,
+                                          const VolumeArgs& vol, const OwnerArgs& own, unsigned int depth,
+                                          unsigned int meta, unsigned int& misses) {
+    bool any_pend = false;
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) any_pend = any_pend || S.pend[q];
+    if (!__any(any_pend)) return;
+    const int wave = threadIdx.x >> 6;
+    unsigned long long* skey = L.skey[wave];
+    unsigned int* scnt = L.scnt[wave];
+    unsigned char* sslot = L.sslot[wave];
     for (int i = lane; i < kSetCap; i += 64) {
-        L.skey[wave][i] = kEmptyKey;
-        L.sruns[wave][i] = 0;
+        skey[i] = kEmptyKey;
+        scnt[i] = 0;
     }
     if (lane == 0) L.nuniq[wave] = 0;
     wave_lds_fence();
-    for (int i = lane; i < n; i += 64) {
-        const unsigned long long key = L.lkey[wave][i];
-        unsigned int h = home_slot(key, kSetCap - 1);
-        for (;;) {     // n <= kSetCap distinct keys at most: the probe always finds room
-            const unsigned long long prev = atomicCAS(&L.skey[wave][h], kEmptyKey, key);
-            if (prev == kEmptyKey) {
-                L.suniq[wave][atomicAdd(&L.nuniq[wave], 1u)] = (unsigned char)h;
-                break;
+    // de-duplicate: each pending run finds (or enters) its key in the set
+    // and takes a rank among the key's runs
+    unsigned int hq[kSlots], rk[kSlots];
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) {
+        hq[q] = 0;
+        rk[q] = 0;
+        if (!__any(S.pend[q])) continue;
+        if (S.pend[q]) {
+            const unsigned long long key = S.key[q];
+            unsigned int h = set_slot(key);
+            for (;;) {     // at most kSetCap distinct keys: the probe always finds room
+                const unsigned long long prev = atomicCAS(&skey[h], kEmptyKey, key);
+                if (prev == kEmptyKey) {
+                    sslot[atomicAdd(&L.nuniq[wave], 1u)] = (unsigned char)h;
+                    break;
+                }
+                if (prev == key) break;
+                h = (h + 1) & (kSetCap - 1);
             }
-            if (prev == key) break;
-            h = (h + 1) & (kSetCap - 1);
+            hq[q] = h;
+            rk[q] = atomicAdd(&scnt[h], 1u);
         }
-        L.lset[wave][i] = (unsigned char)h;
-        atomicAdd(&L.sruns[wave][h], 1u);
     }
     wave_lds_fence();
     const int nu = (int)L.nuniq[wave];
     const unsigned long long below = (1ull << lane) - 1ull;
-    const unsigned int part = (blockIdx.x * kWaves + wave) % kParts;
     FrameCounters* fc = own.fc + own.parity;         // owner mode only
-    for (int j0 = 0; j0 < nu; j0 += 64) {           // wavefront-uniform
-        const int j = j0 + lane;
-        const bool has = j < nu;
-        int h = 0;
-        unsigned int slot = kNoSlot;
+    for (int d0 = 0; d0 < nu; d0 += 64) {           // wavefront-uniform: 64 distinct keys at a time
+        const int d = d0 + lane;
+        const bool has = d < nu;
+        unsigned int h = 0, slot = kNoSlot;
         bool won = false;
         if (has) {
-            h = L.suniq[wave][j];
+            h = sslot[d];
             unsigned int probes;
-            slot = insert_key(vol, L.skey[wave][h], won, probes);
+            slot = insert_key(vol, skey[h], won, probes);
             hist_add(L.hist, &L.pmax, probes);
         }
         claim_pool_indices(vol, won, slot);
         if (!own.build_items) continue;             // the ray-parallel update needs nothing more
-        // first touch of the block this frame: the stamp exchange lets one
-        // caller per frame through; the wavefront's new blocks take item
-        // numbers in its partition with one atomic
-        bool first = false;
-        if (has && slot != kNoSlot && vol.table[slot].stamp != own.stamp)
-            first = atomicExch(&vol.table[slot].stamp, own.stamp) != own.stamp;
+        // Segments and records: one reservation in the partition for the
+        // whole wavefront and, in the same round trip, one add per block on
+        // its counter (segments << 32 | runs).  The wavefront that finds a
+        // block's counter at zero is the first to touch it in this call and
+        // lists it for the update (the update zeroes the counter when it has
+        // finished the block); its new blocks take item numbers in the
+        // partition with one atomic.
+        const bool rsv = has && slot != kNoSlot;
+        const unsigned int runs = rsv ? scnt[h] : 0u;
+        unsigned int x = runs;                       // inclusive prefix of runs over the lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        const unsigned int total = __shfl(x, 63, 64);
+        const unsigned long long rm = __ballot(rsv);
+        unsigned long long bc = 0, r0 = 0;
+        if (rsv) bc = atomicAdd(own.blk_count + slot, (1ull << 32) | runs);
+        if (rm && lane == 0) r0 = atomicAdd(&fc->segrec[part], ((unsigned long long)__popcll(rm) << 32) | total);
+        r0 = __shfl(r0, 0, 64);
+        const bool first = rsv && bc == 0;
         const unsigned long long fm = __ballot(first);
         if (fm) {
             unsigned int ib = 0;
@@ -170,35 +216,19 @@ __device__ void flush_runs(AllocLds& L, int wave, int lane, int n, const VolumeA
                     own.items_spill[atomicAdd(&fc->items_spill, 1u)] = slot;
             }
         }
-        // segments and records: one reservation for the whole wavefront
-        const bool rsv = has && slot != kNoSlot;
-        const unsigned int runs = rsv ? L.sruns[wave][h] : 0u;
-        unsigned int x = runs;                       // inclusive prefix of runs over the lanes
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const unsigned int y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
-        }
-        const unsigned int total = __shfl(x, 63, 64);
-        const unsigned long long rm = __ballot(rsv);
-        unsigned long long r0 = 0;
-        if (rm) {
-            if (lane == 0) r0 = atomicAdd(&fc->segrec[part], ((unsigned long long)__popcll(rm) << 32) | total);
-            r0 = __shfl(r0, 0, 64);
-        }
+        unsigned int rbase = kNoKeyBase;             // the full table refused the key: its kept visits are lost
         if (rsv) {
             const unsigned int seg = (unsigned int)(r0 >> 32) + (unsigned int)__popcll(rm & below);
             const unsigned int rec = (unsigned int)r0 + (x - runs);
             Segment* segs = own.segs + (size_t)part * own.seg_part_cap;
             if (seg < own.seg_part_cap && (unsigned long long)rec + runs <= own.rec_part_cap) {
-                const unsigned long long bc = atomicAdd(own.blk_count + slot, (1ull << 32) | runs);
                 Segment sg;
                 sg.slot = slot;
                 sg.rec_base = part * own.rec_part_cap + rec;
                 sg.block_off = (unsigned int)bc & ~kSegOverflow;
                 sg.seg_pos = (unsigned int)(bc >> 32);
                 segs[seg] = sg;
-                L.sruns[wave][h] = sg.rec_base;
+                rbase = sg.rec_base;
             } else {                                 // out of space: the update rescans the block
                 if (seg < own.seg_part_cap) {        // the placing pass reads every reserved segment
                     Segment sg;
@@ -209,39 +239,84 @@ __device__ void flush_runs(AllocLds& L, int wave, int lane, int n, const VolumeA
                     segs[seg] = sg;
                 }
                 atomicOr(own.blk_count + slot, (unsigned long long)kSegOverflow);
-                L.sruns[wave][h] = kNoBase;
-            }
-        } else if (has) {                            // the full table refused the key: its
-            L.sruns[wave][h] = kNoKeyBase;           // kept visits are lost, counted below
-        }
-    }
-    wave_lds_fence();
-    if (own.build_items) {
-        for (int i0 = 0; i0 < n; i0 += 64) {          // wavefront-uniform: every lane shuffles
-            const int i = i0 + lane;
-            const int src = i < n ? (int)L.llane[wave][i] : 0;
-            const unsigned int d = __shfl(depth, src, 64), m = __shfl(meta, src, 64);
-            if (i >= n) continue;
-            const int h = L.lset[wave][i];
-            const unsigned int base = L.sruns[wave][h];
-            const unsigned long long code = L.lcode[wave][i];
-            if (base == kNoKeyBase) {
-                misses += (unsigned int)code_kept(code);
-            } else if (base != kNoBase) {
-                const unsigned int rec = atomicAdd(&L.sruns[wave][h], 1u);
-                RunRecord r;
-                r.depth = d;
-                r.meta = m;
-                r.code_lo = (unsigned int)code;
-                r.code_hi = (unsigned int)(code >> 32);
-                own.recs[rec] = r;
+                rbase = kNoBase;
             }
         }
+        if (has) scnt[h] = rbase;                    // the key's runs are counted: keep its base instead
     }
+    if (!own.build_items) return;
     wave_lds_fence();
+    // every lane: the records of its runs
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) {
+        if (!S.pend[q]) continue;
+        const unsigned int b = scnt[hq[q]];
+        if (b == kNoKeyBase) {
+            misses += (unsigned int)code_kept(S.code[q]);
+        } else if (b != kNoBase) {
+            RunRecord r;
+            r.depth = depth;
+            r.meta = meta;
+            r.code_lo = (unsigned int)S.code[q];
+            r.code_hi = (unsigned int)(S.code[q] >> 32);
+            own.recs[b + rk[q]] = r;
+        }
+    }
 }
 
-// (at least 5 wavefronts per SIMD: the LDS of five workgroups fits a CU)
+__device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, unsigned int zp, unsigned int cp,
+                                             int itc, int x, int y, int z, int s0, int s1, int s2, AllocLds& L,
+                                             int lane, unsigned int part, const VolumeArgs& vol,
+                                             const OwnerArgs& own, unsigned int depth_bits, unsigned int meta,
+                                             unsigned int& n_upd, unsigned int& misses) {
+    // planes in walk order, bit j = the chunk's cell j: the kept plane's
+    // sentinel marks the n cells this lane walked; the step planes were
+    // shifted once per iteration
+    const int n = 31 - __clz(kp);
+    const unsigned int kf = n ? __builtin_bitreverse32(kp) >> ((unsigned int)(32 - n) & 31u) : 0u;
+    const unsigned int shp = (unsigned int)(32 - itc) & 31u;
+    const unsigned int yf = itc ? __builtin_bitreverse32(yp) >> shp : 0u;
+    const unsigned int zf = itc ? __builtin_bitreverse32(zp) >> shp : 0u;
+    const unsigned int cf = itc ? __builtin_bitreverse32(cp) >> shp : 0u;
+    // cut into runs: a run ends at a cell whose step leaves the block, or
+    // at the lane's last cell of the chunk; up to kSlots runs per lane
+    // between filings
+    for (int j0 = 0; __any(j0 < n);) {
+        RunSlots S;
+#pragma unroll
+        for (int q = 0; q < kSlots; ++q) {
+            S.key[q] = 0;
+            S.code[q] = 0;
+            S.pend[q] = false;
+        }
+#pragma unroll
+        for (int q = 0; q < kSlots; ++q) {
+            if (!__any(j0 < n)) break;
+            if (j0 < n) {
+                const unsigned int rest = cf >> j0;
+                const unsigned int tz = rest ? (unsigned int)__builtin_ctz(rest) : 32u;
+                const unsigned int e = min(tz, (unsigned int)(n - 1 - j0));   // steps inside the run
+                const unsigned int len = e + 1;                                 // its cells
+                const unsigned int kept = __popc(__builtin_amdgcn_ubfe(kf, j0, len));
+                const unsigned int ys = __builtin_amdgcn_ubfe(yf, j0, e);
+                const unsigned int zs = __builtin_amdgcn_ubfe(zf, j0, e);
+                S.key[q] = block_key(x, y, z);
+                S.code[q] = run_code((unsigned int)voxel_in_block(x, y, z), len, ys, zs, kept);
+                S.pend[q] = kept > 0;
+                n_upd += kept;
+                // the next run's first cell: the run's steps and the one leaving it
+                const int cy = __popc(__builtin_amdgcn_ubfe(yf, j0, len));
+                const int cz = __popc(__builtin_amdgcn_ubfe(zf, j0, len));
+                x += __mul24(s0, (int)len - cy - cz);
+                y += __mul24(s1, cy);
+                z += __mul24(s2, cz);
+                j0 += (int)len;
+            }
+        }
+        file_runs(S, L, lane, part, vol, own, depth_bits, meta, misses);
+    }
+}
+
 __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ AllocLds L;
     const int fi = blockIdx.x / B.tile_grid;                 // frame of this workgroup
@@ -261,7 +336,6 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const unsigned long long below = (1ull << lane) - 1ull;
     int u, v;
     thread_pixel(tu, tv, u, v);
     const unsigned int pix = (unsigned int)v * (unsigned int)f.width + (unsigned int)u;
@@ -287,17 +361,14 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
     }
     const unsigned int depth_bits = __float_as_uint(depth);
     unsigned int n_upd = 0, n_guard = 0, misses = 0;
-    int base = 0;                             // wavefront-uniform fill of the run list
+    const unsigned int part = (blockIdx.x * kWaves + wave) % kParts;   // this wavefront's reservations
     const int max_visits = f.max_visits;
     const float vs = vol.vs, trunc = vol.trunc;
     const DepthAxis ax = depth_axis(f);
 
     // Walk state in registers, per axis: cell, next boundary parameter,
-    // start and reciprocal of the direction (both in voxel units), step,
-    // the offset of the next boundary's cell (1 when stepping up), and the
-    // centre's term of the camera depth, axis_r * (centre - t), recomputed
-    // from the cell whenever the cell changes (same operations as a full
-    // evaluation, so the depth sum below is the one the written rule gives).
+    // start and reciprocal of the direction (both in voxel units), step, and
+    // the offset of the next boundary's cell (1 when stepping up).
     int k0 = 0, k1 = 0, k2 = 0, s0 = 0, s1 = 0, s2 = 0;
     float tm0 = 0.f, tm1 = 0.f, tm2 = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, i0 = 0.f, i1 = 0.f, i2 = 0.f;
     if (alive) {
@@ -308,69 +379,62 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
         i0 = w.inv0; i1 = w.inv1; i2 = w.inv2;
     }
     const int o0 = s0 > 0, o1 = s1 > 0, o2 = s2 > 0;
-    float p0 = ax.r2 * ((((float)k0 + 0.5f) * vs) - ax.t0);
-    float p1 = ax.r5 * ((((float)k1 + 0.5f) * vs) - ax.t1);
-    float p2 = ax.r8 * ((((float)k2 + 0.5f) * vs) - ax.t2);
     const float dd = depth;
-    // the centre test of the walk's current cell (evaluated on entering it)
-    bool keep;
+    bool keep;                                // the centre test of the walk's current cell
     {
-        const float sdf = dd - ((p0 + p1) + p2);
-        keep = sdf >= -trunc && sdf <= trunc;
+        float sdf;
+        keep = centre_test(k0, k1, k2, dd, ax, vs, trunc, sdf);
     }
 
     // The walk goes in chunks of up to kChunkCells cells.  All lanes start
     // together, so a lane's cell index within the chunk is the (uniform)
     // iteration count; each iteration shifts one bit into four per-lane
     // planes: the cell was kept, the step after it moved along y, along z,
-    // left the block.  After the chunk the planes are cut into runs (one
-    // per block the chunk's part of the walk crosses), which go to the
-    // wavefront's run list.  A walk longer than a chunk has its run at the
-    // chunk boundary split in two records of the same block: the update
-    // adds both.
-    for (int done = 0; __any(alive); done += kChunkCells) {
-        int x = k0, y = k1, z = k2;           // the chunk's first cell
-        unsigned int kp = 1u, yp = 0u, zp = 0u, cp = 0u;   // kept plane starts with a sentinel bit
+    // left the block.  Every lane runs the step (the stepped axis is chosen
+    // by selects, not branches); a finished walk neither moves nor shifts its
+    // kept plane, and its step bits stay zero.  After the chunk the planes
+    // are cut into runs (one per block the chunk's part of the walk crosses)
+    // and filed.  A walk longer than a chunk has its run at the chunk
+    // boundary split in two records of the same block: the update adds both.
+    int x, y, z;                              // the chunk's first cell
+    unsigned int kp, yp, zp, cp;              // its planes
+    int last_itc = 0;
+    for (int done = 0;; done += kChunkCells) {
+        x = k0;
+        y = k1;
+        z = k2;
+        kp = 1u;                              // the kept plane starts with a sentinel bit
+        yp = zp = cp = 0u;
         // the safety bound on cells per walk limits the chunk (uniform)
         const int lim = min(kChunkCells, max_visits - done);
-        for (int it = 0; it < lim; ++it) {
+        int itc = 0;                                   // iterations of this chunk (uniform)
+        for (; itc < lim; ++itc) {
             if (!__any(alive)) break;
-            if (alive) {
-                kp = kp + kp + (keep ? 1u : 0u);
-                const float tmin = fminf(fminf(tm0, tm1), tm2);
-                const bool more = tmin <= 1.0f;
-                // smallest boundary parameter, ties to x, then y
-                const bool e0 = tm0 == tmin, e1 = tm1 == tmin;
-                const bool a0 = more && e0, a1 = more && !e0 && e1, a2 = more && !e0 && !e1;
-                yp = yp + yp + (a1 ? 1u : 0u);
-                zp = zp + zp + (a2 ? 1u : 0u);
-                bool cr = false;
-                if (a0) {
-                    const int prev = k0;
-                    k0 += s0;
-                    tm0 = ((float)(k0 + o0) - g0) * i0;
-                    p0 = ax.r2 * ((((float)k0 + 0.5f) * vs) - ax.t0);
-                    cr = (unsigned int)(k0 ^ prev) > 7u;   // the block index (k >> 3) changed
-                }
-                if (a1) {
-                    const int prev = k1;
-                    k1 += s1;
-                    tm1 = ((float)(k1 + o1) - g1) * i1;
-                    p1 = ax.r5 * ((((float)k1 + 0.5f) * vs) - ax.t1);
-                    cr = (unsigned int)(k1 ^ prev) > 7u;   // the block index (k >> 3) changed
-                }
-                if (a2) {
-                    const int prev = k2;
-                    k2 += s2;
-                    tm2 = ((float)(k2 + o2) - g2) * i2;
-                    p2 = ax.r8 * ((((float)k2 + 0.5f) * vs) - ax.t2);
-                    cr = (unsigned int)(k2 ^ prev) > 7u;   // the block index (k >> 3) changed
-                }
-                cp = cp + cp + (cr ? 1u : 0u);
-                const float sdf = dd - ((p0 + p1) + p2);       // the cell just entered
-                keep = sdf >= -trunc && sdf <= trunc;
-                alive = more;
-            }
+            const float tmin = fminf(fminf(tm0, tm1), tm2);
+            const bool more = alive && tmin <= 1.0f;
+            kp = alive ? kp + kp + (keep ? 1u : 0u) : kp;
+            const bool e0 = tm0 == tmin, e1 = tm1 == tmin;
+            const bool a0 = more && e0, a1 = more && !e0 && e1, a2 = more && !e0 && !e1;
+            yp = yp + yp + (a1 ? 1u : 0u);
+            zp = zp + zp + (a2 ? 1u : 0u);
+            const int kc = e0 ? k0 : (e1 ? k1 : k2);
+            const int sc = e0 ? s0 : (e1 ? s1 : s2);
+            const int oc = e0 ? o0 : (e1 ? o1 : o2);
+            const float gc = e0 ? g0 : (e1 ? g1 : g2);
+            const float ic = e0 ? i0 : (e1 ? i1 : i2);
+            const int kn = kc + sc;
+            const float tn = ((float)(kn + oc) - gc) * ic;
+            const bool cr = more && (unsigned int)(kn ^ kc) > 7u;
+            cp = cp + cp + (cr ? 1u : 0u);
+            k0 = a0 ? kn : k0;
+            k1 = a1 ? kn : k1;
+            k2 = a2 ? kn : k2;
+            tm0 = a0 ? tn : tm0;
+            tm1 = a1 ? tn : tm1;
+            tm2 = a2 ? tn : tm2;
+            float sdf;
+            keep = centre_test(k0, k1, k2, dd, ax, vs, trunc, sdf);
+            alive = more;
         }
         // A walk still going after max_visits cells is cut there (counted).
         // Its last iteration took one more step; that step's bits sit after
@@ -379,57 +443,16 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
             ++n_guard;
             alive = false;
         }
-        // planes in walk order: bit j = the chunk's cell j (the sentinel marks
-        // how many cells this lane walked in the chunk)
-        const int n = 31 - __clz(kp);
-        const unsigned int sh = (unsigned int)(32 - n) & 31u;
-        const unsigned int kf = n ? __builtin_bitreverse32(kp) >> sh : 0u;
-        const unsigned int yf = n ? __builtin_bitreverse32(yp) >> sh : 0u;
-        const unsigned int zf = n ? __builtin_bitreverse32(zp) >> sh : 0u;
-        const unsigned int cf = n ? __builtin_bitreverse32(cp) >> sh : 0u;
-        // cut into runs: a run ends at a cell whose step leaves the block, or
-        // at the lane's last cell of the chunk
-        for (int j0 = 0; __any(j0 < n);) {
-            bool emit = false;
-            unsigned long long ekey = 0, ecode = 0;
-            if (j0 < n) {
-                const unsigned int rest = cf >> j0;
-                const unsigned int tz = rest ? (unsigned int)__builtin_ctz(rest) : 32u;
-                const unsigned int e = min(tz, (unsigned int)(n - 1 - j0));   // steps inside the run
-                const unsigned int len = e + 1;                                 // its cells
-                const unsigned int kept = __popc(__builtin_amdgcn_ubfe(kf, j0, len));
-                const unsigned int ys = __builtin_amdgcn_ubfe(yf, j0, e);
-                const unsigned int zs = __builtin_amdgcn_ubfe(zf, j0, e);
-                const unsigned int entry = (unsigned int)voxel_in_block(x, y, z);
-                ekey = block_key(x, y, z);
-                ecode = run_code(entry, len, ys, zs, kept);
-                emit = kept > 0;
-                n_upd += kept;
-                // the next run's first cell: the run's steps and the one leaving it
-                const int cy = __popc(__builtin_amdgcn_ubfe(yf, j0, len));
-                const int cz = __popc(__builtin_amdgcn_ubfe(zf, j0, len));
-                x += __mul24(s0, (int)len - cy - cz);
-                y += __mul24(s1, cy);
-                z += __mul24(s2, cz);
-                j0 += (int)len;
-            }
-            const unsigned long long m = __ballot(emit);
-            if (m) {
-                if (base + 64 > kListCap) {
-                    flush_runs(L, wave, lane, base, vol, own, depth_bits, meta, misses);
-                    base = 0;
-                }
-                if (emit) {
-                    const int pos = base + __popcll(m & below);
-                    L.lkey[wave][pos] = ekey;
-                    L.lcode[wave][pos] = ecode;
-                    L.llane[wave][pos] = (unsigned char)lane;
-                }
-                base += __popcll(m);
-            }
+        if (!__any(alive)) {                 // every walk ended: file this chunk after the loop
+            last_itc = itc;
+            break;
         }
+        // a walk goes on into another chunk: file this one's runs now
+        cut_and_file(kp, yp, zp, cp, itc, x, y, z, s0, s1, s2, L, lane, part, vol, own, depth_bits, meta, n_upd,
+                     misses);
     }
-    if (base > 0) flush_runs(L, wave, lane, base, vol, own, depth_bits, meta, misses);
+    cut_and_file(kp, yp, zp, cp, last_itc, x, y, z, s0, s1, s2, L, lane, part, vol, own, depth_bits, meta, n_upd,
+                 misses);
 
     const unsigned int c_valid = wave_sum(cls == kValid);
     const unsigned int c_near = wave_sum(cls == kNear);

@@ -101,7 +101,7 @@ typedef struct {
 /* Device memory owned by the caller, all 16-byte aligned. */
 typedef struct {
     void* table;            /* table_entries * 16 bytes; entry = {uint64 key, uint32 pool index,
-                               uint32 stamp: last frame whose allocate touched the block} */
+                               uint32 padding} */
     float* tsdf;            /* pool_capacity * 512 floats each: per-voxel sums of the */
     float* weight;          /*   normalised signed distance (sdf / trunc), of the weight, */
     float* r;               /*   and of the colour channels (0..1).  Voxel v of block i is */
