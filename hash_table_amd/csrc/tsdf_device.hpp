@@ -483,6 +483,13 @@ __device__ __forceinline__ unsigned int insert_key(const VolumeArgs& vol, unsign
     }
 }
 
+// Lane 0's value, as a wavefront-uniform scalar (lane 0 must be active).
+__device__ __forceinline__ unsigned int read_lane0(unsigned int x) { return __builtin_amdgcn_readlane(x, 0); }
+__device__ __forceinline__ unsigned long long read_lane0(unsigned long long x) {
+    return ((unsigned long long)__builtin_amdgcn_readlane((unsigned int)(x >> 32), 0) << 32) |
+           (unsigned int)__builtin_amdgcn_readlane((unsigned int)x, 0);
+}
+
 // The lanes of a wavefront that inserted keys take consecutive pool indices
 // with one atomic, and publish them (kNoIndex once the pool is full).  Must
 // be called by the whole wavefront.
@@ -492,7 +499,7 @@ __device__ __forceinline__ void claim_pool_indices(const VolumeArgs& vol, bool w
     const int lane = threadIdx.x & 63;
     unsigned long long base = 0;
     if (lane == 0) base = atomicAdd(vol.counters + kBlockCounter, (unsigned long long)__popcll(m));
-    base = __shfl(base, 0, 64);
+    base = read_lane0(base);
     if (won) {
         const unsigned long long idx = base + (unsigned long long)__popcll(m & ((1ull << lane) - 1ull));
         const unsigned int pub = idx < vol.capacity ? (unsigned int)idx : kNoIndex;
@@ -523,11 +530,8 @@ __device__ __forceinline__ unsigned int lookup_key(const VolumeArgs& vol, unsign
     }
 }
 
-__device__ __forceinline__ unsigned int wave_sum(unsigned int x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
-}
+// Sum over the wavefront (every lane active): DPP row operations, no LDS.
+__device__ __forceinline__ unsigned int wave_sum(unsigned int x) { return __reduce_add_sync(~0ull, x); }
 
 __device__ __forceinline__ void unpack_key(unsigned long long key, int& bx, int& by, int& bz) {
     bx = (int)(key & 0x1FFFFFull) - kKeyBias;

@@ -100,6 +100,7 @@ struct AllocLds {
     unsigned int scnt[kWaves][kSetCap];           //   its runs; after the reservation, its first record
     unsigned char sslot[kWaves][kSetCap];         // set slots of the distinct keys, in insertion order
     unsigned int nuniq[kWaves];
+    unsigned int nrec[kWaves];                    // records of a filing round, claimed so far
     unsigned int hist[kProbeBins];
     unsigned int pmax;
     unsigned int cnt[6];
@@ -130,7 +131,7 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, int lane, un
 #pragma unroll
     for (int q = 0; q < kSlots; ++q) any_pend = any_pend || S.pend[q];
     if (!__any(any_pend)) return;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     unsigned long long* skey = L.skey[wave];
     unsigned int* scnt = L.scnt[wave];
     unsigned char* sslot = L.sslot[wave];
@@ -190,24 +191,24 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, int lane, un
         // partition with one atomic.
         const bool rsv = has && slot != kNoSlot;
         const unsigned int runs = rsv ? scnt[h] : 0u;
-        unsigned int x = runs;                       // inclusive prefix of runs over the lanes
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const unsigned int y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
-        }
-        const unsigned int total = __shfl(x, 63, 64);
+        // the key's runs within the wavefront's share of records (disjoint
+        // ranges; their order does not matter)
+        if (lane == 0) L.nrec[wave] = 0;
+        wave_lds_fence();
+        const unsigned int roff = rsv ? atomicAdd(&L.nrec[wave], runs) : 0u;
+        wave_lds_fence();
+        const unsigned int total = L.nrec[wave];
         const unsigned long long rm = __ballot(rsv);
         unsigned long long bc = 0, r0 = 0;
         if (rsv) bc = atomicAdd(own.blk_count + slot, (1ull << 32) | runs);
         if (rm && lane == 0) r0 = atomicAdd(&fc->segrec[part], ((unsigned long long)__popcll(rm) << 32) | total);
-        r0 = __shfl(r0, 0, 64);
+        r0 = read_lane0(r0);
         const bool first = rsv && bc == 0;
         const unsigned long long fm = __ballot(first);
         if (fm) {
             unsigned int ib = 0;
             if (lane == 0) ib = atomicAdd(&fc->items[part], (unsigned int)__popcll(fm));
-            ib = __shfl(ib, 0, 64);
+            ib = read_lane0(ib);
             if (first) {
                 const unsigned int k = ib + (unsigned int)__popcll(fm & below);
                 if (k < own.item_part_cap)
@@ -219,7 +220,7 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, int lane, un
         unsigned int rbase = kNoKeyBase;             // the full table refused the key: its kept visits are lost
         if (rsv) {
             const unsigned int seg = (unsigned int)(r0 >> 32) + (unsigned int)__popcll(rm & below);
-            const unsigned int rec = (unsigned int)r0 + (x - runs);
+            const unsigned int rec = (unsigned int)r0 + roff;
             Segment* segs = own.segs + (size_t)part * own.seg_part_cap;
             if (seg < own.seg_part_cap && (unsigned long long)rec + runs <= own.rec_part_cap) {
                 Segment sg;
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
     if (threadIdx.x == 0) L.pmax = 0;
     __syncthreads();
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     int u, v;
     thread_pixel(tu, tv, u, v);
@@ -347,6 +348,16 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
         cls = setup_walk(w, depth, u, v, f, vol.trunc, vol.inv_vs);
     }
     bool alive = cls == kValid;
+    {   // point classes, counted now so the class is not kept through the walk
+        const unsigned int c_valid = (unsigned int)__popcll(__ballot(cls == kValid));
+        const unsigned int c_near = (unsigned int)__popcll(__ballot(cls == kNear));
+        const unsigned int c_oor = (unsigned int)__popcll(__ballot(cls == kOutside));
+        if (lane == 0) {
+            if (c_valid) atomicAdd(L.cnt + 0, c_valid);
+            if (c_near) atomicAdd(L.cnt + 1, c_near);
+            if (c_oor) atomicAdd(L.cnt + 2, c_oor);
+        }
+    }
     // what the update needs of this point besides the run codes: depth,
     // colour (when the frame has it: an update needs the same frame, colour
     // included), frame of the batch and the directions of the stepping axes
@@ -367,8 +378,7 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
     const DepthAxis ax = depth_axis(f);
 
     // Walk state in registers, per axis: cell, next boundary parameter,
-    // start and reciprocal of the direction (both in voxel units), step, and
-    // the offset of the next boundary's cell (1 when stepping up).
+    // start and reciprocal of the direction (both in voxel units), and step.
     int k0 = 0, k1 = 0, k2 = 0, s0 = 0, s1 = 0, s2 = 0;
     float tm0 = 0.f, tm1 = 0.f, tm2 = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, i0 = 0.f, i1 = 0.f, i2 = 0.f;
     if (alive) {
@@ -378,7 +388,6 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
         g0 = w.gA0; g1 = w.gA1; g2 = w.gA2;
         i0 = w.inv0; i1 = w.inv1; i2 = w.inv2;
     }
-    const int o0 = s0 > 0, o1 = s1 > 0, o2 = s2 > 0;
     const float dd = depth;
     bool keep;                                // the centre test of the walk's current cell
     {
@@ -419,11 +428,10 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
             zp = zp + zp + (a2 ? 1u : 0u);
             const int kc = e0 ? k0 : (e1 ? k1 : k2);
             const int sc = e0 ? s0 : (e1 ? s1 : s2);
-            const int oc = e0 ? o0 : (e1 ? o1 : o2);
             const float gc = e0 ? g0 : (e1 ? g1 : g2);
             const float ic = e0 ? i0 : (e1 ? i1 : i2);
             const int kn = kc + sc;
-            const float tn = ((float)(kn + oc) - gc) * ic;
+            const float tn = ((float)(kn + (sc > 0 ? 1 : 0)) - gc) * ic;   // the new cell's next boundary
             const bool cr = more && (unsigned int)(kn ^ kc) > 7u;
             cp = cp + cp + (cr ? 1u : 0u);
             k0 = a0 ? kn : k0;
@@ -454,16 +462,10 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
     cut_and_file(kp, yp, zp, cp, last_itc, x, y, z, s0, s1, s2, L, lane, part, vol, own, depth_bits, meta, n_upd,
                  misses);
 
-    const unsigned int c_valid = wave_sum(cls == kValid);
-    const unsigned int c_near = wave_sum(cls == kNear);
-    const unsigned int c_oor = wave_sum(cls == kOutside);
     const unsigned int c_upd = wave_sum(n_upd);
     const unsigned int c_guard = wave_sum(n_guard);
     const unsigned int c_miss = wave_sum(misses);
     if (lane == 0) {
-        if (c_valid) atomicAdd(L.cnt + 0, c_valid);
-        if (c_near) atomicAdd(L.cnt + 1, c_near);
-        if (c_oor) atomicAdd(L.cnt + 2, c_oor);
         if (c_upd) atomicAdd(L.cnt + 3, c_upd);
         if (c_guard) atomicAdd(L.cnt + 4, c_guard);
         if (c_miss) atomicAdd(L.cnt + 5, c_miss);
