@@ -227,19 +227,12 @@ struct BandWalk {
 __device__ __forceinline__ void setup_axis(float gA, float gB, int& k, int& s, float& inv, float& tm) {
     k = (int)floorf(gA);
     const float dir = gB - gA;
-    if (dir > kStillAxis) {
-        s = 1;
-        inv = 1.0f / dir;
-        tm = ((float)(k + 1) - gA) * inv;
-    } else if (dir < -kStillAxis) {
-        s = -1;
-        inv = 1.0f / dir;
-        tm = ((float)k - gA) * inv;
-    } else {
-        s = 0;
-        inv = 0.0f;
-        tm = __builtin_inff();
-    }
+    // one division for both signs (a branch each would run both when the
+    // lanes of a wavefront disagree)
+    const float r = 1.0f / dir;
+    s = dir > kStillAxis ? 1 : (dir < -kStillAxis ? -1 : 0);
+    inv = s != 0 ? r : 0.0f;
+    tm = s > 0 ? ((float)(k + 1) - gA) * r : (s < 0 ? ((float)k - gA) * r : __builtin_inff());
 }
 
 // Classify pixel (u, v) with depth d and, for a valid point, set up its walk.
