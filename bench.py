@@ -84,8 +84,8 @@ def load_counts(name):
 MEASURED_TRAFFIC = {
     # (kernel, workload, frames per call, update mode): (bytes per launch, source digest)
     # profiles/integrate_room640x480_batch16.md
-    ("k_allocate", "room640x480", 16, "owner"): (241853658, "4fd5e94bd97e05cc"),
-    ("k_update_owner", "room640x480", 16, "owner"): (753449867, "4fd5e94bd97e05cc"),
+    ("k_allocate", "room640x480", 16, "owner"): (238552015, "c0eb53863e4a8246"),
+    ("k_update_owner", "room640x480", 16, "owner"): (777690282, "c0eb53863e4a8246"),
 }
 
 
