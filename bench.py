@@ -200,6 +200,79 @@ def cpu_baseline(wl, n_frames):
     }
 
 
+def sweep(args, torch, tsdf, scenes, stream):
+    """The paper's two opposite sweep axes on the room scene: point count at
+    fixed geometry (fx proportional to the image width) and extent at fixed
+    angular resolution (fx fixed).  Each cell integrates the scene's first 16
+    frames in one batched call into a freshly reset volume; the first call is
+    the parity gate against the oracle's stored counts for the same frames,
+    then `--sweep-reps` calls are timed (HIP events around allocate and
+    update, reset outside the windows).  Returns one record per cell."""
+    sh = stream.cuda_stream
+    cells = []
+    for axis, W, H, fx in scenes.SWEEP_CELLS:
+        name = scenes.cell_name(W, H, fx) if (W, H, fx) != (640, 480, 525.0) else "room640x480"
+        wl = scenes.workload(name)
+        counts = load_counts(name)
+        n = 16
+        host = [wl.frame(i) for i in range(n)]
+        for i in (0, n - 1):
+            if scenes.frame_digest([host[i]]) != counts["frames"][i]["sha256"]:
+                raise SystemExit(f"{name}: generated frames differ from the stored oracle counts")
+        fr = counts["frames"][:n]
+        want = {"blocks": fr[-1]["blocks_total"], "voxel_updates": sum(f["voxel_updates"] for f in fr),
+                "points_valid": sum(f["points_valid"] for f in fr)}
+        frames = [tsdf.DeviceFrame(f) for f in host]
+        vol = tsdf.Volume(wl.voxel_size, wl.trunc, wl.pool_capacity, wl.table_entries,
+                          max_batch_pixels=n * W * H)
+        arr = tsdf.frame_array([f.desc for f in frames])
+        tsdf.tsdf_integrate_batch(vol.handle, arr, sh, n=n)
+        st = vol.stats()
+        gate = {k: st["pool_used" if k == "blocks" else k] == v for k, v in want.items()}
+        gate["no_loss"] = st["pool_overflow"] == st["table_full"] == st["update_misses"] == st["walk_guard"] == 0
+        if not all(gate.values()):
+            raise SystemExit(f"sweep cell {name}: parity gate failed {gate}")
+        ta, tu = [], []
+        for r in range(args.sweep_reps + 1):
+            vol.reset()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            tsdf.tsdf_allocate_batch(vol.handle, arr, sh, n=n)
+            e[1].record(stream)
+            tsdf.tsdf_update_batch(vol.handle, arr, sh, n=n)
+            e[2].record(stream)
+            e[2].synchronize()
+            if r:                                   # the first repetition warms up
+                ta.append(e[0].elapsed_time(e[1]) * 1e-3)
+                tu.append(e[1].elapsed_time(e[2]) * 1e-3)
+        tt = [a + b for a, b in zip(ta, tu)]
+        ba = sum(frame_bytes(f)[0] for f in fr)
+        bu = sum(frame_bytes(f)[1] for f in fr)
+        med = statistics.median
+        cell = {"axis": axis, "workload": name, "width": W, "height": H, "fx": fx, "frames": n,
+                "points": want["points_valid"], "voxel_updates": want["voxel_updates"], "blocks": want["blocks"],
+                "voxel_updates_per_block_touch": round(want["voxel_updates"] / sum(f["blocks_touched"] for f in fr), 1),
+                "reps": len(tt),
+                "allocate_us": {"median": round(1e6 * med(ta), 1), "p95": round(1e6 * pct(ta, 95), 1),
+                                "p99": round(1e6 * pct(ta, 99), 1)},
+                "update_us": {"median": round(1e6 * med(tu), 1), "p95": round(1e6 * pct(tu, 95), 1),
+                              "p99": round(1e6 * pct(tu, 99), 1)},
+                "allocate_points_per_s": round(want["points_valid"] / med(ta), 1),
+                "update_points_per_s": round(want["points_valid"] / med(tu), 1),
+                "points_per_s": round(want["points_valid"] / med(tt), 1),
+                "voxel_updates_per_s": round(want["voxel_updates"] / med(tt), 1),
+                "path_GBps": round((ba + bu) / med(tt) / 1e9, 1),
+                "path_hbm_frac": round((ba + bu) / med(tt) / 1e9 / HBM_PEAK_GBS, 4),
+                "parity_gate": gate}
+        log(f"[sweep] {axis:6s} {name:22s} alloc {cell['allocate_us']['median']:8.1f} us  "
+            f"update {cell['update_us']['median']:8.1f} us  {cell['points_per_s'] / 1e9:6.2f} G points/s  "
+            f"path {100 * cell['path_hbm_frac']:5.1f} % of HBM")
+        cells.append(cell)
+        del vol, frames
+        torch.cuda.empty_cache()
+    return cells
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +286,10 @@ def main():
     ap.add_argument("--mode", default="owner", choices=["owner", "rays"], help="update organisation")
     ap.add_argument("--batch", type=int, default=16, help="frames per integrate call (1..16)")
     ap.add_argument("--no-variant", action="store_true", help="skip timing the per-frame variants")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also run the sweep cells (point count at fixed geometry, extent at fixed "
+                         "angular resolution), each gated on the oracle's stored counts")
+    ap.add_argument("--sweep-reps", type=int, default=20, help="timed calls per sweep cell")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -411,6 +488,9 @@ def main():
     if not args.no_microbench:
         log("microbenchmarks")
         out["microbench"] = microbench(torch, tsdf, stream)
+    if args.sweep:
+        log("sweep cells")
+        out["sweep"] = sweep(args, torch, tsdf, scenes, stream)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_frames} frames")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_frames)

@@ -21,6 +21,8 @@ namespace {
 constexpr int kOwnerGridDefault = 2048;              // owner-update workgroups if the occupancy query fails
 constexpr int64_t kDefaultFramePixels = 1 << 20;    // owner-mode record buffers, per call
 constexpr int64_t kRunsPerPixel = 4;                // record capacity per pixel (a room frame needs ~2.7)
+constexpr int64_t kSegmentsPerPixel = 2;            // (wavefront, block) segments per pixel: a room
+                                                    //   frame needs ~0.15, coarse 160 x 120 ones ~0.9
 
 // Owner-mode scratch layout: per-frame counters, per-table-entry arrays,
 // then the per-frame segment and record buffers (kParts partitions each).
@@ -33,7 +35,7 @@ ScratchLayout scratch_layout(int64_t entries, int64_t frame_pixels) {
     ScratchLayout L;
     const int64_t px = frame_pixels > 0 ? frame_pixels : kDefaultFramePixels;
     L.item_part_cap = (unsigned int)std::max<int64_t>(64, entries / (kParts / 2));
-    L.seg_part_cap = (unsigned int)((px + kParts - 1) / kParts);
+    L.seg_part_cap = (unsigned int)((kSegmentsPerPixel * px + kParts - 1) / kParts);
     L.rec_part_cap = (unsigned int)((kRunsPerPixel * px + kParts - 1) / kParts);
     size_t o = 0;
     L.fc = o;                         // 16-byte aligned pieces first

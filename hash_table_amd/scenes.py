@@ -26,6 +26,7 @@ from __future__ import annotations
 
 import hashlib
 import math
+import re
 from dataclasses import dataclass, field
 from typing import Callable, Iterator, List, Optional
 
@@ -33,7 +34,7 @@ import numpy as np
 
 __all__ = [
     "Frame", "Workload", "workload", "plane_frame", "random_frame",
-    "frame_digest", "next_pow2", "WORKLOADS",
+    "frame_digest", "next_pow2", "WORKLOADS", "room_cell", "cell_name", "SWEEP_CELLS",
 ]
 
 
@@ -453,6 +454,29 @@ def _room640_workload():
         description="100 frames 640x480 in a 6x6x3 m room with 40 boxes")
 
 
+def room_cell(W: int, H: int, fx: float) -> "Workload":
+    """The 640 x 480 room's scene and trajectory (same seed, boxes, colours,
+    noise and 10% invalid pixels) rendered W x H with focal length fx, for
+    the paper's sweep axes: fx proportional to W keeps the field of view and
+    the geometry (point count at fixed geometry); fixed fx keeps the angular
+    resolution and widens the view (extent at fixed angular resolution).
+    At 640 x 480 and fx = 525 its frames are those of room640x480."""
+    return _room_workload(
+        cell_name(W, H, fx), 3, W, H, float(fx), 100, (-3, -1.5, -3), (3, 1.5, 3),
+        40, (0.2, 1.2), 0, None, 0.001, 0.10, 0.005, 0.02, 1 << 20,
+        description=f"room640x480's scene rendered {W}x{H}, fx = fy = {fx:g}")
+
+
+# The sweep cells: (axis, W, H, fx).  "points": fx = 525 W / 640 (same field
+# of view, 16x the points from the smallest cell to the largest); "extent":
+# fx = 525 (same angle per pixel, the view widens with the image).  The
+# smallest cells hold about 17,000 valid points per frame, near the paper's
+# smallest cell of 20,000 points.
+SWEEP_CELLS = [("points", 160, 120, 131.25), ("points", 320, 240, 262.5), ("points", 640, 480, 525.0),
+               ("points", 1280, 960, 1050.0), ("extent", 160, 120, 525.0), ("extent", 320, 240, 525.0),
+               ("extent", 1280, 960, 525.0)]
+
+
 def _room1280_workload():
     return _room_workload(
         "room1280x720", 5, 1280, 720, 920.0, 300, (-6, -2, -6), (6, 2, 6),
@@ -543,8 +567,15 @@ WORKLOADS = {
 }
 
 
+def cell_name(W: int, H: int, fx: float) -> str:
+    return f"room{W}x{H}_f{fx:g}"
+
+
 def workload(name: str) -> Workload:
-    try:
+    """A named workload: one of WORKLOADS, or a sweep cell room<W>x<H>_f<fx>."""
+    if name in WORKLOADS:
         return WORKLOADS[name]()
-    except KeyError:
-        raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)}") from None
+    m = re.fullmatch(r"room(\d+)x(\d+)_f([0-9.]+)", name)
+    if m:
+        return room_cell(int(m.group(1)), int(m.group(2)), float(m.group(3)))
+    raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)} and room<W>x<H>_f<fx>")

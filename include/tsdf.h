@@ -156,7 +156,7 @@ int64_t tsdf_table_entries_for(int64_t pool_capacity);
 size_t tsdf_counters_bytes(void);
 
 /* Size of the scratch buffer a configuration needs (0 for TSDF_UPDATE_RAYS):
- * about 52 bytes per table entry plus 80 bytes per pixel of max_batch_pixels
+ * about 60 bytes per table entry plus 112 bytes per pixel of max_batch_pixels
  * (run records and their grouping by block).  0 for a NULL or invalid config. */
 size_t tsdf_scratch_bytes(const tsdf_config* config);
 

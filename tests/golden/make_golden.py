@@ -2,6 +2,7 @@
 oracle on the seeded synthetic workloads.
 
     python tests/golden/make_golden.py [workload ...]
+    python tests/golden/make_golden.py sweep      # the benchmark's sweep cells
 
 For each workload it writes <name>_counts.json: per frame the SHA-256 of the
 generated inputs and the oracle's exact integer counts (valid points, voxel
@@ -61,10 +62,18 @@ def make_counts(name: str, n_frames=None) -> dict:
     }
 
 
+SWEEP_FRAMES = 16     # frames of each sweep cell (one batched call)
+
+
 def main(argv):
-    names = argv or ["room640x480", "cube640x480", "spherewall320x240", "plane64x48"]
-    for name in names:
-        out = make_counts(name)
+    if argv == ["sweep"]:
+        # the sweep cells (the 640 x 480 cell is room640x480's first frames)
+        names = [(scenes.cell_name(W, H, fx), SWEEP_FRAMES) for _, W, H, fx in scenes.SWEEP_CELLS
+                 if (W, H) != (640, 480)]
+    else:
+        names = [(n, None) for n in (argv or ["room640x480", "cube640x480", "spherewall320x240", "plane64x48"])]
+    for name, n_frames in names:
+        out = make_counts(name, n_frames)
         path = os.path.join(HERE, f"{name}_counts.json")
         with open(path, "w") as fh:
             json.dump(out, fh, indent=1)

@@ -157,6 +157,30 @@ def test_room1280x720_full_size_prefix():
     assert f == [], f
 
 
+@pytest.mark.timeout(600)
+def test_sweep_cells():
+    """The benchmark's sweep cells (the room scene at 160x120 ... 1280x960,
+    along the point-count and extent axes), 16 frames in one batched call:
+    counts against the oracle's stored counts for every cell, and every voxel
+    against a live oracle run for the two smallest cells."""
+    for axis, W, H, fx in scenes.SWEEP_CELLS:
+        name = scenes.cell_name(W, H, fx) if (W, H, fx) != (640, 480, 525.0) else "room640x480"
+        wl = scenes.workload(name)
+        g = golden(name)
+        frames = list(wl.frames(0, 16))
+        assert scenes.frame_digest([frames[15]]) == g["frames"][15]["sha256"], "generator drifted"
+        say(f"  {axis} cell {name}")
+        _, st, coords, arrays, _ = parity.gpu_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity,
+                                                        batch=16, max_batch_pixels=16 * W * H)
+        assert st["pool_used"] == g["frames"][15]["blocks_total"]
+        assert st["voxel_updates"] == sum(f["voxel_updates"] for f in g["frames"][:16])
+        assert st["points_valid"] == sum(f["points_valid"] for f in g["frames"][:16])
+        assert st["fallback_blocks"] == 0 and st["update_misses"] == 0 and st["table_full"] == 0
+        if W == 160:
+            o = parity.oracle_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity)
+            assert_parity(st, coords, arrays, o)
+
+
 def _lf_case(target):
     """Pool 2^k (table 2^(k+1)) and the longest frame prefix of the room whose
     block count stays within target * table entries."""
