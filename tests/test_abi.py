@@ -43,7 +43,7 @@ def test_table_sizing_rule():
 
 def test_scratch_sizing():
     def expect(entries, px):
-        seg_part, rec_part = -(-px // 64), -(-4 * px // 64)
+        seg_part, rec_part = -(-2 * px // 64), -(-4 * px // 64)      # 2 segments, 4 runs per pixel
         item_part = max(64, entries // 32)
         return (2 * 1920 + 32 * entries + 16 * 64 * seg_part + 16 * 64 * rec_part + 8 * 64 * seg_part
                 + 8 * entries + 4 * 64 * item_part + 12 * entries)
