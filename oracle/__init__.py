@@ -26,6 +26,7 @@ CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
 
 TRACK_TOUCHED = 1
 WATCH_ONLY = 2
+REPROJECT = 4          # the reprojection reading of the occlusion test (C8)
 
 
 def build(source: str = SOURCE, output: str = LIBRARY, extra_flags: Iterable[str] = ()) -> str:
@@ -88,13 +89,15 @@ class Oracle:
 
     pool_capacity bounds the number of blocks; keys beyond it are refused and
     counted.  track_touched enables the per-frame distinct-voxel count U;
-    watch (n x 3 block coordinates) keeps sums only for those blocks."""
+    watch (n x 3 block coordinates) keeps sums only for those blocks;
+    reproject selects the reprojection reading of the occlusion test (C8)."""
 
     def __init__(self, voxel_size: float, trunc: float, pool_capacity: int,
                  track_touched: bool = False, watch: Optional[np.ndarray] = None,
-                 library: str = LIBRARY):
+                 library: str = LIBRARY, reproject: bool = False):
         self._lib = load(library)
-        flags = (TRACK_TOUCHED if track_touched else 0) | (WATCH_ONLY if watch is not None else 0)
+        flags = ((TRACK_TOUCHED if track_touched else 0) | (WATCH_ONLY if watch is not None else 0)
+                 | (REPROJECT if reproject else 0))
         self._h = self._lib.oracle_create(voxel_size, trunc, int(pool_capacity), flags)
         if not self._h:
             raise ValueError("invalid oracle parameters")

@@ -45,6 +45,17 @@
  *   C7  a kept cell contributes tsdf = sdf / trunc, weight 1, colour
  *       channel / 255 to its voxel; block = floor(k / 8) per axis, voxel
  *       index within the block = (k0 mod 8) + 8 (k1 mod 8) + 64 (k2 mod 8).
+ *   C8  (the reprojection reading of the occlusion test, ORACLE_REPROJECT):
+ *       a cell that passes C6 is also hidden, and skipped, when the depth
+ *       image itself shows a surface more than trunc in front of its centre
+ *       along the centre's own line of sight: with q = c - t, the centre in
+ *       camera coordinates is xc = (R_00 q0 + R_10 q1) + R_20 q2, yc likewise
+ *       with column 1, zc as in C6; for zc > 0 it projects to
+ *       uf = ((xc / zc) fx + cx) + 0.5, vf = ((yc / zc) fy + cy) + 0.5 and to
+ *       the pixel (floor(uf), floor(vf)) (nearest pixel centre); if that
+ *       pixel is inside the image and its depth D is finite and > 0, the
+ *       cell is hidden iff zc - D > trunc.  Without such evidence (outside
+ *       the image, no valid depth there, zc <= 0) it is not hidden.
  *
  * The oracle keeps blocks in a std::map keyed by block coordinate and adds
  * each contribution in double (the exact sum the f32 atomics approximate).
@@ -121,7 +132,7 @@ typedef struct {
     int64_t frames;
 } oracle_totals;
 
-enum { ORACLE_TRACK_TOUCHED = 1, ORACLE_WATCH_ONLY = 2 };
+enum { ORACLE_TRACK_TOUCHED = 1, ORACLE_WATCH_ONLY = 2, ORACLE_REPROJECT = 4 };
 
 struct oracle_volume {
     float vs, trunc, inv_vs;
@@ -175,6 +186,23 @@ static void contribute(oracle_volume* o, oracle_frame_stats& s, uint32_t stamp, 
         S.g[local] += (double)col[1] / 255.0;
         S.b[local] += (double)col[2] / 255.0;
     }
+}
+
+/* C8: is the centre c (camera depth zc) of a cell hidden behind the surface
+ * the depth image shows at its own projection? */
+static bool hidden(const float* depth, int32_t W, int32_t H, float fx, float fy, float cx, float cy,
+                   const float* R, const float* t, const float c[3], float zc, float trunc) {
+    if (!(zc > 0.0f)) return false;
+    const float q0 = c[0] - t[0], q1 = c[1] - t[1], q2 = c[2] - t[2];
+    const float xc = (R[0] * q0 + R[3] * q1) + R[6] * q2;
+    const float yc = (R[1] * q0 + R[4] * q1) + R[7] * q2;
+    const float uf = ((xc / zc) * fx + cx) + 0.5f;
+    const float vf = ((yc / zc) * fy + cy) + 0.5f;
+    if (!(uf >= 0.0f && uf < (float)W && vf >= 0.0f && vf < (float)H)) return false;
+    const int64_t iu = (int64_t)std::floor(uf), iv = (int64_t)std::floor(vf);
+    const float D = depth[iv * W + iu];
+    if (!std::isfinite(D) || !(D > 0.0f)) return false;
+    return zc - D > trunc;
 }
 
 void* oracle_create(float voxel_size, float trunc, int64_t pool_capacity, int32_t flags) {
@@ -265,7 +293,10 @@ int oracle_integrate(void* h, const float* depth, const uint8_t* rgb, int32_t W,
                 for (int i = 0; i < 3; ++i) c[i] = ((float)k[i] + 0.5f) * vs;
                 const float zc = (R[2] * (c[0] - t[0]) + R[5] * (c[1] - t[1])) + R[8] * (c[2] - t[2]);
                 const float sdf = d - zc;
-                if (sdf >= -trunc && sdf <= trunc) contribute(o, s, stamp, k, sdf, col);
+                if (sdf >= -trunc && sdf <= trunc) {
+                    if (!(o->flags & ORACLE_REPROJECT) || !hidden(depth, W, H, fx, fy, cx, cy, R, t, c, zc, trunc))
+                        contribute(o, s, stamp, k, sdf, col);
+                }
                 // C5: advance to the next cell along the segment
                 int m = 0;
                 if (tmax[1] < tmax[m]) m = 1;

@@ -17,10 +17,41 @@ from __future__ import annotations
 import numpy as np
 
 
-def point_voxels(frame, u, v, voxel_size, trunc, eps=1e-3, eps_sdf=1e-5):
+def hidden_by_depth(frame, K, vs, tr, eps_px=1e-4, eps_z=1e-5):
+    """The reprojection reading of the occlusion test, in float64, for cells K
+    (n x 3): each centre, in camera coordinates, projected to its nearest
+    pixel; hidden iff that pixel is in the image with a valid depth D and the
+    centre lies more than trunc behind it.  Returns (hidden, tie) per cell;
+    tie marks a projection within eps_px of a pixel edge or a depth gap
+    within eps_z of trunc, which float32 may decide either way."""
+    R = frame.R.astype(np.float64)
+    t = frame.t.astype(np.float64)
+    H, W = frame.depth.shape
+    cam = ((K + 0.5) * vs - t) @ R              # rows: (xc, yc, zc)
+    zc = cam[:, 2]
+    front = zc > 0
+    zs = np.where(front, zc, 1.0)
+    uf = cam[:, 0] / zs * float(frame.fx) + float(frame.cx) + 0.5
+    vf = cam[:, 1] / zs * float(frame.fy) + float(frame.cy) + 0.5
+    inside = front & (uf >= 0) & (uf < W) & (vf >= 0) & (vf < H)
+    iu = np.clip(np.floor(uf), 0, W - 1).astype(np.int64)
+    iv = np.clip(np.floor(vf), 0, H - 1).astype(np.int64)
+    D = frame.depth[iv, iu].astype(np.float64)
+    valid = inside & np.isfinite(D) & (D > 0)
+    gap = zc - D
+    hidden = valid & (gap > tr)
+    edge = lambda x: np.abs(x - np.round(x)) < eps_px
+    tie = front & (edge(uf) | edge(vf) | (valid & (np.abs(gap - tr) < eps_z)))
+    return hidden, tie
+
+
+def point_voxels(frame, u, v, voxel_size, trunc, eps=1e-3, eps_sdf=1e-5, reproject=False):
     """Return (voxels, tie): voxels maps (kx, ky, kz) -> (tsdf, r, g, b) for the
     kept voxels of pixel (u, v); tie is True if any decision was too close to
-    call in float32.  Returns (None, False) for an invalid/near pixel."""
+    call in float32.  Returns (None, False) for an invalid/near pixel.  With
+    reproject, kept cells must also pass hidden_by_depth against the frame's
+    depth image, and the result is (voxels, tie_cells): the set of cells
+    whose decision is a tie (the others are exact)."""
     vs = float(np.float32(voxel_size))
     tr = float(np.float32(trunc))
     d = float(frame.depth[v, u])
@@ -65,11 +96,22 @@ def point_voxels(frame, u, v, voxel_size, trunc, eps=1e-3, eps_sdf=1e-5):
     zc = (c - t) @ R[:, 2]
     sdf = d - zc
     kept = crosses & (sdf >= -tr) & (sdf <= tr)
-    tie |= bool(np.any(crosses & ((np.abs(sdf - tr) < eps_sdf) | (np.abs(sdf + tr) < eps_sdf))))
+    cell_tie = crosses & ((np.abs(sdf - tr) < eps_sdf) | (np.abs(sdf + tr) < eps_sdf))
+    if reproject:
+        # per cell: a walk tie (the segment grazing a cell) makes every cell
+        # of the point uncertain; a band or projection tie only that cell
+        hid, ptie = hidden_by_depth(frame, K, vs, tr)
+        cell_tie |= kept & ptie
+        kept &= ~hid
+        if tie:                                    # every cell the segment may touch
+            cell_tie |= overlap_vox > -eps
+    tie |= bool(np.any(cell_tie))
     rgb = frame.rgb[v, u].astype(np.float64) / 255.0
     out = {}
     for k, s in zip(map(tuple, K[kept]), sdf[kept]):
         out[k] = (s / tr, rgb[0], rgb[1], rgb[2])
+    if reproject:
+        return out, {tuple(k) for k in K[cell_tie]}
     return out, tie
 
 

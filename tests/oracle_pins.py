@@ -173,6 +173,106 @@ def bruteforce_failures(lib=oracle.LIBRARY, tol=1e-4):
     return f
 
 
+def _step_frame():
+    """A two-plane step: columns 0-15 of a 24 x 18 image see a wall at 1.013 m,
+    the rest one at 2.417 m; random colours, identity pose.  With 0.2 m
+    voxels (wider than a pixel there) far-wall cells near the step project
+    onto near-wall pixels, some more than trunc behind them (hidden under the
+    reprojection reading)."""
+    rng = np.random.default_rng(7)
+    W, H = 24, 18
+    depth = np.full((H, W), 2.417, np.float32)
+    depth[:, :16] = 1.013
+    rgb = rng.integers(0, 256, size=(H, W, 3), dtype=np.uint8)
+    # a slightly turned and shifted camera, so that no ray runs along the grid
+    R = scenes.random_rotation(np.random.default_rng(8))
+    R = np.linalg.qr(np.eye(3) + 0.05 * (R - R.T))[0]
+    R *= np.sign(np.diag(R))[None, :]
+    return scenes.Frame(depth, rgb, 20.0, 20.0, (W - 1) / 2.0, (H - 1) / 2.0,
+                        R.astype(np.float32), np.array([0.013, -0.021, 0.007], np.float32))
+
+
+def reprojection_failures(lib=oracle.LIBRARY, tol=1e-4):
+    """The reprojection reading of the occlusion test (C8): on frames with
+    depth discontinuities (random frames, a two-plane step), every voxel's
+    weight lies between the brute-force count of its certain contributions
+    and that count plus its float32 ties, and equals it where there is no
+    tie; the sums of tie-free voxels match; the step's far band loses cells
+    near the step; the fronto-parallel plane is unchanged; and the variant
+    never adds a contribution the projective reading lacks."""
+    f = []
+    cases = [(_step_frame(), 0.2, 0.7)]
+    for seed in range(4):
+        vs = (0.01, 0.013)[seed % 2]
+        cases.append((scenes.random_frame(100 + seed, W=9, H=7, translation_scale=0.5), vs, 4 * vs))
+    n_hidden = n_ties = n_kept = 0
+    for frame, vs, tr in cases:
+        H, W = frame.depth.shape
+        want = {}
+        ties = {}
+        for v in range(H):
+            for u in range(W):
+                vox, tie_cells = bruteforce.point_voxels(frame, u, v, vs, tr, reproject=True)
+                if vox is None:
+                    continue
+                for kk, (ts, r, g, b) in vox.items():
+                    acc = want.setdefault(kk, [0.0, 0.0, 0.0, 0.0, 0.0])
+                    for j, x in enumerate((ts, 1.0, r, g, b)):
+                        acc[j] += x
+                for kk in tie_cells:
+                    ties[kk] = ties.get(kk, 0) + 1
+        n_ties += sum(ties.values())
+        n_kept += int(sum(a[1] for a in want.values()))
+        o = oracle.Oracle(vs, tr, 1 << 20, library=lib, reproject=True)
+        o.integrate(frame)
+        k, s = _voxel_table(o)
+        got = {tuple(int(x) for x in kk): i for i, kk in enumerate(k)}
+        for kk in set(got) | set(want):
+            w_got = float(s["weight"][got[kk]]) if kk in got else 0.0
+            acc = want.get(kk)
+            w_want = acc[1] if acc else 0.0
+            t = ties.get(kk, 0)
+            if not (w_want - t <= w_got <= w_want + t):
+                f.append(f"vs={vs} voxel {kk}: weight {w_got}, brute force {w_want} (+-{t} ties)")
+                break
+            if t == 0 and acc and kk in got:
+                d = max(abs(s[n][got[kk]] - acc[j]) for j, n in ((0, "tsdf"), (2, "r"), (3, "g"), (4, "b")))
+                if not d < tol * acc[1]:
+                    f.append(f"vs={vs} voxel {kk}: sums off by {d:.3g}")
+                    break
+        # the variant only removes contributions
+        base = oracle.Oracle(vs, tr, 1 << 20, library=lib)
+        base.integrate(frame)
+        kb, sb = _voxel_table(base)
+        gb = {tuple(int(x) for x in kk): i for i, kk in enumerate(kb)}
+        extra = [kk for kk in got if kk not in gb or s["weight"][got[kk]] > sb["weight"][gb[kk]]]
+        if extra:
+            f.append(f"vs={vs}: the reprojection variant adds contributions at {extra[:3]}")
+        n_hidden += int(sum(sb["weight"])) - int(sum(s["weight"]))
+    # the step: far-wall cells near the step are hidden (some, not all)
+    step, vs, tr = cases[0]
+    o = oracle.Oracle(vs, tr, 1 << 20, library=lib, reproject=True)
+    o.integrate(step)
+    b = oracle.Oracle(vs, tr, 1 << 20, library=lib)
+    b.integrate(step)
+    lost = b.totals()["voxel_updates"] - o.totals()["voxel_updates"]
+    if not 0 < lost < b.totals()["voxel_updates"] // 4:
+        f.append(f"step frame: {lost} of {b.totals()['voxel_updates']} contributions hidden")
+    # the fronto-parallel plane: nothing is hidden
+    plane = scenes.plane_frame()
+    o = oracle.Oracle(0.01, 0.04, 4096, library=lib, reproject=True)
+    o.integrate(plane)
+    b = oracle.Oracle(0.01, 0.04, 4096, library=lib)
+    b.integrate(plane)
+    if o.totals() != b.totals():
+        f.append("plane: the reprojection variant changed the result")
+    if n_hidden == 0:
+        f.append("no contribution was hidden: the pin did not exercise the test")
+    if n_ties > 0.05 * n_kept:
+        f.append(f"{n_ties} tie decisions against {n_kept} contributions")
+    return f
+
+
 def sphere_failures(lib=oracle.LIBRARY, frames=range(10)):
     """Analytic sphere r = 0.5 m at (0, 0, 1.5), noise-free depth: along each
     voxel column near the optical axis the linear zero crossing of the mean
@@ -329,6 +429,7 @@ def edge_failures(lib=oracle.LIBRARY):
 PINS = {
     "plane": plane_failures,
     "bruteforce": bruteforce_failures,
+    "reprojection": reprojection_failures,
     "sphere": sphere_failures,
     "invariants": invariant_failures,
     "edges": edge_failures,

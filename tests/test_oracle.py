@@ -74,6 +74,11 @@ MUTATIONS = [
      "(k[2] - kBlockEdge * bc.z) + kBlockEdge * (k[1] - kBlockEdge * bc.y) +\n"
      "                      kBlockEdge * kBlockEdge * (k[0] - kBlockEdge * bc.x)", 1, "plane"),
     ("weight of two", "S.weight[local] += 1.0;", "S.weight[local] += 2.0;", 1, "plane,bruteforce"),
+    # the reprojection reading of the occlusion test (C8)
+    ("projection rounds down", "((xc / zc) * fx + cx) + 0.5f", "((xc / zc) * fx + cx) + 0.0f", 1, "reprojection"),
+    ("hidden when in front", "return zc - D > trunc;", "return D - zc > trunc;", 1, "reprojection"),
+    ("projection uses rotation rows", "const float xc = (R[0] * q0 + R[3] * q1) + R[6] * q2;",
+     "const float xc = (R[0] * q0 + R[1] * q1) + R[2] * q2;", 1, "reprojection"),
 ]
 
 
