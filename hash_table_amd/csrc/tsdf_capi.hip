@@ -164,6 +164,7 @@ VolumeArgs volume_args(const tsdf_volume* h) {
     a.trunc = h->cfg.trunc;
     a.inv_trunc = 1.0f / h->cfg.trunc;
     a.probe_limit = h->cfg.probe_limit > 0 ? (unsigned int)h->cfg.probe_limit : 0xFFFFFFFFu;
+    a.reproject = h->cfg.occlusion == TSDF_OCCLUSION_REPROJECT ? 1 : 0;
     return a;
 }
 
@@ -317,6 +318,7 @@ tsdf_status tsdf_create(const tsdf_config* config, const tsdf_buffers* buffers, 
     if (config->update_mode != TSDF_UPDATE_OWNER && config->update_mode != TSDF_UPDATE_RAYS) return TSDF_EINVAL;
     if (config->max_batch_pixels < 0 || config->max_batch_pixels > ((int64_t)1 << 28)) return TSDF_EINVAL;
     if (config->probe_limit < 0) return TSDF_EINVAL;
+    if (config->occlusion != TSDF_OCCLUSION_RAY && config->occlusion != TSDF_OCCLUSION_REPROJECT) return TSDF_EINVAL;
     const int64_t entries = resolved_entries(config);
     if (!is_pow2(entries) || entries < 2 * config->pool_capacity || entries > TSDF_MAX_TABLE_ENTRIES)
         return TSDF_EINVAL;

@@ -205,6 +205,7 @@ struct VolumeArgs {
     unsigned long long* counters;
     float vs, inv_vs, trunc, inv_trunc;
     unsigned int probe_limit;        // slots a table operation may probe (0xFFFFFFFF: no limit)
+    int reproject;                   // occlusion test: 0 the point's own depth, 1 also the depth image
 };
 
 enum PointClass { kInvalid = 0, kNear = 1, kOutside = 2, kValid = 3 };
@@ -325,6 +326,68 @@ __device__ __forceinline__ bool centre_test(int k0, int k1, int k2, float d, con
     const float zc = (a.r2 * (c0 - a.t0) + a.r5 * (c1 - a.t1)) + a.r8 * (c2 - a.t2);
     sdf = d - zc;
     return sdf >= -trunc && sdf <= trunc;
+}
+
+// The reprojection reading of the occlusion test: what a frame contributes
+// to it (the camera's x and y axes in world coordinates, i.e. columns 0 and 1
+// of the rotation, the intrinsics and the depth image).
+struct Projection {
+    float rx0, rx1, rx2;      // R[0][0], R[1][0], R[2][0]
+    float ry0, ry1, ry2;      // R[0][1], R[1][1], R[2][1]
+    float fx, fy, cx, cy;
+    float fw, fh;             // image width and height
+    const float* depth;
+    int width;
+};
+
+__device__ __forceinline__ Projection projection(const FrameArgs& f) {
+    Projection p;
+    p.rx0 = f.R[0];
+    p.rx1 = f.R[3];
+    p.rx2 = f.R[6];
+    p.ry0 = f.R[1];
+    p.ry1 = f.R[4];
+    p.ry2 = f.R[7];
+    p.fx = f.fx;
+    p.fy = f.fy;
+    p.cx = f.cx;
+    p.cy = f.cy;
+    p.fw = (float)f.width;
+    p.fh = (float)f.height;
+    p.depth = f.depth;
+    p.width = f.width;
+    return p;
+}
+
+// Is a voxel centre (q = centre - camera position, camera depth zc) hidden
+// behind the surface the depth image shows along its own line of sight?
+// It projects to ((x / zc) fx + cx, (y / zc) fy + cy) in pixel units; the
+// pixel whose centre is nearest (floor of coordinate + 0.5) holds depth D.
+// Hidden iff that pixel is inside the image, D is finite and > 0, and the
+// centre lies more than trunc behind it; a centre at or behind the camera
+// plane, or with no valid depth at its pixel, is not hidden.
+__device__ __forceinline__ bool hidden_in_image(float q0, float q1, float q2, float zc, const Projection& p,
+                                                float trunc) {
+    if (!(zc > 0.0f)) return false;
+    const float x = (p.rx0 * q0 + p.rx1 * q1) + p.rx2 * q2;
+    const float y = (p.ry0 * q0 + p.ry1 * q1) + p.ry2 * q2;
+    const float uf = ((x / zc) * p.fx + p.cx) + 0.5f;
+    const float vf = ((y / zc) * p.fy + p.cy) + 0.5f;
+    if (!(uf >= 0.0f && uf < p.fw && vf >= 0.0f && vf < p.fh)) return false;
+    const float D = p.depth[(size_t)(unsigned int)floorf(vf) * (unsigned int)p.width + (unsigned int)floorf(uf)];
+    if (!__builtin_isfinite(D) || !(D > 0.0f)) return false;
+    return zc - D > trunc;
+}
+
+// centre_test with the reprojection reading added (same centre arithmetic).
+__device__ __forceinline__ bool centre_test_reproject(int k0, int k1, int k2, float d, const DepthAxis& a,
+                                                      const Projection& p, float vs, float trunc, float& sdf) {
+    const float q0 = (((float)k0 + 0.5f) * vs) - a.t0;
+    const float q1 = (((float)k1 + 0.5f) * vs) - a.t1;
+    const float q2 = (((float)k2 + 0.5f) * vs) - a.t2;
+    const float zc = (a.r2 * q0 + a.r5 * q1) + a.r8 * q2;
+    sdf = d - zc;
+    return sdf >= -trunc && sdf <= trunc && !hidden_in_image(q0, q1, q2, zc, p, trunc);
 }
 
 // Step to the next cell: the axis with the smallest boundary parameter (ties

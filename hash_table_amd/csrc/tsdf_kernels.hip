@@ -318,6 +318,9 @@ __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, u
     }
 }
 
+// kReproject: the reprojection reading of the occlusion test (see
+// hidden_in_image) on top of the band test.
+template <bool kReproject>
 __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ AllocLds L;
     const int fi = blockIdx.x / B.tile_grid;                 // frame of this workgroup
@@ -389,11 +392,13 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
         i0 = w.inv0; i1 = w.inv1; i2 = w.inv2;
     }
     const float dd = depth;
-    bool keep;                                // the centre test of the walk's current cell
-    {
+    const Projection proj = projection(f);
+    auto test = [&](int c0, int c1, int c2) {
         float sdf;
-        keep = centre_test(k0, k1, k2, dd, ax, vs, trunc, sdf);
-    }
+        return kReproject ? centre_test_reproject(c0, c1, c2, dd, ax, proj, vs, trunc, sdf)
+                          : centre_test(c0, c1, c2, dd, ax, vs, trunc, sdf);
+    };
+    bool keep = test(k0, k1, k2);             // the centre test of the walk's current cell
 
     // The walk goes in chunks of up to kChunkCells cells.  All lanes start
     // together, so a lane's cell index within the chunk is the (uniform)
@@ -440,8 +445,7 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
             tm0 = a0 ? tn : tm0;
             tm1 = a1 ? tn : tm1;
             tm2 = a2 ? tn : tm2;
-            float sdf;
-            keep = centre_test(k0, k1, k2, dd, ax, vs, trunc, sdf);
+            keep = test(k0, k1, k2);
             alive = more;
         }
         // A walk still going after max_visits cells is cut there (counted).
@@ -660,11 +664,15 @@ __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, 
 __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ OwnerLds L;
     __shared__ DepthAxis s_axis[kMaxBatch];                 // per-record frame lookups from LDS
+    __shared__ Projection s_proj[kMaxBatch];
     __shared__ unsigned int s_item[2];                      // alternates: read k while k + 1 is written
     __shared__ unsigned int s_rec[kSegWindow];
     __shared__ unsigned int s_off[kSegWindow + 1];
     const int tid = threadIdx.x;
-    if (tid < B.n) s_axis[tid] = depth_axis(B.f[tid]);
+    if (tid < B.n) {
+        s_axis[tid] = depth_axis(B.f[tid]);
+        s_proj[tid] = projection(B.f[tid]);
+    }
     for (int j = tid; j < kBlockVoxels; j += kOwnerThreads) {
         L.tsdf[j] = 0;
         L.wrgb[j] = 0;
@@ -728,7 +736,8 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
                         continue;
                     }
                     const float dep = __uint_as_float(rec.depth);
-                    const DepthAxis ax = s_axis[meta_frame(rec.meta)];
+                    const int rf = meta_frame(rec.meta);
+                    const DepthAxis ax = s_axis[rf];
                     const unsigned long long c = 1ull | ((unsigned long long)(rec.meta & 0xFFu) << 10) |
                                                  ((unsigned long long)((rec.meta >> 8) & 0xFFu) << 28) |
                                                  ((unsigned long long)((rec.meta >> 16) & 0xFFu) << 46);
@@ -740,7 +749,8 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
                     unsigned int ys = code_ysteps(code), zs = code_zsteps(code);
                     for (int q = 0;;) {
                         float sdf;
-                        if (centre_test(k0, k1, k2, dep, ax, vol.vs, vol.trunc, sdf)) {
+                        if (vol.reproject ? centre_test_reproject(k0, k1, k2, dep, ax, s_proj[rf], vol.vs, vol.trunc, sdf)
+                                          : centre_test(k0, k1, k2, dep, ax, vol.vs, vol.trunc, sdf)) {
                             const int j = (k0 & 7) | ((k1 & 7) << 3) | ((k2 & 7) << 6);
                             atomicAdd(L.tsdf + j, __float2int_rn(sdf * vol.inv_trunc * kTsdfScale));
                             atomicAdd(L.wrgb + j, c);
@@ -796,6 +806,8 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_rescan(BatchArgs B, Vo
         const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
         for (int fi = 0; fi < B.n; ++fi) {
             const FrameArgs& f = B.f[fi];
+            const Projection pr = projection(f);
+            const DepthAxis fax = depth_axis(f);
             const PixelRect rc = block_rect(bx, by, bz, f, vol.vs);
             if (rc.u0 > rc.u1 || rc.v0 > rc.v1) continue;
             const int rw = rc.u1 - rc.u0 + 1;
@@ -820,7 +832,9 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_rescan(BatchArgs B, Vo
                     if ((unsigned)(w.k0 - lo0) < 8u && (unsigned)(w.k1 - lo1) < 8u && (unsigned)(w.k2 - lo2) < 8u) {
                         inside = true;
                         float sdf;
-                        if (centre_test(w, f, vol.vs, vol.trunc, sdf)) {
+                        if (vol.reproject
+                                ? centre_test_reproject(w.k0, w.k1, w.k2, w.d, fax, pr, vol.vs, vol.trunc, sdf)
+                                : centre_test(w, f, vol.vs, vol.trunc, sdf)) {
                             const int j = voxel_in_block(w.k0, w.k1, w.k2);
                             atomicAdd(L.tsdf + j, sdf * vol.inv_trunc);
                             atomicAdd(L.wr + j, c_wr);
@@ -899,13 +913,16 @@ __global__ __launch_bounds__(kThreads) void k_update_rays(BatchArgs B, VolumeArg
         }
     }
     unsigned int n_miss = 0;
+    const Projection pr = projection(f);
+    const DepthAxis fax = depth_axis(f);
     if (cls == kValid) {
         unsigned long long cur = kEmptyKey;
         unsigned int idx = kNoIndex;
         int visits = 0;
         for (;;) {
             float sdf;
-            if (centre_test(w, f, vol.vs, vol.trunc, sdf)) {
+            if (vol.reproject ? centre_test_reproject(w.k0, w.k1, w.k2, w.d, fax, pr, vol.vs, vol.trunc, sdf)
+                              : centre_test(w, f, vol.vs, vol.trunc, sdf)) {
                 const unsigned long long key = block_key(w.k0, w.k1, w.k2);
                 if (key != cur) {
                     unsigned int probes;
@@ -1025,7 +1042,10 @@ const char* kernel_name(int id) {
 
 bool launch_allocate(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, hipStream_t s,
                      const LaunchTimer* t) {
-    TSDF_TIMED_LAUNCH(t, kKAllocate, k_allocate, dim3(b.n * b.tile_grid), dim3(kThreads), s, b, v, o);
+    if (v.reproject)
+        TSDF_TIMED_LAUNCH(t, kKAllocate, k_allocate<true>, dim3(b.n * b.tile_grid), dim3(kThreads), s, b, v, o);
+    else
+        TSDF_TIMED_LAUNCH(t, kKAllocate, k_allocate<false>, dim3(b.n * b.tile_grid), dim3(kThreads), s, b, v, o);
     return launched();
 }
 

@@ -21,6 +21,8 @@ LIBRARY = os.path.join(HERE, "libtsdf_hip.so")
 TSDF_OK, TSDF_EINVAL, TSDF_EALIGN, TSDF_EHIP, TSDF_ESMALL = 0, -1, -2, -3, -4
 TSDF_UPDATE_OWNER, TSDF_UPDATE_RAYS = 0, 1
 UPDATE_MODES = {"owner": TSDF_UPDATE_OWNER, "rays": TSDF_UPDATE_RAYS}
+TSDF_OCCLUSION_RAY, TSDF_OCCLUSION_REPROJECT = 0, 1
+OCCLUSION_MODES = {"ray": TSDF_OCCLUSION_RAY, "reproject": TSDF_OCCLUSION_REPROJECT}
 TSDF_PROBE_BINS = 32
 TSDF_MAX_BATCH = 16
 TSDF_MAX_FRAME_SIDE = 65535
@@ -50,7 +52,7 @@ class tsdf_config(ctypes.Structure):
     _fields_ = [("voxel_size", ctypes.c_float), ("trunc", ctypes.c_float),
                 ("pool_capacity", ctypes.c_int64), ("table_entries", ctypes.c_int64),
                 ("update_mode", ctypes.c_int32), ("max_batch_pixels", ctypes.c_int64),
-                ("probe_limit", ctypes.c_int32)]
+                ("probe_limit", ctypes.c_int32), ("occlusion", ctypes.c_int32)]
 
 
 class tsdf_buffers(ctypes.Structure):
@@ -293,7 +295,7 @@ class Volume:
 
     def __init__(self, voxel_size: float, trunc: float, pool_capacity: int, table_entries: int = 0,
                  update_mode: str = "owner", max_batch_pixels: int = 0, device="cuda", stream=None,
-                 probe_limit: int = 0):
+                 probe_limit: int = 0, occlusion: str = "ray"):
         import torch
         entries = table_entries or tsdf_table_entries_for(pool_capacity)
         if entries <= 0:
@@ -303,7 +305,7 @@ class Volume:
         self.update_mode = update_mode
         self.device = device
         self._cfg = tsdf_config(voxel_size, trunc, int(pool_capacity), int(table_entries), UPDATE_MODES[update_mode],
-                                int(max_batch_pixels), int(probe_limit))
+                                int(max_batch_pixels), int(probe_limit), OCCLUSION_MODES[occlusion])
         n = int(pool_capacity) * BLOCK_VOXELS
         self.table = torch.empty(int(entries) * 2, dtype=torch.int64, device=device)
         self.pool = {k: torch.empty(n, dtype=torch.float32, device=device) for k in ("tsdf", "weight", "r", "g", "b")}

@@ -78,6 +78,21 @@ typedef struct tsdf_volume tsdf_volume;     /* opaque host-side handle */
  *                      paper's section 3 shape). */
 typedef enum { TSDF_UPDATE_OWNER = 0, TSDF_UPDATE_RAYS = 1 } tsdf_update_mode;
 
+/* The occlusion test both passes apply to every voxel a band walk visits
+ * (section 3 of the paper: allocate and update apply the same test; the
+ * pages do not define it).  Both readings keep a voxel only inside the band,
+ * |d - zc| <= trunc, where d is the point's depth and zc the camera depth of
+ * the voxel centre:
+ *   TSDF_OCCLUSION_RAY        nothing more: a centre more than trunc behind
+ *                             the point's own depth is hidden (the band's far
+ *                             end), evaluable from the point alone (default);
+ *   TSDF_OCCLUSION_REPROJECT  also hidden when the depth image shows a
+ *                             surface more than trunc in front of the centre
+ *                             at the pixel nearest to the centre's projection
+ *                             (no valid depth there, or a projection outside
+ *                             the image or behind the camera: not hidden). */
+typedef enum { TSDF_OCCLUSION_RAY = 0, TSDF_OCCLUSION_REPROJECT = 1 } tsdf_occlusion;
+
 typedef struct {
     float voxel_size;       /* metres, finite, > 0 */
     float trunc;            /* truncation distance, metres, finite, > 0 */
@@ -96,6 +111,7 @@ typedef struct {
                                paper's Triton arm (section 7): a table operation gives up
                                after n slots; such keys are counted in probe_exhausted and
                                their contributions in update_misses.  Not for production. */
+    int32_t occlusion;      /* tsdf_occlusion (zero-initialised configs get TSDF_OCCLUSION_RAY) */
 } tsdf_config;
 
 /* Device memory owned by the caller, all 16-byte aligned. */

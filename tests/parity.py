@@ -30,7 +30,7 @@ def sort_blocks(coords: np.ndarray, arrays: Dict[str, np.ndarray]):
 
 
 def gpu_integrate(frames: Iterable, voxel_size, trunc, pool_capacity, table_entries=0, split=False,
-                  per_frame_stats=False, mode="owner", batch=1, max_batch_pixels=0):
+                  per_frame_stats=False, mode="owner", batch=1, max_batch_pixels=0, occlusion="ray"):
     """Integrate on the GPU (one frame per call, or `batch` frames per
     tsdf_integrate_batch call); returns (volume, stats, coords, arrays,
     per-call stats)."""
@@ -38,7 +38,7 @@ def gpu_integrate(frames: Iterable, voxel_size, trunc, pool_capacity, table_entr
     from hash_table_amd import tsdf
     frames = list(frames)
     vol = tsdf.Volume(voxel_size, trunc, pool_capacity, table_entries, update_mode=mode,
-                      max_batch_pixels=max_batch_pixels)
+                      max_batch_pixels=max_batch_pixels, occlusion=occlusion)
     history = []
     if batch > 1:
         for i in range(0, len(frames), batch):
@@ -61,8 +61,9 @@ def gpu_integrate(frames: Iterable, voxel_size, trunc, pool_capacity, table_entr
     return vol, st, coords, arrays, history
 
 
-def oracle_integrate(frames: Iterable, voxel_size, trunc, pool_capacity, watch=None) -> oracle.Oracle:
-    o = oracle.Oracle(voxel_size, trunc, pool_capacity, watch=watch)
+def oracle_integrate(frames: Iterable, voxel_size, trunc, pool_capacity, watch=None,
+                     reproject=False) -> oracle.Oracle:
+    o = oracle.Oracle(voxel_size, trunc, pool_capacity, watch=watch, reproject=reproject)
     for f in frames:
         o.integrate(f)
     return o

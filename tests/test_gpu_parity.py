@@ -181,6 +181,43 @@ def test_sweep_cells():
             assert_parity(st, coords, arrays, o)
 
 
+def _reproject_cases():
+    from tests import oracle_pins
+    cases = [("step", [oracle_pins._step_frame()], 0.2, 0.7, 1 << 16)]
+    for seed in (11, 12):
+        cases.append((f"random{seed}", [scenes.random_frame(seed, W=37, H=23, translation_scale=0.5)],
+                      0.013, 0.052, 1 << 18))
+    wl = scenes.workload("spherewall320x240")
+    cases.append(("spherewall", list(wl.frames()), wl.voxel_size, wl.trunc, wl.pool_capacity))
+    wl = scenes.workload("room640x480")
+    cases.append(("room16", list(wl.frames(0, 16)), wl.voxel_size, wl.trunc, wl.pool_capacity))
+    return cases
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("mode", MODES)
+def test_reprojection_occlusion_parity(mode):
+    """The reprojection reading of the occlusion test (the centre also hidden
+    behind the depth seen at its own pixel) in both passes: block set,
+    weights exact and means within 1e-4 against the oracle with the same
+    reading, one frame per call and 16 per call; on the scenes with depth
+    discontinuities it must hide contributions the projective reading keeps."""
+    for name, frames, vs, tr, cap in _reproject_cases():
+        for batch in (1, 16):
+            if batch > 1 and len(frames) == 1:
+                continue
+            W, H = frames[0].width, frames[0].height
+            say(f"  {mode} {name} batch {batch}: {len(frames)} frame(s) {W}x{H}")
+            _, st, coords, arrays, _ = parity.gpu_integrate(frames, vs, tr, cap, mode=mode, batch=batch,
+                                                            max_batch_pixels=batch * W * H, occlusion="reproject")
+            o = parity.oracle_integrate(frames, vs, tr, cap, reproject=True)
+            assert_parity(st, coords, arrays, o)
+        base = parity.oracle_integrate(frames, vs, tr, cap).totals()["voxel_updates"]
+        say(f"    hidden by the image: {base - st['voxel_updates']} of {base}")
+        if name in ("step", "spherewall", "room16"):
+            assert st["voxel_updates"] < base
+
+
 def _lf_case(target):
     """Pool 2^k (table 2^(k+1)) and the longest frame prefix of the room whose
     block count stays within target * table entries."""
