@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload room640x480]
 
 A step integrates the whole 100-frame, 640 x 480 room sequence into a
-freshly reset volume, `--batch` frames per call (one allocate launch and one
-update over those frames; the result equals frame-by-frame integration);
+freshly reset volume, in calls of at most `--batch` frames (one allocate
+launch and one update over a call's frames; the result equals
+frame-by-frame integration);
 inputs are resident in device memory before timing starts.  Timing is gated
 on parity: the run first checks the volume against the oracle's stored
 counts for the same seeded frames.  Per-call durations come from HIP events
@@ -103,6 +104,13 @@ def measured_traffic(kernel, workload, batch, mode):
     if e is None or e[1] != kernel_source_digest():
         return None
     return e[0]
+
+
+def split_calls(n, batch):
+    """n frames in ceil(n / batch) calls of (nearly) equal size."""
+    k = -(-n // batch)
+    b = [round(i * n / k) for i in range(k + 1)]
+    return [list(range(b[i], b[i + 1])) for i in range(k)]
 
 
 def alloc_alu_ops(counts, calls):
@@ -284,7 +292,8 @@ def main():
     ap.add_argument("--no-microbench", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="time whole steps only")
     ap.add_argument("--mode", default="owner", choices=["owner", "rays"], help="update organisation")
-    ap.add_argument("--batch", type=int, default=16, help="frames per integrate call (1..16)")
+    ap.add_argument("--batch", type=int, default=32,
+                    help="most frames per integrate call (1..32); the step's frames are split into equal calls")
     ap.add_argument("--no-variant", action="store_true", help="skip timing the per-frame variants")
     ap.add_argument("--sweep", action="store_true",
                     help="also run the sweep cells (point count at fixed geometry, extent at fixed "
@@ -320,7 +329,7 @@ def main():
         per-call allocate and update seconds, frame lists per call, stats, gate)."""
         vol = tsdf.Volume(wl.voxel_size, wl.trunc, wl.pool_capacity, wl.table_entries, update_mode=mode,
                           max_batch_pixels=batch * wl.width * wl.height)
-        calls = [list(range(i, min(i + batch, len(frames)))) for i in range(0, len(frames), batch)]
+        calls = split_calls(len(frames), batch)
         arrays = [tsdf.frame_array([frames[i].desc for i in c]) for c in calls]
         torch.cuda.synchronize()
         for arr, c in zip(arrays, calls):      # parity gate: one full pass vs the oracle's counts
@@ -362,13 +371,15 @@ def main():
         wall = time.perf_counter() - t0
         st = vol.stats()
         kt = {}
+        kt_steps = 0
         if use_events:
             # per-kernel durations from further steps of the same work with the
             # library's kernel events on (kept out of the timed steps above,
             # whose windows then hold only the kernels and their launch gaps)
             vol.set_kernel_timing(True)
             vol.kernel_times()
-            for _ in range(max(2, steps // 2)):
+            kt_steps = max(2, steps // 2)
+            for _ in range(kt_steps):
                 step(False)
             torch.cuda.synchronize()
             kt = vol.kernel_times()
@@ -378,6 +389,8 @@ def main():
         idx = [c for c, _ in ev]
         del vol
         torch.cuda.empty_cache()
+        kt["_steps"] = kt_steps
+        kt["_calls"] = calls
         return wall, t_alloc, t_upd, idx, st, gate, kt
 
     def kernel_report(t_alloc, t_upd, idx, steps):
@@ -408,6 +421,7 @@ def main():
 
     use_events = not args.no_events
     wall, t_alloc, t_upd, idx, st, gate, ktimes = measure(args.mode, args.batch, args.steps, args.warmup, use_events)
+    kt_steps, step_calls = ktimes.pop("_steps"), ktimes.pop("_calls")
 
     n_frames = wl.n_frames
     ms_per_step = wall / args.steps * 1e3
@@ -427,9 +441,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "frames_per_step": n_frames, "width": wl.width, "height": wl.height,
                    "voxel_size": wl.voxel_size, "trunc": wl.trunc, "pool_capacity": wl.pool_capacity,
-                   "table_entries": wl.table_entries, "update_mode": args.mode, "frames_per_call": args.batch,
+                   "table_entries": wl.table_entries, "update_mode": args.mode, "max_frames_per_call": args.batch,
+                   "calls_per_step": len(split_calls(wl.n_frames, args.batch)),
                    "points_per_step": pts, "voxel_updates_per_step": vox,
-                   "step": "reset used pool + table, then allocate+update of all frames, batch frames per call"},
+                   "step": "reset used pool + table, then allocate+update of all frames in equal calls"},
         "parity_gate": gate,
     }
     if use_events:
@@ -438,7 +453,10 @@ def main():
         # per-kernel durations: HIP events the library records on the launch
         # stream around each of its kernels (tsdf_set_kernel_timing)
         upd_kernel = "k_update_owner" if args.mode == "owner" else "k_update_rays"
-        alg = {"k_allocate": ba, upd_kernel: bu}          # algorithmic bytes over the timed steps
+        # algorithmic work of the kernel-timing steps (kt_steps steps of the same calls)
+        ba_kt = kt_steps * sum(frame_bytes(counts["frames"][i])[0] for c in step_calls for i in c)
+        bu_kt = kt_steps * sum(frame_bytes(counts["frames"][i])[1] for c in step_calls for i in c)
+        alg = {"k_allocate": ba_kt, upd_kernel: bu_kt}
         kt = {}
         for name, v in sorted(ktimes.items(), key=lambda kv: -kv[1]["total_ms"]):
             e = {"launches": v["launches"], "avg_us": round(v["total_ms"] * 1e3 / v["launches"], 3),
@@ -450,9 +468,9 @@ def main():
         # each stage kernel against the roof that binds it: allocate walks
         # every cell (integer/float vector work, no dense contraction), the
         # update moves the pool sums (HBM)
-        ops = alloc_alu_ops(counts, idx)                   # algorithmic vector ops over the timed steps
+        ops = kt_steps * alloc_alu_ops(counts, step_calls)   # algorithmic vector ops, kernel-timing steps
         models = {"k_allocate": ("alu", ops / 1e12, ALU_PEAK_TOPS, "TOP/s"),
-                  upd_kernel: ("hbm", bu / 1e9, HBM_PEAK_GBS, "GB/s")}
+                  upd_kernel: ("hbm", bu_kt / 1e9, HBM_PEAK_GBS, "GB/s")}
         dom = max((k for k in models if k in ktimes), key=lambda k: ktimes[k]["total_ms"])
         bound, amount, peak, unit = models[dom]
         launches = ktimes[dom]["launches"]

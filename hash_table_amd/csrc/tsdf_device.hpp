@@ -66,8 +66,8 @@ constexpr float kNearPlane = 1e-4f;                 // block corners closer than
 // One run of a walk inside one block, as allocate records it for the
 // update (16 bytes):
 //   depth     the point's depth (f32 bits)
-//   meta      colour R | G << 8 | B << 16, frame of the batch << 24 (4 bits),
-//             axis direction bits << 28 (bit set: that axis steps by -1)
+//   meta      colour R | G << 8 | B << 16, frame of the batch << 24 (5 bits),
+//             axis direction bits << 29 (bit set: that axis steps by -1)
 //   code      first cell (voxel index in the block, 9 bits) | cells - 1 << 9
 //             (5 bits) | y-step plane << 14 (21 bits) | z-step plane << 35
 //             (21 bits) | kept cells << 56 (6 bits)
@@ -106,7 +106,7 @@ __device__ __forceinline__ unsigned int code_zsteps(unsigned long long c) {
     return (unsigned int)(c >> (kStepShift + kPlaneBits)) & ((1u << kPlaneBits) - 1u);
 }
 __device__ __forceinline__ int code_kept(unsigned long long c) { return (int)((c >> kKeptShift) & 63u); }
-__device__ __forceinline__ int meta_frame(unsigned int m) { return (int)((m >> 24) & 15u); }
+__device__ __forceinline__ int meta_frame(unsigned int m) { return (int)((m >> 24) & 31u); }
 
 // A wavefront's runs through one block, as recorded by allocate.  One
 // 64-bit atomic on the block's counter (segments << 32 | runs) gives both
@@ -186,7 +186,7 @@ struct FrameArgs {
 // uses workgroups [i * tile_grid, (i + 1) * tile_grid) of the per-pixel
 // kernels; tile_grid is a multiple of 8, so the workgroup -> XCD mapping is
 // the same for every frame.
-constexpr int kMaxBatch = 16;
+constexpr int kMaxBatch = 32;
 struct BatchArgs {
     FrameArgs f[kMaxBatch];
     int n;

@@ -370,8 +370,8 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
             const uint8_t* c = f.rgb + 3 * (size_t)pix;
             meta = (unsigned int)c[0] | ((unsigned int)c[1] << 8) | ((unsigned int)c[2] << 16);
         }
-        meta |= ((unsigned int)fi << 24) | (w.s0 < 0 ? 1u << 28 : 0u) | (w.s1 < 0 ? 1u << 29 : 0u) |
-                (w.s2 < 0 ? 1u << 30 : 0u);
+        meta |= ((unsigned int)fi << 24) | (w.s0 < 0 ? 1u << 29 : 0u) | (w.s1 < 0 ? 1u << 30 : 0u) |
+                (w.s2 < 0 ? 1u << 31 : 0u);
     }
     const unsigned int depth_bits = __float_as_uint(depth);
     unsigned int n_upd = 0, n_guard = 0, misses = 0;
@@ -619,45 +619,45 @@ __global__ __launch_bounds__(kThreads) void k_discard_items(VolumeArgs vol, Owne
 // buffers are left to k_update_rescan.
 // ---------------------------------------------------------------------------
 constexpr int kOwnerThreads = 128;
-// A run adds at most once to each voxel, so a chunk of up to 1023 runs keeps
-// every per-voxel count below 2^10 and every colour sum below 255 * 1023 <
-// 2^18: weight | R << 10 | G << 28 | B << 46 then adds without carries.
-// The normalised signed distance (in [-1, 1]) is summed in LDS as a 32-bit
-// integer in units of 2^-20: LDS float atomics issue far slower than integer
-// ones on this chip, and |sum| <= 1023 < 2^11 fits.  Rounding each term to
-// the nearest 2^-20 moves a mean by at most 2^-21.
-constexpr unsigned int kChunkRuns = 1023;
+// The chunk's sums per voxel live in two 64-bit LDS words added with integer
+// atomics (LDS float atomics issue far slower than integer ones on this
+// chip).  A run adds at most once to each voxel, so a chunk of at most
+// kChunkRuns = 8191 runs keeps every per-voxel count below 2^13:
+//   tw   (normalised signed distance + 1) in units of 2^-16, rounded to
+//        nearest (each term in [0, 2^17], the sum below 2^31), | count << 32
+//   rgb  R | G << 21 | B << 42 (each sum at most 255 * 8191 < 2^21)
+// so no field carries into the next.  The signed-distance sum is recovered
+// exactly from the two fields; rounding each term to the nearest 2^-16 moves
+// a mean by at most 2^-17.
+constexpr unsigned int kChunkRuns = 8191;
 constexpr int kSegWindow = 512;                      // segments of a block held in LDS at once
-constexpr float kTsdfScale = 1048576.0f;           // 2^20
-constexpr float kTsdfUnit = 1.0f / 1048576.0f;
+constexpr float kTsdfScale = 65536.0f;               // 2^16
+constexpr float kTsdfUnit = 1.0f / 65536.0f;
 
 struct OwnerLds {
-    int tsdf[kBlockVoxels];
-    unsigned long long wrgb[kBlockVoxels];
+    unsigned long long tw[kBlockVoxels];
+    unsigned long long rgb[kBlockVoxels];
 };
-
-__device__ __forceinline__ unsigned long long packed_colour(const FrameArgs& f, size_t pix) {
-    const uint8_t* c = f.rgb + 3 * pix;
-    return 1ull | ((unsigned long long)c[0] << 10) | ((unsigned long long)c[1] << 28) |
-           ((unsigned long long)c[2] << 46);
-}
 
 // Add the chunk's sums to the pool block and clear them for the next chunk.
 __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, size_t base) {
     for (int j = threadIdx.x; j < kBlockVoxels; j += kOwnerThreads) {
-        const unsigned long long s = L.wrgb[j];
-        const unsigned int cnt = (unsigned int)s & 1023u;
+        const unsigned long long tw = L.tw[j];
+        const unsigned int cnt = (unsigned int)(tw >> 32);
         if (!cnt) continue;
-        const float ts = (float)L.tsdf[j] * kTsdfUnit;
-        L.tsdf[j] = 0;
-        L.wrgb[j] = 0;
+        const unsigned long long c = L.rgb[j];
+        // sum of the signed distances, in units of 2^-16 (the +1 offsets removed)
+        const long long tq = (long long)(unsigned int)tw - ((long long)cnt << 16);
+        const float ts = (float)tq * kTsdfUnit;
+        L.tw[j] = 0;
+        L.rgb[j] = 0;
         const size_t off = base + j;
         const float t0 = vol.tsdf[off], w0 = vol.weight[off], r0 = vol.r[off], g0 = vol.g[off], b0 = vol.b[off];
         vol.tsdf[off] = t0 + ts;
         vol.weight[off] = w0 + (float)cnt;
-        vol.r[off] = r0 + (float)((unsigned int)(s >> 10) & 0x3FFFFu) * kInv255;
-        vol.g[off] = g0 + (float)((unsigned int)(s >> 28) & 0x3FFFFu) * kInv255;
-        vol.b[off] = b0 + (float)((unsigned int)(s >> 46) & 0x3FFFFu) * kInv255;
+        vol.r[off] = r0 + (float)((unsigned int)c & 0x1FFFFFu) * kInv255;
+        vol.g[off] = g0 + (float)((unsigned int)(c >> 21) & 0x1FFFFFu) * kInv255;
+        vol.b[off] = b0 + (float)((unsigned int)(c >> 42) & 0x1FFFFFu) * kInv255;
     }
 }
 
@@ -674,8 +674,8 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
         s_proj[tid] = projection(B.f[tid]);
     }
     for (int j = tid; j < kBlockVoxels; j += kOwnerThreads) {
-        L.tsdf[j] = 0;
-        L.wrgb[j] = 0;
+        L.tw[j] = 0;
+        L.rgb[j] = 0;
     }
     FrameCounters& fc = own.fc[own.parity];
     const unsigned int n_items = fc.items_total;
@@ -738,12 +738,12 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
                     const float dep = __uint_as_float(rec.depth);
                     const int rf = meta_frame(rec.meta);
                     const DepthAxis ax = s_axis[rf];
-                    const unsigned long long c = 1ull | ((unsigned long long)(rec.meta & 0xFFu) << 10) |
-                                                 ((unsigned long long)((rec.meta >> 8) & 0xFFu) << 28) |
-                                                 ((unsigned long long)((rec.meta >> 16) & 0xFFu) << 46);
-                    const int d0 = (rec.meta >> 28) & 1u ? -1 : 1;
-                    const int d1 = (rec.meta >> 29) & 1u ? -1 : 1;
-                    const int d2 = (rec.meta >> 30) & 1u ? -1 : 1;
+                    const unsigned long long c = (unsigned long long)(rec.meta & 0xFFu) |
+                                                 ((unsigned long long)((rec.meta >> 8) & 0xFFu) << 21) |
+                                                 ((unsigned long long)((rec.meta >> 16) & 0xFFu) << 42);
+                    const int d0 = (rec.meta >> 29) & 1u ? -1 : 1;
+                    const int d1 = (rec.meta >> 30) & 1u ? -1 : 1;
+                    const int d2 = (rec.meta >> 31) & 1u ? -1 : 1;
                     const int e = code_entry(code), cells = code_cells(code);
                     int k0 = lo0 + (e & 7), k1 = lo1 + ((e >> 3) & 7), k2 = lo2 + (e >> 6);
                     unsigned int ys = code_ysteps(code), zs = code_zsteps(code);
@@ -752,8 +752,10 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
                         if (vol.reproject ? centre_test_reproject(k0, k1, k2, dep, ax, s_proj[rf], vol.vs, vol.trunc, sdf)
                                           : centre_test(k0, k1, k2, dep, ax, vol.vs, vol.trunc, sdf)) {
                             const int j = (k0 & 7) | ((k1 & 7) << 3) | ((k2 & 7) << 6);
-                            atomicAdd(L.tsdf + j, __float2int_rn(sdf * vol.inv_trunc * kTsdfScale));
-                            atomicAdd(L.wrgb + j, c);
+                            const unsigned int tq =
+                                (unsigned int)__float2int_rn((sdf * vol.inv_trunc + 1.0f) * kTsdfScale);
+                            atomicAdd(L.tw + j, (1ull << 32) | tq);
+                            atomicAdd(L.rgb + j, c);
                         }
                         if (++q >= cells) break;
                         const bool sy = ys & 1u, sz = zs & 1u;

@@ -56,7 +56,7 @@ typedef enum {
  * intrinsics allow more is rejected with TSDF_EINVAL). */
 #define TSDF_MAX_WALK 4096
 /* Most frames one tsdf_integrate_batch call takes. */
-#define TSDF_MAX_BATCH 16
+#define TSDF_MAX_BATCH 32
 /* Largest frame width and height, in pixels (a pixel position is recorded
  * as two 16-bit halves). */
 #define TSDF_MAX_FRAME_SIDE 65535

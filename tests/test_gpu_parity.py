@@ -374,9 +374,9 @@ def test_batch_limits():
     tsdf.tsdf_integrate_batch(vol.handle, [])          # nothing to do
     vol.integrate_batch([f] * tsdf.TSDF_MAX_BATCH)
     st = vol.stats()
-    assert st["pool_used"] == 234 and st["voxel_updates"] == 16 * 38688
+    assert st["pool_used"] == 234 and st["voxel_updates"] == tsdf.TSDF_MAX_BATCH * 38688
     c, a = vol.export()
-    assert float(a["weight"].sum()) == 16 * 38688
+    assert float(a["weight"].sum()) == tsdf.TSDF_MAX_BATCH * 38688
 
 
 # ---------------------------------------------------------------------------
