@@ -631,6 +631,7 @@ constexpr int kOwnerThreads = 128;
 // a mean by at most 2^-17.
 constexpr unsigned int kChunkRuns = 8191;
 constexpr int kSegWindow = 512;                      // segments of a block held in LDS at once
+constexpr unsigned int kRunGroup = 8;                // threads reading consecutive records
 constexpr float kTsdfScale = 65536.0f;               // 2^16
 constexpr float kTsdfUnit = 1.0f / 65536.0f;
 
@@ -661,6 +662,8 @@ __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, 
     }
 }
 
+// kReproject: the reprojection reading of the occlusion test (as in k_allocate).
+template <bool kReproject>
 __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ OwnerLds L;
     __shared__ DepthAxis s_axis[kMaxBatch];                 // per-record frame lookups from LDS
@@ -671,7 +674,7 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
     const int tid = threadIdx.x;
     if (tid < B.n) {
         s_axis[tid] = depth_axis(B.f[tid]);
-        s_proj[tid] = projection(B.f[tid]);
+        if (kReproject) s_proj[tid] = projection(B.f[tid]);
     }
     for (int j = tid; j < kBlockVoxels; j += kOwnerThreads) {
         L.tw[j] = 0;
@@ -713,11 +716,17 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
             const unsigned int wr0 = s_off[0], wr1 = s_off[wn];
             for (unsigned int c0 = wr0; c0 < wr1; c0 += kChunkRuns) {
                 const unsigned int c1 = min(wr1, c0 + kChunkRuns);
-                // each thread takes a contiguous share of the chunk: runs next
-                // to each other come from neighbouring pixels and hit the same
-                // voxels, so spreading the lanes apart spreads their LDS atomics
-                const unsigned int share = (c1 - c0 + kOwnerThreads - 1) / kOwnerThreads;
-                const unsigned int r0 = c0 + tid * share, r1 = min(c1, r0 + share);
+                // Threads go in groups of kRunGroup: a group takes a contiguous
+                // share of the chunk and its threads take consecutive runs of
+                // it, so one load instruction reads whole cache lines of
+                // records.  The groups' shares lie apart: runs next to each
+                // other come from neighbouring pixels and hit the same voxels,
+                // so the lanes of a wavefront mostly add to different voxels.
+                const unsigned int groups = kOwnerThreads / kRunGroup;
+                const unsigned int share = ((c1 - c0 + groups - 1) / groups + kRunGroup - 1) / kRunGroup * kRunGroup;
+                const unsigned int grp = (unsigned int)tid / kRunGroup;
+                const unsigned int r0 = c0 + grp * share + (unsigned int)tid % kRunGroup;
+                const unsigned int r1 = min(c1, c0 + (grp + 1) * share);
                 unsigned int si = 0;
                 if (r0 < r1) {                               // last segment starting at or before r0
                     unsigned int lo = 0, hi = wn - 1;
@@ -727,7 +736,7 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
                     }
                     si = lo;
                 }
-                for (unsigned int r = r0; r < r1; ++r) {
+                for (unsigned int r = r0; r < r1; r += kRunGroup) {
                     while (r >= s_off[si + 1]) ++si;         // s_off[wn] = wr1 > r ends it
                     const RunRecord rec = own.recs[s_rec[si] + (r - s_off[si])];
                     const unsigned long long code = record_code(rec);
@@ -749,8 +758,8 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
                     unsigned int ys = code_ysteps(code), zs = code_zsteps(code);
                     for (int q = 0;;) {
                         float sdf;
-                        if (vol.reproject ? centre_test_reproject(k0, k1, k2, dep, ax, s_proj[rf], vol.vs, vol.trunc, sdf)
-                                          : centre_test(k0, k1, k2, dep, ax, vol.vs, vol.trunc, sdf)) {
+                        if (kReproject ? centre_test_reproject(k0, k1, k2, dep, ax, s_proj[rf], vol.vs, vol.trunc, sdf)
+                                       : centre_test(k0, k1, k2, dep, ax, vol.vs, vol.trunc, sdf)) {
                             const int j = (k0 & 7) | ((k1 & 7) << 3) | ((k2 & 7) << 6);
                             const unsigned int tq =
                                 (unsigned int)__float2int_rn((sdf * vol.inv_trunc + 1.0f) * kTsdfScale);
@@ -1055,7 +1064,10 @@ bool launch_update_owner(const BatchArgs& b, const VolumeArgs& v, const OwnerArg
                          const LaunchTimer* t) {
     TSDF_TIMED_LAUNCH(t, kKPlaceItems, k_place_items, dim3(256), dim3(kThreads), s, v, o);
     TSDF_TIMED_LAUNCH(t, kKPlaceSegments, k_place_segments, dim3(1024), dim3(kThreads), s, v, o);
-    TSDF_TIMED_LAUNCH(t, kKUpdateOwner, k_update_owner, dim3(grid), dim3(kOwnerThreads), s, b, v, o);
+    if (v.reproject)
+        TSDF_TIMED_LAUNCH(t, kKUpdateOwner, k_update_owner<true>, dim3(grid), dim3(kOwnerThreads), s, b, v, o);
+    else
+        TSDF_TIMED_LAUNCH(t, kKUpdateOwner, k_update_owner<false>, dim3(grid), dim3(kOwnerThreads), s, b, v, o);
     TSDF_TIMED_LAUNCH(t, kKUpdateRescan, k_update_rescan, dim3(256), dim3(kOwnerThreads), s, b, v, o);
     return launched();
 }
@@ -1064,7 +1076,7 @@ int owner_grid() {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_update_owner),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_update_owner<false>),
                                                      kOwnerThreads, 0) != hipSuccess)
         return 0;
     return std::max(1, cus) * std::max(1, per_cu);
