@@ -589,6 +589,17 @@ __device__ __forceinline__ unsigned int lookup_key(const VolumeArgs& vol, unsign
 // Sum over the wavefront (every lane active): DPP row operations, no LDS.
 __device__ __forceinline__ unsigned int wave_sum(unsigned int x) { return __reduce_add_sync(~0ull, x); }
 
+// Inclusive prefix sum over the wavefront's lanes (every lane active).
+__device__ __forceinline__ unsigned int wave_inclusive_sum(unsigned int x) {
+    const int lane = (int)(threadIdx.x & 63u);
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const unsigned int y = __shfl_up(x, (unsigned int)d);
+        x += lane >= d ? y : 0u;
+    }
+    return x;
+}
+
 __device__ __forceinline__ void unpack_key(unsigned long long key, int& bx, int& by, int& bz) {
     bx = (int)(key & 0x1FFFFFull) - kKeyBias;
     by = (int)((key >> 21) & 0x1FFFFFull) - kKeyBias;

@@ -610,15 +610,16 @@ __global__ __launch_bounds__(kThreads) void k_discard_items(VolumeArgs vol, Owne
 
 // ---------------------------------------------------------------------------
 // owner update: one workgroup per touched block at a time, blocks handed out
-// through one work counter per XCD.  The block's runs are replayed from their
-// recorded first cell (the exact walk state there follows from the cell);
-// kept voxels add into LDS (signed distance as f32, weight and colour bytes
-// as one packed integer word), and the block's touched voxels are then read,
-// added to and written with plain coalesced loads and stores: the block has
-// no other writer in this call.  Blocks whose runs did not fit the record
-// buffers are left to k_update_rescan.
+// through one work counter per XCD.  The block's run records are staged in
+// LDS with coalesced loads and sorted by length, so the lanes of a wavefront
+// replay runs of about the same length together; each run's cells follow
+// from its recorded first cell and step planes (the walk's arithmetic is not
+// repeated) and get the centre test.  Kept voxels add into LDS (integer
+// words, see below), and the block's touched voxels are then read, added to
+// and written with plain coalesced loads and stores: the block has no other
+// writer in this call.  Blocks whose runs did not fit the record buffers are
+// left to k_update_rescan.
 // ---------------------------------------------------------------------------
-constexpr int kOwnerThreads = 128;
 // The chunk's sums per voxel live in two 64-bit LDS words added with integer
 // atomics (LDS float atomics issue far slower than integer ones on this
 // chip).  A run adds at most once to each voxel, so a chunk of at most
@@ -630,10 +631,15 @@ constexpr int kOwnerThreads = 128;
 // exactly from the two fields; rounding each term to the nearest 2^-16 moves
 // a mean by at most 2^-17.
 constexpr unsigned int kChunkRuns = 8191;
-constexpr int kSegWindow = 512;                      // segments of a block held in LDS at once
-constexpr unsigned int kRunGroup = 8;                // threads reading consecutive records
+constexpr int kSegWindow = 256;                      // segments of a block held in LDS at once
+constexpr int kUpdateThreads = 256;                  // workgroup of the owner update
+constexpr int kRunsPerThread = 4;                    // runs each thread stages
+constexpr int kSubRuns = kUpdateThreads * kRunsPerThread;   // runs staged in LDS at a time
+constexpr int kLengths = 32;                         // run lengths a record can state (5 bits)
+constexpr unsigned int kNoRank = 0xFFFFFFFFu;
 constexpr float kTsdfScale = 65536.0f;               // 2^16
 constexpr float kTsdfUnit = 1.0f / 65536.0f;
+constexpr int kRescanThreads = 128;
 
 struct OwnerLds {
     unsigned long long tw[kBlockVoxels];
@@ -642,7 +648,7 @@ struct OwnerLds {
 
 // Add the chunk's sums to the pool block and clear them for the next chunk.
 __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, size_t base) {
-    for (int j = threadIdx.x; j < kBlockVoxels; j += kOwnerThreads) {
+    for (int j = threadIdx.x; j < kBlockVoxels; j += kUpdateThreads) {
         const unsigned long long tw = L.tw[j];
         const unsigned int cnt = (unsigned int)(tw >> 32);
         if (!cnt) continue;
@@ -664,19 +670,23 @@ __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, 
 
 // kReproject: the reprojection reading of the occlusion test (as in k_allocate).
 template <bool kReproject>
-__global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
+__global__ __launch_bounds__(kUpdateThreads) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ OwnerLds L;
     __shared__ DepthAxis s_axis[kMaxBatch];                 // per-record frame lookups from LDS
     __shared__ Projection s_proj[kMaxBatch];
     __shared__ unsigned int s_item[2];                      // alternates: read k while k + 1 is written
     __shared__ unsigned int s_rec[kSegWindow];
     __shared__ unsigned int s_off[kSegWindow + 1];
+    __shared__ RunRecord s_run[kSubRuns];                   // staged runs, sorted by length
+    __shared__ unsigned int s_hist[kLengths];               // staged runs of each length
+    __shared__ unsigned int s_hbase[kLengths];              // first place of each length in the order
     const int tid = threadIdx.x;
+    if (tid < kLengths) s_hist[tid] = 0;
     if (tid < B.n) {
         s_axis[tid] = depth_axis(B.f[tid]);
         if (kReproject) s_proj[tid] = projection(B.f[tid]);
     }
-    for (int j = tid; j < kBlockVoxels; j += kOwnerThreads) {
+    for (int j = tid; j < kBlockVoxels; j += kUpdateThreads) {
         L.tw[j] = 0;
         L.rgb[j] = 0;
     }
@@ -703,7 +713,7 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
         // [s_off[i], s_off[i + 1]) of the block, stored from s_rec[i] on
         for (unsigned int w0 = 0; w0 < d.seg_count; w0 += kSegWindow) {
             const unsigned int wn = min(d.seg_count - w0, (unsigned int)kSegWindow);
-            for (unsigned int i = tid; i <= wn; i += kOwnerThreads) {
+            for (unsigned int i = tid; i <= wn; i += kUpdateThreads) {
                 if (i < wn) {
                     const uint2 e = own.seg_list[d.seg_first + w0 + i];
                     s_rec[i] = e.x;
@@ -716,64 +726,95 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_owner(BatchArgs B, Vol
             const unsigned int wr0 = s_off[0], wr1 = s_off[wn];
             for (unsigned int c0 = wr0; c0 < wr1; c0 += kChunkRuns) {
                 const unsigned int c1 = min(wr1, c0 + kChunkRuns);
-                // Threads go in groups of kRunGroup: a group takes a contiguous
-                // share of the chunk and its threads take consecutive runs of
-                // it, so one load instruction reads whole cache lines of
-                // records.  The groups' shares lie apart: runs next to each
-                // other come from neighbouring pixels and hit the same voxels,
-                // so the lanes of a wavefront mostly add to different voxels.
-                const unsigned int groups = kOwnerThreads / kRunGroup;
-                const unsigned int share = ((c1 - c0 + groups - 1) / groups + kRunGroup - 1) / kRunGroup * kRunGroup;
-                const unsigned int grp = (unsigned int)tid / kRunGroup;
-                const unsigned int r0 = c0 + grp * share + (unsigned int)tid % kRunGroup;
-                const unsigned int r1 = min(c1, c0 + (grp + 1) * share);
-                unsigned int si = 0;
-                if (r0 < r1) {                               // last segment starting at or before r0
-                    unsigned int lo = 0, hi = wn - 1;
-                    while (lo < hi) {
-                        const unsigned int m = (lo + hi + 1) >> 1;
-                        if (s_off[m] <= r0) lo = m; else hi = m - 1;
-                    }
-                    si = lo;
-                }
-                for (unsigned int r = r0; r < r1; r += kRunGroup) {
-                    while (r >= s_off[si + 1]) ++si;         // s_off[wn] = wr1 > r ends it
-                    const RunRecord rec = own.recs[s_rec[si] + (r - s_off[si])];
-                    const unsigned long long code = record_code(rec);
-                    if (!store) {
-                        misses += (unsigned int)code_kept(code);
-                        continue;
-                    }
-                    const float dep = __uint_as_float(rec.depth);
-                    const int rf = meta_frame(rec.meta);
-                    const DepthAxis ax = s_axis[rf];
-                    const unsigned long long c = (unsigned long long)(rec.meta & 0xFFu) |
-                                                 ((unsigned long long)((rec.meta >> 8) & 0xFFu) << 21) |
-                                                 ((unsigned long long)((rec.meta >> 16) & 0xFFu) << 42);
-                    const int d0 = (rec.meta >> 29) & 1u ? -1 : 1;
-                    const int d1 = (rec.meta >> 30) & 1u ? -1 : 1;
-                    const int d2 = (rec.meta >> 31) & 1u ? -1 : 1;
-                    const int e = code_entry(code), cells = code_cells(code);
-                    int k0 = lo0 + (e & 7), k1 = lo1 + ((e >> 3) & 7), k2 = lo2 + (e >> 6);
-                    unsigned int ys = code_ysteps(code), zs = code_zsteps(code);
-                    for (int q = 0;;) {
-                        float sdf;
-                        if (kReproject ? centre_test_reproject(k0, k1, k2, dep, ax, s_proj[rf], vol.vs, vol.trunc, sdf)
-                                       : centre_test(k0, k1, k2, dep, ax, vol.vs, vol.trunc, sdf)) {
-                            const int j = (k0 & 7) | ((k1 & 7) << 3) | ((k2 & 7) << 6);
-                            const unsigned int tq =
-                                (unsigned int)__float2int_rn((sdf * vol.inv_trunc + 1.0f) * kTsdfScale);
-                            atomicAdd(L.tw + j, (1ull << 32) | tq);
-                            atomicAdd(L.rgb + j, c);
+                // The chunk's runs go through LDS kSubRuns at a time: each
+                // thread loads kRunsPerThread neighbouring runs (a wavefront's
+                // loads cover whole cache lines of records), the staged runs
+                // are sorted by length (a counting sort over LDS), and each
+                // thread then replays every kUpdateThreads-th run in that
+                // order.  The lanes of a wavefront so replay runs of nearly
+                // the same length in step, and few idle while the longest
+                // finishes.
+                for (unsigned int b0 = c0; b0 < c1; b0 += kSubRuns) {
+                    const unsigned int nb = min(c1 - b0, (unsigned int)kSubRuns);
+                    const unsigned int p0 = (unsigned int)tid * kRunsPerThread;
+                    RunRecord rec[kRunsPerThread];
+                    unsigned int rank[kRunsPerThread];
+#pragma unroll
+                    for (int i = 0; i < kRunsPerThread; ++i) rank[i] = kNoRank;
+                    if (p0 < nb) {
+                        unsigned int r = b0 + p0;
+                        unsigned int lo = 0, hi = wn - 1;    // last segment starting at or before r
+                        while (lo < hi) {
+                            const unsigned int m = (lo + hi + 1) >> 1;
+                            if (s_off[m] <= r) lo = m; else hi = m - 1;
                         }
-                        if (++q >= cells) break;
-                        const bool sy = ys & 1u, sz = zs & 1u;
-                        ys >>= 1;
-                        zs >>= 1;
-                        k0 += (sy || sz) ? 0 : d0;
-                        k1 += sy ? d1 : 0;
-                        k2 += sz ? d2 : 0;
+                        unsigned int si = lo;
+#pragma unroll
+                        for (int i = 0; i < kRunsPerThread; ++i) {
+                            if (p0 + i < nb) {
+                                while (r >= s_off[si + 1]) ++si;   // s_off[wn] = wr1 > r ends it
+                                rec[i] = own.recs[s_rec[si] + (r - s_off[si])];
+                                ++r;
+                            }
+                        }
+#pragma unroll
+                        for (int i = 0; i < kRunsPerThread; ++i) {
+                            if (p0 + i < nb) {
+                                const unsigned long long code = record_code(rec[i]);
+                                if (store) rank[i] = atomicAdd(s_hist + code_cells(code) - 1, 1u);
+                                else misses += (unsigned int)code_kept(code);
+                            }
+                        }
                     }
+                    if (!store) continue;                    // (uniform) a refused block: counted above
+                    __syncthreads();
+                    if (tid < 64) {                          // each length's first place in the order
+                        const unsigned int h = tid < kLengths ? s_hist[tid] : 0u;
+                        const unsigned int incl = wave_inclusive_sum(h);
+                        if (tid < kLengths) s_hbase[tid] = incl - h;
+                    }
+                    __syncthreads();
+                    if (tid < kLengths) s_hist[tid] = 0;     // for the next sub-batch
+#pragma unroll
+                    for (int i = 0; i < kRunsPerThread; ++i)
+                        if (rank[i] != kNoRank)
+                            s_run[s_hbase[code_cells(record_code(rec[i])) - 1] + rank[i]] = rec[i];
+                    __syncthreads();
+                    for (unsigned int p = (unsigned int)tid; p < nb; p += kUpdateThreads) {
+                        const RunRecord rr = s_run[p];
+                        const unsigned long long code = record_code(rr);
+                        const float dep = __uint_as_float(rr.depth);
+                        const int rf = meta_frame(rr.meta);
+                        const DepthAxis ax = s_axis[rf];
+                        const unsigned long long c = (unsigned long long)(rr.meta & 0xFFu) |
+                                                     ((unsigned long long)((rr.meta >> 8) & 0xFFu) << 21) |
+                                                     ((unsigned long long)((rr.meta >> 16) & 0xFFu) << 42);
+                        const int d0 = (rr.meta >> 29) & 1u ? -1 : 1;
+                        const int d1 = (rr.meta >> 30) & 1u ? -1 : 1;
+                        const int d2 = (rr.meta >> 31) & 1u ? -1 : 1;
+                        const int e = code_entry(code), cells = code_cells(code);
+                        int k0 = lo0 + (e & 7), k1 = lo1 + ((e >> 3) & 7), k2 = lo2 + (e >> 6);
+                        unsigned int ys = code_ysteps(code), zs = code_zsteps(code);
+                        for (int q = 0;;) {
+                            float sdf;
+                            if (kReproject ? centre_test_reproject(k0, k1, k2, dep, ax, s_proj[rf], vol.vs, vol.trunc, sdf)
+                                           : centre_test(k0, k1, k2, dep, ax, vol.vs, vol.trunc, sdf)) {
+                                const int j = (k0 & 7) | ((k1 & 7) << 3) | ((k2 & 7) << 6);
+                                const unsigned int tq =
+                                    (unsigned int)__float2int_rn((sdf * vol.inv_trunc + 1.0f) * kTsdfScale);
+                                atomicAdd(L.tw + j, (1ull << 32) | tq);
+                                atomicAdd(L.rgb + j, c);
+                            }
+                            if (++q >= cells) break;
+                            const bool sy = ys & 1u, sz = zs & 1u;
+                            ys >>= 1;
+                            zs >>= 1;
+                            k0 += (sy || sz) ? 0 : d0;
+                            k1 += sy ? d1 : 0;
+                            k2 += sz ? d2 : 0;
+                        }
+                    }
+                    __syncthreads();                         // s_run is rewritten next
                 }
                 __syncthreads();
                 if (store) flush_owner(L, vol, base);
@@ -798,7 +839,7 @@ struct RescanLds {
     unsigned long long gb[kBlockVoxels];          // G sum | B sum << 32
 };
 
-__global__ __launch_bounds__(kOwnerThreads) void k_update_rescan(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
+__global__ __launch_bounds__(kRescanThreads) void k_update_rescan(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ RescanLds L;
     FrameCounters& fc = own.fc[own.parity];
     const unsigned int n = fc.n_rescan;
@@ -807,7 +848,7 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_rescan(BatchArgs B, Vo
         const ItemDesc d = own.desc[own.rescan[q]];
         int bx, by, bz;
         unpack_key(d.key, bx, by, bz);
-        for (int j = threadIdx.x; j < kBlockVoxels; j += kOwnerThreads) {
+        for (int j = threadIdx.x; j < kBlockVoxels; j += kRescanThreads) {
             L.tsdf[j] = 0.0f;
             L.wr[j] = 0;
             L.gb[j] = 0;
@@ -824,7 +865,7 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_rescan(BatchArgs B, Vo
             const int rw = rc.u1 - rc.u0 + 1;
             const long long area = (long long)rw * (rc.v1 - rc.v0 + 1);
             const float zlo = rc.zmin - vol.vs, zhi = rc.zmax + vol.vs;
-            for (long long p = threadIdx.x; p < area; p += kOwnerThreads) {
+            for (long long p = threadIdx.x; p < area; p += kRescanThreads) {
                 const int u = rc.u0 + (int)(p % rw);
                 const int v = rc.v0 + (int)(p / rw);
                 const size_t pix = (size_t)v * f.width + u;
@@ -862,7 +903,7 @@ __global__ __launch_bounds__(kOwnerThreads) void k_update_rescan(BatchArgs B, Vo
         __syncthreads();
         if (d.idx < vol.capacity) {
             const size_t base = (size_t)d.idx * kBlockVoxels;
-            for (int j = threadIdx.x; j < kBlockVoxels; j += kOwnerThreads) {
+            for (int j = threadIdx.x; j < kBlockVoxels; j += kRescanThreads) {
                 const unsigned long long wr = L.wr[j];
                 const unsigned int cnt = (unsigned int)wr;
                 if (!cnt) continue;
@@ -1065,10 +1106,10 @@ bool launch_update_owner(const BatchArgs& b, const VolumeArgs& v, const OwnerArg
     TSDF_TIMED_LAUNCH(t, kKPlaceItems, k_place_items, dim3(256), dim3(kThreads), s, v, o);
     TSDF_TIMED_LAUNCH(t, kKPlaceSegments, k_place_segments, dim3(1024), dim3(kThreads), s, v, o);
     if (v.reproject)
-        TSDF_TIMED_LAUNCH(t, kKUpdateOwner, k_update_owner<true>, dim3(grid), dim3(kOwnerThreads), s, b, v, o);
+        TSDF_TIMED_LAUNCH(t, kKUpdateOwner, k_update_owner<true>, dim3(grid), dim3(kUpdateThreads), s, b, v, o);
     else
-        TSDF_TIMED_LAUNCH(t, kKUpdateOwner, k_update_owner<false>, dim3(grid), dim3(kOwnerThreads), s, b, v, o);
-    TSDF_TIMED_LAUNCH(t, kKUpdateRescan, k_update_rescan, dim3(256), dim3(kOwnerThreads), s, b, v, o);
+        TSDF_TIMED_LAUNCH(t, kKUpdateOwner, k_update_owner<false>, dim3(grid), dim3(kUpdateThreads), s, b, v, o);
+    TSDF_TIMED_LAUNCH(t, kKUpdateRescan, k_update_rescan, dim3(256), dim3(kRescanThreads), s, b, v, o);
     return launched();
 }
 
@@ -1077,7 +1118,7 @@ int owner_grid() {
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_update_owner<false>),
-                                                     kOwnerThreads, 0) != hipSuccess)
+                                                     kUpdateThreads, 0) != hipSuccess)
         return 0;
     return std::max(1, cus) * std::max(1, per_cu);
 }
