@@ -139,9 +139,17 @@ struct __align__(16) ItemDesc {
 constexpr int kParts = 64;
 constexpr int kXcds = 8;
 constexpr int kFetchStride = 32;        // words between the XCDs' work counters
+// One partition's counters, 128 bytes apart from the next partition's:
+// atomics on one cache line are carried out one after another, so counters
+// that many wavefronts add to must not share a line.
+struct PartCounters {
+    unsigned long long segrec;          // segments << 32 | records reserved
+    unsigned int items;                 // blocks first touched
+    unsigned int pad[29];
+};
+static_assert(sizeof(PartCounters) == 128, "one partition per 128 bytes");
 struct FrameCounters {
-    unsigned long long segrec[kParts];  // segments << 32 | records reserved, per partition
-    unsigned int items[kParts];         // blocks first touched, per partition
+    PartCounters part[kParts];
     unsigned int items_spill;           // blocks beyond their partition's share
     unsigned int items_total;           // all blocks (set when the blocks are placed)
     unsigned long long placed;          // segments given to blocks

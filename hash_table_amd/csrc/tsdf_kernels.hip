@@ -201,13 +201,13 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, int lane, un
         const unsigned long long rm = __ballot(rsv);
         unsigned long long bc = 0, r0 = 0;
         if (rsv) bc = atomicAdd(own.blk_count + slot, (1ull << 32) | runs);
-        if (rm && lane == 0) r0 = atomicAdd(&fc->segrec[part], ((unsigned long long)__popcll(rm) << 32) | total);
+        if (rm && lane == 0) r0 = atomicAdd(&fc->part[part].segrec, ((unsigned long long)__popcll(rm) << 32) | total);
         r0 = read_lane0(r0);
         const bool first = rsv && bc == 0;
         const unsigned long long fm = __ballot(first);
         if (fm) {
             unsigned int ib = 0;
-            if (lane == 0) ib = atomicAdd(&fc->items[part], (unsigned int)__popcll(fm));
+            if (lane == 0) ib = atomicAdd(&fc->part[part].items, (unsigned int)__popcll(fm));
             ib = read_lane0(ib);
             if (first) {
                 const unsigned int k = ib + (unsigned int)__popcll(fm & below);
@@ -519,11 +519,14 @@ __device__ __forceinline__ int find_partition(const unsigned int* pre, unsigned 
 }
 
 __global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerArgs own) {
+    __shared__ unsigned int s_cnt[kParts];
     __shared__ unsigned int s_pre[kParts + 2];
     __shared__ unsigned int s_wave[kWaves];
     __shared__ unsigned int s_base;
     FrameCounters& fc = own.fc[own.parity];
-    partition_prefix(fc.items, own.item_part_cap, fc.items_spill, s_pre);
+    if (threadIdx.x < kParts) s_cnt[threadIdx.x] = fc.part[threadIdx.x].items;
+    __syncthreads();
+    partition_prefix(s_cnt, own.item_part_cap, fc.items_spill, s_pre);
     const unsigned int n = s_pre[kParts + 1];
     if (blockIdx.x == 0 && threadIdx.x == 0) fc.items_total = n;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -579,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void k_place_segments(VolumeArgs vol, Own
     __shared__ unsigned int s_cnt[kParts];
     __shared__ unsigned int s_pre[kParts + 2];
     FrameCounters& fc = own.fc[own.parity];
-    if (threadIdx.x < kParts) s_cnt[threadIdx.x] = (unsigned int)(fc.segrec[threadIdx.x] >> 32);
+    if (threadIdx.x < kParts) s_cnt[threadIdx.x] = (unsigned int)(fc.part[threadIdx.x].segrec >> 32);
     __syncthreads();
     partition_prefix(s_cnt, own.seg_part_cap, 0, s_pre);
     const unsigned int n = s_pre[kParts];
@@ -596,9 +599,12 @@ __global__ __launch_bounds__(kThreads) void k_place_segments(VolumeArgs vol, Own
 // Drop a frame's records without updating (an allocate that no update
 // followed): clear the per-block run counts it left.
 __global__ __launch_bounds__(kThreads) void k_discard_items(VolumeArgs vol, OwnerArgs own) {
+    __shared__ unsigned int s_cnt[kParts];
     __shared__ unsigned int s_pre[kParts + 2];
     FrameCounters& fc = own.fc[own.parity];
-    partition_prefix(fc.items, own.item_part_cap, fc.items_spill, s_pre);
+    if (threadIdx.x < kParts) s_cnt[threadIdx.x] = fc.part[threadIdx.x].items;
+    __syncthreads();
+    partition_prefix(s_cnt, own.item_part_cap, fc.items_spill, s_pre);
     const unsigned int n = s_pre[kParts + 1];
     for (unsigned int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
         const int p = find_partition(s_pre, i);
