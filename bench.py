@@ -85,8 +85,8 @@ def load_counts(name):
 MEASURED_TRAFFIC = {
     # (kernel, workload, most frames per call, update mode): (bytes per launch, source digest)
     # profiles/integrate_room640x480.md
-    ("k_allocate", "room640x480", 32, "owner"): (415842921, "7f3cd409536bd0f4"),
-    ("k_update_owner", "room640x480", 32, "owner"): (1259349221, "7f3cd409536bd0f4"),
+    ("k_allocate", "room640x480", 32, "owner"): (415688502, "6a90024a83cfa719"),
+    ("k_update_owner", "room640x480", 32, "owner"): (625155986, "6a90024a83cfa719"),
 }
 
 
