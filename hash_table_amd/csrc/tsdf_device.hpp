@@ -154,7 +154,8 @@ struct FrameCounters {
     unsigned int items_total;           // all blocks (set when the blocks are placed)
     unsigned long long placed;          // segments given to blocks
     unsigned int n_rescan;              // blocks whose runs did not fit (rescanned)
-    unsigned int pad[27];
+    unsigned int front, back;           // items placed from the front (big blocks) and from the back
+    unsigned int pad[25];
     unsigned int fetch[kXcds * kFetchStride];   // next item of XCD x at fetch[x * kFetchStride]
 };
 static_assert(sizeof(FrameCounters) % 128 == 0, "FrameCounters keeps the work counters in their own lines");

@@ -523,11 +523,21 @@ __global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerA
     __shared__ unsigned int s_pre[kParts + 2];
     __shared__ unsigned int s_wave[kWaves];
     __shared__ unsigned int s_base;
+    __shared__ unsigned int s_runs;
+    __shared__ unsigned int s_front[kWaves], s_back[kWaves];
+    __shared__ unsigned int s_fbase, s_bbase;
     FrameCounters& fc = own.fc[own.parity];
     if (threadIdx.x < kParts) s_cnt[threadIdx.x] = fc.part[threadIdx.x].items;
+    if (threadIdx.x < 64) {                  // the call's runs (records reserved in all partitions)
+        const unsigned int r = (unsigned int)fc.part[threadIdx.x].segrec;
+        const unsigned int t = wave_sum(r);
+        if (threadIdx.x == 0) s_runs = t;
+    }
+    static_assert(kParts == 64, "one wavefront sums the partitions' records");
     __syncthreads();
     partition_prefix(s_cnt, own.item_part_cap, fc.items_spill, s_pre);
     const unsigned int n = s_pre[kParts + 1];
+    const unsigned int mean_runs = s_runs / max(n, 1u);
     if (blockIdx.x == 0 && threadIdx.x == 0) fc.items_total = n;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (unsigned int b = blockIdx.x * kThreads; b < n; b += gridDim.x * kThreads) {
@@ -542,6 +552,18 @@ __global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerA
             nseg = (unsigned int)(bc >> 32);
             cnt = (rc & kSegOverflow) ? 0u : nseg;
         }
+        // The item's number, the order the update takes blocks in: blocks
+        // with more runs than the call's mean from the front, the others
+        // from the back, so that no long block starts when the rest of the
+        // work is nearly done.  One add per workgroup and class, with the
+        // segment placement's.
+        const bool big = i < n && (rc & ~kSegOverflow) > mean_runs;
+        const bool small = i < n && !big;
+        const unsigned long long mb = __ballot(big), ms = __ballot(small);
+        if (lane == 0) {
+            s_front[wave] = (unsigned int)__popcll(mb);
+            s_back[wave] = (unsigned int)__popcll(ms);
+        }
         unsigned int x = cnt;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -551,15 +573,24 @@ __global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerA
         if (lane == 63) s_wave[wave] = x;
         __syncthreads();
         if (tid == 0) {
-            unsigned int acc = 0;
+            unsigned int acc = 0, af = 0, ab = 0;
             for (int k = 0; k < kWaves; ++k) {
-                const unsigned int t = s_wave[k];
+                const unsigned int t = s_wave[k], tf = s_front[k], tb = s_back[k];
                 s_wave[k] = acc;
+                s_front[k] = af;
+                s_back[k] = ab;
                 acc += t;
+                af += tf;
+                ab += tb;
             }
             s_base = (unsigned int)atomicAdd(&fc.placed, (unsigned long long)acc);
+            s_fbase = af ? atomicAdd(&fc.front, af) : 0u;
+            s_bbase = ab ? atomicAdd(&fc.back, ab) : 0u;
         }
         __syncthreads();
+        const unsigned long long below = (1ull << lane) - 1ull;
+        const unsigned int j = big ? s_fbase + s_front[wave] + (unsigned int)__popcll(mb & below)
+                                   : n - 1u - (s_bbase + s_back[wave] + (unsigned int)__popcll(ms & below));
         if (i < n) {
             const ulonglong2 e = *reinterpret_cast<const ulonglong2*>(vol.table + slot);
             ItemDesc d;
@@ -570,9 +601,9 @@ __global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerA
             d.seg_count = cnt;
             d.slot = slot;
             d.pad = 0;
-            own.desc[i] = d;
-            own.item_of[slot] = i;
-            if (rc & kSegOverflow) own.rescan[atomicAdd(&fc.n_rescan, 1u)] = i;
+            own.desc[j] = d;
+            own.item_of[slot] = j;
+            if (rc & kSegOverflow) own.rescan[atomicAdd(&fc.n_rescan, 1u)] = j;
         }
         __syncthreads();
     }

@@ -103,8 +103,8 @@ def _check_history(label, hist, g, calls):
 @pytest.mark.timeout(600)
 def test_room_full_parity():
     """All 100 frames of the 640 x 480 room: in the launch configuration the
-    benchmark times (owner update, 16 frames per call) and one frame per call
-    with both update modes; counts after every call against the stored
+    benchmark times (owner update, 4 calls of 25 frames) and one frame per
+    call with both update modes; counts after every call against the stored
     oracle counts, then every voxel against a live oracle run."""
     wl = scenes.workload("room640x480")
     g = golden("room640x480")
@@ -112,7 +112,7 @@ def test_room_full_parity():
     for i, f in enumerate(frames[:3]):
         assert scenes.frame_digest([f]) == g["frames"][i]["sha256"], "generator drifted from the stored counts"
     results = {}
-    for mode, batch in (("owner", 16), ("owner", 1), ("rays", 1)):
+    for mode, batch in (("owner", 25), ("owner", 1), ("rays", 1)):
         say(f"  gpu ({mode}, {batch} frames per call): 100 frames 640x480")
         _, st, coords, arrays, hist = parity.gpu_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity,
                                                            per_frame_stats=True, mode=mode, batch=batch,
@@ -355,8 +355,9 @@ def test_record_overflow_rescans_exactly():
 def test_dense_blocks_span_several_segment_windows(mode):
     # planes 0.1 m in front of a 640 x 480 camera: a 4 cm block covers about
     # 210 x 210 pixels, so one block gathers ~44,000 runs from ~700 wavefront
-    # segments per frame -- more than one LDS window of segments and more
-    # than one 1023-run chunk of packed sums in the owner update
+    # segments per frame -- more than one LDS window of segments, many
+    # staged sub-batches of runs and more than one 8191-run pass of packed
+    # sums in the owner update
     frames = [scenes.plane_frame(seed=s, W=640, H=480, depth=d, fx=525.0, fy=525.0, cx=319.5, cy=239.5)
               for s, d in ((3, 0.1), (4, 0.1037))]
     _, st, coords, arrays, o = run_both(frames, 0.005, 0.02, 4096, mode=mode, batch=2)
