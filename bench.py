@@ -292,8 +292,8 @@ def main():
     ap.add_argument("--no-microbench", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="time whole steps only")
     ap.add_argument("--mode", default="owner", choices=["owner", "rays"], help="update organisation")
-    ap.add_argument("--batch", type=int, default=32,
-                    help="most frames per integrate call (1..32); the step's frames are split into equal calls")
+    ap.add_argument("--batch", type=int, default=128,
+                    help="most frames per integrate call (1..128); the step's frames are split into equal calls")
     ap.add_argument("--no-variant", action="store_true", help="skip timing the per-frame variants")
     ap.add_argument("--sweep", action="store_true",
                     help="also run the sweep cells (point count at fixed geometry, extent at fixed "

@@ -121,6 +121,13 @@ struct KernelClock {
 
 }  // namespace
 
+namespace {
+constexpr int kMoreFrames = kMaxBatch - kArgFrames;   // frames of a call beyond the kernel arguments
+constexpr int kStageSlots = 4;                        // pinned host slots staging them
+constexpr size_t kCounterBytes = sizeof(unsigned long long) * kReplicas * kCounterWords;
+static_assert(kCounterBytes % 16 == 0, "the frame table after the counters stays 16-byte aligned");
+}  // namespace
+
 struct tsdf_volume {
     tsdf_config cfg;
     tsdf_buffers buf;
@@ -132,6 +139,15 @@ struct tsdf_volume {
     tsdf_frame last[TSDF_MAX_BATCH];
     KernelClock* clock;         // non-null while kernel timing is on
     LaunchTimer timer;
+    // Frames of a call beyond the kernel arguments go to the device table
+    // after the counters (tsdf_counters_bytes) by an asynchronous copy on
+    // the call's stream, from one of kStageSlots pinned host slots (made on
+    // first use); a slot is written again only once its last copy is done.
+    FrameArgs* stage;
+    hipEvent_t stage_done[kStageSlots];
+    int stage_events;           // events created
+    bool stage_used[kStageSlots];
+    int stage_next;
 };
 
 namespace {
@@ -256,20 +272,63 @@ tsdf_status frame_args(const tsdf_volume* h, const tsdf_frame* fr, bool need_rgb
 
 bool same_frame(const tsdf_frame& a, const tsdf_frame& b) { return std::memcmp(&a, &b, sizeof(a)) == 0; }
 
+// A call's frames: the first kArgFrames in the kernel arguments, the rest
+// staged for the device table.
+struct Batch {
+    BatchArgs args;
+    FrameArgs more[kMoreFrames];
+};
+
 // Validate n frames and gather the non-empty ones into a batch.
-tsdf_status batch_args(const tsdf_volume* h, const tsdf_frame* frames, int32_t n, bool need_rgb, BatchArgs* b) {
+tsdf_status batch_args(const tsdf_volume* h, const tsdf_frame* frames, int32_t n, bool need_rgb, Batch* b) {
     if (!frames || n < 0 || n > TSDF_MAX_BATCH) return TSDF_EINVAL;
-    b->n = 0;
-    b->tile_grid = 8;
+    BatchArgs& a = b->args;
+    a.n = 0;
+    a.tile_grid = 8;
+    a.more = nullptr;
     for (int32_t i = 0; i < n; ++i) {
         FrameArgs fa;
         bool empty = false;
         const tsdf_status st = frame_args(h, frames + i, need_rgb, &fa, &empty);
         if (st != TSDF_OK) return st;
         if (empty) continue;
-        b->f[b->n++] = fa;
-        b->tile_grid = std::max(b->tile_grid, tile_grid(fa));
+        if (a.n < kArgFrames)
+            a.f[a.n] = fa;
+        else
+            b->more[a.n - kArgFrames] = fa;
+        ++a.n;
+        a.tile_grid = std::max(a.tile_grid, tile_grid(fa));
     }
+    return TSDF_OK;
+}
+
+// Copy the frames beyond the kernel arguments to the device table, ahead of
+// the call's kernels on stream s.
+tsdf_status stage_frames(tsdf_volume* h, Batch* b, hipStream_t s) {
+    const int n_more = b->args.n - kArgFrames;
+    if (n_more <= 0) return TSDF_OK;
+    if (!h->stage) {
+        void* p = nullptr;
+        if (hipHostMalloc(&p, sizeof(FrameArgs) * kMoreFrames * kStageSlots, hipHostMallocDefault) != hipSuccess)
+            return TSDF_EHIP;
+        h->stage = static_cast<FrameArgs*>(p);
+    }
+    while (h->stage_events < kStageSlots) {
+        if (hipEventCreateWithFlags(&h->stage_done[h->stage_events], hipEventDisableTiming) != hipSuccess)
+            return TSDF_EHIP;
+        ++h->stage_events;
+    }
+    const int k = h->stage_next;
+    if (h->stage_used[k] && hipEventSynchronize(h->stage_done[k]) != hipSuccess) return TSDF_EHIP;
+    FrameArgs* slot = h->stage + (size_t)k * kMoreFrames;
+    std::memcpy(slot, b->more, sizeof(FrameArgs) * (size_t)n_more);
+    FrameArgs* table = reinterpret_cast<FrameArgs*>(static_cast<char*>(h->buf.counters) + kCounterBytes);
+    if (hipMemcpyAsync(table, slot, sizeof(FrameArgs) * (size_t)n_more, hipMemcpyHostToDevice, s) != hipSuccess)
+        return TSDF_EHIP;
+    if (hipEventRecord(h->stage_done[k], s) != hipSuccess) return TSDF_EHIP;
+    h->stage_used[k] = true;
+    h->stage_next = (k + 1) % kStageSlots;
+    b->args.more = table;
     return TSDF_OK;
 }
 
@@ -301,7 +360,7 @@ int64_t tsdf_table_entries_for(int64_t pool_capacity) {
     return t;
 }
 
-size_t tsdf_counters_bytes(void) { return sizeof(unsigned long long) * kReplicas * kCounterWords; }
+size_t tsdf_counters_bytes(void) { return kCounterBytes + sizeof(FrameArgs) * kMoreFrames; }
 
 size_t tsdf_scratch_bytes(const tsdf_config* config) {
     if (!config || config->update_mode != TSDF_UPDATE_OWNER) return 0;
@@ -354,10 +413,13 @@ tsdf_status tsdf_reset(tsdf_volume* h, void* stream) {
 
 tsdf_status tsdf_allocate_batch(tsdf_volume* h, const tsdf_frame* frames, int32_t n_frames, void* stream) {
     if (!h) return TSDF_EINVAL;
-    BatchArgs b;
+    Batch b;
     const tsdf_status st = batch_args(h, frames, n_frames, false, &b);
-    if (st != TSDF_OK || b.n == 0) return st;
-    const tsdf_status a = do_allocate(h, b, static_cast<hipStream_t>(stream));
+    if (st != TSDF_OK || b.args.n == 0) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const tsdf_status sf = stage_frames(h, &b, s);
+    if (sf != TSDF_OK) return sf;
+    const tsdf_status a = do_allocate(h, b.args, s);
     if (a == TSDF_OK && h->cfg.update_mode == TSDF_UPDATE_OWNER) {
         h->pending = true;
         h->n_last = n_frames;
@@ -368,16 +430,19 @@ tsdf_status tsdf_allocate_batch(tsdf_volume* h, const tsdf_frame* frames, int32_
 
 tsdf_status tsdf_update_batch(tsdf_volume* h, const tsdf_frame* frames, int32_t n_frames, void* stream) {
     if (!h) return TSDF_EINVAL;
-    BatchArgs b;
+    Batch b;
     const tsdf_status st = batch_args(h, frames, n_frames, true, &b);
-    if (st != TSDF_OK || b.n == 0) return st;
+    if (st != TSDF_OK || b.args.n == 0) return st;
     if (h->cfg.update_mode == TSDF_UPDATE_OWNER) {
         if (!h->pending || h->n_last != n_frames) return TSDF_EINVAL;
         for (int32_t i = 0; i < n_frames; ++i)
             if (!same_frame(h->last[i], frames[i])) return TSDF_EINVAL;
-        h->pending = false;
     }
-    return do_update(h, b, static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const tsdf_status sf = stage_frames(h, &b, s);
+    if (sf != TSDF_OK) return sf;
+    if (h->cfg.update_mode == TSDF_UPDATE_OWNER) h->pending = false;
+    return do_update(h, b.args, s);
 }
 
 tsdf_status tsdf_allocate(tsdf_volume* h, const tsdf_frame* frame, void* stream) {
@@ -390,13 +455,15 @@ tsdf_status tsdf_update(tsdf_volume* h, const tsdf_frame* frame, void* stream) {
 
 tsdf_status tsdf_integrate_batch(tsdf_volume* h, const tsdf_frame* frames, int32_t n_frames, void* stream) {
     if (!h) return TSDF_EINVAL;
-    BatchArgs b;
+    Batch b;
     const tsdf_status st = batch_args(h, frames, n_frames, true, &b);
-    if (st != TSDF_OK || b.n == 0) return st;
+    if (st != TSDF_OK || b.args.n == 0) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const tsdf_status a = do_allocate(h, b, s);
+    const tsdf_status sf = stage_frames(h, &b, s);
+    if (sf != TSDF_OK) return sf;
+    const tsdf_status a = do_allocate(h, b.args, s);
     if (a != TSDF_OK) return a;
-    return do_update(h, b, s);
+    return do_update(h, b.args, s);
 }
 
 tsdf_status tsdf_integrate(tsdf_volume* h, const tsdf_frame* frame, void* stream) {
@@ -518,6 +585,11 @@ tsdf_status tsdf_kernel_times(tsdf_volume* h, tsdf_kernel_time* out, int32_t max
 
 void tsdf_destroy(tsdf_volume* h) {
     if (!h) return;
+    for (int k = 0; k < h->stage_events; ++k) {
+        if (h->stage_used[k]) (void)hipEventSynchronize(h->stage_done[k]);   // no copy still reads the slot
+        (void)hipEventDestroy(h->stage_done[k]);
+    }
+    if (h->stage) (void)hipHostFree(h->stage);
     delete h->clock;
     delete h;
 }

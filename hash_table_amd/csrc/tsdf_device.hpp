@@ -66,11 +66,13 @@ constexpr float kNearPlane = 1e-4f;                 // block corners closer than
 // One run of a walk inside one block, as allocate records it for the
 // update (16 bytes):
 //   depth     the point's depth (f32 bits)
-//   meta      colour R | G << 8 | B << 16, frame of the batch << 24 (5 bits),
-//             axis direction bits << 29 (bit set: that axis steps by -1)
+//   meta      colour R | G << 8 | B << 16, frame of the batch << 24 (its low
+//             5 bits), axis direction bits << 29 (bit set: that axis steps
+//             by -1)
 //   code      first cell (voxel index in the block, 9 bits) | cells - 1 << 9
 //             (5 bits) | y-step plane << 14 (21 bits) | z-step plane << 35
-//             (21 bits) | kept cells << 56 (6 bits)
+//             (21 bits) | kept cells << 56 (6 bits) | frame of the batch >> 5
+//             << 62 (its high 2 bits)
 // Bit q of the y-step (z-step) plane is set when the run's step q, the one
 // from its cell q to cell q + 1, moves along y (z); a step with neither bit
 // moves along x.  The walk is monotonic on every axis and a block spans 8
@@ -106,7 +108,11 @@ __device__ __forceinline__ unsigned int code_zsteps(unsigned long long c) {
     return (unsigned int)(c >> (kStepShift + kPlaneBits)) & ((1u << kPlaneBits) - 1u);
 }
 __device__ __forceinline__ int code_kept(unsigned long long c) { return (int)((c >> kKeptShift) & 63u); }
-__device__ __forceinline__ int meta_frame(unsigned int m) { return (int)((m >> 24) & 31u); }
+constexpr int kFrameHighShift = 62;
+// The frame (of the batch) a record belongs to: 5 bits in meta, 2 in the code.
+__device__ __forceinline__ int record_frame(unsigned int meta, unsigned long long code) {
+    return (int)(((meta >> 24) & 31u) | ((unsigned int)(code >> kFrameHighShift) << 5));
+}
 
 // A wavefront's runs through one block, as recorded by allocate.  One
 // 64-bit atomic on the block's counter (segments << 32 | runs) gives both
@@ -194,13 +200,40 @@ struct FrameArgs {
 // The frames of one call (tsdf_integrate_batch, or one frame).  Frame i
 // uses workgroups [i * tile_grid, (i + 1) * tile_grid) of the per-pixel
 // kernels; tile_grid is a multiple of 8, so the workgroup -> XCD mapping is
-// the same for every frame.
-constexpr int kMaxBatch = 32;
+// the same for every frame.  The first kArgFrames frames travel in the
+// kernel arguments; the others (a call of more frames) in a device table
+// the library fills before the call's kernels (`more`, frame kArgFrames
+// first).
+constexpr int kMaxBatch = 128;              // 7-bit frame index in the run records
+constexpr int kArgFrames = 32;
 struct BatchArgs {
-    FrameArgs f[kMaxBatch];
+    FrameArgs f[kArgFrames];
+    const FrameArgs* more;
     int n;
     int tile_grid;
 };
+
+// Where frame i of the batch is (kernel arguments or the device table).
+__device__ __forceinline__ const FrameArgs* frame_ptr(const BatchArgs& b, int i) {
+    return i < kArgFrames ? b.f + i : b.more + (i - kArgFrames);
+}
+
+// Frame i of the batch, i the same in every lane and every lane active: lane
+// k loads the frame's word k and the wavefront reads each word into a
+// scalar register (a plain load through frame_ptr would be one load per
+// lane and field, the pointer being either of two memories).
+__device__ __forceinline__ FrameArgs batch_frame(const BatchArgs& b, int i) {
+    constexpr int kWords = (int)(sizeof(FrameArgs) / 4);
+    static_assert(sizeof(FrameArgs) % 4 == 0 && kWords <= 64, "a frame's words fit a wavefront");
+    const unsigned int* src = reinterpret_cast<const unsigned int*>(frame_ptr(b, i));
+    const int lane = (int)(threadIdx.x & 63u);
+    const unsigned int w = lane < kWords ? src[lane] : 0u;
+    FrameArgs f;
+    unsigned int* dst = reinterpret_cast<unsigned int*>(&f);
+#pragma unroll
+    for (int k = 0; k < kWords; ++k) dst[k] = (unsigned int)__builtin_amdgcn_readlane(w, k);
+    return f;
+}
 
 struct VolumeArgs {
     Entry* table;

@@ -126,7 +126,7 @@ static_assert(kSetCap == 256, "set_slot yields 8 bits");
 // wavefront.
 __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, int lane, unsigned int part,
                                           const VolumeArgs& vol, const OwnerArgs& own, unsigned int depth,
-                                          unsigned int meta, unsigned int& misses) {
+                                          unsigned int meta, unsigned int frame_hi, unsigned int& misses) {
     bool any_pend = false;
 #pragma unroll
     for (int q = 0; q < kSlots; ++q) any_pend = any_pend || S.pend[q];
@@ -259,7 +259,7 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, int lane, un
             r.depth = depth;
             r.meta = meta;
             r.code_lo = (unsigned int)S.code[q];
-            r.code_hi = (unsigned int)(S.code[q] >> 32);
+            r.code_hi = (unsigned int)(S.code[q] >> 32) | frame_hi;
             own.recs[b + rk[q]] = r;
         }
     }
@@ -269,7 +269,7 @@ __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, u
                                              int itc, int x, int y, int z, int s0, int s1, int s2, AllocLds& L,
                                              int lane, unsigned int part, const VolumeArgs& vol,
                                              const OwnerArgs& own, unsigned int depth_bits, unsigned int meta,
-                                             unsigned int& n_upd, unsigned int& misses) {
+                                             unsigned int frame_hi, unsigned int& n_upd, unsigned int& misses) {
     // planes in walk order, bit j = the chunk's cell j: the kept plane's
     // sentinel marks the n cells this lane walked; the step planes were
     // shifted once per iteration
@@ -314,7 +314,7 @@ __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, u
                 j0 += (int)len;
             }
         }
-        file_runs(S, L, lane, part, vol, own, depth_bits, meta, misses);
+        file_runs(S, L, lane, part, vol, own, depth_bits, meta, frame_hi, misses);
     }
 }
 
@@ -324,7 +324,7 @@ template <bool kReproject>
 __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ AllocLds L;
     const int fi = blockIdx.x / B.tile_grid;                 // frame of this workgroup
-    const FrameArgs& f = B.f[fi];
+    const FrameArgs f = batch_frame(B, fi);
     if (blockIdx.x == 0 && own.build_items) {
         // clear the next frame's counters (their last users finished before
         // this kernel started)
@@ -370,10 +370,11 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
             const uint8_t* c = f.rgb + 3 * (size_t)pix;
             meta = (unsigned int)c[0] | ((unsigned int)c[1] << 8) | ((unsigned int)c[2] << 16);
         }
-        meta |= ((unsigned int)fi << 24) | (w.s0 < 0 ? 1u << 29 : 0u) | (w.s1 < 0 ? 1u << 30 : 0u) |
+        meta |= (((unsigned int)fi & 31u) << 24) | (w.s0 < 0 ? 1u << 29 : 0u) | (w.s1 < 0 ? 1u << 30 : 0u) |
                 (w.s2 < 0 ? 1u << 31 : 0u);
     }
     const unsigned int depth_bits = __float_as_uint(depth);
+    const unsigned int frame_hi = ((unsigned int)fi >> 5) << (kFrameHighShift - 32);   // into the code's top bits
     unsigned int n_upd = 0, n_guard = 0, misses = 0;
     const unsigned int part = (blockIdx.x * kWaves + wave) % kParts;   // this wavefront's reservations
     const int max_visits = f.max_visits;
@@ -460,11 +461,11 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
             break;
         }
         // a walk goes on into another chunk: file this one's runs now
-        cut_and_file(kp, yp, zp, cp, itc, x, y, z, s0, s1, s2, L, lane, part, vol, own, depth_bits, meta, n_upd,
-                     misses);
+        cut_and_file(kp, yp, zp, cp, itc, x, y, z, s0, s1, s2, L, lane, part, vol, own, depth_bits, meta,
+                     frame_hi, n_upd, misses);
     }
-    cut_and_file(kp, yp, zp, cp, last_itc, x, y, z, s0, s1, s2, L, lane, part, vol, own, depth_bits, meta, n_upd,
-                 misses);
+    cut_and_file(kp, yp, zp, cp, last_itc, x, y, z, s0, s1, s2, L, lane, part, vol, own, depth_bits, meta,
+                 frame_hi, n_upd, misses);
 
     const unsigned int c_upd = wave_sum(n_upd);
     const unsigned int c_guard = wave_sum(n_guard);
@@ -720,8 +721,8 @@ __global__ __launch_bounds__(kUpdateThreads) void k_update_owner(BatchArgs B, Vo
     const int tid = threadIdx.x;
     if (tid < kLengths) s_hist[tid] = 0;
     if (tid < B.n) {
-        s_axis[tid] = depth_axis(B.f[tid]);
-        if (kReproject) s_proj[tid] = projection(B.f[tid]);
+        s_axis[tid] = depth_axis(*frame_ptr(B, tid));
+        if (kReproject) s_proj[tid] = projection(*frame_ptr(B, tid));
     }
     for (int j = tid; j < kBlockVoxels; j += kUpdateThreads) {
         L.tw[j] = 0;
@@ -821,7 +822,7 @@ __global__ __launch_bounds__(kUpdateThreads) void k_update_owner(BatchArgs B, Vo
                         const RunRecord rr = s_run[p];
                         const unsigned long long code = record_code(rr);
                         const float dep = __uint_as_float(rr.depth);
-                        const int rf = meta_frame(rr.meta);
+                        const int rf = record_frame(rr.meta, code);
                         const DepthAxis ax = s_axis[rf];
                         const unsigned long long c = (unsigned long long)(rr.meta & 0xFFu) |
                                                      ((unsigned long long)((rr.meta >> 8) & 0xFFu) << 21) |
@@ -894,7 +895,7 @@ __global__ __launch_bounds__(kRescanThreads) void k_update_rescan(BatchArgs B, V
         unsigned int n_kept = 0;
         const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
         for (int fi = 0; fi < B.n; ++fi) {
-            const FrameArgs& f = B.f[fi];
+            const FrameArgs f = batch_frame(B, fi);
             const Projection pr = projection(f);
             const DepthAxis fax = depth_axis(f);
             const PixelRect rc = block_rect(bx, by, bz, f, vol.vs);
@@ -974,7 +975,7 @@ __global__ __launch_bounds__(kRescanThreads) void k_update_rescan(BatchArgs B, V
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_update_rays(BatchArgs B, VolumeArgs vol) {
     const int fi = blockIdx.x / B.tile_grid;
-    const FrameArgs& f = B.f[fi];
+    const FrameArgs f = batch_frame(B, fi);
     __shared__ unsigned int s_hist[kProbeBins];
     __shared__ unsigned int s_pmax;
     __shared__ unsigned int s_miss;

@@ -24,7 +24,7 @@ UPDATE_MODES = {"owner": TSDF_UPDATE_OWNER, "rays": TSDF_UPDATE_RAYS}
 TSDF_OCCLUSION_RAY, TSDF_OCCLUSION_REPROJECT = 0, 1
 OCCLUSION_MODES = {"ray": TSDF_OCCLUSION_RAY, "reproject": TSDF_OCCLUSION_REPROJECT}
 TSDF_PROBE_BINS = 32
-TSDF_MAX_BATCH = 32
+TSDF_MAX_BATCH = 128
 TSDF_MAX_FRAME_SIDE = 65535
 TSDF_MAX_POOL_BLOCKS = 1 << 30
 TSDF_MAX_TABLE_ENTRIES = 1 << 31

@@ -56,7 +56,7 @@ typedef enum {
  * intrinsics allow more is rejected with TSDF_EINVAL). */
 #define TSDF_MAX_WALK 4096
 /* Most frames one tsdf_integrate_batch call takes. */
-#define TSDF_MAX_BATCH 32
+#define TSDF_MAX_BATCH 128
 /* Largest frame width and height, in pixels (a pixel position is recorded
  * as two 16-bit halves). */
 #define TSDF_MAX_FRAME_SIDE 65535
@@ -123,7 +123,8 @@ typedef struct {
     float* r;               /*   and of the colour channels (0..1).  Voxel v of block i is */
     float* g;               /*   element i * 512 + v, v = x + 8 y + 64 z within the block. */
     float* b;
-    void* counters;         /* tsdf_counters_bytes() bytes */
+    void* counters;         /* tsdf_counters_bytes() bytes: statistics, then the launch
+                               parameters of a batch's frames beyond the 32nd */
     void* scratch;          /* tsdf_scratch_bytes(config) bytes (the owner update's work
                                list); may be NULL when that is 0 */
 } tsdf_buffers;
@@ -168,7 +169,8 @@ typedef struct {
  * (section 3 of the paper: at most half full).  Returns -1 for an invalid capacity. */
 int64_t tsdf_table_entries_for(int64_t pool_capacity);
 
-/* Size of the counters buffer. */
+/* Size of the counters buffer (the statistics, and a device table of the
+ * launch parameters of up to TSDF_MAX_BATCH - 32 frames). */
 size_t tsdf_counters_bytes(void);
 
 /* Size of the scratch buffer a configuration needs (0 for TSDF_UPDATE_RAYS):
@@ -213,7 +215,11 @@ tsdf_status tsdf_integrate(tsdf_volume* volume, const tsdf_frame* frame, void* s
  * over all of them followed by one update: the result equals integrating
  * them one by one (the block set is the union, sums commute; which keys an
  * exhausted pool refuses may differ, their number does not), but each block
- * the batch touches is read and written once.  Frames may differ in size. */
+ * the batch touches is read and written once.  Frames may differ in size.
+ * The launch parameters of frames beyond the 32nd are copied to the device
+ * table in the counters buffer by an asynchronous copy on the stream, from
+ * pinned host memory the volume allocates on first use (released by
+ * tsdf_destroy); TSDF_EHIP if that allocation or copy fails. */
 tsdf_status tsdf_integrate_batch(tsdf_volume* volume, const tsdf_frame* frames, int32_t n_frames, void* stream);
 
 /* The two halves of tsdf_integrate_batch.  In owner mode tsdf_update_batch

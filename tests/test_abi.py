@@ -38,7 +38,7 @@ def test_table_sizing_rule():
     assert tsdf.tsdf_table_entries_for(1 << 22) == 1 << 23
     assert tsdf.tsdf_table_entries_for(0) == -1
     assert tsdf.tsdf_table_entries_for(tsdf.TSDF_MAX_POOL_BLOCKS + 1) == -1
-    assert tsdf.tsdf_counters_bytes() == 64 * 640
+    assert tsdf.tsdf_counters_bytes() == 64 * 640 + 96 * 104     # statistics + 96 frames of launch parameters
 
 
 def test_scratch_sizing():

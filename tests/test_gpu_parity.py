@@ -103,16 +103,16 @@ def _check_history(label, hist, g, calls):
 @pytest.mark.timeout(600)
 def test_room_full_parity():
     """All 100 frames of the 640 x 480 room: in the launch configuration the
-    benchmark times (owner update, 4 calls of 25 frames) and one frame per
-    call with both update modes; counts after every call against the stored
-    oracle counts, then every voxel against a live oracle run."""
+    benchmark times (owner update, all 100 frames in one call) and one frame
+    per call with both update modes; counts after every call against the
+    stored oracle counts, then every voxel against a live oracle run."""
     wl = scenes.workload("room640x480")
     g = golden("room640x480")
     frames = list(wl.frames())
     for i, f in enumerate(frames[:3]):
         assert scenes.frame_digest([f]) == g["frames"][i]["sha256"], "generator drifted from the stored counts"
     results = {}
-    for mode, batch in (("owner", 25), ("owner", 1), ("rays", 1)):
+    for mode, batch in (("owner", 100), ("owner", 1), ("rays", 1)):
         say(f"  gpu ({mode}, {batch} frames per call): 100 frames 640x480")
         _, st, coords, arrays, hist = parity.gpu_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity,
                                                            per_frame_stats=True, mode=mode, batch=batch,
@@ -321,10 +321,12 @@ def tsdf_bins():
 # batched integration (one allocate and one update for several frames)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("batch", [3, 16])
+@pytest.mark.parametrize("batch", [3, 16, 40])
 def test_batched_room_parity(mode, batch):
+    # 40: one call whose frames 32.. travel in the device frame table and
+    # whose run records carry the frame's high bits
     wl = scenes.workload("room640x480")
-    frames = list(wl.frames(0, 20))
+    frames = list(wl.frames(0, max(20, batch)))
     _, st, coords, arrays, o = run_both(frames, wl.voxel_size, wl.trunc, wl.pool_capacity, mode=mode,
                                         batch=batch, max_batch_pixels=batch * 640 * 480)
     assert_parity(st, coords, arrays, o)
