@@ -85,8 +85,8 @@ def load_counts(name):
 MEASURED_TRAFFIC = {
     # (kernel, workload, most frames per call, update mode): (bytes per launch, source digest)
     # profiles/integrate_room640x480.md
-    ("k_allocate", "room640x480", 32, "owner"): (415688502, "6a90024a83cfa719"),
-    ("k_update_owner", "room640x480", 32, "owner"): (625155986, "6a90024a83cfa719"),
+    ("k_allocate", "room640x480", 128, "owner"): (1655233935, "4a5e6530e24821cb"),
+    ("k_update_owner", "room640x480", 128, "owner"): (2064912250, "4a5e6530e24821cb"),
 }
 
 
