@@ -679,23 +679,29 @@ constexpr float kTsdfScale = 65536.0f;               // 2^16
 constexpr float kTsdfUnit = 1.0f / 65536.0f;
 constexpr int kRescanThreads = 128;
 
+// Voxel j's sums sit at sum_slot(j): one spare word after every 16, so that
+// voxels 32 apart (neighbouring rays' cells four rows apart, say) no longer
+// fall on the same LDS banks.
+constexpr int kSumSlots = kBlockVoxels + kBlockVoxels / 16;
+__device__ __forceinline__ int sum_slot(int j) { return j + (j >> 4); }
+
 struct OwnerLds {
-    unsigned long long tw[kBlockVoxels];
-    unsigned long long rgb[kBlockVoxels];
+    unsigned long long tw[kSumSlots];
+    unsigned long long rgb[kSumSlots];
 };
 
 // Add the chunk's sums to the pool block and clear them for the next chunk.
 __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, size_t base) {
     for (int j = threadIdx.x; j < kBlockVoxels; j += kUpdateThreads) {
-        const unsigned long long tw = L.tw[j];
+        const unsigned long long tw = L.tw[sum_slot(j)];
         const unsigned int cnt = (unsigned int)(tw >> 32);
         if (!cnt) continue;
-        const unsigned long long c = L.rgb[j];
+        const unsigned long long c = L.rgb[sum_slot(j)];
         // sum of the signed distances, in units of 2^-16 (the +1 offsets removed)
         const long long tq = (long long)(unsigned int)tw - ((long long)cnt << 16);
         const float ts = (float)tq * kTsdfUnit;
-        L.tw[j] = 0;
-        L.rgb[j] = 0;
+        L.tw[sum_slot(j)] = 0;
+        L.rgb[sum_slot(j)] = 0;
         const size_t off = base + j;
         const float t0 = vol.tsdf[off], w0 = vol.weight[off], r0 = vol.r[off], g0 = vol.g[off], b0 = vol.b[off];
         vol.tsdf[off] = t0 + ts;
@@ -725,8 +731,8 @@ __global__ __launch_bounds__(kUpdateThreads) void k_update_owner(BatchArgs B, Vo
         if (kReproject) s_proj[tid] = projection(*frame_ptr(B, tid));
     }
     for (int j = tid; j < kBlockVoxels; j += kUpdateThreads) {
-        L.tw[j] = 0;
-        L.rgb[j] = 0;
+        L.tw[sum_slot(j)] = 0;
+        L.rgb[sum_slot(j)] = 0;
     }
     FrameCounters& fc = own.fc[own.parity];
     const unsigned int n_items = fc.items_total;
@@ -840,8 +846,8 @@ __global__ __launch_bounds__(kUpdateThreads) void k_update_owner(BatchArgs B, Vo
                                 const int j = (k0 & 7) | ((k1 & 7) << 3) | ((k2 & 7) << 6);
                                 const unsigned int tq =
                                     (unsigned int)__float2int_rn((sdf * vol.inv_trunc + 1.0f) * kTsdfScale);
-                                atomicAdd(L.tw + j, (1ull << 32) | tq);
-                                atomicAdd(L.rgb + j, c);
+                                atomicAdd(L.tw + sum_slot(j), (1ull << 32) | tq);
+                                atomicAdd(L.rgb + sum_slot(j), c);
                             }
                             if (++q >= cells) break;
                             const bool sy = ys & 1u, sz = zs & 1u;
