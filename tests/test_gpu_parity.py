@@ -191,6 +191,7 @@ def _reproject_cases():
     cases.append(("spherewall", list(wl.frames()), wl.voxel_size, wl.trunc, wl.pool_capacity))
     wl = scenes.workload("room640x480")
     cases.append(("room16", list(wl.frames(0, 16)), wl.voxel_size, wl.trunc, wl.pool_capacity))
+    cases.append(("room40", list(wl.frames(0, 40)), wl.voxel_size, wl.trunc, wl.pool_capacity))
     return cases
 
 
@@ -200,10 +201,11 @@ def test_reprojection_occlusion_parity(mode):
     """The reprojection reading of the occlusion test (the centre also hidden
     behind the depth seen at its own pixel) in both passes: block set,
     weights exact and means within 1e-4 against the oracle with the same
-    reading, one frame per call and 16 per call; on the scenes with depth
+    reading, one frame per call and 16 per call (40 frames: one call, frames
+    32.. from the device frame table); on the scenes with depth
     discontinuities it must hide contributions the projective reading keeps."""
     for name, frames, vs, tr, cap in _reproject_cases():
-        for batch in (1, 16):
+        for batch in ((40,) if len(frames) > 32 else (1, 16)):
             if batch > 1 and len(frames) == 1:
                 continue
             W, H = frames[0].width, frames[0].height
@@ -214,7 +216,7 @@ def test_reprojection_occlusion_parity(mode):
             assert_parity(st, coords, arrays, o)
         base = parity.oracle_integrate(frames, vs, tr, cap).totals()["voxel_updates"]
         say(f"    hidden by the image: {base - st['voxel_updates']} of {base}")
-        if name in ("step", "spherewall", "room16"):
+        if name in ("step", "spherewall", "room16", "room40"):
             assert st["voxel_updates"] < base
 
 
