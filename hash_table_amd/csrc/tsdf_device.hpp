@@ -360,14 +360,20 @@ __device__ __forceinline__ bool centre_test(const BandWalk& w, const DepthAxis& 
 }
 
 // The same test for cell (k0, k1, k2) of a point with depth d.
-__device__ __forceinline__ bool centre_test(int k0, int k1, int k2, float d, const DepthAxis& a, float vs,
-                                            float trunc, float& sdf) {
-    const float c0 = ((float)k0 + 0.5f) * vs;
-    const float c1 = ((float)k1 + 0.5f) * vs;
-    const float c2 = ((float)k2 + 0.5f) * vs;
+// The centre test from the centre's coordinates in voxels, (float)k + 0.5f
+// per axis (the walk keeps them exactly, see k_allocate).
+__device__ __forceinline__ bool centre_test_at(float x, float y, float z, float d, const DepthAxis& a, float vs,
+                                               float trunc, float& sdf) {
+    const float c0 = x * vs;
+    const float c1 = y * vs;
+    const float c2 = z * vs;
     const float zc = (a.r2 * (c0 - a.t0) + a.r5 * (c1 - a.t1)) + a.r8 * (c2 - a.t2);
     sdf = d - zc;
     return sdf >= -trunc && sdf <= trunc;
+}
+__device__ __forceinline__ bool centre_test(int k0, int k1, int k2, float d, const DepthAxis& a, float vs,
+                                            float trunc, float& sdf) {
+    return centre_test_at((float)k0 + 0.5f, (float)k1 + 0.5f, (float)k2 + 0.5f, d, a, vs, trunc, sdf);
 }
 
 // The reprojection reading of the occlusion test: what a frame contributes
@@ -422,14 +428,19 @@ __device__ __forceinline__ bool hidden_in_image(float q0, float q1, float q2, fl
 }
 
 // centre_test with the reprojection reading added (same centre arithmetic).
-__device__ __forceinline__ bool centre_test_reproject(int k0, int k1, int k2, float d, const DepthAxis& a,
-                                                      const Projection& p, float vs, float trunc, float& sdf) {
-    const float q0 = (((float)k0 + 0.5f) * vs) - a.t0;
-    const float q1 = (((float)k1 + 0.5f) * vs) - a.t1;
-    const float q2 = (((float)k2 + 0.5f) * vs) - a.t2;
+__device__ __forceinline__ bool centre_test_reproject_at(float x, float y, float z, float d, const DepthAxis& a,
+                                                         const Projection& p, float vs, float trunc, float& sdf) {
+    const float q0 = (x * vs) - a.t0;
+    const float q1 = (y * vs) - a.t1;
+    const float q2 = (z * vs) - a.t2;
     const float zc = (a.r2 * q0 + a.r5 * q1) + a.r8 * q2;
     sdf = d - zc;
     return sdf >= -trunc && sdf <= trunc && !hidden_in_image(q0, q1, q2, zc, p, trunc);
+}
+__device__ __forceinline__ bool centre_test_reproject(int k0, int k1, int k2, float d, const DepthAxis& a,
+                                                      const Projection& p, float vs, float trunc, float& sdf) {
+    return centre_test_reproject_at((float)k0 + 0.5f, (float)k1 + 0.5f, (float)k2 + 0.5f, d, a, p, vs, trunc,
+                                    sdf);
 }
 
 // Step to the next cell: the axis with the smallest boundary parameter (ties

@@ -381,25 +381,32 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
     const float vs = vol.vs, trunc = vol.trunc;
     const DepthAxis ax = depth_axis(f);
 
-    // Walk state in registers, per axis: cell, next boundary parameter,
-    // start and reciprocal of the direction (both in voxel units), and step.
-    int k0 = 0, k1 = 0, k2 = 0, s0 = 0, s1 = 0, s2 = 0;
+    // Walk state in registers, per axis: the index of the next cell boundary
+    // the walk will cross and the step (both as floats holding integers,
+    // exactly), the boundary's parameter, the start and reciprocal of the
+    // direction (in voxel units), and the offset from the boundary index to
+    // the current cell's centre (k + 1/2 is b - 1/2 stepping up, b + 1/2
+    // stepping down or still: exactly, for any cell a key can hold).
+    int s0 = 0, s1 = 0, s2 = 0;
+    float b0 = 0.f, b1 = 0.f, b2 = 0.f, f0 = 0.f, f1 = 0.f, f2 = 0.f, h0 = 0.f, h1 = 0.f, h2 = 0.f;
     float tm0 = 0.f, tm1 = 0.f, tm2 = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, i0 = 0.f, i1 = 0.f, i2 = 0.f;
     if (alive) {
-        k0 = w.k0; k1 = w.k1; k2 = w.k2;
         s0 = w.s0; s1 = w.s1; s2 = w.s2;
+        f0 = (float)s0; f1 = (float)s1; f2 = (float)s2;
+        b0 = (float)(w.k0 + (s0 > 0)); b1 = (float)(w.k1 + (s1 > 0)); b2 = (float)(w.k2 + (s2 > 0));
+        h0 = s0 > 0 ? -0.5f : 0.5f; h1 = s1 > 0 ? -0.5f : 0.5f; h2 = s2 > 0 ? -0.5f : 0.5f;
         tm0 = w.tm0; tm1 = w.tm1; tm2 = w.tm2;
         g0 = w.gA0; g1 = w.gA1; g2 = w.gA2;
         i0 = w.inv0; i1 = w.inv1; i2 = w.inv2;
     }
     const float dd = depth;
     const Projection proj = projection(f);
-    auto test = [&](int c0, int c1, int c2) {
+    auto test = [&]() {                       // the centre test of the walk's current cell
         float sdf;
-        return kReproject ? centre_test_reproject(c0, c1, c2, dd, ax, proj, vs, trunc, sdf)
-                          : centre_test(c0, c1, c2, dd, ax, vs, trunc, sdf);
+        return kReproject ? centre_test_reproject_at(b0 + h0, b1 + h1, b2 + h2, dd, ax, proj, vs, trunc, sdf)
+                          : centre_test_at(b0 + h0, b1 + h1, b2 + h2, dd, ax, vs, trunc, sdf);
     };
-    bool keep = test(k0, k1, k2);             // the centre test of the walk's current cell
+    bool keep = test();
 
     // The walk goes in chunks of up to kChunkCells cells.  All lanes start
     // together, so a lane's cell index within the chunk is the (uniform)
@@ -415,9 +422,9 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
     unsigned int kp, yp, zp, cp;              // its planes
     int last_itc = 0;
     for (int done = 0;; done += kChunkCells) {
-        x = k0;
-        y = k1;
-        z = k2;
+        x = (int)(b0 + h0 - 0.5f);            // the current cell (exact: integers and halves)
+        y = (int)(b1 + h1 - 0.5f);
+        z = (int)(b2 + h2 - 0.5f);
         kp = 1u;                              // the kept plane starts with a sentinel bit
         yp = zp = cp = 0u;
         // the safety bound on cells per walk limits the chunk (uniform)
@@ -432,21 +439,22 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
             const bool a0 = more && e0, a1 = more && !e0 && e1, a2 = more && !e0 && !e1;
             yp = yp + yp + (a1 ? 1u : 0u);
             zp = zp + zp + (a2 ? 1u : 0u);
-            const int kc = e0 ? k0 : (e1 ? k1 : k2);
-            const int sc = e0 ? s0 : (e1 ? s1 : s2);
+            const float bc = e0 ? b0 : (e1 ? b1 : b2);   // the boundary this step crosses
+            const float fc = e0 ? f0 : (e1 ? f1 : f2);
             const float gc = e0 ? g0 : (e1 ? g1 : g2);
             const float ic = e0 ? i0 : (e1 ? i1 : i2);
-            const int kn = kc + sc;
-            const float tn = ((float)(kn + (sc > 0 ? 1 : 0)) - gc) * ic;   // the new cell's next boundary
-            const bool cr = more && (unsigned int)(kn ^ kc) > 7u;
+            const float bn = bc + fc;                     // the new cell's next boundary
+            const float tn = (bn - gc) * ic;
+            // the step leaves the block iff the boundary it crosses is a block face
+            const bool cr = more && __builtin_amdgcn_fractf(bc * 0.125f) == 0.0f;
             cp = cp + cp + (cr ? 1u : 0u);
-            k0 = a0 ? kn : k0;
-            k1 = a1 ? kn : k1;
-            k2 = a2 ? kn : k2;
+            b0 = a0 ? bn : b0;
+            b1 = a1 ? bn : b1;
+            b2 = a2 ? bn : b2;
             tm0 = a0 ? tn : tm0;
             tm1 = a1 ? tn : tm1;
             tm2 = a2 ? tn : tm2;
-            keep = test(k0, k1, k2);
+            keep = test();
             alive = more;
         }
         // A walk still going after max_visits cells is cut there (counted).
