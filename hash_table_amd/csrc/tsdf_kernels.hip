@@ -10,10 +10,11 @@
 // organised is this library's choice for the MI355X memory system:
 //
 //   * owner update (default): allocate cuts every walk into runs, one per
-//     block it crosses, and records each run with a kept voxel (pixel, first
-//     cell, cells, kept, frame); the records are grouped by block, and one
-//     workgroup per block replays the exact walk of each of its runs, sums
-//     the block's contributions in LDS and then read-modify-writes the five
+//     block it crosses, and records each run with a kept voxel (depth,
+//     colour, frame, first cell and the axis of each step: 16 bytes); the
+//     records are grouped by block, and one workgroup per block enumerates
+//     the cells of each of its runs (no walk arithmetic repeated), sums the
+//     block's contributions in LDS and then read-modify-writes the five
 //     pool arrays with plain coalesced loads and stores: a block has one
 //     writer per call, so no device-scope float atomics are needed.  A block
 //     whose runs did not fit the record buffers is rescanned from the pixel
