@@ -349,15 +349,6 @@ __device__ __forceinline__ DepthAxis depth_axis(const FrameArgs& f) {
     return a;
 }
 
-__device__ __forceinline__ bool centre_test(const BandWalk& w, const DepthAxis& a, float vs, float trunc,
-                                            float& sdf) {
-    const float c0 = ((float)w.k0 + 0.5f) * vs;
-    const float c1 = ((float)w.k1 + 0.5f) * vs;
-    const float c2 = ((float)w.k2 + 0.5f) * vs;
-    const float zc = (a.r2 * (c0 - a.t0) + a.r5 * (c1 - a.t1)) + a.r8 * (c2 - a.t2);
-    sdf = w.d - zc;
-    return sdf >= -trunc && sdf <= trunc;
-}
 
 // The same test for cell (k0, k1, k2) of a point with depth d.
 // The centre test from the centre's coordinates in voxels, (float)k + 0.5f
@@ -513,22 +504,6 @@ __device__ __forceinline__ bool advance_select(BandWalk& w, bool& crossed, int& 
     crossed = more && (k >> 3) != (k_old >> 3);
     axis = c2 ? 2 : (c1 ? 1 : 0);
     return more;
-}
-
-// Put the walk at cell k.  A walk's next-boundary parameters depend only on
-// its current cell (advance recomputes them with this formula), so a walk
-// resumed at a cell it visits continues exactly as the full walk would.
-__device__ __forceinline__ float boundary_param(int k, int s, float gA, float inv) {
-    return s > 0 ? ((float)(k + 1) - gA) * inv : (s < 0 ? ((float)k - gA) * inv : __builtin_inff());
-}
-
-__device__ __forceinline__ void resume_at(BandWalk& w, int k0, int k1, int k2) {
-    w.k0 = k0;
-    w.k1 = k1;
-    w.k2 = k2;
-    w.tm0 = boundary_param(k0, w.s0, w.gA0, w.inv0);
-    w.tm1 = boundary_param(k1, w.s1, w.gA1, w.inv1);
-    w.tm2 = boundary_param(k2, w.s2, w.gA2, w.inv2);
 }
 
 // 64-bit key: block coordinate (cell >> 3, i.e. floor(cell / 8)) + 2^20 per

@@ -377,7 +377,12 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
     const unsigned int depth_bits = __float_as_uint(depth);
     const unsigned int frame_hi = ((unsigned int)fi >> 5) << (kFrameHighShift - 32);   // into the code's top bits
     unsigned int n_upd = 0, n_guard = 0, misses = 0;
-    const unsigned int part = (blockIdx.x * kWaves + wave) % kParts;   // this wavefront's reservations
+    // this wavefront's reservations: partitions in turn as if the call's
+    // frames were laid end to end by their tile counts (numbering by launch
+    // index instead, every frame would start at a multiple of 8 workgroups
+    // and the first tiles of many small frames would all fill the same few)
+    const unsigned int wg = blockIdx.x - (unsigned int)fi * (unsigned int)B.tile_grid;
+    const unsigned int part = (((unsigned int)fi * (unsigned int)f.n_tiles + wg) * kWaves + wave) % kParts;
     const int max_visits = f.max_visits;
     const float vs = vol.vs, trunc = vol.trunc;
     const DepthAxis ax = depth_axis(f);

@@ -344,6 +344,27 @@ def test_batch_of_mixed_frames(mode):
     assert_parity(st, coords, arrays, o)
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_full_batch_of_mixed_frames(mode):
+    # TSDF_MAX_BATCH frames in one call: sizes from 1 x 1 to 129 x 65, some
+    # empty (skipped, so a frame's place in the batch and in the call's
+    # frame table differ), poses all different: frames past the first 32
+    # travel in the device frame table and their records carry the frame's
+    # high bits
+    from hash_table_amd import tsdf
+    rng = np.random.default_rng(7)
+    sizes = [(1, 1), (37, 23), (16, 16), (129, 65), (1, 33), (64, 48), (9, 6)]
+    frames = []
+    for i in range(tsdf.TSDF_MAX_BATCH):
+        W, H = sizes[int(rng.integers(len(sizes)))]
+        fr = scenes.random_frame(100 + i, W=W, H=H, invalid_frac=0.1, translation_scale=0.3)
+        frames.append(_frame_like(fr, np.zeros((0, 0))) if i % 17 == 5 else fr)
+    _, st, coords, arrays, o = run_both(frames, 0.01, 0.04, 1 << 18, mode=mode, batch=len(frames),
+                                        max_batch_pixels=sum(f.width * f.height for f in frames))
+    assert st["fallback_blocks"] == 0          # the frames' runs spread over the record partitions
+    assert_parity(st, coords, arrays, o)
+
+
 def test_record_overflow_rescans_exactly():
     # run records sized for 2,000 pixels per call: most blocks cannot keep
     # their runs and are rescanned from their pixel rectangles instead
