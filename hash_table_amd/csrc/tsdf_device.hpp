@@ -159,9 +159,14 @@ struct FrameCounters {
     unsigned int items_spill;           // blocks beyond their partition's share
     unsigned int items_total;           // all blocks (set when the blocks are placed)
     unsigned long long placed;          // segments given to blocks
+    // Pool indices from here on were claimed after the last update placed
+    // its blocks: no update has written those pool blocks since the pool was
+    // cleared, so they still hold zeros (set by the previous call's placing
+    // kernel; 0 after create and reset).
+    unsigned long long pool_start;
     unsigned int n_rescan;              // blocks whose runs did not fit (rescanned)
     unsigned int front, back;           // items placed from the front (big blocks) and from the back
-    unsigned int pad[25];
+    unsigned int pad[23];
     unsigned int fetch[kXcds * kFetchStride];   // next item of XCD x at fetch[x * kFetchStride]
 };
 static_assert(sizeof(FrameCounters) % 128 == 0, "FrameCounters keeps the work counters in their own lines");

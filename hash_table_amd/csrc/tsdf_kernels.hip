@@ -553,7 +553,12 @@ __global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerA
     partition_prefix(s_cnt, own.item_part_cap, fc.items_spill, s_pre);
     const unsigned int n = s_pre[kParts + 1];
     const unsigned int mean_runs = s_runs / max(n, 1u);
-    if (blockIdx.x == 0 && threadIdx.x == 0) fc.items_total = n;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        fc.items_total = n;
+        // this call's allocate has claimed its pool indices: the next call's
+        // fresh blocks start where they end
+        own.fc[own.parity ^ 1].pool_start = min(vol.counters[kBlockCounter], vol.capacity);
+    }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (unsigned int b = blockIdx.x * kThreads; b < n; b += gridDim.x * kThreads) {
         const unsigned int i = b + tid;
@@ -705,7 +710,9 @@ struct OwnerLds {
 };
 
 // Add the chunk's sums to the pool block and clear them for the next chunk.
-__device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, size_t base) {
+// fresh: the pool block still holds the zeros the pool was cleared to, so the
+// sums are written without reading it first (0 + x is x exactly).
+__device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, size_t base, bool fresh) {
     for (int j = threadIdx.x; j < kBlockVoxels; j += kUpdateThreads) {
         const unsigned long long tw = L.tw[sum_slot(j)];
         const unsigned int cnt = (unsigned int)(tw >> 32);
@@ -717,7 +724,14 @@ __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, 
         L.tw[sum_slot(j)] = 0;
         L.rgb[sum_slot(j)] = 0;
         const size_t off = base + j;
-        const float t0 = vol.tsdf[off], w0 = vol.weight[off], r0 = vol.r[off], g0 = vol.g[off], b0 = vol.b[off];
+        float t0 = 0.0f, w0 = 0.0f, r0 = 0.0f, g0 = 0.0f, b0 = 0.0f;
+        if (!fresh) {
+            t0 = vol.tsdf[off];
+            w0 = vol.weight[off];
+            r0 = vol.r[off];
+            g0 = vol.g[off];
+            b0 = vol.b[off];
+        }
         vol.tsdf[off] = t0 + ts;
         vol.weight[off] = w0 + (float)cnt;
         vol.r[off] = r0 + (float)((unsigned int)c & 0x1FFFFFu) * kInv255;
@@ -750,6 +764,7 @@ __global__ __launch_bounds__(kUpdateThreads) void k_update_owner(BatchArgs B, Vo
     }
     FrameCounters& fc = own.fc[own.parity];
     const unsigned int n_items = fc.items_total;
+    const unsigned long long fresh_from = fc.pool_start;
     const unsigned int xcd = blockIdx.x % kXcds;
     unsigned int* fetch = fc.fetch + xcd * kFetchStride;
     unsigned int misses = 0;
@@ -763,6 +778,7 @@ __global__ __launch_bounds__(kUpdateThreads) void k_update_owner(BatchArgs B, Vo
         if (d.rec_count & kSegOverflow) continue;            // rescanned (and its count cleared) later
         if (tid == 0) own.blk_count[d.slot] = 0;
         const bool store = d.idx < vol.capacity;             // else refused a pool index: count, not store
+        bool fresh = d.idx >= fresh_from;                    // no update has written the block yet
         int bx, by, bz;
         unpack_key(d.key, bx, by, bz);
         const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
@@ -875,7 +891,8 @@ __global__ __launch_bounds__(kUpdateThreads) void k_update_owner(BatchArgs B, Vo
                     __syncthreads();                         // s_run is rewritten next
                 }
                 __syncthreads();
-                if (store) flush_owner(L, vol, base);
+                if (store) flush_owner(L, vol, base, fresh);
+                fresh = false;                               // a later pass adds to what this one wrote
                 __syncthreads();                             // also: the window may be reloaded
             }
         }

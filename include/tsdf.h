@@ -122,7 +122,9 @@ typedef struct {
     float* weight;          /*   normalised signed distance (sdf / trunc), of the weight, */
     float* r;               /*   and of the colour channels (0..1).  Voxel v of block i is */
     float* g;               /*   element i * 512 + v, v = x + 8 y + 64 z within the block. */
-    float* b;
+    float* b;               /* The library relies on pool blocks it has not handed out
+                               holding zeros (tsdf_create and tsdf_reset clear them): a
+                               block's first sums are written without reading it. */
     void* counters;         /* tsdf_counters_bytes() bytes: statistics, then the launch
                                parameters of a batch's frames beyond the 32nd */
     void* scratch;          /* tsdf_scratch_bytes(config) bytes (the owner update's work
