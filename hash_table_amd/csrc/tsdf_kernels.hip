@@ -657,6 +657,11 @@ __global__ __launch_bounds__(kThreads) void k_discard_items(VolumeArgs vol, Owne
     __syncthreads();
     partition_prefix(s_cnt, own.item_part_cap, fc.items_spill, s_pre);
     const unsigned int n = s_pre[kParts + 1];
+    // this call's allocate cleared its successor's counters, pool_start
+    // included, and no k_place_items will run for it: record here where the
+    // next call's fresh pool blocks start
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        own.fc[own.parity ^ 1].pool_start = min(vol.counters[kBlockCounter], vol.capacity);
     for (unsigned int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
         const int p = find_partition(s_pre, i);
         const unsigned int slot = p < kParts ? own.items[(size_t)p * own.item_part_cap + (i - s_pre[p])]

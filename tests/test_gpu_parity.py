@@ -525,6 +525,31 @@ def test_owner_update_must_follow_its_allocate():
     assert vol.stats()["pool_used"] > 0
 
 
+def test_unwritten_blocks_of_a_dropped_allocate():
+    # frame 1's allocate is dropped (another allocate follows it): its new
+    # blocks hold pool indices but no sums; the next calls must still add to
+    # them correctly (they are still zero), and the result is frames 0, 3, 1
+    # and 2 integrated once each; then the same after a reset
+    from hash_table_amd import tsdf
+    wl = scenes.workload("spherewall320x240")
+    host = [wl.frame(i) for i in range(4)]
+    f = [tsdf.DeviceFrame(h) for h in host]
+    vol = tsdf.Volume(wl.voxel_size, wl.trunc, wl.pool_capacity, update_mode="owner")
+    for rep in range(2):
+        vol.integrate(f[0])
+        vol.allocate(f[1])                            # dropped by the next allocate
+        vol.allocate(f[3])
+        vol.update(f[3])
+        vol.integrate_batch([f[1], f[2]])
+        coords, arrays = vol.export()
+        o = parity.oracle_integrate([host[0], host[3], host[1], host[2]], wl.voxel_size, wl.trunc,
+                                    wl.pool_capacity)
+        # (the dropped allocate counted its points: compare blocks and sums)
+        bad = parity.compare_blocks(coords, arrays, o)
+        assert bad == [], bad
+        vol.reset()
+
+
 def test_repeat_runs_identical_blocks_and_weights():
     wl = scenes.workload("cube640x480")
     f = wl.frame(0)
