@@ -623,6 +623,10 @@ __device__ __forceinline__ unsigned int lookup_key(const VolumeArgs& vol, unsign
 __device__ __forceinline__ unsigned int wave_sum(unsigned int x) { return __reduce_add_sync(~0ull, x); }
 
 // Inclusive prefix sum over the wavefront's lanes (every lane active).
+// Does any active lane hold b?  (The ballot of the lane mask itself: no
+// detour through a 0/1 value in a vector register.)
+__device__ __forceinline__ bool wave_any(bool b) { return __builtin_amdgcn_ballot_w64(b) != 0; }
+
 __device__ __forceinline__ unsigned int wave_inclusive_sum(unsigned int x) {
     const int lane = (int)(threadIdx.x & 63u);
 #pragma unroll

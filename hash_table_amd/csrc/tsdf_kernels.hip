@@ -407,12 +407,37 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
     }
     const float dd = depth;
     const Projection proj = projection(f);
-    auto test = [&]() {                       // the centre test of the walk's current cell
-        float sdf;
+    auto test_sdf = [&](float& sdf) {         // the centre test of the walk's current cell
         return kReproject ? centre_test_reproject_at(b0 + h0, b1 + h1, b2 + h2, dd, ax, proj, vs, trunc, sdf)
                           : centre_test_at(b0 + h0, b1 + h1, b2 + h2, dd, ax, vs, trunc, sdf);
     };
-    bool keep = test();
+    auto test = [&]() {
+        float sdf;
+        return test_sdf(sdf);
+    };
+    // Stepped sdf (band test alone).  A step moves the centre by one voxel
+    // along one axis, which changes d - zc by the pose's depth-axis entry
+    // for that axis times vs.  From the exact value at a chunk's first cell
+    // the walk carries sa, that value less the steps' changes in float.  The
+    // band decision taken on sa is the exact test's wherever |sa| is further
+    // than m from trunc, m a bound on |exact - sa| (below); lanes inside that
+    // margin take the exact test.  Bound, with u = 2^-24, n <= 31 steps
+    // since the first cell and r = max(1, |R entries of the depth axis|):
+    // the exact test's own rounding error at a cell is at most
+    // 6.001 u (r (sum_k |X_k| + sum_k |t_k|) + d) (X: the centre in world
+    // units), and sum_k |X_k| grows by at most n vs, so the errors at the
+    // first cell and the current one add up to at most
+    // 12.01 u (r (sum |X| + sum |t| + 16 vs) + d) with X at the first cell;
+    // the steps add at most u r vs each (the rounded R vs) and u |sa| each
+    // (the subtraction; |sa| <= |sdf0| + 32 r vs), i.e.
+    // 31 u |sdf0| + 1023 u r vs in all.
+    // m = 2^-20 (r (sum |X| + sum |t| + 80 vs) + d + 2 |sdf0|) covers the sum
+    // with room for the rounding of m itself, and 2^-22 trunc covers that
+    // of trunc -+ m.
+    const float t_abs = (fabsf(ax.t0) + fabsf(ax.t1)) + fabsf(ax.t2);
+    const float r_max = fmaxf(fmaxf(fabsf(ax.r2), fabsf(ax.r5)), fmaxf(fabsf(ax.r8), 1.0f));
+    float sa = 0.f, lo = 0.f, hi = 0.f, dl0 = 0.f, dl1 = 0.f, dl2 = 0.f;
+    bool keep = false;
 
     // The walk goes in chunks of up to kChunkCells cells.  All lanes start
     // together, so a lane's cell index within the chunk is the (uniform)
@@ -431,13 +456,35 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
         x = (int)(b0 + h0 - 0.5f);            // the current cell (exact: integers and halves)
         y = (int)(b1 + h1 - 0.5f);
         z = (int)(b2 + h2 - 0.5f);
+        {   // the exact test at the chunk's first cell (its keep was stepped, if
+            // the walk comes from the last chunk: the same decision)
+            float sdf0;
+            keep = test_sdf(sdf0);
+            if constexpr (!kReproject) {
+                sa = sdf0;
+                // the steps' changes, (f R) vs = f (R vs) (f is -1, 0 or 1 and
+                // rounding is symmetric), made per chunk: the empty asm keeps
+                // the compiler from hoisting them out of the chunk loop and
+                // holding them through the filing
+                float q0 = f0, q1 = f1, q2 = f2;
+                asm volatile("" : "+v"(q0), "+v"(q1), "+v"(q2));
+                dl0 = (q0 * ax.r2) * vs;
+                dl1 = (q1 * ax.r5) * vs;
+                dl2 = (q2 * ax.r8) * vs;
+                const float xs = (fabsf((b0 + h0) * vs) + fabsf((b1 + h1) * vs)) + fabsf((b2 + h2) * vs);
+                const float m = 0x1p-20f * ((r_max * ((xs + t_abs) + 80.0f * vs) + fabsf(dd)) + 2.0f * fabsf(sdf0)) +
+                                0x1p-22f * trunc;
+                lo = trunc - m;
+                hi = trunc + m;
+            }
+        }
         kp = 1u;                              // the kept plane starts with a sentinel bit
         yp = zp = cp = 0u;
         // the safety bound on cells per walk limits the chunk (uniform)
         const int lim = min(kChunkCells, max_visits - done);
         int itc = 0;                                   // iterations of this chunk (uniform)
         for (; itc < lim; ++itc) {
-            if (!__any(alive)) break;
+            if (!wave_any(alive)) break;
             const float tmin = fminf(fminf(tm0, tm1), tm2);
             const bool more = alive && tmin <= 1.0f;
             kp = alive ? kp + kp + (keep ? 1u : 0u) : kp;
@@ -460,7 +507,18 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
             tm0 = a0 ? tn : tm0;
             tm1 = a1 ? tn : tm1;
             tm2 = a2 ? tn : tm2;
-            keep = test();
+            if constexpr (kReproject) {
+                keep = test();
+            } else {
+                sa = sa - (e0 ? dl0 : (e1 ? dl1 : dl2));
+                const float as = fabsf(sa);
+                keep = as <= lo;
+                const bool unsure = more && !keep && as <= hi;
+                if (wave_any(unsure)) {       // rare: some lane is within the margin
+                    const bool ex = test();
+                    keep = unsure ? ex : keep;
+                }
+            }
             alive = more;
         }
         // A walk still going after max_visits cells is cut there (counted).
@@ -470,7 +528,7 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
             ++n_guard;
             alive = false;
         }
-        if (!__any(alive)) {                 // every walk ended: file this chunk after the loop
+        if (!wave_any(alive)) {               // every walk ended: file this chunk after the loop
             last_itc = itc;
             break;
         }

@@ -6,7 +6,8 @@ sphere-and-wall arc, the 640 x 480 room (a prefix element by element, and
 all 100 frames in the benchmark's launch configuration), the 1280 x 720 room
 at its full sizes, the 0.2 m contention cube, the load-factor sweep and the
 bounded-probe control on it, tiny random frames with ragged sizes, dense
-blocks spanning several LDS windows, batches, and the edge cases.
+blocks spanning several LDS windows, batches, band ends hit exactly and
+far cameras, and the edge cases.
 """
 from __future__ import annotations
 
@@ -453,6 +454,38 @@ def test_edge_inputs(mode):
     _, st, coords, arrays, o = run_both([fr], vs, tr, 1024, mode=mode)
     assert st["points_valid"] == 54
     assert_parity(st, coords, arrays, o)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_band_ends_and_far_poses(mode):
+    """Cells whose centres lie exactly on the band's ends, and cameras far
+    from the origin (a wide margin around the ends): the walk's band
+    decisions, taken on a stepped sdf away from the ends, must be the exact
+    test's everywhere."""
+    vs, tr = 2.0 ** -7, 2.0 ** -5
+    W, H = 48, 40
+    rng = np.random.default_rng([11, 3])
+    k = rng.integers(40, 200, size=(H, W))
+    # grid-aligned cameras: a centre's camera depth is a world coordinate
+    # plus a lattice offset, (k + 1/2) vs exactly, and so is every sdf, many
+    # of them exactly +-trunc
+    depth = ((k + 0.5) * vs + tr).astype(np.float32)
+    rgb = rng.integers(0, 256, size=(H, W, 3), dtype=np.uint8)
+    cyclic = np.array([[0, 0, 1], [1, 0, 0], [0, 1, 0]], np.float32)   # camera z along world x
+    for name, R, t in (("identity", np.eye(3, dtype=np.float32), np.zeros(3, np.float32)),
+                       ("axis permutation", cyclic, np.array([-3.0, 0.5, 1.25], np.float32))):
+        fr = scenes.Frame(depth, rgb, 40.0, 40.0, 23.5, 19.5, R, t)
+        say(f"  grid-aligned camera ({name}), depths on the voxel lattice")
+        _, st, coords, arrays, o = run_both([fr], vs, tr, 1 << 16, mode=mode)
+        assert st["points_valid"] == W * H
+        assert_parity(st, coords, arrays, o)
+    for seed, dist in ((31, 40.0), (32, 300.0)):
+        base = scenes.random_frame(seed, W=33, H=21)
+        fr = scenes.Frame(base.depth, base.rgb, base.fx, base.fy, base.cx, base.cy, base.R,
+                          np.asarray(base.t, np.float32) + np.float32(dist))
+        say(f"  camera {dist:g} m out on each axis")
+        _, st, coords, arrays, o = run_both([fr], 0.01, 0.04, 1 << 16, mode=mode)
+        assert_parity(st, coords, arrays, o)
 
 
 # ---------------------------------------------------------------------------
