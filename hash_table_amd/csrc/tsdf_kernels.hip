@@ -53,6 +53,13 @@ __device__ __forceinline__ bool workgroup_tile(const FrameArgs& f, int wg, int& 
     return true;
 }
 
+// One of three values by two conditions.  (Taking the values, not
+// references: a conditional over references to a lambda's captures would
+// select between their addresses and keep the variables in memory.)
+__device__ __forceinline__ float pick3(bool first, bool second, float a, float b, float c) {
+    return first ? a : (second ? b : c);
+}
+
 __device__ __forceinline__ void thread_pixel(int tile_u0, int tile_v0, int& u, int& v) {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -100,6 +107,7 @@ struct AllocLds {
     unsigned long long skey[kWaves][kSetCap];     // set: key (empty: all ones),
     unsigned int scnt[kWaves][kSetCap];           //   its runs; after the reservation, its first record
     unsigned char sslot[kWaves][kSetCap];         // set slots of the distinct keys, in insertion order
+    unsigned long long scode[kWaves][kSlots][64]; // the lanes' run codes, held here while the keys are filed
     unsigned int nuniq[kWaves];
     unsigned int nrec[kWaves];                    // records of a filing round, claimed so far
     unsigned int hist[kProbeBins];
@@ -127,7 +135,7 @@ static_assert(kSetCap == 256, "set_slot yields 8 bits");
 // wavefront.
 __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, int lane, unsigned int part,
                                           const VolumeArgs& vol, const OwnerArgs& own, unsigned int depth,
-                                          unsigned int meta, unsigned int frame_hi, unsigned int& misses) {
+                                          unsigned int meta, unsigned int frame_hi) {
     bool any_pend = false;
 #pragma unroll
     for (int q = 0; q < kSlots; ++q) any_pend = any_pend || S.pend[q];
@@ -144,11 +152,10 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, int lane, un
     wave_lds_fence();
     // de-duplicate: each pending run finds (or enters) its key in the set
     // and takes a rank among the key's runs
-    unsigned int hq[kSlots], rk[kSlots];
+    unsigned int hr[kSlots];                      // per run: set slot | rank << 8
 #pragma unroll
     for (int q = 0; q < kSlots; ++q) {
-        hq[q] = 0;
-        rk[q] = 0;
+        hr[q] = 0;
         if (!__any(S.pend[q])) continue;
         if (S.pend[q]) {
             const unsigned long long key = S.key[q];
@@ -162,8 +169,8 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, int lane, un
                 if (prev == key) break;
                 h = (h + 1) & (kSetCap - 1);
             }
-            hq[q] = h;
-            rk[q] = atomicAdd(&scnt[h], 1u);
+            hr[q] = h | (atomicAdd(&scnt[h], 1u) << 8);
+            L.scode[wave][q][lane] = S.code[q];
         }
     }
     wave_lds_fence();
@@ -252,16 +259,17 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, int lane, un
 #pragma unroll
     for (int q = 0; q < kSlots; ++q) {
         if (!S.pend[q]) continue;
-        const unsigned int b = scnt[hq[q]];
+        const unsigned int b = scnt[hr[q] & 255u];
+        const unsigned long long code = L.scode[wave][q][lane];
         if (b == kNoKeyBase) {
-            misses += (unsigned int)code_kept(S.code[q]);
+            atomicAdd(L.cnt + 5, (unsigned int)code_kept(code));   // rare: counted at once
         } else if (b != kNoBase) {
             RunRecord r;
             r.depth = depth;
             r.meta = meta;
-            r.code_lo = (unsigned int)S.code[q];
-            r.code_hi = (unsigned int)(S.code[q] >> 32) | frame_hi;
-            own.recs[b + rk[q]] = r;
+            r.code_lo = (unsigned int)code;
+            r.code_hi = (unsigned int)(code >> 32) | frame_hi;
+            own.recs[b + (hr[q] >> 8)] = r;
         }
     }
 }
@@ -270,7 +278,7 @@ __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, u
                                              int itc, int x, int y, int z, int s0, int s1, int s2, AllocLds& L,
                                              int lane, unsigned int part, const VolumeArgs& vol,
                                              const OwnerArgs& own, unsigned int depth_bits, unsigned int meta,
-                                             unsigned int frame_hi, unsigned int& n_upd, unsigned int& misses) {
+                                             unsigned int frame_hi, unsigned int& n_upd) {
     // planes in walk order, bit j = the chunk's cell j: the kept plane's
     // sentinel marks the n cells this lane walked; the step planes were
     // shifted once per iteration
@@ -315,14 +323,14 @@ __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, u
                 j0 += (int)len;
             }
         }
-        file_runs(S, L, lane, part, vol, own, depth_bits, meta, frame_hi, misses);
+        file_runs(S, L, lane, part, vol, own, depth_bits, meta, frame_hi);
     }
 }
 
 // kReproject: the reprojection reading of the occlusion test (see
 // hidden_in_image) on top of the band test.
 template <bool kReproject>
-__global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
+__global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ AllocLds L;
     const int fi = blockIdx.x / B.tile_grid;                 // frame of this workgroup
     const FrameArgs f = batch_frame(B, fi);
@@ -344,39 +352,13 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
     int u, v;
     thread_pixel(tu, tv, u, v);
     const unsigned int pix = (unsigned int)v * (unsigned int)f.width + (unsigned int)u;
-    BandWalk w;
-    int cls = kInvalid;
     float depth = 0.0f;
-    if (u < f.width && v < f.height) {
-        depth = f.depth[pix];
-        cls = setup_walk(w, depth, u, v, f, vol.trunc, vol.inv_vs);
-    }
-    bool alive = cls == kValid;
-    {   // point classes, counted now so the class is not kept through the walk
-        const unsigned int c_valid = (unsigned int)__popcll(__ballot(cls == kValid));
-        const unsigned int c_near = (unsigned int)__popcll(__ballot(cls == kNear));
-        const unsigned int c_oor = (unsigned int)__popcll(__ballot(cls == kOutside));
-        if (lane == 0) {
-            if (c_valid) atomicAdd(L.cnt + 0, c_valid);
-            if (c_near) atomicAdd(L.cnt + 1, c_near);
-            if (c_oor) atomicAdd(L.cnt + 2, c_oor);
-        }
-    }
-    // what the update needs of this point besides the run codes: depth,
-    // colour (when the frame has it: an update needs the same frame, colour
-    // included), frame of the batch and the directions of the stepping axes
+    const bool in_image = u < f.width && v < f.height;
+    if (in_image) depth = f.depth[pix];
     unsigned int meta = 0;
-    if (alive && own.build_items) {
-        if (f.rgb) {
-            const uint8_t* c = f.rgb + 3 * (size_t)pix;
-            meta = (unsigned int)c[0] | ((unsigned int)c[1] << 8) | ((unsigned int)c[2] << 16);
-        }
-        meta |= (((unsigned int)fi & 31u) << 24) | (w.s0 < 0 ? 1u << 29 : 0u) | (w.s1 < 0 ? 1u << 30 : 0u) |
-                (w.s2 < 0 ? 1u << 31 : 0u);
-    }
     const unsigned int depth_bits = __float_as_uint(depth);
     const unsigned int frame_hi = ((unsigned int)fi >> 5) << (kFrameHighShift - 32);   // into the code's top bits
-    unsigned int n_upd = 0, n_guard = 0, misses = 0;
+    unsigned int n_upd = 0;
     // this wavefront's reservations: partitions in turn as if the call's
     // frames were laid end to end by their tile counts (numbering by launch
     // index instead, every frame would start at a multiple of 8 workgroups
@@ -393,25 +375,58 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
     // direction (in voxel units), and the offset from the boundary index to
     // the current cell's centre (k + 1/2 is b - 1/2 stepping up, b + 1/2
     // stepping down or still: exactly, for any cell a key can hold).
-    int s0 = 0, s1 = 0, s2 = 0;
-    float b0 = 0.f, b1 = 0.f, b2 = 0.f, f0 = 0.f, f1 = 0.f, f2 = 0.f, h0 = 0.f, h1 = 0.f, h2 = 0.f;
-    float tm0 = 0.f, tm1 = 0.f, tm2 = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, i0 = 0.f, i1 = 0.f, i2 = 0.f;
-    if (alive) {
-        s0 = w.s0; s1 = w.s1; s2 = w.s2;
+    int s0, s1, s2;
+    float b0, b1, b2, f0, f1, f2, h0, h1, h2, tm0, tm1, tm2, g0, g1, g2, i0, i1, i2;
+    bool alive;
+    auto load_walk = [&](const BandWalk& w, bool valid) __attribute__((always_inline)) {
+        alive = valid;
+        s0 = valid ? w.s0 : 0; s1 = valid ? w.s1 : 0; s2 = valid ? w.s2 : 0;
         f0 = (float)s0; f1 = (float)s1; f2 = (float)s2;
-        b0 = (float)(w.k0 + (s0 > 0)); b1 = (float)(w.k1 + (s1 > 0)); b2 = (float)(w.k2 + (s2 > 0));
+        b0 = valid ? (float)(w.k0 + (s0 > 0)) : 0.f;
+        b1 = valid ? (float)(w.k1 + (s1 > 0)) : 0.f;
+        b2 = valid ? (float)(w.k2 + (s2 > 0)) : 0.f;
         h0 = s0 > 0 ? -0.5f : 0.5f; h1 = s1 > 0 ? -0.5f : 0.5f; h2 = s2 > 0 ? -0.5f : 0.5f;
-        tm0 = w.tm0; tm1 = w.tm1; tm2 = w.tm2;
-        g0 = w.gA0; g1 = w.gA1; g2 = w.gA2;
-        i0 = w.inv0; i1 = w.inv1; i2 = w.inv2;
-    }
+        tm0 = valid ? w.tm0 : 0.f; tm1 = valid ? w.tm1 : 0.f; tm2 = valid ? w.tm2 : 0.f;
+        g0 = valid ? w.gA0 : 0.f; g1 = valid ? w.gA1 : 0.f; g2 = valid ? w.gA2 : 0.f;
+        i0 = valid ? w.inv0 : 0.f; i1 = valid ? w.inv1 : 0.f; i2 = valid ? w.inv2 : 0.f;
+    };
+    // One step of the walk (every lane; a finished walk does not move).  The
+    // stepped axis is the one whose boundary comes first (ties: x, then y).
+    struct Step {
+        bool more, e0, e1, a1, a2;
+        float bc;                              // the boundary the step crosses
+    };
+    auto step = [&]() __attribute__((always_inline)) {
+        Step st;
+        const float tmin = fminf(fminf(tm0, tm1), tm2);
+        st.more = alive && tmin <= 1.0f;
+        st.e0 = tm0 == tmin;
+        st.e1 = tm1 == tmin;
+        const bool a0 = st.more && st.e0;
+        st.a1 = st.more && !st.e0 && st.e1;
+        st.a2 = st.more && !st.e0 && !st.e1;
+        st.bc = pick3(st.e0, st.e1, b0, b1, b2);
+        const float fc = pick3(st.e0, st.e1, f0, f1, f2);
+        const float gc = pick3(st.e0, st.e1, g0, g1, g2);
+        const float ic = pick3(st.e0, st.e1, i0, i1, i2);
+        const float bn = st.bc + fc;           // the new cell's next boundary
+        const float tn = (bn - gc) * ic;
+        b0 = a0 ? bn : b0;
+        b1 = st.a1 ? bn : b1;
+        b2 = st.a2 ? bn : b2;
+        tm0 = a0 ? tn : tm0;
+        tm1 = st.a1 ? tn : tm1;
+        tm2 = st.a2 ? tn : tm2;
+        alive = st.more;
+        return st;
+    };
     const float dd = depth;
     const Projection proj = projection(f);
-    auto test_sdf = [&](float& sdf) {         // the centre test of the walk's current cell
+    auto test_sdf = [&](float& sdf) __attribute__((always_inline)) {         // the centre test of the walk's current cell
         return kReproject ? centre_test_reproject_at(b0 + h0, b1 + h1, b2 + h2, dd, ax, proj, vs, trunc, sdf)
                           : centre_test_at(b0 + h0, b1 + h1, b2 + h2, dd, ax, vs, trunc, sdf);
     };
-    auto test = [&]() {
+    auto test = [&]() __attribute__((always_inline)) {
         float sdf;
         return test_sdf(sdf);
     };
@@ -436,8 +451,6 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
     // of trunc -+ m.
     const float t_abs = (fabsf(ax.t0) + fabsf(ax.t1)) + fabsf(ax.t2);
     const float r_max = fmaxf(fmaxf(fabsf(ax.r2), fabsf(ax.r5)), fmaxf(fabsf(ax.r8), 1.0f));
-    float sa = 0.f, lo = 0.f, hi = 0.f, dl0 = 0.f, dl1 = 0.f, dl2 = 0.f;
-    bool keep = false;
 
     // The walk goes in chunks of up to kChunkCells cells.  All lanes start
     // together, so a lane's cell index within the chunk is the (uniform)
@@ -451,102 +464,107 @@ __global__ __launch_bounds__(kThreads, 5) void k_allocate(BatchArgs B, VolumeArg
     // boundary split in two records of the same block: the update adds both.
     int x, y, z;                              // the chunk's first cell
     unsigned int kp, yp, zp, cp;              // its planes
-    int last_itc = 0;
-    for (int done = 0;; done += kChunkCells) {
+    auto walk_chunk = [&](int done) __attribute__((always_inline)) {
         x = (int)(b0 + h0 - 0.5f);            // the current cell (exact: integers and halves)
         y = (int)(b1 + h1 - 0.5f);
         z = (int)(b2 + h2 - 0.5f);
-        {   // the exact test at the chunk's first cell (its keep was stepped, if
-            // the walk comes from the last chunk: the same decision)
-            float sdf0;
-            keep = test_sdf(sdf0);
-            if constexpr (!kReproject) {
-                sa = sdf0;
-                // the steps' changes, (f R) vs = f (R vs) (f is -1, 0 or 1 and
-                // rounding is symmetric), made per chunk: the empty asm keeps
-                // the compiler from hoisting them out of the chunk loop and
-                // holding them through the filing
-                float q0 = f0, q1 = f1, q2 = f2;
-                asm volatile("" : "+v"(q0), "+v"(q1), "+v"(q2));
-                dl0 = (q0 * ax.r2) * vs;
-                dl1 = (q1 * ax.r5) * vs;
-                dl2 = (q2 * ax.r8) * vs;
-                const float xs = (fabsf((b0 + h0) * vs) + fabsf((b1 + h1) * vs)) + fabsf((b2 + h2) * vs);
-                const float m = 0x1p-20f * ((r_max * ((xs + t_abs) + 80.0f * vs) + fabsf(dd)) + 2.0f * fabsf(sdf0)) +
-                                0x1p-22f * trunc;
-                lo = trunc - m;
-                hi = trunc + m;
-            }
+        float sa = 0.f, lo = 0.f, hi = 0.f, dl0 = 0.f, dl1 = 0.f, dl2 = 0.f;
+        float sdf0;
+        bool keep = test_sdf(sdf0);           // the exact test at the chunk's first cell
+        if constexpr (!kReproject) {
+            sa = sdf0;
+            dl0 = f0 * ax.r2 * vs;            // f (R vs), exact: f is -1, 0 or 1
+            dl1 = f1 * ax.r5 * vs;            // (and rounding is symmetric)
+            dl2 = f2 * ax.r8 * vs;
+            // (opaque: the compiler would otherwise select f R and multiply
+            // by vs in every step)
+            asm volatile("" : "+v"(dl0), "+v"(dl1), "+v"(dl2));
+            const float xs = (fabsf((b0 + h0) * vs) + fabsf((b1 + h1) * vs)) + fabsf((b2 + h2) * vs);
+            const float m = 0x1p-20f * ((r_max * ((xs + t_abs) + 80.0f * vs) + fabsf(dd)) + 2.0f * fabsf(sdf0)) +
+                            0x1p-22f * trunc;
+            lo = trunc - m;
+            hi = trunc + m;
         }
         kp = 1u;                              // the kept plane starts with a sentinel bit
         yp = zp = cp = 0u;
         // the safety bound on cells per walk limits the chunk (uniform)
         const int lim = min(kChunkCells, max_visits - done);
-        int itc = 0;                                   // iterations of this chunk (uniform)
+        int itc = 0;                          // iterations of this chunk (uniform)
         for (; itc < lim; ++itc) {
             if (!wave_any(alive)) break;
-            const float tmin = fminf(fminf(tm0, tm1), tm2);
-            const bool more = alive && tmin <= 1.0f;
             kp = alive ? kp + kp + (keep ? 1u : 0u) : kp;
-            const bool e0 = tm0 == tmin, e1 = tm1 == tmin;
-            const bool a0 = more && e0, a1 = more && !e0 && e1, a2 = more && !e0 && !e1;
-            yp = yp + yp + (a1 ? 1u : 0u);
-            zp = zp + zp + (a2 ? 1u : 0u);
-            const float bc = e0 ? b0 : (e1 ? b1 : b2);   // the boundary this step crosses
-            const float fc = e0 ? f0 : (e1 ? f1 : f2);
-            const float gc = e0 ? g0 : (e1 ? g1 : g2);
-            const float ic = e0 ? i0 : (e1 ? i1 : i2);
-            const float bn = bc + fc;                     // the new cell's next boundary
-            const float tn = (bn - gc) * ic;
+            const Step st = step();
+            yp = yp + yp + (st.a1 ? 1u : 0u);
+            zp = zp + zp + (st.a2 ? 1u : 0u);
             // the step leaves the block iff the boundary it crosses is a block face
-            const bool cr = more && __builtin_amdgcn_fractf(bc * 0.125f) == 0.0f;
+            const bool cr = st.more && __builtin_amdgcn_fractf(st.bc * 0.125f) == 0.0f;
             cp = cp + cp + (cr ? 1u : 0u);
-            b0 = a0 ? bn : b0;
-            b1 = a1 ? bn : b1;
-            b2 = a2 ? bn : b2;
-            tm0 = a0 ? tn : tm0;
-            tm1 = a1 ? tn : tm1;
-            tm2 = a2 ? tn : tm2;
             if constexpr (kReproject) {
                 keep = test();
             } else {
-                sa = sa - (e0 ? dl0 : (e1 ? dl1 : dl2));
+                sa = sa - (st.e0 ? dl0 : (st.e1 ? dl1 : dl2));
                 const float as = fabsf(sa);
                 keep = as <= lo;
-                const bool unsure = more && !keep && as <= hi;
+                const bool unsure = st.more && !keep && as <= hi;
                 if (wave_any(unsure)) {       // rare: some lane is within the margin
                     const bool ex = test();
                     keep = unsure ? ex : keep;
                 }
             }
-            alive = more;
         }
         // A walk still going after max_visits cells is cut there (counted).
         // Its last iteration took one more step; that step's bits sit after
         // the lane's last cell and no run reads them.
-        if (done + lim >= max_visits && alive) {
-            ++n_guard;
+        if (done + lim >= max_visits) {
+            const unsigned int cut = (unsigned int)__popcll(__ballot(alive));
+            if (cut && lane == 0) atomicAdd(L.cnt + 4, cut);
             alive = false;
         }
-        if (!wave_any(alive)) {               // every walk ended: file this chunk after the loop
-            last_itc = itc;
-            break;
+        return itc;
+    };
+    for (int done = 0;; done += kChunkCells) {
+        // the walk's state for this chunk: set up from the pixel, then the
+        // first done steps replayed (the empty asm keeps the compiler from
+        // hoisting the set-up out of the loop and holding its results)
+        float dr = depth;
+        int ur, vr;
+        thread_pixel(tu, tv, ur, vr);
+        asm volatile("" : "+v"(dr), "+v"(ur), "+v"(vr));
+        BandWalk w = {};
+        const int cls = in_image ? setup_walk(w, dr, ur, vr, f, vol.trunc, vol.inv_vs) : kInvalid;
+        load_walk(w, cls == kValid);
+        if (done == 0) {
+            // point classes, counted once
+            const unsigned int c_valid = (unsigned int)__popcll(__ballot(cls == kValid));
+            const unsigned int c_near = (unsigned int)__popcll(__ballot(cls == kNear));
+            const unsigned int c_oor = (unsigned int)__popcll(__ballot(cls == kOutside));
+            if (lane == 0) {
+                if (c_valid) atomicAdd(L.cnt + 0, c_valid);
+                if (c_near) atomicAdd(L.cnt + 1, c_near);
+                if (c_oor) atomicAdd(L.cnt + 2, c_oor);
+            }
+            // what the update needs of this point besides the run codes:
+            // colour (when the frame has it), frame of the batch and the
+            // directions of the stepping axes
+            if (cls == kValid) {
+                if (own.build_items && f.rgb) {
+                    const uint8_t* c = f.rgb + 3 * (size_t)pix;
+                    meta = (unsigned int)c[0] | ((unsigned int)c[1] << 8) | ((unsigned int)c[2] << 16);
+                }
+                meta |= (((unsigned int)fi & 31u) << 24) | (w.s0 < 0 ? 1u << 29 : 0u) | (w.s1 < 0 ? 1u << 30 : 0u) |
+                        (w.s2 < 0 ? 1u << 31 : 0u);
+            }
         }
-        // a walk goes on into another chunk: file this one's runs now
-        cut_and_file(kp, yp, zp, cp, itc, x, y, z, s0, s1, s2, L, lane, part, vol, own, depth_bits, meta,
-                     frame_hi, n_upd, misses);
+        for (int i = 0; i < done; ++i) step();
+        const int itc = walk_chunk(done);
+        const bool go_on = wave_any(alive);
+        cut_and_file(kp, yp, zp, cp, itc, x, y, z, (meta >> 29) & 1u ? -1 : 1, (meta >> 30) & 1u ? -1 : 1,
+                     (meta >> 31) & 1u ? -1 : 1, L, lane, part, vol, own, depth_bits, meta, frame_hi, n_upd);
+        if (!go_on) break;
     }
-    cut_and_file(kp, yp, zp, cp, last_itc, x, y, z, s0, s1, s2, L, lane, part, vol, own, depth_bits, meta,
-                 frame_hi, n_upd, misses);
 
     const unsigned int c_upd = wave_sum(n_upd);
-    const unsigned int c_guard = wave_sum(n_guard);
-    const unsigned int c_miss = wave_sum(misses);
-    if (lane == 0) {
-        if (c_upd) atomicAdd(L.cnt + 3, c_upd);
-        if (c_guard) atomicAdd(L.cnt + 4, c_guard);
-        if (c_miss) atomicAdd(L.cnt + 5, c_miss);
-    }
+    if (lane == 0 && c_upd) atomicAdd(L.cnt + 3, c_upd);
     __syncthreads();
     flush_hist(L.hist, &L.pmax, vol.counters, kHistAlloc);
     if (threadIdx.x < 6 && L.cnt[threadIdx.x]) {

@@ -5,7 +5,7 @@ counts.  Within 1e-4: mean TSDF and mean colour.  Workloads: the plane, the
 sphere-and-wall arc, the 640 x 480 room (a prefix element by element, and
 all 100 frames in the benchmark's launch configuration), the 1280 x 720 room
 at its full sizes, the 0.2 m contention cube, the load-factor sweep and the
-bounded-probe control on it, tiny random frames with ragged sizes, dense
+bounded-probe control on it, tiny random frames with ragged sizes, walks several chunks long, dense
 blocks spanning several LDS windows, batches, band ends hit exactly and
 far cameras, and the edge cases.
 """
@@ -416,6 +416,20 @@ def test_random_frames_parity(seed, W, H, mode):
               for j in range(3)]
     for vs, tr in ((0.01, 0.04), (0.013, 0.05)):
         _, st, coords, arrays, o = run_both(frames, vs, tr, 1 << 16, mode=mode)
+        assert_parity(st, coords, arrays, o)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_long_walks_parity(mode):
+    """Bands many voxels deep, so walks run through several of allocate's
+    31-cell chunks: every chunk after the first is filed separately and
+    starts from a walk set up again and replayed to where the last one
+    stopped.  Block set, weights and counts must still match exactly."""
+    frames = [scenes.random_frame(90 + j, W=37, H=23, invalid_frac=0.1, translation_scale=0.5)
+              for j in range(3)]
+    for vs, tr in ((0.01, 0.2), (0.005, 0.31)):
+        _, st, coords, arrays, o = run_both(frames, vs, tr, 1 << 18, mode=mode)
+        assert st["walk_guard"] == 0
         assert_parity(st, coords, arrays, o)
 
 
