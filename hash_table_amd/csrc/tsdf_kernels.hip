@@ -948,13 +948,18 @@ __global__ __launch_bounds__(kUpdateThreads) void k_update_owner(BatchArgs B, Vo
                         const int d1 = (rr.meta >> 30) & 1u ? -1 : 1;
                         const int d2 = (rr.meta >> 31) & 1u ? -1 : 1;
                         const int e = code_entry(code), cells = code_cells(code);
-                        int k0 = lo0 + (e & 7), k1 = lo1 + ((e >> 3) & 7), k2 = lo2 + (e >> 6);
+                        // the cell's centre in voxels, k + 1/2 per axis (exact:
+                        // integers and halves), and its voxel within the block
+                        // (a run stays in its block)
+                        float x0 = (float)(lo0 + (e & 7)) + 0.5f;
+                        float x1 = (float)(lo1 + ((e >> 3) & 7)) + 0.5f;
+                        float x2 = (float)(lo2 + (e >> 6)) + 0.5f;
+                        int j = e;
                         unsigned int ys = code_ysteps(code), zs = code_zsteps(code);
                         for (int q = 0;;) {
                             float sdf;
-                            if (kReproject ? centre_test_reproject(k0, k1, k2, dep, ax, s_proj[rf], vol.vs, vol.trunc, sdf)
-                                           : centre_test(k0, k1, k2, dep, ax, vol.vs, vol.trunc, sdf)) {
-                                const int j = (k0 & 7) | ((k1 & 7) << 3) | ((k2 & 7) << 6);
+                            if (kReproject ? centre_test_reproject_at(x0, x1, x2, dep, ax, s_proj[rf], vol.vs, vol.trunc, sdf)
+                                           : centre_test_at(x0, x1, x2, dep, ax, vol.vs, vol.trunc, sdf)) {
                                 const unsigned int tq =
                                     (unsigned int)__float2int_rn((sdf * vol.inv_trunc + 1.0f) * kTsdfScale);
                                 atomicAdd(L.tw + sum_slot(j), (1ull << 32) | tq);
@@ -964,9 +969,10 @@ __global__ __launch_bounds__(kUpdateThreads) void k_update_owner(BatchArgs B, Vo
                             const bool sy = ys & 1u, sz = zs & 1u;
                             ys >>= 1;
                             zs >>= 1;
-                            k0 += (sy || sz) ? 0 : d0;
-                            k1 += sy ? d1 : 0;
-                            k2 += sz ? d2 : 0;
+                            x0 = (sy || sz) ? x0 : x0 + (float)d0;
+                            x1 = sy ? x1 + (float)d1 : x1;
+                            x2 = sz ? x2 + (float)d2 : x2;
+                            j += sy ? 8 * d1 : (sz ? 64 * d2 : d0);
                         }
                     }
                     __syncthreads();                         // s_run is rewritten next
