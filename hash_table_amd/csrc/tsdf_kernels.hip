@@ -771,7 +771,8 @@ __global__ __launch_bounds__(kThreads) void k_discard_items(VolumeArgs vol, Owne
 constexpr unsigned int kChunkRuns = 8191;
 constexpr int kSegWindow = 256;                      // segments of a block held in LDS at once
 constexpr int kUpdateThreads = 256;                  // workgroup of the owner update
-constexpr int kRunsPerThread = 4;                    // runs each thread stages
+constexpr int kRunsPerThread = 2;                    // runs each thread stages (2: 22 KB of LDS and
+                                                     // 71 VGPRs, 7 workgroups per CU)
 constexpr int kSubRuns = kUpdateThreads * kRunsPerThread;   // runs staged in LDS at a time
 constexpr int kLengths = 32;                         // run lengths a record can state (5 bits)
 constexpr unsigned int kNoRank = 0xFFFFFFFFu;
@@ -823,7 +824,7 @@ __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, 
 
 // kReproject: the reprojection reading of the occlusion test (as in k_allocate).
 template <bool kReproject>
-__global__ __launch_bounds__(kUpdateThreads) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
+__global__ __launch_bounds__(kUpdateThreads, 7) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ OwnerLds L;
     __shared__ DepthAxis s_axis[kMaxBatch];                 // per-record frame lookups from LDS
     __shared__ Projection s_proj[kMaxBatch];
