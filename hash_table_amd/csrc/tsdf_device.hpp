@@ -286,10 +286,11 @@ __device__ __forceinline__ void setup_axis(float gA, float gB, int& k, int& s, f
 // Classify pixel (u, v) with depth d and, for a valid point, set up its walk.
 // The band is the camera-z interval [d - trunc, d + trunc] along the pixel
 // ray, mapped to the world by the pose and to voxel units by 1/vs.
+// Every field is computed for every pixel, whatever its class (no branches:
+// the lanes of a wavefront need no masking); a pixel whose class is not
+// kValid gets values that must not be used.
 __device__ __forceinline__ int setup_walk(BandWalk& w, float d, int u, int v, const FrameArgs& f,
                                           float trunc, float inv_vs) {
-    if (!__builtin_isfinite(d) || !(d > 0.0f)) return kInvalid;
-    if (d <= trunc) return kNear;
     const float xn = ((float)u - f.cx) / f.fx;
     const float yn = ((float)v - f.cy) / f.fy;
     const float z0 = d - trunc;
@@ -306,7 +307,6 @@ __device__ __forceinline__ int setup_walk(BandWalk& w, float d, int u, int v, co
     const bool in_range = fabsf(gA0) <= kRangeLimit && fabsf(gA1) <= kRangeLimit &&
                           fabsf(gA2) <= kRangeLimit && fabsf(gB0) <= kRangeLimit &&
                           fabsf(gB1) <= kRangeLimit && fabsf(gB2) <= kRangeLimit;
-    if (!in_range) return kOutside;
     w.d = d;
     w.gA0 = gA0;
     w.gA1 = gA1;
@@ -321,7 +321,9 @@ __device__ __forceinline__ int setup_walk(BandWalk& w, float d, int u, int v, co
     w.span_hi0 = max(w.k0, e0);
     w.span_hi1 = max(w.k1, e1);
     w.span_hi2 = max(w.k2, e2);
-    return kValid;
+    if (!__builtin_isfinite(d) || !(d > 0.0f)) return kInvalid;
+    if (d <= trunc) return kNear;
+    return in_range ? kValid : kOutside;
 }
 
 // Occlusion and band test at the centre of the current cell.  sdf is the

@@ -379,16 +379,15 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
     float b0, b1, b2, f0, f1, f2, h0, h1, h2, tm0, tm1, tm2, g0, g1, g2, i0, i1, i2;
     bool alive;
     auto load_walk = [&](const BandWalk& w, bool valid) __attribute__((always_inline)) {
+        // (a lane that is not valid never walks: its values go unused)
         alive = valid;
-        s0 = valid ? w.s0 : 0; s1 = valid ? w.s1 : 0; s2 = valid ? w.s2 : 0;
+        s0 = w.s0; s1 = w.s1; s2 = w.s2;
         f0 = (float)s0; f1 = (float)s1; f2 = (float)s2;
-        b0 = valid ? (float)(w.k0 + (s0 > 0)) : 0.f;
-        b1 = valid ? (float)(w.k1 + (s1 > 0)) : 0.f;
-        b2 = valid ? (float)(w.k2 + (s2 > 0)) : 0.f;
+        b0 = (float)(w.k0 + (s0 > 0)); b1 = (float)(w.k1 + (s1 > 0)); b2 = (float)(w.k2 + (s2 > 0));
         h0 = s0 > 0 ? -0.5f : 0.5f; h1 = s1 > 0 ? -0.5f : 0.5f; h2 = s2 > 0 ? -0.5f : 0.5f;
-        tm0 = valid ? w.tm0 : 0.f; tm1 = valid ? w.tm1 : 0.f; tm2 = valid ? w.tm2 : 0.f;
-        g0 = valid ? w.gA0 : 0.f; g1 = valid ? w.gA1 : 0.f; g2 = valid ? w.gA2 : 0.f;
-        i0 = valid ? w.inv0 : 0.f; i1 = valid ? w.inv1 : 0.f; i2 = valid ? w.inv2 : 0.f;
+        tm0 = w.tm0; tm1 = w.tm1; tm2 = w.tm2;
+        g0 = w.gA0; g1 = w.gA1; g2 = w.gA2;
+        i0 = w.inv0; i1 = w.inv1; i2 = w.inv2;
     };
     // One step of the walk (every lane; a finished walk does not move).  The
     // stepped axis is the one whose boundary comes first (ties: x, then y).
@@ -530,8 +529,8 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
         int ur, vr;
         thread_pixel(tu, tv, ur, vr);
         asm volatile("" : "+v"(dr), "+v"(ur), "+v"(vr));
-        BandWalk w = {};
-        const int cls = in_image ? setup_walk(w, dr, ur, vr, f, vol.trunc, vol.inv_vs) : kInvalid;
+        BandWalk w;                           // (a pixel outside the image has depth 0: invalid)
+        const int cls = setup_walk(w, dr, ur, vr, f, vol.trunc, vol.inv_vs);
         load_walk(w, cls == kValid);
         if (done == 0) {
             // point classes, counted once
