@@ -823,7 +823,7 @@ __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, 
 
 // kReproject: the reprojection reading of the occlusion test (as in k_allocate).
 template <bool kReproject>
-__global__ __launch_bounds__(kUpdateThreads, 7) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
+__global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ OwnerLds L;
     __shared__ DepthAxis s_axis[kMaxBatch];                 // per-record frame lookups from LDS
     __shared__ Projection s_proj[kMaxBatch];
