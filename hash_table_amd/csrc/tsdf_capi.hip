@@ -395,7 +395,7 @@ tsdf_status tsdf_create(const tsdf_config* config, const tsdf_buffers* buffers, 
     h->cfg.table_entries = entries;
     h->buf = b;
     h->mask = (unsigned int)(entries - 1);
-    h->owner_grid = owner_grid();
+    h->owner_grid = owner_grid(config->occlusion == TSDF_OCCLUSION_REPROJECT);
     if (h->owner_grid <= 0) h->owner_grid = kOwnerGridDefault;
     if (!init_volume(h, true, static_cast<hipStream_t>(stream))) {
         delete h;

@@ -761,12 +761,15 @@ __global__ __launch_bounds__(kThreads) void k_discard_items(VolumeArgs vol, Owne
 // atomics (LDS float atomics issue far slower than integer ones on this
 // chip).  A run adds at most once to each voxel, so a chunk of at most
 // kChunkRuns = 8191 runs keeps every per-voxel count below 2^13:
-//   tw   (normalised signed distance + 1) in units of 2^-16, rounded to
-//        nearest (each term in [0, 2^17], the sum below 2^31), | count << 32
+//   tw   normalised signed distance in units of 2^-24, rounded to nearest,
+//        plus 2^25 (the distance times 1/trunc may pass +-1 by an ulp, so each
+//        term lies in (0, 2^26), the sum below 2^39) in bits 0-50,
+//        | count << 51
 //   rgb  R | G << 21 | B << 42 (each sum at most 255 * 8191 < 2^21)
 // so no field carries into the next.  The signed-distance sum is recovered
-// exactly from the two fields; rounding each term to the nearest 2^-16 moves
-// a mean by at most 2^-17.
+// exactly from the two fields; rounding each term to the nearest 2^-24 (the
+// float's own spacing for terms of magnitude 1/2 to 1) moves a mean by at
+// most 2^-25.
 constexpr unsigned int kChunkRuns = 8191;
 constexpr int kSegWindow = 256;                      // segments of a block held in LDS at once
 constexpr int kUpdateThreads = 256;                  // workgroup of the owner update
@@ -775,8 +778,10 @@ constexpr int kRunsPerThread = 2;                    // runs each thread stages 
 constexpr int kSubRuns = kUpdateThreads * kRunsPerThread;   // runs staged in LDS at a time
 constexpr int kLengths = 32;                         // run lengths a record can state (5 bits)
 constexpr unsigned int kNoRank = 0xFFFFFFFFu;
-constexpr float kTsdfScale = 65536.0f;               // 2^16
-constexpr float kTsdfUnit = 1.0f / 65536.0f;
+constexpr float kTsdfScale = 16777216.0f;            // 2^24
+constexpr float kTsdfUnit = 1.0f / 16777216.0f;
+constexpr int kCountShift = 51;                      // the count's place in the tw word
+constexpr unsigned long long kTsdfMask = (1ull << kCountShift) - 1ull;
 constexpr int kRescanThreads = 128;
 
 // Voxel j's sums sit at sum_slot(j): one spare word after every 16, so that
@@ -796,11 +801,11 @@ struct OwnerLds {
 __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, size_t base, bool fresh) {
     for (int j = threadIdx.x; j < kBlockVoxels; j += kUpdateThreads) {
         const unsigned long long tw = L.tw[sum_slot(j)];
-        const unsigned int cnt = (unsigned int)(tw >> 32);
+        const unsigned int cnt = (unsigned int)(tw >> kCountShift);
         if (!cnt) continue;
         const unsigned long long c = L.rgb[sum_slot(j)];
-        // sum of the signed distances, in units of 2^-16 (the +1 offsets removed)
-        const long long tq = (long long)(unsigned int)tw - ((long long)cnt << 16);
+        // sum of the signed distances, in units of 2^-24 (the 2^25 offsets removed)
+        const long long tq = (long long)(tw & kTsdfMask) - ((long long)cnt << 25);
         const float ts = (float)tq * kTsdfUnit;
         L.tw[sum_slot(j)] = 0;
         L.rgb[sum_slot(j)] = 0;
@@ -961,8 +966,8 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                             if (kReproject ? centre_test_reproject_at(x0, x1, x2, dep, ax, s_proj[rf], vol.vs, vol.trunc, sdf)
                                            : centre_test_at(x0, x1, x2, dep, ax, vol.vs, vol.trunc, sdf)) {
                                 const unsigned int tq =
-                                    (unsigned int)__float2int_rn((sdf * vol.inv_trunc + 1.0f) * kTsdfScale);
-                                atomicAdd(L.tw + sum_slot(j), (1ull << 32) | tq);
+                                    (unsigned int)(__float2int_rn((sdf * vol.inv_trunc) * kTsdfScale) + (1 << 25));
+                                atomicAdd(L.tw + sum_slot(j), (1ull << kCountShift) + tq);
                                 atomicAdd(L.rgb + sum_slot(j), c);
                             }
                             if (++q >= cells) break;
@@ -1275,13 +1280,13 @@ bool launch_update_owner(const BatchArgs& b, const VolumeArgs& v, const OwnerArg
     return launched();
 }
 
-int owner_grid() {
+int owner_grid(bool reproject) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_update_owner<false>),
-                                                     kUpdateThreads, 0) != hipSuccess)
-        return 0;
+    const void* k = reproject ? reinterpret_cast<const void*>(k_update_owner<true>)
+                              : reinterpret_cast<const void*>(k_update_owner<false>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kUpdateThreads, 0) != hipSuccess) return 0;
     return std::max(1, cus) * std::max(1, per_cu);
 }
 

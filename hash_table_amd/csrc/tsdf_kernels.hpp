@@ -35,10 +35,11 @@ int tile_grid(const FrameArgs& f);
 bool launch_allocate(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, hipStream_t s,
                      const LaunchTimer* t);
 // group the batch's run records by block, then update every touched block
-// (`grid` workgroups; owner_grid() is the number the device holds at once)
+// (`grid` workgroups; owner_grid(reproject) is the number of the matching
+// instantiation the device holds at once)
 bool launch_update_owner(const BatchArgs& b, const VolumeArgs& v, const OwnerArgs& o, int grid, hipStream_t s,
                          const LaunchTimer* t);
-int owner_grid();
+int owner_grid(bool reproject);
 // forget an allocate's records (no update followed it)
 bool launch_discard(const VolumeArgs& v, const OwnerArgs& o, hipStream_t s, const LaunchTimer* t);
 bool launch_update_rays(const BatchArgs& b, const VolumeArgs& v, hipStream_t s, const LaunchTimer* t);

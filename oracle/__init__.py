@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
-from typing import Dict, Iterable, Optional
+from typing import Dict, Iterable
 
 import numpy as np
 
@@ -25,7 +25,6 @@ CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
             "-fno-fast-math", "-mfpmath=sse", "-fno-finite-math-only"]
 
 TRACK_TOUCHED = 1
-WATCH_ONLY = 2
 REPROJECT = 4          # the reprojection reading of the occlusion test (C8)
 
 
@@ -43,6 +42,11 @@ class _FrameStats(ctypes.Structure):
         "pixels", "points_valid", "near_skipped", "out_of_range", "cells_visited",
         "voxel_updates", "blocks_touched", "blocks_new", "voxels_touched",
         "update_misses", "pool_overflow_new")]
+
+
+class _CallStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "frames", "blocks_touched", "blocks_new", "voxels_fresh", "voxels_old")]
 
 
 class _Totals(ctypes.Structure):
@@ -66,7 +70,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.oracle_create.restype = P
     lib.oracle_create.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_int64, ctypes.c_int32]
     lib.oracle_destroy.argtypes = [P]
-    lib.oracle_watch.argtypes = [P, P, ctypes.c_int64]
+    lib.oracle_begin_call.argtypes = [P]
+    lib.oracle_get_call_stats.argtypes = [P, ctypes.POINTER(_CallStats)]
     lib.oracle_integrate.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                      P, P, ctypes.POINTER(_FrameStats)]
@@ -88,23 +93,17 @@ class Oracle:
     """One volume integrated by the reference implementation.
 
     pool_capacity bounds the number of blocks; keys beyond it are refused and
-    counted.  track_touched enables the per-frame distinct-voxel count U;
-    watch (n x 3 block coordinates) keeps sums only for those blocks;
-    reproject selects the reprojection reading of the occlusion test (C8)."""
+    counted.  track_touched enables the distinct-voxel counts (U per frame,
+    voxels_fresh / voxels_old per call); reproject selects the reprojection
+    reading of the occlusion test (C8)."""
 
     def __init__(self, voxel_size: float, trunc: float, pool_capacity: int,
-                 track_touched: bool = False, watch: Optional[np.ndarray] = None,
-                 library: str = LIBRARY, reproject: bool = False):
+                 track_touched: bool = False, library: str = LIBRARY, reproject: bool = False):
         self._lib = load(library)
-        flags = ((TRACK_TOUCHED if track_touched else 0) | (WATCH_ONLY if watch is not None else 0)
-                 | (REPROJECT if reproject else 0))
+        flags = (TRACK_TOUCHED if track_touched else 0) | (REPROJECT if reproject else 0)
         self._h = self._lib.oracle_create(voxel_size, trunc, int(pool_capacity), flags)
         if not self._h:
             raise ValueError("invalid oracle parameters")
-        if watch is not None:
-            w = np.ascontiguousarray(watch, np.int32).reshape(-1, 3)
-            if self._lib.oracle_watch(self._h, _ptr(w), w.shape[0]) != 0:
-                raise RuntimeError("oracle_watch after integration")
         self.frame_stats = []
 
     def __del__(self):
@@ -129,6 +128,18 @@ class Oracle:
         d = {n: int(getattr(st, n)) for n, _ in _FrameStats._fields_}
         self.frame_stats.append(d)
         return d
+
+    def begin_call(self) -> None:
+        """Count the frames integrated from here on as one call (batch)."""
+        self._lib.oracle_begin_call(self._h)
+
+    def call_stats(self) -> dict:
+        """Counts of the current call: frames, distinct blocks touched (B_call),
+        blocks created, distinct voxels touched in blocks the call created
+        (voxels_fresh) and in older blocks (voxels_old)."""
+        c = _CallStats()
+        self._lib.oracle_get_call_stats(self._h, ctypes.byref(c))
+        return {n: int(getattr(c, n)) for n, _ in _CallStats._fields_}
 
     def totals(self) -> dict:
         t = _Totals()

@@ -94,9 +94,12 @@ struct Sums {
 };
 
 struct Block {
-    std::unique_ptr<Sums> sums;               // null when not watched
-    std::unique_ptr<uint32_t[]> voxel_frame;  // last frame + 1 per voxel
+    std::unique_ptr<Sums> sums;
+    std::unique_ptr<uint32_t[]> voxel_frame;  // last frame + 1 per voxel (counts only)
+    std::unique_ptr<uint32_t[]> voxel_call;   // last call that touched the voxel (counts only)
     uint32_t block_frame = 0;                 // last frame + 1 that touched it
+    uint32_t block_call = 0;                  // last call that touched it
+    uint32_t created_call = 0;                // the call that created it
 };
 
 int floor_div8(int k) {
@@ -124,6 +127,17 @@ typedef struct {
     int64_t pool_overflow_new; /* distinct keys refused this frame */
 } oracle_frame_stats;
 
+/* counts of one call: the frames integrated since the last oracle_begin_call
+ * (or since creation).  A call stands for one batched launch of several
+ * frames: it reads and writes each block it touches once. */
+typedef struct {
+    int64_t frames;            /* frames in the call */
+    int64_t blocks_touched;    /* distinct pool blocks with a kept voxel in the call: B_call */
+    int64_t blocks_new;        /* blocks the call created */
+    int64_t voxels_fresh;      /* distinct voxels with a kept visit, in blocks the call created */
+    int64_t voxels_old;        /* distinct voxels with a kept visit, in blocks created earlier */
+} oracle_call_stats;
+
 typedef struct {
     int64_t blocks;            /* blocks in the pool */
     int64_t pool_overflow;     /* distinct keys refused (pool full) */
@@ -132,7 +146,7 @@ typedef struct {
     int64_t frames;
 } oracle_totals;
 
-enum { ORACLE_TRACK_TOUCHED = 1, ORACLE_WATCH_ONLY = 2, ORACLE_REPROJECT = 4 };
+enum { ORACLE_TRACK_TOUCHED = 1, ORACLE_REPROJECT = 4 };
 
 struct oracle_volume {
     float vs, trunc, inv_vs;
@@ -140,8 +154,9 @@ struct oracle_volume {
     int32_t flags;
     std::map<Coord, Block> blocks;
     std::set<Coord> refused;
-    std::set<Coord> watch;
     oracle_totals tot;
+    uint32_t call = 1;         // the current call
+    oracle_call_stats cs;      // its counts
 };
 
 /* C7: one kept cell k of a point with signed distance sdf and colour col. */
@@ -160,13 +175,15 @@ static void contribute(oracle_volume* o, oracle_frame_stats& s, uint32_t stamp, 
         }
         it = o->blocks.emplace(bc, Block()).first;
         s.blocks_new++;
-        if (!(o->flags & ORACLE_WATCH_ONLY) || o->watch.count(bc)) {
-            it->second.sums.reset(new Sums());
-            std::memset(it->second.sums.get(), 0, sizeof(Sums));
-        }
+        o->cs.blocks_new++;
+        it->second.created_call = o->call;
+        it->second.sums.reset(new Sums());
+        std::memset(it->second.sums.get(), 0, sizeof(Sums));
         if (o->flags & ORACLE_TRACK_TOUCHED) {
             it->second.voxel_frame.reset(new uint32_t[kBlockVoxels]);
             std::memset(it->second.voxel_frame.get(), 0, sizeof(uint32_t) * kBlockVoxels);
+            it->second.voxel_call.reset(new uint32_t[kBlockVoxels]);
+            std::memset(it->second.voxel_call.get(), 0, sizeof(uint32_t) * kBlockVoxels);
         }
     }
     Block& blk = it->second;
@@ -174,18 +191,27 @@ static void contribute(oracle_volume* o, oracle_frame_stats& s, uint32_t stamp, 
         blk.block_frame = stamp;
         s.blocks_touched++;
     }
+    if (blk.block_call != o->call) {
+        blk.block_call = o->call;
+        o->cs.blocks_touched++;
+    }
     if (blk.voxel_frame && blk.voxel_frame[local] != stamp) {
         blk.voxel_frame[local] = stamp;
         s.voxels_touched++;
     }
-    if (blk.sums) {
-        Sums& S = *blk.sums;
-        S.tsdf[local] += (double)sdf / (double)o->trunc;
-        S.weight[local] += 1.0;
-        S.r[local] += (double)col[0] / 255.0;
-        S.g[local] += (double)col[1] / 255.0;
-        S.b[local] += (double)col[2] / 255.0;
+    if (blk.voxel_call && blk.voxel_call[local] != o->call) {
+        blk.voxel_call[local] = o->call;
+        if (blk.created_call == o->call)
+            o->cs.voxels_fresh++;
+        else
+            o->cs.voxels_old++;
     }
+    Sums& S = *blk.sums;
+    S.tsdf[local] += (double)sdf / (double)o->trunc;
+    S.weight[local] += 1.0;
+    S.r[local] += (double)col[0] / 255.0;
+    S.g[local] += (double)col[1] / 255.0;
+    S.b[local] += (double)col[2] / 255.0;
 }
 
 /* C8: is the centre c (camera depth zc) of a cell hidden behind the surface
@@ -214,19 +240,21 @@ void* oracle_create(float voxel_size, float trunc, int64_t pool_capacity, int32_
     o->capacity = pool_capacity;
     o->flags = flags;
     std::memset(&o->tot, 0, sizeof(o->tot));
+    std::memset(&o->cs, 0, sizeof(o->cs));
     return o;
 }
 
 void oracle_destroy(void* h) { delete static_cast<oracle_volume*>(h); }
 
-/* Restrict the stored sums to these blocks (n x 3 coords); only meaningful
- * with ORACLE_WATCH_ONLY.  Must be called before the first frame. */
-int oracle_watch(void* h, const int32_t* coords, int64_t n) {
+/* Start a new call: the frames integrated from here on are counted as one
+ * batch by oracle_get_call_stats. */
+void oracle_begin_call(void* h) {
     oracle_volume* o = static_cast<oracle_volume*>(h);
-    if (!o->blocks.empty()) return -1;
-    for (int64_t i = 0; i < n; ++i) o->watch.insert(Coord{coords[3 * i], coords[3 * i + 1], coords[3 * i + 2]});
-    return 0;
+    o->call++;
+    std::memset(&o->cs, 0, sizeof(o->cs));
 }
+
+void oracle_get_call_stats(void* h, oracle_call_stats* out) { *out = static_cast<oracle_volume*>(h)->cs; }
 
 int oracle_integrate(void* h, const float* depth, const uint8_t* rgb, int32_t W, int32_t H,
                      float fx, float fy, float cx, float cy, const float* R, const float* t,
@@ -310,6 +338,7 @@ int oracle_integrate(void* h, const float* depth, const uint8_t* rgb, int32_t W,
     }
 
     o->tot.frames++;
+    o->cs.frames++;
     o->tot.blocks = (int64_t)o->blocks.size();
     o->tot.pool_overflow += s.pool_overflow_new;
     o->tot.update_misses += s.update_misses;
@@ -337,8 +366,8 @@ void oracle_block_coords(void* h, int32_t* coords) {
 }
 
 /* Sums of the requested blocks, 512 per block in voxel-index order.  Blocks
- * that are absent or not watched are filled with NaN.  Returns how many of
- * the requested blocks had sums. */
+ * that are absent are filled with NaN.  Returns how many of the requested
+ * blocks exist. */
 int64_t oracle_block_sums(void* h, const int32_t* coords, int64_t n, double* tsdf, double* weight,
                           double* r, double* g, double* b) {
     oracle_volume* o = static_cast<oracle_volume*>(h);

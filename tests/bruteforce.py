@@ -45,18 +45,27 @@ def hidden_by_depth(frame, K, vs, tr, eps_px=1e-4, eps_z=1e-5):
     return hidden, tie
 
 
-def point_voxels(frame, u, v, voxel_size, trunc, eps=1e-3, eps_sdf=1e-5, reproject=False):
-    """Return (voxels, tie): voxels maps (kx, ky, kz) -> (tsdf, r, g, b) for the
-    kept voxels of pixel (u, v); tie is True if any decision was too close to
-    call in float32.  Returns (None, False) for an invalid/near pixel.  With
-    reproject, kept cells must also pass hidden_by_depth against the frame's
-    depth image, and the result is (voxels, tie_cells): the set of cells
-    whose decision is a tie (the others are exact)."""
+def crossed_cells(frame, u, v, voxel_size, trunc, eps=1e-3):
+    """Number of unit cells the closed band segment of pixel (u, v) crosses
+    (length of segment inside the cell > eps voxels), and whether any cell is
+    too close to call (the segment grazing a cell edge or face).  None for an
+    invalid or near pixel."""
+    r = _segment_cells(frame, u, v, voxel_size, trunc, eps)
+    if r is None:
+        return None, False
+    K, crosses, tie, _, _, _ = r
+    return int(crosses.sum()), tie
+
+
+def _segment_cells(frame, u, v, voxel_size, trunc, eps):
+    """The cells of the band segment's bounding box (plus one of margin),
+    which of them the segment crosses, and whether any is a tie; with the
+    point's depth, the pose and the float32 voxel size / trunc."""
     vs = float(np.float32(voxel_size))
     tr = float(np.float32(trunc))
     d = float(frame.depth[v, u])
     if not np.isfinite(d) or d <= tr:
-        return None, False
+        return None
     R = frame.R.astype(np.float64)
     t = frame.t.astype(np.float64)
     xn = (u - float(frame.cx)) / float(frame.fx)
@@ -91,7 +100,20 @@ def point_voxels(frame, u, v, voxel_size, trunc, eps=1e-3, eps_sdf=1e-5, reproje
     overlap_vox = overlap * seg_len          # length of segment inside the cell, voxels
     crosses = overlap_vox > eps
     tie = bool(np.any((np.abs(overlap_vox) <= eps) | (grazing & (overlap_vox > -eps))))
+    return K, crosses, tie, overlap_vox, d, (vs, tr, R, t)
 
+
+def point_voxels(frame, u, v, voxel_size, trunc, eps=1e-3, eps_sdf=1e-5, reproject=False):
+    """Return (voxels, tie): voxels maps (kx, ky, kz) -> (tsdf, r, g, b) for the
+    kept voxels of pixel (u, v); tie is True if any decision was too close to
+    call in float32.  Returns (None, False) for an invalid/near pixel.  With
+    reproject, kept cells must also pass hidden_by_depth against the frame's
+    depth image, and the result is (voxels, tie_cells): the set of cells
+    whose decision is a tie (the others are exact)."""
+    r = _segment_cells(frame, u, v, voxel_size, trunc, eps)
+    if r is None:
+        return None, False
+    K, crosses, tie, overlap_vox, d, (vs, tr, R, t) = r
     c = (K + 0.5) * vs
     zc = (c - t) @ R[:, 2]
     sdf = d - zc

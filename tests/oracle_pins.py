@@ -387,6 +387,97 @@ def invariant_failures(lib=oracle.LIBRARY):
     return f
 
 
+def _weighted_voxels(o):
+    """Set of global voxel indices with weight > 0, and the block set."""
+    coords = o.block_coords()
+    k, _ = _voxel_table(o, coords)
+    return {tuple(int(x) for x in kk) for kk in k}, {tuple(int(x) for x in c) for c in coords}
+
+
+def counter_failures(lib=oracle.LIBRARY):
+    """The measurement counts the benchmark divides by, pinned to independent
+    recounts: cells visited per point equals the number of cells a
+    float64 brute force finds the band segment crossing (tie-free points);
+    over an overlapping frame sequence, each frame's distinct blocks B_t and
+    distinct voxels U equal the block count and weighted-voxel count of that
+    frame integrated alone into a fresh volume, and its new blocks B_n the
+    growth of the block count; per call (several frames counted as one
+    batch) the distinct blocks, the new blocks and the distinct voxels split
+    into those of blocks the call created and of older blocks equal the same
+    recounts over the call's frames."""
+    f = []
+    # cells visited, point by point and per frame
+    n_checked = 0
+    for frame, vs, tr in _bf_cases():
+        H, W = frame.depth.shape
+        depth = frame.depth.copy()
+        want_frame = 0
+        for v in range(H):
+            for u in range(W):
+                n, tie = bruteforce.crossed_cells(frame, u, v, vs, tr)
+                if n is None:
+                    continue
+                if tie:
+                    depth[v, u] = 0.0
+                    continue
+                o = oracle.Oracle(vs, tr, 1 << 20, library=lib)
+                st = o.integrate(_single_pixel(frame, u, v))
+                if st["cells_visited"] != n:
+                    f.append(f"point ({u},{v}) vs={vs}: {st['cells_visited']} cells visited, brute force {n}")
+                    if len(f) > 5:
+                        return f
+                want_frame += n
+                n_checked += 1
+        fr = scenes.Frame(depth, frame.rgb, frame.fx, frame.fy, frame.cx, frame.cy, frame.R, frame.t)
+        st = oracle.Oracle(vs, tr, 1 << 20, library=lib).integrate(fr)
+        if st["cells_visited"] != want_frame:
+            f.append(f"frame vs={vs}: {st['cells_visited']} cells visited, brute force {want_frame}")
+    if n_checked < 150:
+        f.append(f"only {n_checked} points with a cell count")
+
+    # per frame: B_t, U, B_n over an overlapping sequence
+    wl = scenes.workload("spherewall320x240")
+    frames = [wl.frame(i) for i in (0, 4, 9, 4)]
+    vs, tr = wl.voxel_size, wl.trunc
+    a = oracle.Oracle(vs, tr, 1 << 20, track_touched=True, library=lib)
+    for i, fr in enumerate(frames):
+        before = a.block_count()
+        st = a.integrate(fr)
+        alone = oracle.Oracle(vs, tr, 1 << 20, library=lib)
+        alone.integrate(fr)
+        vox, blocks = _weighted_voxels(alone)
+        if st["blocks_touched"] != len(blocks):
+            f.append(f"frame {i}: B_t {st['blocks_touched']} != {len(blocks)} blocks of the frame alone")
+        if st["voxels_touched"] != len(vox):
+            f.append(f"frame {i}: U {st['voxels_touched']} != {len(vox)} weighted voxels of the frame alone")
+        if st["blocks_new"] != a.block_count() - before:
+            f.append(f"frame {i}: B_n {st['blocks_new']} != growth {a.block_count() - before}")
+    # per call: two calls of two frames each, the second overlapping the first
+    calls = [[frames[0], frames[1]], [frames[2], frames[1]]]
+    c = oracle.Oracle(vs, tr, 1 << 20, track_touched=True, library=lib)
+    prev_blocks = set()
+    for j, call in enumerate(calls):
+        if j:
+            c.begin_call()
+        before = c.block_count()
+        for fr in call:
+            c.integrate(fr)
+        cs = c.call_stats()
+        alone = oracle.Oracle(vs, tr, 1 << 20, library=lib)
+        for fr in call:
+            alone.integrate(fr)
+        vox, blocks = _weighted_voxels(alone)
+        fresh = {k for k in vox if tuple(x // 8 for x in k) not in prev_blocks}
+        want = {"frames": len(call), "blocks_touched": len(blocks), "blocks_new": c.block_count() - before,
+                "voxels_fresh": len(fresh), "voxels_old": len(vox) - len(fresh)}
+        if cs != want:
+            f.append(f"call {j}: counts {cs} != recount {want}")
+        _, prev_blocks = _weighted_voxels(c)
+    if calls and not want["voxels_old"]:
+        f.append("the second call touched no older voxel: the pin did not exercise the split")
+    return f
+
+
 def edge_failures(lib=oracle.LIBRARY):
     """Empty, invalid, near and out-of-range inputs."""
     f = []
@@ -432,6 +523,7 @@ PINS = {
     "reprojection": reprojection_failures,
     "sphere": sphere_failures,
     "invariants": invariant_failures,
+    "counters": counter_failures,
     "edges": edge_failures,
 }
 

@@ -113,6 +113,16 @@ def test_null_handle_calls():
     tsdf.tsdf_destroy(None)
 
 
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="passes made-up device addresses: host-side validation only, "
+                                           "never where a kernel could be launched")
 def test_microbench_rejects_bad_arguments():
     with pytest.raises(tsdf.TsdfError):
         tsdf.tsdf_mb_copy(0x1000, 0x2000, 17)

@@ -126,44 +126,58 @@ def test_room_full_parity():
     o = parity.oracle_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity)
     for key, (st, coords, arrays) in results.items():
         say(f"  compare {key}")
-        assert_parity(st, coords, arrays, o)
+        err = {}
+        f = parity.compare_stats(st, o) + parity.compare_blocks(coords, arrays, o, errors=err)
+        say(f"    largest mean differences: " + ", ".join(f"{k} {v:.3g}" for k, v in err.items()))
+        assert f == [], f
+        if key == ("owner", 100):
+            # one call: each block's sums are added in LDS (signed distance
+            # in 2^-24 units) and written once, so a mean differs from the
+            # oracle's by float rounding only, far inside 1e-4
+            assert max(err.values()) <= 2.0 ** -20, err
 
 
-@pytest.mark.timeout(900)
-def test_room1280x720_full_size_prefix():
-    """The 1280 x 720 room at its full sizes -- 921,600-pixel frames, a pool
-    of 2^22 blocks (40 GiB of sums), a 2^24-entry table -- in the benchmark's
-    launch configuration (owner update, 16 frames per call): counts after
-    every call against the stored oracle counts of all 300 frames' run, then
-    the block set in full and 64 sampled blocks voxel by voxel against a live
-    oracle run of the same 48 frames."""
+@pytest.mark.timeout(1200)
+def test_room1280x720_full_sequence():
+    """The 1280 x 720 room at its full sizes and length -- 300 frames of
+    921,600 pixels, a pool of 2^22 blocks (40 GiB of sums), a 2^24-entry
+    table -- in the benchmark's launch configuration (owner update, calls of
+    100 frames): counts after every call against the stored oracle counts,
+    then the block set in full and every voxel's weight and means against the
+    oracle run over all 300 frames (in eight worker processes, each over a
+    contiguous range of frames, their sums added)."""
     wl = scenes.workload("room1280x720")
     g = golden("room1280x720")
-    n, batch = 48, 16
-    frames = list(wl.frames(0, n))
-    for i in (0, n - 1):
+    n, batch = wl.n_frames, 100
+    say(f"  oracle and frames: {n} frames 1280x720 in 8 worker processes")
+    frames, o = parity.oracle_ranges("room1280x720", n, workers=8)
+    for i in (0, n // 2, n - 1):
         assert scenes.frame_digest([frames[i]]) == g["frames"][i]["sha256"], "generator drifted"
-    say(f"  gpu: {n} frames 1280x720, pool {wl.pool_capacity}, table {wl.table_entries}")
-    _, st, coords, arrays, hist = parity.gpu_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity,
-                                                       wl.table_entries, per_frame_stats=True, batch=batch,
-                                                       max_batch_pixels=batch * wl.width * wl.height)
-    _check_history("1280x720", hist, g, [list(range(i, i + batch)) for i in range(0, n, batch)])
+    assert o.block_count() == g["frames"][-1]["blocks_total"]
+    assert o.totals()["voxel_updates"] == g["totals"]["voxel_updates"]
+    say(f"  gpu: {n} frames, pool {wl.pool_capacity}, table {wl.table_entries}, {batch} frames per call")
+    vol, st, coords, arrays, hist = parity.gpu_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity,
+                                                         wl.table_entries, per_frame_stats=True, batch=batch,
+                                                         max_batch_pixels=batch * wl.width * wl.height)
+    _check_history("1280x720", hist, g, [list(range(i, min(i + batch, n))) for i in range(0, n, batch)])
     assert st["fallback_blocks"] == 0
-    say(f"  oracle: {n} frames")
-    o = parity.oracle_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity)
-    rng = np.random.default_rng(1280)
-    oc = o.block_coords()
-    sample = oc[rng.choice(len(oc), size=64, replace=False)]
-    f = parity.compare_stats(st, o) + parity.compare_blocks(coords, arrays, o, sample=sample)
+    del frames
+    say(f"  compare {len(coords)} blocks voxel by voxel")
+    err = {}
+    f = parity.compare_stats(st, o) + parity.compare_blocks(coords, arrays, o, errors=err)
+    say(f"    largest mean differences: " + ", ".join(f"{k} {v:.3g}" for k, v in err.items()))
+    assert f == [], f
+    table = vol.table.view(-1, 2).cpu().numpy().view(np.uint64)
+    f = parity.table_layout_failures(table, o.block_coords(), wl.pool_capacity)
     assert f == [], f
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_sweep_cells():
     """The benchmark's sweep cells (the room scene at 160x120 ... 1280x960,
     along the point-count and extent axes), 16 frames in one batched call:
-    counts against the oracle's stored counts for every cell, and every voxel
-    against a live oracle run for the two smallest cells."""
+    counts against the oracle's stored counts, and every voxel against a live
+    oracle run, for every cell."""
     for axis, W, H, fx in scenes.SWEEP_CELLS:
         name = scenes.cell_name(W, H, fx) if (W, H, fx) != (640, 480, 525.0) else "room640x480"
         wl = scenes.workload(name)
@@ -177,9 +191,8 @@ def test_sweep_cells():
         assert st["voxel_updates"] == sum(f["voxel_updates"] for f in g["frames"][:16])
         assert st["points_valid"] == sum(f["points_valid"] for f in g["frames"][:16])
         assert st["fallback_blocks"] == 0 and st["update_misses"] == 0 and st["table_full"] == 0
-        if W == 160:
-            o = parity.oracle_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity)
-            assert_parity(st, coords, arrays, o)
+        o = parity.oracle_integrate(frames, wl.voxel_size, wl.trunc, wl.pool_capacity)
+        assert_parity(st, coords, arrays, o)
 
 
 def _reproject_cases():
@@ -241,17 +254,24 @@ def test_load_factor_parity(target, mode):
     say(f"  load factor target {target}: pool {cap}, table {2 * cap}, {n} frames, achieved {lf:.3f}")
     assert target - 0.1 < lf <= target
     wl = scenes.workload("room640x480")
-    _, st, coords, arrays, o = run_both(wl.frames(0, n), wl.voxel_size, wl.trunc, cap, 2 * cap, mode=mode)
+    vol, st, coords, arrays, o = run_both(wl.frames(0, n), wl.voxel_size, wl.trunc, cap, 2 * cap, mode=mode)
     assert_parity(st, coords, arrays, o)
+    # the table itself: the slots linear probing fills, and the total
+    # displacement, do not depend on the insertion order (exact)
+    table = vol.table.view(-1, 2).cpu().numpy().view(np.uint64)
+    f = parity.table_layout_failures(table, o.block_coords(), cap)
+    assert f == [], f
     bins = np.arange(1, tsdf_bins() + 1)
     ha = st["probe_hist_alloc"]
     mean_a = float((ha * bins).sum() / ha.sum())
-    # allocate mixes hits and inserts: Knuth's linear-probing expectations for
-    # a successful search 1/2 (1 + 1/(1 - a)) and an insertion
-    # 1/2 (1 + 1/(1 - a)^2) bound its mean (loosely: the load grows during the run)
-    lo, hi = 1.0, 0.5 * (1 + 1 / (1 - lf) ** 2)
-    say(f"  allocate probes: mean {mean_a:.3f} in [{lo}, {hi:.3f}], max {st['probe_max']}")
-    assert lo <= mean_a <= 1.3 * hi
+    # the histogram counts every probe sequence (one per distinct key and
+    # wavefront): at least one slot each, and at most the longest sequence
+    # the final layout allows
+    disp = table_displacements(table, o.block_coords())
+    say(f"  allocate probes: mean {mean_a:.3f} (Knuth's insertion expectation "
+        f"{0.5 * (1 + 1 / (1 - lf) ** 2):.3f}), max {st['probe_max']}, longest final displacement {disp.max()}")
+    assert ha.sum() > 0 and mean_a >= 1.0
+    assert st["probe_max"] <= disp.max() + 1
     if mode == "rays":
         # lookups after allocation: near the successful-search expectation
         h = st["probe_hist_update"]
@@ -313,6 +333,18 @@ class _OracleSubset:
 
     def block_sums(self, coords):
         return self.o.block_sums(coords)
+
+
+def table_displacements(table, coords):
+    """Slots past its home slot of every key, from an exported table."""
+    T = table.shape[0]
+    tk = table[:, 0]
+    occ = np.nonzero(tk != np.uint64(0xFFFFFFFFFFFFFFFF))[0]
+    where = {int(k): int(i) for k, i in zip(tk[occ].tolist(), occ.tolist())}
+    keys = parity._pack(coords).astype(np.uint64)
+    home = (parity.fmix64(keys) & np.uint64(T - 1)).astype(np.int64)
+    pos = np.array([where[int(k)] for k in keys.tolist()], np.int64)
+    return (pos - home) & (T - 1)
 
 
 def tsdf_bins():
@@ -519,6 +551,23 @@ def test_pool_exhaustion_is_counted_exactly(mode):
     assert int(w.sum()) + st["update_misses"] == st["voxel_updates"] == o.totals()["voxel_updates"]
     assert np.all(w.max(1) > 0)                      # every block that got an index got contributions
     assert len(np.unique(coords, axis=0)) == cap
+    _survivors_exact(frames, wl.voxel_size, wl.trunc, st, coords, arrays)
+
+
+def _survivors_exact(frames, vs, tr, st, coords, arrays):
+    """A block's contributions do not depend on which other keys an exhausted
+    pool or a full table refused: every block the GPU kept equals that block
+    of an oracle run with unlimited capacity, and the refused blocks' weight
+    is exactly the counted misses."""
+    full = parity.oracle_integrate(frames, vs, tr, 1 << 24)
+    keep = {tuple(c) for c in coords.tolist()}
+    allc = {tuple(c) for c in full.block_coords().tolist()}
+    assert keep <= allc
+    lost = sorted(allc - keep)
+    w_lost = float(full.block_sums(np.array(lost, np.int32).reshape(-1, 3))["weight"].sum()) if lost else 0.0
+    assert st["update_misses"] == w_lost
+    f = parity.compare_blocks(coords, arrays, _OracleSubset(full, keep))
+    assert f == [], f
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -530,6 +579,7 @@ def test_full_table_terminates_and_counts(mode):
     assert st["table_full"] > 0
     assert int(arrays["weight"].astype(np.float64).sum()) + st["update_misses"] == st["voxel_updates"]
     assert st["voxel_updates"] == o.totals()["voxel_updates"]
+    _survivors_exact([base], 0.01, 0.04, st, coords, arrays)
 
 
 @pytest.mark.parametrize("mode", MODES)

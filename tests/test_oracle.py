@@ -79,6 +79,16 @@ MUTATIONS = [
     ("hidden when in front", "return zc - D > trunc;", "return D - zc > trunc;", 1, "reprojection"),
     ("projection uses rotation rows", "const float xc = (R[0] * q0 + R[3] * q1) + R[6] * q2;",
      "const float xc = (R[0] * q0 + R[1] * q1) + R[2] * q2;", 1, "reprojection"),
+    # the measurement counts (per frame and per call)
+    ("U counts a voxel's first touch only", "if (blk.voxel_frame && blk.voxel_frame[local] != stamp) {",
+     "if (blk.voxel_frame && blk.voxel_frame[local] == 0) {", 1, "counters"),
+    ("cells counted twice", "s.cells_visited++;", "s.cells_visited += 2;", 1, "counters"),
+    ("B_t counts new blocks only", "if (blk.block_frame != stamp) {", "if (blk.block_frame == 0) {", 1,
+     "counters"),
+    ("call's B counts new blocks only", "if (blk.block_call != o->call) {", "if (blk.block_call == 0) {", 1,
+     "counters"),
+    ("call's fresh and old voxels swapped", "if (blk.created_call == o->call)",
+     "if (blk.created_call != o->call)", 1, "counters"),
 ]
 
 
