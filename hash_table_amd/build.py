@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libtsdf_hip.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("tsdf_kernels.hip", "tsdf_capi.hip", "microbench.hip")]
+SOURCES = [os.path.join(CSRC, n) for n in ("tsdf_kernels.hip", "tsdf_mesh.hip", "tsdf_capi.hip", "microbench.hip")]
 HEADERS = [os.path.join(CSRC, "tsdf_device.hpp"), os.path.join(CSRC, "tsdf_kernels.hpp"), os.path.join(ROOT, "include", "tsdf.h"),
            os.path.join(ROOT, "include", "tsdf_microbench.h")]
 ARCH = os.environ.get("TSDF_OFFLOAD_ARCH", "gfx950")

@@ -184,14 +184,16 @@ VolumeArgs volume_args(const tsdf_volume* h) {
     return a;
 }
 
-OwnerArgs owner_args(const tsdf_volume* h, unsigned int serial) {
+// The owner update's work lists laid out in `scratch_base` for calls of up to
+// `pixels` pixels (the volume's scratch: its configured max_batch_pixels).
+OwnerArgs owner_args_at(const tsdf_volume* h, unsigned int serial, void* scratch_base, int64_t pixels) {
     OwnerArgs o;
     std::memset(&o, 0, sizeof(o));
     o.build_items = h->cfg.update_mode == TSDF_UPDATE_OWNER;
     o.parity = serial & 1u;
     if (!o.build_items) return o;
-    const ScratchLayout L = scratch_layout(h->cfg.table_entries, h->cfg.max_batch_pixels);
-    char* base = static_cast<char*>(h->buf.scratch);
+    const ScratchLayout L = scratch_layout(h->cfg.table_entries, pixels);
+    char* base = static_cast<char*>(scratch_base);
     o.fc = reinterpret_cast<FrameCounters*>(base + L.fc);
     o.items = reinterpret_cast<unsigned int*>(base + L.items);
     o.items_spill = reinterpret_cast<unsigned int*>(base + L.items_spill);
@@ -207,6 +209,12 @@ OwnerArgs owner_args(const tsdf_volume* h, unsigned int serial) {
     o.rec_part_cap = L.rec_part_cap;
     return o;
 }
+
+OwnerArgs owner_args(const tsdf_volume* h, unsigned int serial) {
+    return owner_args_at(h, serial, h->buf.scratch, h->cfg.max_batch_pixels);
+}
+
+unsigned int next_serial(const tsdf_volume* h) { return h->serial + 1 == 0xFFFFFFFFu ? 1u : h->serial + 1; }
 
 // init arguments: the owner-mode arrays that must start zeroed
 bool init_volume(const tsdf_volume* h, bool whole_pool, hipStream_t s) {
@@ -335,7 +343,7 @@ tsdf_status stage_frames(tsdf_volume* h, Batch* b, hipStream_t s) {
 tsdf_status do_allocate(tsdf_volume* h, const BatchArgs& b, hipStream_t s) {
     if (h->pending && !launch_discard(volume_args(h), owner_args(h, h->serial), s, timer_of(h))) return TSDF_EHIP;
     h->pending = false;
-    const unsigned int serial = h->serial + 1 == 0xFFFFFFFFu ? 1u : h->serial + 1;
+    const unsigned int serial = next_serial(h);
     if (!launch_allocate(b, volume_args(h), owner_args(h, serial), s, timer_of(h))) return TSDF_EHIP;
     h->serial = serial;
     return TSDF_OK;
@@ -530,6 +538,22 @@ tsdf_status tsdf_export_blocks(tsdf_volume* h, int32_t* coords, float* tsdf, flo
             return TSDF_EHIP;
     if (hipStreamSynchronize(s) != hipSuccess) return TSDF_EHIP;
     return TSDF_OK;
+}
+
+tsdf_status tsdf_extract_mesh(tsdf_volume* h, float* positions, int32_t* keys, int64_t max_triangles,
+                              int64_t* n_triangles, void* stream) {
+    if (!h || !n_triangles || max_triangles < 0 || (max_triangles > 0 && !positions)) return TSDF_EINVAL;
+    if ((uintptr_t)positions % 4 != 0 || (uintptr_t)keys % 4 != 0) return TSDF_EALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned long long* counter = static_cast<unsigned long long*>(h->buf.counters) + kMeshTriangles;
+    if (!launch_mesh(volume_args(h), (unsigned long long)h->cfg.table_entries, counter, positions,
+                     reinterpret_cast<int*>(keys), (unsigned long long)max_triangles, s))
+        return TSDF_EHIP;
+    unsigned long long n = 0;
+    if (hipMemcpyAsync(&n, counter, sizeof(n), hipMemcpyDeviceToHost, s) != hipSuccess) return TSDF_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return TSDF_EHIP;
+    *n_triangles = (int64_t)n;
+    return (int64_t)n > max_triangles ? TSDF_ESMALL : TSDF_OK;
 }
 
 tsdf_status tsdf_set_kernel_timing(tsdf_volume* h, int32_t enable) {

@@ -42,6 +42,7 @@ enum CounterWord {
     kProbeMax,
     kFallbackBlocks,     // owner update: blocks rescanned because their runs did not fit
     kProbeExhausted,     // table operations that stopped at the configured probe limit
+    kMeshTriangles,      // triangles of the last surface extraction (copy 0 only; not a statistic)
     kHistAlloc = 16,
     kHistUpdate = kHistAlloc + kProbeBins,
     kCounterWords = kHistUpdate + kProbeBins,

@@ -47,6 +47,10 @@ bool launch_update_rays(const BatchArgs& b, const VolumeArgs& v, hipStream_t s, 
 // and (owner mode) the per-slot run counts and per-frame counters
 bool launch_init(const VolumeArgs& v, unsigned long long table_entries, bool whole_pool, const OwnerArgs* own,
                  hipStream_t s);
+// surface extraction (tsdf_mesh.hip): clears *counter, then counts every
+// triangle in it and writes those below max_triangles (key may be null)
+bool launch_mesh(const VolumeArgs& v, unsigned long long table_entries, unsigned long long* counter, float* pos,
+                 int* key, unsigned long long max_triangles, hipStream_t s);
 bool launch_export_coords(const VolumeArgs& v, unsigned long long table_entries, unsigned long long n_blocks,
                           int* coords, hipStream_t s);
 

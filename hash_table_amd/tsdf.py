@@ -36,8 +36,9 @@ MB_LDS_DISTINCT, MB_LDS_RANDOM, MB_LDS_SAME, MB_LDS_GROUPS = 0, 1, 2, 3
 # every symbol the headers declare
 EXPORTS = [
     "tsdf_table_entries_for", "tsdf_counters_bytes", "tsdf_scratch_bytes", "tsdf_create", "tsdf_reset", "tsdf_allocate",
-    "tsdf_update", "tsdf_integrate", "tsdf_integrate_batch", "tsdf_allocate_batch", "tsdf_update_batch",
-    "tsdf_export_blocks", "tsdf_get_stats", "tsdf_set_kernel_timing", "tsdf_kernel_times", "tsdf_destroy",
+    "tsdf_update", "tsdf_integrate", "tsdf_integrate_batch", "tsdf_allocate_batch",
+    "tsdf_update_batch",
+    "tsdf_export_blocks", "tsdf_extract_mesh", "tsdf_get_stats", "tsdf_set_kernel_timing", "tsdf_kernel_times", "tsdf_destroy",
     "tsdf_status_str", "tsdf_mb_copy", "tsdf_mb_atomic_add_f32", "tsdf_mb_cas_u64", "tsdf_mb_lds_atomic",
 ]
 
@@ -104,6 +105,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         "tsdf_allocate_batch": (I32, [P, ctypes.POINTER(tsdf_frame), I32, P]),
         "tsdf_update_batch": (I32, [P, ctypes.POINTER(tsdf_frame), I32, P]),
         "tsdf_export_blocks": (I32, [P, P, P, P, P, P, P, I64, ctypes.POINTER(I64), P]),
+        "tsdf_extract_mesh": (I32, [P, P, P, I64, ctypes.POINTER(I64), P]),
         "tsdf_get_stats": (I32, [P, ctypes.POINTER(tsdf_stats), P]),
         "tsdf_set_kernel_timing": (I32, [P, I32]),
         "tsdf_kernel_times": (I32, [P, ctypes.POINTER(tsdf_kernel_time), I32, ctypes.POINTER(I32)]),
@@ -209,6 +211,20 @@ def tsdf_export_blocks(volume, coords: int, tsdf: int, weight: int, r: int, g: i
     if st == TSDF_ESMALL:
         raise TsdfError(st, f"tsdf_export_blocks ({n.value} blocks > {max_blocks})")
     _check(st, "tsdf_export_blocks")
+    return int(n.value)
+
+
+def tsdf_extract_mesh(volume, positions: int, keys: int, max_triangles: int, stream: int = 0) -> int:
+    """Returns the number of triangles (raises TsdfError(TSDF_ESMALL) if more
+    than max_triangles; the count is then in the error's `n_triangles`)."""
+    n = ctypes.c_int64(0)
+    st = load().tsdf_extract_mesh(volume, ctypes.c_void_p(positions), ctypes.c_void_p(keys), max_triangles,
+                                  ctypes.byref(n), ctypes.c_void_p(stream))
+    if st == TSDF_ESMALL:
+        e = TsdfError(st, f"tsdf_extract_mesh ({n.value} triangles > {max_triangles})")
+        e.n_triangles = int(n.value)
+        raise e
+    _check(st, "tsdf_extract_mesh")
     return int(n.value)
 
 
@@ -349,6 +365,26 @@ class Volume:
 
     def kernel_times(self) -> Dict[str, Dict[str, float]]:
         return tsdf_kernel_times(self.handle)
+
+    def extract_mesh(self, stream=None, with_keys=True):
+        """Marching tetrahedra on the device: host arrays positions
+        (n, 3, 3) float32 metres and keys (n, 3, 4) int32 (vertex names).
+        A count-only call sizes the output first."""
+        import torch
+        sh = _stream_handle(stream)
+        try:
+            n = tsdf_extract_mesh(self.handle, 0, 0, 0, sh)
+        except TsdfError as e:
+            if e.status != TSDF_ESMALL:
+                raise
+            n = e.n_triangles
+        pos = torch.empty((max(n, 1), 9), dtype=torch.float32, device=self.device)
+        key = torch.empty((max(n, 1), 12), dtype=torch.int32, device=self.device) if with_keys else None
+        got = tsdf_extract_mesh(self.handle, pos.data_ptr(), key.data_ptr() if with_keys else 0, n, sh)
+        assert got == n, (got, n)
+        out_pos = pos[:n].cpu().numpy().reshape(n, 3, 3)
+        out_key = key[:n].cpu().numpy().reshape(n, 3, 4) if with_keys else None
+        return out_pos, out_key
 
     def export(self, stream=None, arrays=("tsdf", "weight", "r", "g", "b")):
         """All pool blocks as host numpy arrays: coords (n, 3) int32 and

@@ -239,6 +239,30 @@ tsdf_status tsdf_export_blocks(tsdf_volume* volume, int32_t* coords, float* tsdf
                                float* r, float* g, float* b, int64_t max_blocks, int64_t* n_blocks,
                                void* stream);
 
+/* Surface extraction by marching tetrahedra (the paper extracts the surface
+ * once, after integration, by marching tetrahedra: section 3; its gates
+ * compare extracted surfaces: section 3a).  Samples are the voxel centres;
+ * a voxel is observed iff its weight sum is > 0, inside iff its TSDF sum is
+ * < 0, its value is the mean TSDF.  The cell between voxels k and k + (1,1,1)
+ * is cut into six tetrahedra along that diagonal (for each ordering a, b, c
+ * of the axes -- xyz, xzy, yxz, yzx, zxy, zyx -- the corners k, k + e_a,
+ * k + e_a + e_b, k + (1,1,1)); tetrahedra with an unobserved corner are
+ * skipped; each edge between an inside and an outside corner, from lattice
+ * point p to p + d (d in {0,1}^3), holds one vertex at p + t d in voxel
+ * units, t = v_p / (v_p - v_{p+d}), position ((p + t d) + 1/2) vs metres.
+ * Triangles face from inside to outside.  Output, caller device memory:
+ * positions (9 floats per triangle: x, y, z of its three vertices, metres)
+ * and, if keys is not NULL, the vertices' names (12 int32 per triangle:
+ * p_x, p_y, p_z, d_x | d_y << 1 | d_z << 2 per vertex; a vertex shared by
+ * several triangles has the same name in each, so the soup can be welded).
+ * *n_triangles (host) receives the number of triangles; only the first
+ * max_triangles are written, and TSDF_ESMALL is returned if there are more.
+ * Triangles come in no particular order.  Reads the volume; writes nothing
+ * of it but a word of its counters buffer (not a statistic).  Waits for the
+ * stream. */
+tsdf_status tsdf_extract_mesh(tsdf_volume* volume, float* positions, int32_t* keys, int64_t max_triangles,
+                              int64_t* n_triangles, void* stream);
+
 /* Read the counters into *stats (host memory).  Waits for the stream. */
 tsdf_status tsdf_get_stats(tsdf_volume* volume, tsdf_stats* stats, void* stream);
 

@@ -1,7 +1,9 @@
-"""Reference ("oracle") integrator for hash-blocked TSDF fusion.
+"""Reference ("oracle") integrator and surface extraction for hash-blocked
+TSDF fusion.
 
 TEST INFRASTRUCTURE ONLY.  A plain, single-threaded C++ implementation
-(``tsdf_oracle.cpp``, a ``std::map`` keyed by block coordinate) that the
+(``tsdf_oracle.cpp``, a ``std::map`` keyed by block coordinate; and
+``mesh_oracle.cpp``, marching tetrahedra over the fused volume) that the
 tests, the smoke check and the benchmark's CPU-baseline leg use to check and
 time the HIP library.  The HIP library and its Python binding never import,
 load or call anything here, and share no code with it.
@@ -18,6 +20,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(HERE, "tsdf_oracle.cpp")
 LIBRARY = os.path.join(HERE, "libtsdf_oracle.so")
+MESH_SOURCE = os.path.join(HERE, "mesh_oracle.cpp")          # marching tetrahedra (surface extraction)
+MESH_LIBRARY = os.path.join(HERE, "libmesh_oracle.so")
 
 # Strict IEEE single precision: no contraction into FMA, no fast-math, SSE
 # arithmetic (x86-64 default) so no excess precision.
@@ -29,11 +33,14 @@ REPROJECT = 4          # the reprojection reading of the occlusion test (C8)
 
 
 def build(source: str = SOURCE, output: str = LIBRARY, extra_flags: Iterable[str] = ()) -> str:
-    """Compile the oracle (or a copy of its source) into a shared library."""
+    """Compile the oracle (or a copy of its source) into a shared library;
+    with no arguments also the extraction oracle."""
     tmp = output + f".tmp{os.getpid()}"
     cmd = ["g++", *CXXFLAGS, *extra_flags, "-o", tmp, source]
     subprocess.run(cmd, check=True)
     os.replace(tmp, output)
+    if source == SOURCE and output == LIBRARY:
+        build(MESH_SOURCE, MESH_LIBRARY, extra_flags)
     return output
 
 
@@ -87,6 +94,62 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
 
 def _ptr(a: np.ndarray) -> ctypes.c_void_p:
     return ctypes.c_void_p(a.ctypes.data)
+
+
+def load_mesh(path: str = MESH_LIBRARY) -> ctypes.CDLL:
+    if path in _LIBS:
+        return _LIBS[path]
+    if not os.path.exists(path):
+        if path != MESH_LIBRARY:
+            raise FileNotFoundError(path)
+        build(MESH_SOURCE, MESH_LIBRARY)
+    lib = ctypes.CDLL(path)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    lib.oracle_mesh.restype = P
+    lib.oracle_mesh.argtypes = [P, P, P, I64, ctypes.c_double]
+    lib.oracle_mesh_vertex_count.restype = I64
+    lib.oracle_mesh_vertex_count.argtypes = [P]
+    lib.oracle_mesh_triangle_count.restype = I64
+    lib.oracle_mesh_triangle_count.argtypes = [P]
+    lib.oracle_mesh_vertices.argtypes = [P, P, P]
+    lib.oracle_mesh_triangles.argtypes = [P, P]
+    lib.oracle_mesh_destroy.argtypes = [P]
+    _LIBS[path] = lib
+    return lib
+
+
+class Mesh:
+    """The extraction oracle's surface: keys (nv, 4) int32 -- the edge's lower
+    lattice point (voxel coordinates) and direction d = dx | dy << 1 | dz << 2
+    --, positions (nv, 3) float64 in metres, triangles (nt, 3) indices into
+    the vertex arrays, each oriented with its normal from inside to outside."""
+
+    def __init__(self, keys, pos, tris):
+        self.keys, self.pos, self.tris = keys, pos, tris
+
+
+def extract_mesh(coords: np.ndarray, tsdf: np.ndarray, weight: np.ndarray, voxel_size: float,
+                 library: str = MESH_LIBRARY) -> Mesh:
+    """Marching tetrahedra over blocks (coords (n, 3); tsdf and weight sums
+    (n, 512)): the extraction oracle of mesh_oracle.cpp."""
+    lib = load_mesh(library)
+    c = np.ascontiguousarray(coords, np.int32).reshape(-1, 3)
+    t = np.ascontiguousarray(tsdf, np.float64).reshape(-1, 512)
+    w = np.ascontiguousarray(weight, np.float64).reshape(-1, 512)
+    assert t.shape[0] == w.shape[0] == c.shape[0]
+    h = lib.oracle_mesh(_ptr(c), _ptr(t), _ptr(w), c.shape[0], float(voxel_size))
+    try:
+        nv, nt = int(lib.oracle_mesh_vertex_count(h)), int(lib.oracle_mesh_triangle_count(h))
+        keys = np.empty((nv, 4), np.int32)
+        pos = np.empty((nv, 3), np.float64)
+        tris = np.empty((nt, 3), np.int64)
+        if nv:
+            lib.oracle_mesh_vertices(h, _ptr(keys), _ptr(pos))
+        if nt:
+            lib.oracle_mesh_triangles(h, _ptr(tris))
+    finally:
+        lib.oracle_mesh_destroy(h)
+    return Mesh(keys, pos, tris)
 
 
 class Oracle:

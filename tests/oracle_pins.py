@@ -517,6 +517,191 @@ def edge_failures(lib=oracle.LIBRARY):
     return f
 
 
+# ---------------------------------------------------------------------------
+# surface extraction (marching tetrahedra, mesh_oracle.cpp)
+# ---------------------------------------------------------------------------
+def _field_volume(nb, vs, value, observed=None, origin=(-2, -2, -2)):
+    """Blocks origin + [0, nb)^3 with the sums of a field sampled at voxel
+    centres: tsdf = value(centres) (weight 1) where observed."""
+    o = np.asarray(origin)
+    coords = np.array([[x, y, z] for x in range(nb) for y in range(nb) for z in range(nb)], np.int32) + o
+    li = np.arange(512)
+    local = np.stack([li % 8, (li // 8) % 8, li // 64], 1)
+    k = coords[:, None, :].astype(np.int64) * 8 + local[None]
+    centres = (k + 0.5) * vs
+    w = np.ones(k.shape[:2]) if observed is None else observed(k).astype(np.float64)
+    t = value(centres) * w
+    return coords, t, w
+
+
+def _mesh_edges(tris):
+    """Directed edges (a, b) of every triangle, as an (3 nt, 2) array."""
+    return np.concatenate([tris[:, [0, 1]], tris[:, [1, 2]], tris[:, [2, 0]]])
+
+
+def _orientation_failures(m, label, closed):
+    """Every undirected edge is used by at most two triangles (exactly two if
+    the surface is closed), and two triangles sharing an edge run it in
+    opposite directions (a consistently oriented surface)."""
+    f = []
+    e = _mesh_edges(m.tris)
+    und = np.sort(e, 1)
+    _, inv, cnt = np.unique(und, axis=0, return_inverse=True, return_counts=True)
+    if cnt.max(initial=0) > 2:
+        f.append(f"{label}: an edge shared by {cnt.max()} triangles")
+    if closed and cnt.min(initial=2) != 2:
+        f.append(f"{label}: {int((cnt != 2).sum())} edges not shared by exactly two triangles (not closed)")
+    directed, dcnt = np.unique(e, axis=0, return_counts=True)
+    if dcnt.max(initial=0) > 1:
+        f.append(f"{label}: a directed edge used twice (inconsistent orientation)")
+    return f
+
+
+def _normals(m):
+    a, b, c = (m.pos[m.tris[:, i]] for i in range(3))
+    return np.cross(b - a, c - a), (a + b + c) / 3.0
+
+
+def mesh_field_failures(lib=oracle.MESH_LIBRARY):
+    """Extraction on fields sampled at voxel centres (no integration): a
+    linear field's vertices lie exactly on its zero plane and its triangles
+    face along the gradient; a sphere's signed distance, observed in a box
+    around it, gives a closed, consistently oriented surface with Euler
+    characteristic 2, outward normals and vertices on the sphere; a random
+    field gives a consistently oriented manifold; no vertex sits on an edge
+    with an unobserved end."""
+    f = []
+    vs = 0.02
+    rng = np.random.default_rng(31)
+    # linear fields: linear interpolation of a linear function is exact
+    for trial in range(3):
+        n = rng.normal(size=3)
+        n /= np.linalg.norm(n)
+        c = float(rng.uniform(-0.05, 0.05))
+        coords, t, w = _field_volume(4, vs, lambda x: (x @ n - c) / (4 * vs))
+        m = oracle.extract_mesh(coords, t, w, vs, library=lib)
+        if len(m.tris) < 100:
+            f.append(f"plane field {trial}: only {len(m.tris)} triangles")
+            continue
+        err = np.abs(m.pos @ n - c).max()
+        if not err < 1e-12:
+            f.append(f"plane field {trial}: a vertex {err:.3g} m off the plane")
+        nrm, _ = _normals(m)
+        if np.any(nrm @ n < -1e-15):
+            f.append(f"plane field {trial}: a triangle faces against the gradient")
+        f += _orientation_failures(m, f"plane field {trial}", closed=False)
+    # a sphere's signed distance (truncated), observed in a 0.64 m box
+    centre, r = np.array([0.013, -0.021, 0.007]), 0.2
+    trunc = 4 * vs
+    coords, t, w = _field_volume(4, vs, lambda x: np.clip((np.linalg.norm(x - centre, axis=-1) - r) / trunc, -1, 1))
+    m = oracle.extract_mesh(coords, t, w, vs, library=lib)
+    f += _orientation_failures(m, "sphere field", closed=True)
+    V, F = len(m.pos), len(m.tris)
+    E = len(np.unique(np.sort(_mesh_edges(m.tris), 1), axis=0))
+    if V - E + F != 2:
+        f.append(f"sphere field: Euler characteristic {V - E + F} != 2")
+    d = np.linalg.norm(m.pos - centre, axis=1) - r
+    if not np.abs(d).max() <= vs / 4:
+        f.append(f"sphere field: a vertex {np.abs(d).max() * 1000:.3f} mm off the sphere")
+    nrm, cen = _normals(m)
+    if np.any(np.einsum("ij,ij->i", nrm, cen - centre) <= 0):
+        f.append("sphere field: a triangle faces inwards")
+    # a random field over a region with unobserved voxels
+    vals = rng.uniform(-1, 1, size=(64, 512))
+    obs = rng.random((64, 512)) > 0.1
+    coords = np.array([[x, y, z] for x in range(4) for y in range(4) for z in range(4)], np.int32) - 2
+    m = oracle.extract_mesh(coords, vals * obs, obs.astype(np.float64), vs, library=lib)
+    f += _orientation_failures(m, "random field", closed=False)
+    li = np.arange(512)
+    observed = {tuple(int(x) for x in cc * 8 + np.array([l % 8, (l // 8) % 8, l // 64]))
+                for b, cc in enumerate(coords) for l in li[obs[b]]}
+    ends = [(tuple(int(x) for x in k[:3]), tuple(int(k[i]) + ((int(k[3]) >> i) & 1) for i in range(3)))
+            for k in m.keys]
+    if any(a not in observed or b not in observed for a, b in ends):
+        f.append("random field: a vertex on an edge with an unobserved end")
+    if len(m.tris) < 1000:
+        f.append(f"random field: only {len(m.tris)} triangles")
+    # the vertex key names a lattice edge whose ends straddle the surface
+    sums = {}
+    for b, cc in enumerate(coords):
+        for l in range(512):
+            sums[tuple(int(x) for x in cc * 8 + np.array([l % 8, (l // 8) % 8, l // 64]))] = vals[b, l] * obs[b, l]
+    if any((sums[a] < 0) == (sums[b] < 0) for a, b in ends):
+        f.append("random field: a vertex on an edge whose ends lie on the same side")
+    return f
+
+
+def _dense_plane():
+    """The plane workload's geometry (z = 1 m, identity pose) seen with 5 mm
+    pixels at 1 m, finer than the 1 cm voxels: every voxel column of the
+    view is observed."""
+    return scenes.plane_frame(W=160, H=120, fx=200.0, fy=200.0, cx=79.5, cy=59.5)
+
+
+def mesh_plane_failures(lib=oracle.MESH_LIBRARY):
+    """Integration and extraction of a fronto-parallel plane at z = 1 m
+    (vs 1 cm, trunc 4 cm): every voxel of layer 99 holds +0.125 and of layer
+    100 -0.125, so every vertex lies at z = 1.000 m, only on edges from layer
+    99 to layer 100; every cell of those layers with eight observed corners
+    holds exactly 8 triangles covering its cross-section, area vs^2, each
+    facing the camera (-z: from behind the surface to in front of it)."""
+    f = []
+    vs, tr = 0.01, 0.04
+    o = oracle.Oracle(vs, tr, 1 << 16)
+    o.integrate(_dense_plane())
+    coords = o.block_coords()
+    s = o.block_sums(coords)
+    m = oracle.extract_mesh(coords, s["tsdf"], s["weight"], vs, library=lib)
+    if len(m.tris) < 1000:
+        return [f"dense plane: only {len(m.tris)} triangles"]
+    if not np.abs(m.pos[:, 2] - 1.0).max() < 1e-6:
+        f.append(f"dense plane: a vertex at z = {m.pos[np.argmax(np.abs(m.pos[:, 2] - 1.0)), 2]:.7f}")
+    if not (np.all(m.keys[:, 2] == 99) and np.all(m.keys[:, 3] & 4)):
+        f.append("dense plane: a vertex on an edge that is not from layer 99 to layer 100")
+    k, _ = _voxel_table(o, coords)
+    obs = {tuple(int(x) for x in kk) for kk in k}
+    full = {(i, j) for (i, j, z) in obs if z == 99 and all(
+        (i + a, j + b, 99 + c) in obs for a in (0, 1) for b in (0, 1) for c in (0, 1))}
+    nrm, cen = _normals(m)
+    cell = np.floor(cen[:, :2] / vs - 0.5).astype(np.int64)
+    area = 0.5 * np.linalg.norm(nrm, axis=1)
+    per = {}
+    for (i, j), a in zip(map(tuple, cell.tolist()), area):
+        n_, s_ = per.get((i, j), (0, 0.0))
+        per[(i, j)] = (n_ + 1, s_ + a)
+    bad = [c for c in full if per.get(c, (0, 0.0))[0] != 8 or abs(per[c][1] - vs * vs) > 1e-12]
+    if bad:
+        f.append(f"dense plane: {len(bad)} of {len(full)} fully observed cells without 8 triangles of area vs^2")
+    if len(full) < 3000:
+        f.append(f"dense plane: only {len(full)} fully observed cells")
+    if np.any(nrm[:, 2] >= 0):
+        f.append("dense plane: a triangle faces away from the camera")
+    return f
+
+
+def mesh_sphere_failures(lib=oracle.MESH_LIBRARY):
+    """The analytic sphere gate: the noise-free sphere-and-wall sequence
+    integrated, then extracted: every vertex on the sphere's front cap (seen
+    head-on by the arc of cameras) lies within a quarter voxel of the sphere
+    r = 0.5 m at (0, 0, 1.5)."""
+    f = []
+    wl = scenes.workload("spherewall320x240_noisefree")
+    o = oracle.Oracle(wl.voxel_size, wl.trunc, wl.pool_capacity)
+    for i in range(wl.n_frames):
+        o.integrate(wl.frame(i))
+    coords = o.block_coords()
+    s = o.block_sums(coords)
+    m = oracle.extract_mesh(coords, s["tsdf"], s["weight"], wl.voxel_size, library=lib)
+    cap = (m.pos[:, 2] < 1.2) & (np.hypot(m.pos[:, 0], m.pos[:, 1]) < 0.2)
+    if cap.sum() < 500:
+        return [f"sphere: only {int(cap.sum())} vertices on the front cap"]
+    d = np.abs(np.linalg.norm(m.pos[cap] - np.array([0.0, 0.0, 1.5]), axis=1) - 0.5)
+    if not d.max() <= wl.voxel_size / 4:
+        f.append(f"sphere: a cap vertex {d.max() * 1000:.3f} mm off the sphere (> {wl.voxel_size / 4 * 1000:.2f} mm)")
+    f += _orientation_failures(m, "sphere scene", closed=False)
+    return f
+
+
 PINS = {
     "plane": plane_failures,
     "bruteforce": bruteforce_failures,
@@ -526,6 +711,12 @@ PINS = {
     "counters": counter_failures,
     "edges": edge_failures,
 }
+# pins of the extraction oracle (their `lib` is the mesh library)
+MESH_PINS = {
+    "mesh_fields": mesh_field_failures,
+    "mesh_plane": mesh_plane_failures,
+    "mesh_sphere": mesh_sphere_failures,
+}
 
 
 if __name__ == "__main__":
@@ -534,7 +725,7 @@ if __name__ == "__main__":
     out = {}
     for n in names:
         try:
-            out[n] = PINS[n](lib_path)
+            out[n] = {**PINS, **MESH_PINS}[n](lib_path)
         except Exception as e:           # a planted mistake may break a check outright
             out[n] = [f"exception: {type(e).__name__}: {e}"]
     print(json.dumps(out))

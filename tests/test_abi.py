@@ -109,6 +109,8 @@ def test_null_handle_calls():
         with pytest.raises(tsdf.TsdfError):
             fn(None, f)
     with pytest.raises(tsdf.TsdfError):
+        tsdf.tsdf_extract_mesh(None, 0, 0, 0)
+    with pytest.raises(tsdf.TsdfError):
         tsdf.tsdf_get_stats(None)
     tsdf.tsdf_destroy(None)
 

@@ -28,6 +28,12 @@ def test_pin(pin):
     assert failures == [], failures
 
 
+@pytest.mark.parametrize("pin", sorted(oracle_pins.MESH_PINS))
+def test_mesh_pin(pin):
+    failures = oracle_pins.MESH_PINS[pin]()
+    assert failures == [], failures
+
+
 def test_plane_every_voxel_single_ray():
     # 2 cm pixel footprint on 1 cm voxels: every kept voxel receives one ray,
     # so its colour is exactly one pixel's colour / 255
@@ -90,6 +96,47 @@ MUTATIONS = [
     ("call's fresh and old voxels swapped", "if (blk.created_call == o->call)",
      "if (blk.created_call != o->call)", 1, "counters"),
 ]
+
+
+# the extraction oracle (mesh_oracle.cpp)
+MESH_MUTATIONS = [
+    ("interpolation from the wrong end", "const double t = p.v / (p.v - q.v);",
+     "const double t = q.v / (q.v - p.v);", 1, "mesh_fields,mesh_plane"),
+    ("inside where the sum is positive", "c.inside = tsdf[q] < 0.0;", "c.inside = tsdf[q] > 0.0;", 1,
+     "mesh_fields,mesh_plane"),
+    ("one tetrahedron's orientation wrong", "kOrderSign[6] = {+1, -1, -1, +1, +1, -1};",
+     "kOrderSign[6] = {+1, -1, -1, -1, +1, -1};", 1, "mesh_fields"),
+    ("a tetrahedron missing, another twice", "{2, 0, 1}, {2, 1, 0}};", "{2, 0, 1}, {2, 0, 1}};", 1,
+     "mesh_fields,mesh_plane"),
+    ("unobserved voxels used", "if (!(weight[q] > 0.0)) return false;", "if (!(weight[q] >= 0.0)) return false;",
+     1, "mesh_fields"),
+    ("lone outside corner faces inwards", "const bool fwd = (perm_sign(perm) * s > 0) == (ni == 1);",
+     "const bool fwd = perm_sign(perm) * s > 0;", 1, "mesh_fields"),
+    ("block of a negative voxel truncated", "k[0] >= 0 ? k[0] / kEdge : -((-k[0] + kEdge - 1) / kEdge)",
+     "k[0] / kEdge", 1, "mesh_fields"),
+    ("vertex at the edge midpoint", "m->vpos.push_back(P + t * (Q - P));", "m->vpos.push_back(P + 0.5 * (Q - P));",
+     1, "mesh_fields,mesh_plane,mesh_sphere"),
+]
+
+
+def _run_mutant(tmp_path, source, old, new, count, pins, output="libmutant.so"):
+    src = open(source).read()
+    assert src.count(old) == count, f"mutation target not found: {old!r}"
+    mutant = tmp_path / "mutant.cpp"
+    mutant.write_text(src.replace(old, new))
+    lib = oracle.build(str(mutant), str(tmp_path / output))
+    return subprocess.run([sys.executable, os.path.join(ROOT, "tests", "oracle_pins.py"), lib, pins],
+                          capture_output=True, text=True, timeout=300, cwd=ROOT)
+
+
+@pytest.mark.parametrize("name,old,new,count,pins", MESH_MUTATIONS, ids=[m[0] for m in MESH_MUTATIONS])
+def test_mesh_mutant_is_caught(tmp_path, name, old, new, count, pins):
+    proc = _run_mutant(tmp_path, oracle.MESH_SOURCE, old, new, count, pins, "libmeshmutant.so")
+    if proc.returncode != 0:
+        return                                     # the mutant crashed: caught
+    result = json.loads(proc.stdout.strip().splitlines()[-1])
+    caught = {p: f for p, f in result.items() if f}
+    assert caught, f"mutation '{name}' passed every pin: {result}"
 
 
 @pytest.mark.parametrize("name,old,new,count,pins", MUTATIONS, ids=[m[0] for m in MUTATIONS])
