@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -128,9 +129,40 @@ constexpr size_t kCounterBytes = sizeof(unsigned long long) * kReplicas * kCount
 static_assert(kCounterBytes % 16 == 0, "the frame table after the counters stays 16-byte aligned");
 }  // namespace
 
+// The scratch of tsdf_integrate_batch_noalloc: the owner update's per-call
+// work lists (counters, segments, run records, per-slot run counts, item
+// lists) for callers that cannot allocate.  One copy per GPU, held while the
+// library is loaded.  Host code never uses this name as an address: its
+// device address on each GPU comes from hipGetSymbolAddress (noalloc_base).
+static __device__ __align__(256) unsigned char scratch[TSDF_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_lock;
+void* g_scratch_base[kMaxDevices];   // `scratch` on device d, once looked up
+
+// The device address of `scratch` on device `dev` (looked up once per
+// device, with that device current); nullptr if the lookup fails.
+void* noalloc_base(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_lock);
+    if (g_scratch_base[dev]) return g_scratch_base[dev];
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return nullptr;
+    g_scratch_base[dev] = p;
+    return p;
+}
+}  // namespace
+
 struct tsdf_volume {
     tsdf_config cfg;
     tsdf_buffers buf;
+    int device;                 // the GPU current at tsdf_create (where the buffers live)
     unsigned int mask;
     unsigned int serial;        // allocate calls so far (selects the per-call counter set)
     int owner_grid;             // owner-update workgroups: as many as the device holds at once
@@ -403,6 +435,8 @@ tsdf_status tsdf_create(const tsdf_config* config, const tsdf_buffers* buffers, 
     h->cfg.table_entries = entries;
     h->buf = b;
     h->mask = (unsigned int)(entries - 1);
+    if (hipGetDevice(&h->device) != hipSuccess) h->device = 0;
+    (void)noalloc_base(h->device);   // the no-allocation entry point's scratch, looked up once per GPU
     h->owner_grid = owner_grid(config->occlusion == TSDF_OCCLUSION_REPROJECT);
     if (h->owner_grid <= 0) h->owner_grid = kOwnerGridDefault;
     if (!init_volume(h, true, static_cast<hipStream_t>(stream))) {
@@ -476,6 +510,44 @@ tsdf_status tsdf_integrate_batch(tsdf_volume* h, const tsdf_frame* frames, int32
 
 tsdf_status tsdf_integrate(tsdf_volume* h, const tsdf_frame* frame, void* stream) {
     return tsdf_integrate_batch(h, frame, 1, stream);
+}
+
+tsdf_status tsdf_integrate_batch_noalloc(tsdf_volume* h, const tsdf_frame* frames, int32_t n_frames, void* stream) {
+    if (!h) return TSDF_EINVAL;
+    if (n_frames > kArgFrames) return TSDF_ELIMIT;           // more would need the staged frame table
+    Batch b;
+    const tsdf_status st = batch_args(h, frames, n_frames, true, &b);
+    if (st != TSDF_OK || b.args.n == 0) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const VolumeArgs v = volume_args(h);
+    if (h->cfg.update_mode == TSDF_UPDATE_RAYS) {            // no work lists: nothing to place
+        const unsigned int serial = next_serial(h);
+        if (!launch_allocate(b.args, v, owner_args(h, serial), s, nullptr)) return TSDF_EHIP;
+        h->serial = serial;
+        return launch_update_rays(b.args, v, s, nullptr) ? TSDF_OK : TSDF_EHIP;
+    }
+    int64_t pixels = 0;
+    for (int32_t i = 0; i < n_frames; ++i) pixels += (int64_t)frames[i].width * frames[i].height;
+    // (the layout's per-partition capacities are 32-bit: size them only for
+    // pixel counts a configuration may state)
+    if (pixels > ((int64_t)1 << 28) ||
+        scratch_layout(h->cfg.table_entries, pixels).bytes > TSDF_NOALLOC_SCRATCH_BYTES)
+        return TSDF_ELIMIT;
+    void* base = noalloc_base(h->device);
+    if (!base) return TSDF_EHIP;
+    // an allocate still waiting for its update is dropped, as by any allocate
+    if (h->pending && !launch_discard(v, owner_args(h, h->serial), s, nullptr)) return TSDF_EHIP;
+    h->pending = false;
+    const unsigned int serial = next_serial(h);
+    const OwnerArgs own = owner_args_at(h, serial, base, pixels);
+    if (!launch_fresh_call(v, own, (unsigned long long)h->cfg.table_entries, s)) return TSDF_EHIP;
+    if (!launch_allocate(b.args, v, own, s, nullptr)) return TSDF_EHIP;
+    if (!launch_update_owner(b.args, v, own, h->owner_grid, s, nullptr)) return TSDF_EHIP;
+    // the volume's own work lists: ready for its next call, whose fresh
+    // blocks start after this call's
+    h->serial = serial;
+    const OwnerArgs mine = owner_args(h, next_serial(h));
+    return launch_hand_back(v, mine.fc + mine.parity, s) ? TSDF_OK : TSDF_EHIP;
 }
 
 tsdf_status tsdf_get_stats(tsdf_volume* h, tsdf_stats* out, void* stream) {
@@ -625,6 +697,7 @@ const char* tsdf_status_str(tsdf_status st) {
         case TSDF_EALIGN: return "TSDF_EALIGN";
         case TSDF_EHIP: return "TSDF_EHIP";
         case TSDF_ESMALL: return "TSDF_ESMALL";
+        case TSDF_ELIMIT: return "TSDF_ELIMIT";
     }
     return "TSDF_UNKNOWN";
 }

@@ -1210,6 +1210,16 @@ __global__ __launch_bounds__(kThreads) void k_zero_words(unsigned int* a, unsign
         a[i] = 0;
 }
 
+// The call's fresh-block start: pool indices from the block counter's
+// current value on have never been written by an update.
+__global__ void k_set_pool_start(FrameCounters* fc, const unsigned long long* counters,
+                                 unsigned long long capacity) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        const unsigned long long used = counters[kBlockCounter];
+        fc->pool_start = used < capacity ? used : capacity;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void k_zero_counters(unsigned long long* counters) {
     for (int i = threadIdx.x; i < kReplicas * kCounterWords; i += blockDim.x) counters[i] = 0;
 }
@@ -1315,6 +1325,24 @@ bool launch_init(const VolumeArgs& v, unsigned long long table_entries, bool who
     hipLaunchKernelGGL(k_fill_table, dim3(grid_for(table_entries)), dim3(kThreads), 0, s, (uint4*)v.table,
                        table_entries);
     hipLaunchKernelGGL(k_zero_counters, dim3(1), dim3(kThreads), 0, s, v.counters);
+    return launched();
+}
+
+bool launch_fresh_call(const VolumeArgs& v, const OwnerArgs& o, unsigned long long table_entries, hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(kThreads), 0, s, reinterpret_cast<unsigned int*>(o.fc),
+                       (unsigned long long)(2 * sizeof(FrameCounters) / 4));
+    hipLaunchKernelGGL(k_zero_words, dim3(grid_for(2 * table_entries)), dim3(kThreads), 0, s,
+                       reinterpret_cast<unsigned int*>(o.blk_count), 2 * table_entries);
+    hipLaunchKernelGGL(k_set_pool_start, dim3(1), dim3(64), 0, s, o.fc + o.parity,
+                       (const unsigned long long*)v.counters, v.capacity);
+    return launched();
+}
+
+bool launch_hand_back(const VolumeArgs& v, FrameCounters* next, hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(kThreads), 0, s, reinterpret_cast<unsigned int*>(next),
+                       (unsigned long long)(sizeof(FrameCounters) / 4));
+    hipLaunchKernelGGL(k_set_pool_start, dim3(1), dim3(64), 0, s, next, (const unsigned long long*)v.counters,
+                       v.capacity);
     return launched();
 }
 

@@ -47,6 +47,13 @@ bool launch_update_rays(const BatchArgs& b, const VolumeArgs& v, hipStream_t s, 
 // and (owner mode) the per-slot run counts and per-frame counters
 bool launch_init(const VolumeArgs& v, unsigned long long table_entries, bool whole_pool, const OwnerArgs* own,
                  hipStream_t s);
+// a call whose owner-mode work lists live in memory other than the volume's
+// scratch: clear its two per-call counter sets and per-slot run counts, and
+// set its fresh-block start to the block counter's value before the call
+bool launch_fresh_call(const VolumeArgs& v, const OwnerArgs& o, unsigned long long table_entries, hipStream_t s);
+// after such a call: leave the volume's own counter set `next` (the one the
+// volume's next call will use) as a call of its own would have
+bool launch_hand_back(const VolumeArgs& v, FrameCounters* next, hipStream_t s);
 // surface extraction (tsdf_mesh.hip): clears *counter, then counts every
 // triangle in it and writes those below max_triangles (key may be null)
 bool launch_mesh(const VolumeArgs& v, unsigned long long table_entries, unsigned long long* counter, float* pos,

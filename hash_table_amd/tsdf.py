@@ -18,7 +18,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libtsdf_hip.so")
 
-TSDF_OK, TSDF_EINVAL, TSDF_EALIGN, TSDF_EHIP, TSDF_ESMALL = 0, -1, -2, -3, -4
+TSDF_OK, TSDF_EINVAL, TSDF_EALIGN, TSDF_EHIP, TSDF_ESMALL, TSDF_ELIMIT = 0, -1, -2, -3, -4, -5
+TSDF_NOALLOC_SCRATCH_BYTES = 64 << 20
 TSDF_UPDATE_OWNER, TSDF_UPDATE_RAYS = 0, 1
 UPDATE_MODES = {"owner": TSDF_UPDATE_OWNER, "rays": TSDF_UPDATE_RAYS}
 TSDF_OCCLUSION_RAY, TSDF_OCCLUSION_REPROJECT = 0, 1
@@ -36,7 +37,7 @@ MB_LDS_DISTINCT, MB_LDS_RANDOM, MB_LDS_SAME, MB_LDS_GROUPS = 0, 1, 2, 3
 # every symbol the headers declare
 EXPORTS = [
     "tsdf_table_entries_for", "tsdf_counters_bytes", "tsdf_scratch_bytes", "tsdf_create", "tsdf_reset", "tsdf_allocate",
-    "tsdf_update", "tsdf_integrate", "tsdf_integrate_batch", "tsdf_allocate_batch",
+    "tsdf_update", "tsdf_integrate", "tsdf_integrate_batch", "tsdf_integrate_batch_noalloc", "tsdf_allocate_batch",
     "tsdf_update_batch",
     "tsdf_export_blocks", "tsdf_extract_mesh", "tsdf_get_stats", "tsdf_set_kernel_timing", "tsdf_kernel_times", "tsdf_destroy",
     "tsdf_status_str", "tsdf_mb_copy", "tsdf_mb_atomic_add_f32", "tsdf_mb_cas_u64", "tsdf_mb_lds_atomic",
@@ -102,6 +103,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         "tsdf_update": (I32, [P, ctypes.POINTER(tsdf_frame), P]),
         "tsdf_integrate": (I32, [P, ctypes.POINTER(tsdf_frame), P]),
         "tsdf_integrate_batch": (I32, [P, ctypes.POINTER(tsdf_frame), I32, P]),
+        "tsdf_integrate_batch_noalloc": (I32, [P, ctypes.POINTER(tsdf_frame), I32, P]),
         "tsdf_allocate_batch": (I32, [P, ctypes.POINTER(tsdf_frame), I32, P]),
         "tsdf_update_batch": (I32, [P, ctypes.POINTER(tsdf_frame), I32, P]),
         "tsdf_export_blocks": (I32, [P, P, P, P, P, P, P, I64, ctypes.POINTER(I64), P]),
@@ -189,6 +191,12 @@ def tsdf_integrate_batch(volume, frames, stream: int = 0, n: Optional[int] = Non
     arr = frame_array(frames)
     _check(load().tsdf_integrate_batch(volume, arr, len(frames) if n is None else n, ctypes.c_void_p(stream)),
            "tsdf_integrate_batch")
+
+
+def tsdf_integrate_batch_noalloc(volume, frames, stream: int = 0, n: Optional[int] = None) -> None:
+    arr = frame_array(frames)
+    _check(load().tsdf_integrate_batch_noalloc(volume, arr, len(frames) if n is None else n,
+                                               ctypes.c_void_p(stream)), "tsdf_integrate_batch_noalloc")
 
 
 def tsdf_allocate_batch(volume, frames, stream: int = 0, n: Optional[int] = None) -> None:

@@ -44,7 +44,8 @@ typedef enum {
     TSDF_EINVAL = -1,   /* invalid argument: null pointer, bad size or parameter */
     TSDF_EALIGN = -2,   /* a buffer is not 16-byte aligned */
     TSDF_EHIP = -3,     /* a HIP launch or copy failed */
-    TSDF_ESMALL = -4    /* the caller's output buffers are too small */
+    TSDF_ESMALL = -4,   /* the caller's output buffers are too small */
+    TSDF_ELIMIT = -5    /* the call needs more than tsdf_integrate_batch_noalloc's fixed scratch */
 } tsdf_status;
 
 /* Largest pool, in blocks; the pool index of a block must fit 32 bits with
@@ -223,6 +224,29 @@ tsdf_status tsdf_integrate(tsdf_volume* volume, const tsdf_frame* frame, void* s
  * pinned host memory the volume allocates on first use (released by
  * tsdf_destroy); TSDF_EHIP if that allocation or copy fails. */
 tsdf_status tsdf_integrate_batch(tsdf_volume* volume, const tsdf_frame* frames, int32_t n_frames, void* stream);
+
+/* tsdf_integrate_batch for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * it): the same kernels and the same result, but the owner update's per-call
+ * work lists live in a fixed scratch array inside the library, of
+ * TSDF_NOALLOC_SCRATCH_BYTES per GPU (held from the moment the library is
+ * loaded until the process ends), instead of the volume's scratch buffer.
+ * The call allocates nothing: no device, pinned or event memory, and no
+ * kernel timing (tsdf_set_kernel_timing does not cover it).
+ * Limits (TSDF_ELIMIT, nothing enqueued): at most 32 frames (their launch
+ * parameters travel in the kernel arguments), and in owner mode the work
+ * lists of the call must fit the array: tsdf_scratch_bytes of the volume's
+ * config with max_batch_pixels set to the call's total pixels, i.e. about
+ * 60 bytes per table entry plus 112 per pixel, at most
+ * TSDF_NOALLOC_SCRATCH_BYTES.  Ray-parallel volumes need no work lists.
+ * Every call on one GPU shares that GPU's array, which keeps the previous
+ * call's contents (each call clears what it needs): calls that overlap in
+ * time on one GPU, on any volume or stream, race and must not be issued.
+ * Mixing it with the other entry points on one volume is allowed: the
+ * volume's own scratch is left ready for its next call. */
+#define TSDF_NOALLOC_SCRATCH_BYTES (64u << 20)
+tsdf_status tsdf_integrate_batch_noalloc(tsdf_volume* volume, const tsdf_frame* frames, int32_t n_frames,
+                                         void* stream);
 
 /* The two halves of tsdf_integrate_batch.  In owner mode tsdf_update_batch
  * must directly follow tsdf_allocate_batch of identical frames, else

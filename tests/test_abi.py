@@ -59,8 +59,8 @@ def test_scratch_sizing():
 
 
 def test_status_strings():
-    assert [tsdf.tsdf_status_str(s) for s in (0, -1, -2, -3, -4, 7)] == [
-        "TSDF_OK", "TSDF_EINVAL", "TSDF_EALIGN", "TSDF_EHIP", "TSDF_ESMALL", "TSDF_UNKNOWN"]
+    assert [tsdf.tsdf_status_str(s) for s in (0, -1, -2, -3, -4, -5, 7)] == [
+        "TSDF_OK", "TSDF_EINVAL", "TSDF_EALIGN", "TSDF_EHIP", "TSDF_ESMALL", "TSDF_ELIMIT", "TSDF_UNKNOWN"]
 
 
 def _buffers(base=0x10000, step=0x100000):
@@ -108,6 +108,8 @@ def test_null_handle_calls():
     for fn in (tsdf.tsdf_allocate, tsdf.tsdf_update, tsdf.tsdf_integrate):
         with pytest.raises(tsdf.TsdfError):
             fn(None, f)
+    with pytest.raises(tsdf.TsdfError):
+        tsdf.tsdf_integrate_batch_noalloc(None, [f])
     with pytest.raises(tsdf.TsdfError):
         tsdf.tsdf_extract_mesh(None, 0, 0, 0)
     with pytest.raises(tsdf.TsdfError):
