@@ -28,7 +28,7 @@ constexpr int64_t kSegmentsPerPixel = 2;            // (wavefront, block) segmen
 // Owner-mode scratch layout: per-frame counters, per-table-entry arrays,
 // then the per-frame segment and record buffers (kParts partitions each).
 struct ScratchLayout {
-    size_t fc, desc, segs, recs, seg_list, blk_count, items, items_spill, item_of, rescan, bytes;
+    size_t fc, desc, segs, recs, units, seg_list, blk_count, items, items_spill, item_of, rescan, bytes;
     unsigned int item_part_cap, seg_part_cap, rec_part_cap;
 };
 
@@ -47,7 +47,9 @@ ScratchLayout scratch_layout(int64_t entries, int64_t frame_pixels) {
     o += sizeof(Segment) * (size_t)kParts * L.seg_part_cap;
     L.recs = o;
     o += sizeof(RunRecord) * (size_t)kParts * L.rec_part_cap;
-    L.seg_list = o;                   // 8-byte pieces
+    L.units = o;                      // 8-byte pieces
+    o += sizeof(uint2) * (size_t)kMaxUnits;
+    L.seg_list = o;
     o += sizeof(uint2) * (size_t)kParts * L.seg_part_cap;
     L.blk_count = o;
     o += 8 * (size_t)entries;
@@ -235,6 +237,8 @@ OwnerArgs owner_args_at(const tsdf_volume* h, unsigned int serial, void* scratch
     o.desc = reinterpret_cast<ItemDesc*>(base + L.desc);
     o.segs = reinterpret_cast<Segment*>(base + L.segs);
     o.recs = reinterpret_cast<RunRecord*>(base + L.recs);
+    o.units = reinterpret_cast<uint2*>(base + L.units);
+    o.unit_target = (unsigned int)std::min<int64_t>(kMaxUnits, 4 * (int64_t)std::max(1, h->owner_grid));
     o.seg_list = reinterpret_cast<uint2*>(base + L.seg_list);
     o.item_part_cap = L.item_part_cap;
     o.seg_part_cap = L.seg_part_cap;

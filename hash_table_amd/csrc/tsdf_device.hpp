@@ -135,7 +135,7 @@ struct __align__(16) ItemDesc {
     unsigned int seg_first;   // its first segment in the block-ordered segment list
     unsigned int seg_count;
     unsigned int slot;
-    unsigned int pad;
+    unsigned int units;       // work units the update splits the block's runs into (1: not split)
 };
 
 // Per-frame counters of the owner update, in the caller's scratch buffer,
@@ -167,10 +167,19 @@ struct FrameCounters {
     unsigned long long pool_start;
     unsigned int n_rescan;              // blocks whose runs did not fit (rescanned)
     unsigned int front, back;           // items placed from the front (big blocks) and from the back
-    unsigned int pad[23];
+    unsigned int n_extra;               // work units beyond each split block's first
+    unsigned int unit_runs;             // runs per work unit of a split block
+    unsigned int pad[21];
     unsigned int fetch[kXcds * kFetchStride];   // next item of XCD x at fetch[x * kFetchStride]
 };
 static_assert(sizeof(FrameCounters) % 128 == 0, "FrameCounters keeps the work counters in their own lines");
+
+// A block whose runs are many next to the call's total is split into work
+// units of unit_runs runs (at least kMinUnitRuns), each taken by its own
+// workgroup, which adds its sums into the pool with float atomics; the
+// extra units are listed (at most kMaxUnits of them) and taken first.
+constexpr unsigned int kMinUnitRuns = 256;
+constexpr unsigned int kMaxUnits = 8192;
 
 // Owner-update bookkeeping in the caller's scratch buffer.
 struct OwnerArgs {
@@ -184,6 +193,9 @@ struct OwnerArgs {
     Segment* segs;             // [kParts * seg_part_cap] allocate order
     uint2* seg_list;           // [kParts * seg_part_cap] (rec_base, block_off), grouped by block
     RunRecord* recs;           // [kParts * rec_part_cap] allocate order (read in place)
+    uint2* units;              // [kMaxUnits] (item, chunk >= 1) of split blocks
+    unsigned int unit_target;  // work units a call aims for (<= kMaxUnits): blocks with more
+                               // runs than the call's runs / unit_target are split
     unsigned int item_part_cap, seg_part_cap, rec_part_cap;
     unsigned int parity;       // call serial & 1
     int build_items;           // 0: ray-parallel update, nothing recorded

@@ -628,8 +628,12 @@ __global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerA
     partition_prefix(s_cnt, own.item_part_cap, fc.items_spill, s_pre);
     const unsigned int n = s_pre[kParts + 1];
     const unsigned int mean_runs = s_runs / max(n, 1u);
+    // runs per work unit: a block with more is split (the call's runs over
+    // unit_target units, so the units of all split blocks fit the list)
+    const unsigned int unit_runs = max(kMinUnitRuns, (s_runs + own.unit_target - 1) / max(own.unit_target, 1u));
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         fc.items_total = n;
+        fc.unit_runs = unit_runs;
         // this call's allocate has claimed its pool indices: the next call's
         // fresh blocks start where they end
         own.fc[own.parity ^ 1].pool_start = min(vol.counters[kBlockCounter], vol.capacity);
@@ -695,7 +699,21 @@ __global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerA
             d.seg_first = s_base + s_wave[wave] + x - cnt;
             d.seg_count = cnt;
             d.slot = slot;
-            d.pad = 0;
+            d.units = 1;
+            if (!(rc & kSegOverflow) && rc > unit_runs) {
+                // chunks 1.. of the block go to the list of extra units
+                // (their number over all blocks is at most the call's runs
+                // over unit_runs <= unit_target <= kMaxUnits)
+                const unsigned int extra = (rc + unit_runs - 1) / unit_runs - 1;
+                const unsigned int u0 = atomicAdd(&fc.n_extra, extra);
+                if (u0 + extra <= kMaxUnits) {
+                    for (unsigned int c = 1; c <= extra; ++c) own.units[u0 + c - 1] = make_uint2(j, c);
+                    d.units = extra + 1;
+                } else {                     // (cannot happen, see above) entries marked void
+                    for (unsigned int c = 1; c <= extra && u0 + c - 1 < kMaxUnits; ++c)
+                        own.units[u0 + c - 1] = make_uint2(0xFFFFFFFFu, 0u);
+                }
+            }
             own.desc[j] = d;
             own.item_of[slot] = j;
             if (rc & kSegOverflow) own.rescan[atomicAdd(&fc.n_rescan, 1u)] = j;
@@ -826,6 +844,27 @@ __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, 
     }
 }
 
+// The same for one work unit of a split block: other workgroups add to the
+// same voxels, so the sums go in with no-return float atomics (weights stay
+// exact: integer-valued floats far below 2^24).
+__device__ __forceinline__ void flush_atomic(OwnerLds& L, const VolumeArgs& vol, size_t base) {
+    for (int j = threadIdx.x; j < kBlockVoxels; j += kUpdateThreads) {
+        const unsigned long long tw = L.tw[sum_slot(j)];
+        const unsigned int cnt = (unsigned int)(tw >> kCountShift);
+        if (!cnt) continue;
+        const unsigned long long c = L.rgb[sum_slot(j)];
+        const long long tq = (long long)(tw & kTsdfMask) - ((long long)cnt << 25);
+        L.tw[sum_slot(j)] = 0;
+        L.rgb[sum_slot(j)] = 0;
+        const size_t off = base + j;
+        unsafeAtomicAdd(vol.tsdf + off, (float)tq * kTsdfUnit);
+        unsafeAtomicAdd(vol.weight + off, (float)cnt);
+        unsafeAtomicAdd(vol.r + off, (float)((unsigned int)c & 0x1FFFFFu) * kInv255);
+        unsafeAtomicAdd(vol.g + off, (float)((unsigned int)(c >> 21) & 0x1FFFFFu) * kInv255);
+        unsafeAtomicAdd(vol.b + off, (float)((unsigned int)(c >> 42) & 0x1FFFFFu) * kInv255);
+    }
+}
+
 // kReproject: the reprojection reading of the occlusion test (as in k_allocate).
 template <bool kReproject>
 __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
@@ -851,20 +890,39 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
     FrameCounters& fc = own.fc[own.parity];
     const unsigned int n_items = fc.items_total;
     const unsigned long long fresh_from = fc.pool_start;
+    // sdf / trunc in units of 2^-24: (sdf * (1/trunc)) * 2^24 rounds exactly
+    // as sdf * ((1/trunc) * 2^24) (scaling by a power of two is exact)
+    const float tsdf_scale = vol.inv_trunc * kTsdfScale;
     const unsigned int xcd = blockIdx.x % kXcds;
     unsigned int* fetch = fc.fetch + xcd * kFetchStride;
     unsigned int misses = 0;
+    // work: the extra units of split blocks first, then every block (a split
+    // block's own entry does its first unit)
+    const unsigned int n_extra = min(fc.n_extra, kMaxUnits);
+    const unsigned int unit_runs = fc.unit_runs;
 
     for (unsigned int k = 0;; ++k) {
         if (tid == 0) s_item[k & 1] = xcd + kXcds * atomicAdd(fetch, 1u);
         __syncthreads();                                     // also: LDS sums clear, frames loaded
-        const unsigned int it = s_item[k & 1];
-        if (it >= n_items) break;
+        const unsigned int wi = s_item[k & 1];
+        if (wi >= n_extra + n_items) break;
+        unsigned int it = wi - n_extra, chunk = 0;
+        if (wi < n_extra) {
+            const uint2 u = own.units[wi];
+            it = u.x;
+            chunk = u.y;
+            if (it >= n_items) continue;                     // a void entry
+        }
         const ItemDesc d = own.desc[it];
         if (d.rec_count & kSegOverflow) continue;            // rescanned (and its count cleared) later
-        if (tid == 0) own.blk_count[d.slot] = 0;
+        if (chunk >= d.units) continue;
+        if (chunk == 0 && tid == 0) own.blk_count[d.slot] = 0;
+        const bool split = d.units > 1;
+        // this unit's runs of the block, in block order
+        const unsigned int r_lo = split ? chunk * unit_runs : 0u;
+        const unsigned int r_hi = split ? min(d.rec_count, r_lo + unit_runs) : d.rec_count;
         const bool store = d.idx < vol.capacity;             // else refused a pool index: count, not store
-        bool fresh = d.idx >= fresh_from;                    // no update has written the block yet
+        bool fresh = !split && d.idx >= fresh_from;          // no update has written the block yet
         int bx, by, bz;
         unpack_key(d.key, bx, by, bz);
         const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
@@ -883,7 +941,8 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                 }
             }
             __syncthreads();
-            const unsigned int wr0 = s_off[0], wr1 = s_off[wn];
+            const unsigned int wr0 = max(s_off[0], r_lo), wr1 = min(s_off[wn], r_hi);
+            const bool past = s_off[wn] >= r_hi;             // (uniform) no later window holds this unit's runs
             for (unsigned int c0 = wr0; c0 < wr1; c0 += kChunkRuns) {
                 const unsigned int c1 = min(wr1, c0 + kChunkRuns);
                 // The chunk's runs go through LDS kSubRuns at a time: each
@@ -952,6 +1011,7 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                         const int d0 = (rr.meta >> 29) & 1u ? -1 : 1;
                         const int d1 = (rr.meta >> 30) & 1u ? -1 : 1;
                         const int d2 = (rr.meta >> 31) & 1u ? -1 : 1;
+                        const float f0 = (float)d0, f1 = (float)d1, f2 = (float)d2;
                         const int e = code_entry(code), cells = code_cells(code);
                         // the cell's centre in voxels, k + 1/2 per axis (exact:
                         // integers and halves), and its voxel within the block
@@ -960,33 +1020,41 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                         float x1 = (float)(lo1 + ((e >> 3) & 7)) + 0.5f;
                         float x2 = (float)(lo2 + (e >> 6)) + 0.5f;
                         int j = e;
-                        unsigned int ys = code_ysteps(code), zs = code_zsteps(code);
+                        const unsigned int ys = code_ysteps(code), zs = code_zsteps(code);
+                        // q counts the cells every active lane has done (the
+                        // same in all of them): step q's bits are tested
+                        // against one wavefront-uniform mask
                         for (int q = 0;;) {
                             float sdf;
                             if (kReproject ? centre_test_reproject_at(x0, x1, x2, dep, ax, s_proj[rf], vol.vs, vol.trunc, sdf)
                                            : centre_test_at(x0, x1, x2, dep, ax, vol.vs, vol.trunc, sdf)) {
-                                const unsigned int tq =
-                                    (unsigned int)(__float2int_rn((sdf * vol.inv_trunc) * kTsdfScale) + (1 << 25));
+                                const unsigned int tq = (unsigned int)(__float2int_rn(sdf * tsdf_scale) + (1 << 25));
                                 atomicAdd(L.tw + sum_slot(j), (1ull << kCountShift) + tq);
                                 atomicAdd(L.rgb + sum_slot(j), c);
                             }
+                            const unsigned int bit = 1u << q;
                             if (++q >= cells) break;
-                            const bool sy = ys & 1u, sz = zs & 1u;
-                            ys >>= 1;
-                            zs >>= 1;
-                            x0 = (sy || sz) ? x0 : x0 + (float)d0;
-                            x1 = sy ? x1 + (float)d1 : x1;
-                            x2 = sz ? x2 + (float)d2 : x2;
+                            const bool sy = (ys & bit) != 0u, sz = (zs & bit) != 0u;
+                            x0 = (sy || sz) ? x0 : x0 + f0;
+                            x1 = sy ? x1 + f1 : x1;
+                            x2 = sz ? x2 + f2 : x2;
                             j += sy ? 8 * d1 : (sz ? 64 * d2 : d0);
                         }
                     }
                     __syncthreads();                         // s_run is rewritten next
                 }
                 __syncthreads();
-                if (store) flush_owner(L, vol, base, fresh);
+                if (store) {
+                    if (split)
+                        flush_atomic(L, vol, base);
+                    else
+                        flush_owner(L, vol, base, fresh);
+                }
                 fresh = false;                               // a later pass adds to what this one wrote
-                __syncthreads();                             // also: the window may be reloaded
+                __syncthreads();
             }
+            __syncthreads();                                 // the window may be reloaded
+            if (past) break;
         }
     }
     const unsigned int c_miss = wave_sum(misses);

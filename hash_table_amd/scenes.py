@@ -35,6 +35,7 @@ import numpy as np
 __all__ = [
     "Frame", "Workload", "workload", "plane_frame", "random_frame",
     "frame_digest", "next_pow2", "WORKLOADS", "room_cell", "cell_name", "SWEEP_CELLS",
+    "load_factor_cell", "LOAD_FACTORS", "BENCH_CALLS",
 ]
 
 
@@ -477,6 +478,23 @@ SWEEP_CELLS = [("points", 160, 120, 131.25), ("points", 320, 240, 262.5), ("poin
                ("extent", 1280, 960, 525.0)]
 
 
+def load_factor_cell(blocks_total: List[int], target: float):
+    """The load-factor cells on the room640x480 sequence: pool 2^k (table
+    2^(k+1), so the table rule holds) and the longest frame prefix whose
+    block count (blocks_total[i]: blocks after frames 0..i, from the stored
+    oracle counts) stays within target * table entries.  Returns (pool
+    capacity, frames, achieved load factor)."""
+    k = 10
+    while blocks_total[0] > target * (1 << (k + 1)):
+        k += 1
+    cap = 1 << k
+    n = max(i + 1 for i, t in enumerate(blocks_total) if t <= target * 2 * cap)
+    return cap, n, blocks_total[n - 1] / (2 * cap)
+
+
+LOAD_FACTORS = (0.1, 0.25, 0.5)
+
+
 def _room1280_workload():
     return _room_workload(
         "room1280x720", 5, 1280, 720, 920.0, 300, (-6, -2, -6), (6, 2, 6),
@@ -579,3 +597,15 @@ def workload(name: str) -> Workload:
     if m:
         return room_cell(int(m.group(1)), int(m.group(2)), float(m.group(3)))
     raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)} and room<W>x<H>_f<fx>")
+
+
+# How the benchmark splits each workload into calls (tsdf_integrate_batch
+# of a call's frames): contiguous (first, end) frame ranges.  The stored
+# oracle counts hold the compulsory traffic of exactly these calls.
+BENCH_CALLS = {
+    "plane64x48": [(0, 1)],
+    "spherewall320x240": [(0, 10)],
+    "cube640x480": [(0, 1)],
+    "room640x480": [(0, 100)],
+    "room1280x720": [(0, 100), (100, 200), (200, 300)],
+}

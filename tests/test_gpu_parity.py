@@ -238,13 +238,7 @@ def _lf_case(target):
     """Pool 2^k (table 2^(k+1)) and the longest frame prefix of the room whose
     block count stays within target * table entries."""
     g = golden("room640x480")
-    totals = [f["blocks_total"] for f in g["frames"]]
-    k = 10
-    while totals[0] > target * (1 << (k + 1)):
-        k += 1
-    cap = 1 << k
-    n = max(i + 1 for i, t in enumerate(totals) if t <= target * 2 * cap)
-    return cap, n, totals[n - 1] / (2 * cap)
+    return scenes.load_factor_cell([f["blocks_total"] for f in g["frames"]], target)
 
 
 @pytest.mark.parametrize("mode", MODES)
