@@ -126,7 +126,6 @@ struct KernelClock {
 
 namespace {
 constexpr int kMoreFrames = kMaxBatch - kArgFrames;   // frames of a call beyond the kernel arguments
-constexpr int kStageSlots = 4;                        // pinned host slots staging them
 constexpr size_t kCounterBytes = sizeof(unsigned long long) * kReplicas * kCounterWords;
 static_assert(kCounterBytes % 16 == 0, "the frame table after the counters stays 16-byte aligned");
 }  // namespace
@@ -173,15 +172,6 @@ struct tsdf_volume {
     tsdf_frame last[TSDF_MAX_BATCH];
     KernelClock* clock;         // non-null while kernel timing is on
     LaunchTimer timer;
-    // Frames of a call beyond the kernel arguments go to the device table
-    // after the counters (tsdf_counters_bytes) by an asynchronous copy on
-    // the call's stream, from one of kStageSlots pinned host slots (made on
-    // first use); a slot is written again only once its last copy is done.
-    FrameArgs* stage;
-    hipEvent_t stage_done[kStageSlots];
-    int stage_events;           // events created
-    bool stage_used[kStageSlots];
-    int stage_next;
 };
 
 namespace {
@@ -346,32 +336,15 @@ tsdf_status batch_args(const tsdf_volume* h, const tsdf_frame* frames, int32_t n
     return TSDF_OK;
 }
 
-// Copy the frames beyond the kernel arguments to the device table, ahead of
-// the call's kernels on stream s.
+// Write the launch parameters of the frames beyond the kernel arguments to
+// the device table (after the statistics in the counters buffer), ahead of
+// the call's kernels on stream s: small kernels carry them in their own
+// arguments, so nothing is allocated and no host memory must outlive the call.
 tsdf_status stage_frames(tsdf_volume* h, Batch* b, hipStream_t s) {
     const int n_more = b->args.n - kArgFrames;
     if (n_more <= 0) return TSDF_OK;
-    if (!h->stage) {
-        void* p = nullptr;
-        if (hipHostMalloc(&p, sizeof(FrameArgs) * kMoreFrames * kStageSlots, hipHostMallocDefault) != hipSuccess)
-            return TSDF_EHIP;
-        h->stage = static_cast<FrameArgs*>(p);
-    }
-    while (h->stage_events < kStageSlots) {
-        if (hipEventCreateWithFlags(&h->stage_done[h->stage_events], hipEventDisableTiming) != hipSuccess)
-            return TSDF_EHIP;
-        ++h->stage_events;
-    }
-    const int k = h->stage_next;
-    if (h->stage_used[k] && hipEventSynchronize(h->stage_done[k]) != hipSuccess) return TSDF_EHIP;
-    FrameArgs* slot = h->stage + (size_t)k * kMoreFrames;
-    std::memcpy(slot, b->more, sizeof(FrameArgs) * (size_t)n_more);
     FrameArgs* table = reinterpret_cast<FrameArgs*>(static_cast<char*>(h->buf.counters) + kCounterBytes);
-    if (hipMemcpyAsync(table, slot, sizeof(FrameArgs) * (size_t)n_more, hipMemcpyHostToDevice, s) != hipSuccess)
-        return TSDF_EHIP;
-    if (hipEventRecord(h->stage_done[k], s) != hipSuccess) return TSDF_EHIP;
-    h->stage_used[k] = true;
-    h->stage_next = (k + 1) % kStageSlots;
+    if (!launch_store_frames(b->more, n_more, table, s)) return TSDF_EHIP;
     b->args.more = table;
     return TSDF_OK;
 }
@@ -518,13 +491,13 @@ tsdf_status tsdf_integrate(tsdf_volume* h, const tsdf_frame* frame, void* stream
 
 tsdf_status tsdf_integrate_batch_noalloc(tsdf_volume* h, const tsdf_frame* frames, int32_t n_frames, void* stream) {
     if (!h) return TSDF_EINVAL;
-    if (n_frames > kArgFrames) return TSDF_ELIMIT;           // more would need the staged frame table
     Batch b;
     const tsdf_status st = batch_args(h, frames, n_frames, true, &b);
     if (st != TSDF_OK || b.args.n == 0) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const VolumeArgs v = volume_args(h);
     if (h->cfg.update_mode == TSDF_UPDATE_RAYS) {            // no work lists: nothing to place
+        if (stage_frames(h, &b, s) != TSDF_OK) return TSDF_EHIP;
         const unsigned int serial = next_serial(h);
         if (!launch_allocate(b.args, v, owner_args(h, serial), s, nullptr)) return TSDF_EHIP;
         h->serial = serial;
@@ -539,6 +512,7 @@ tsdf_status tsdf_integrate_batch_noalloc(tsdf_volume* h, const tsdf_frame* frame
         return TSDF_ELIMIT;
     void* base = noalloc_base(h->device);
     if (!base) return TSDF_EHIP;
+    if (stage_frames(h, &b, s) != TSDF_OK) return TSDF_EHIP;
     // an allocate still waiting for its update is dropped, as by any allocate
     if (h->pending && !launch_discard(v, owner_args(h, h->serial), s, nullptr)) return TSDF_EHIP;
     h->pending = false;
@@ -685,11 +659,6 @@ tsdf_status tsdf_kernel_times(tsdf_volume* h, tsdf_kernel_time* out, int32_t max
 
 void tsdf_destroy(tsdf_volume* h) {
     if (!h) return;
-    for (int k = 0; k < h->stage_events; ++k) {
-        if (h->stage_used[k]) (void)hipEventSynchronize(h->stage_done[k]);   // no copy still reads the slot
-        (void)hipEventDestroy(h->stage_done[k]);
-    }
-    if (h->stage) (void)hipHostFree(h->stage);
     delete h->clock;
     delete h;
 }

@@ -1278,6 +1278,20 @@ __global__ __launch_bounds__(kThreads) void k_zero_words(unsigned int* a, unsign
         a[i] = 0;
 }
 
+// Launch parameters of up to kArgFrames frames, copied word by word from the
+// kernel arguments into the device frame table (frames beyond the kernel
+// arguments of a call's own kernels).
+struct FrameGroup {
+    FrameArgs f[kArgFrames];
+};
+
+__global__ __launch_bounds__(kThreads) void k_store_frames(FrameGroup g, FrameArgs* table, int n) {
+    constexpr int kWords = (int)(sizeof(FrameArgs) / 4);
+    const unsigned int* src = reinterpret_cast<const unsigned int*>(g.f);
+    unsigned int* dst = reinterpret_cast<unsigned int*>(table);
+    for (int i = threadIdx.x; i < n * kWords; i += blockDim.x) dst[i] = src[i];
+}
+
 // The call's fresh-block start: pool indices from the block counter's
 // current value on have never been written by an update.
 __global__ void k_set_pool_start(FrameCounters* fc, const unsigned long long* counters,
@@ -1393,6 +1407,16 @@ bool launch_init(const VolumeArgs& v, unsigned long long table_entries, bool who
     hipLaunchKernelGGL(k_fill_table, dim3(grid_for(table_entries)), dim3(kThreads), 0, s, (uint4*)v.table,
                        table_entries);
     hipLaunchKernelGGL(k_zero_counters, dim3(1), dim3(kThreads), 0, s, v.counters);
+    return launched();
+}
+
+bool launch_store_frames(const FrameArgs* frames, int n, FrameArgs* table, hipStream_t s) {
+    for (int i = 0; i < n; i += kArgFrames) {
+        FrameGroup g;
+        const int k = std::min(kArgFrames, n - i);
+        for (int j = 0; j < k; ++j) g.f[j] = frames[i + j];
+        hipLaunchKernelGGL(k_store_frames, dim3(1), dim3(kThreads), 0, s, g, table + i, k);
+    }
     return launched();
 }
 

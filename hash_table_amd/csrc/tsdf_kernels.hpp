@@ -47,6 +47,9 @@ bool launch_update_rays(const BatchArgs& b, const VolumeArgs& v, hipStream_t s, 
 // and (owner mode) the per-slot run counts and per-frame counters
 bool launch_init(const VolumeArgs& v, unsigned long long table_entries, bool whole_pool, const OwnerArgs* own,
                  hipStream_t s);
+// write the launch parameters of n frames into the device frame table, in
+// stream order (small kernels carrying them in their arguments)
+bool launch_store_frames(const FrameArgs* frames, int n, FrameArgs* table, hipStream_t s);
 // a call whose owner-mode work lists live in memory other than the volume's
 // scratch: clear its two per-call counter sets and per-slot run counts, and
 // set its fresh-block start to the block counter's value before the call

@@ -219,10 +219,9 @@ tsdf_status tsdf_integrate(tsdf_volume* volume, const tsdf_frame* frame, void* s
  * them one by one (the block set is the union, sums commute; which keys an
  * exhausted pool refuses may differ, their number does not), but each block
  * the batch touches is read and written once.  Frames may differ in size.
- * The launch parameters of frames beyond the 32nd are copied to the device
- * table in the counters buffer by an asynchronous copy on the stream, from
- * pinned host memory the volume allocates on first use (released by
- * tsdf_destroy); TSDF_EHIP if that allocation or copy fails. */
+ * The launch parameters of frames beyond the 32nd are written to the device
+ * table in the counters buffer by small kernels on the stream that carry
+ * them in their arguments (the library allocates nothing for them). */
 tsdf_status tsdf_integrate_batch(tsdf_volume* volume, const tsdf_frame* frames, int32_t n_frames, void* stream);
 
 /* tsdf_integrate_batch for callers that cannot allocate device memory
@@ -233,12 +232,11 @@ tsdf_status tsdf_integrate_batch(tsdf_volume* volume, const tsdf_frame* frames, 
  * loaded until the process ends), instead of the volume's scratch buffer.
  * The call allocates nothing: no device, pinned or event memory, and no
  * kernel timing (tsdf_set_kernel_timing does not cover it).
- * Limits (TSDF_ELIMIT, nothing enqueued): at most 32 frames (their launch
- * parameters travel in the kernel arguments), and in owner mode the work
- * lists of the call must fit the array: tsdf_scratch_bytes of the volume's
- * config with max_batch_pixels set to the call's total pixels, i.e. about
- * 60 bytes per table entry plus 112 per pixel, at most
- * TSDF_NOALLOC_SCRATCH_BYTES.  Ray-parallel volumes need no work lists.
+ * Limit (TSDF_ELIMIT, nothing enqueued): in owner mode the work lists of the
+ * call must fit the array: tsdf_scratch_bytes of the volume's config with
+ * max_batch_pixels set to the call's total pixels, i.e. about 60 bytes per
+ * table entry plus 112 per pixel, at most TSDF_NOALLOC_SCRATCH_BYTES.
+ * Ray-parallel volumes need no work lists.  Up to TSDF_MAX_BATCH frames.
  * Every call on one GPU shares that GPU's array, which keeps the previous
  * call's contents (each call clears what it needs): calls that overlap in
  * time on one GPU, on any volume or stream, race and must not be issued.
