@@ -302,10 +302,10 @@ __device__ __forceinline__ void setup_axis(float gA, float gB, int& k, int& s, f
 // Every field is computed for every pixel, whatever its class (no branches:
 // the lanes of a wavefront need no masking); a pixel whose class is not
 // kValid gets values that must not be used.
-__device__ __forceinline__ int setup_walk(BandWalk& w, float d, int u, int v, const FrameArgs& f,
+// xn = (u - cx) / fx and yn = (v - cy) / fy are the pixel ray's slopes
+// (callers that share them between pixels compute them once).
+__device__ __forceinline__ int setup_walk(BandWalk& w, float d, float xn, float yn, const FrameArgs& f,
                                           float trunc, float inv_vs) {
-    const float xn = ((float)u - f.cx) / f.fx;
-    const float yn = ((float)v - f.cy) / f.fy;
     const float z0 = d - trunc;
     const float z1 = d + trunc;
     const float a0 = xn * z0, a1 = yn * z0, a2 = z0;
@@ -337,6 +337,28 @@ __device__ __forceinline__ int setup_walk(BandWalk& w, float d, int u, int v, co
     if (!__builtin_isfinite(d) || !(d > 0.0f)) return kInvalid;
     if (d <= trunc) return kNear;
     return in_range ? kValid : kOutside;
+}
+__device__ __forceinline__ int setup_walk(BandWalk& w, float d, int u, int v, const FrameArgs& f,
+                                          float trunc, float inv_vs) {
+    return setup_walk(w, d, ((float)u - f.cx) / f.fx, ((float)v - f.cy) / f.fy, f, trunc, inv_vs);
+}
+
+// The lane's own bit of a wavefront lane mask, as its condition.
+__device__ __forceinline__ bool lane_on(unsigned long long mask) { return __builtin_amdgcn_inverse_ballot_w64(mask); }
+
+// x + x + (this lane's bit of mask): one add with the mask as carry-in.
+__device__ __forceinline__ unsigned int shift_in(unsigned int x, unsigned long long mask) {
+    unsigned int r;
+    unsigned long long carry_out;
+    asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(x), "s"(mask));
+    return r;
+}
+// x + (this lane's bit of mask), the same way
+__device__ __forceinline__ unsigned int count_in(unsigned int x, unsigned long long mask) {
+    unsigned int r;
+    unsigned long long carry_out;
+    asm("v_addc_co_u32_e64 %0, %1, %2, 0, %3" : "=v"(r), "=s"(carry_out) : "v"(x), "s"(mask));
+    return r;
 }
 
 // Occlusion and band test at the centre of the current cell.  sdf is the

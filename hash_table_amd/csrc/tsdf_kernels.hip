@@ -113,6 +113,7 @@ struct AllocLds {
     unsigned int hist[kProbeBins];
     unsigned int pmax;
     unsigned int cnt[6];
+    float xn[kTile], yn[kTile];                   // the tile's pixel-ray slopes per column and row
 };
 
 // A lane's runs since the last filing: slot q holds its q-th run (pend: a
@@ -275,16 +276,15 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, int lane, un
 }
 
 __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, unsigned int zp, unsigned int cp,
-                                             int itc, int x, int y, int z, int s0, int s1, int s2, AllocLds& L,
+                                             int n, int itc, int x, int y, int z, int s0, int s1, int s2, AllocLds& L,
                                              int lane, unsigned int part, const VolumeArgs& vol,
                                              const OwnerArgs& own, unsigned int depth_bits, unsigned int meta,
                                              unsigned int frame_hi, unsigned int& n_upd) {
-    // planes in walk order, bit j = the chunk's cell j: the kept plane's
-    // sentinel marks the n cells this lane walked; the step planes were
-    // shifted once per iteration
-    const int n = 31 - __clz(kp);
-    const unsigned int kf = n ? __builtin_bitreverse32(kp) >> ((unsigned int)(32 - n) & 31u) : 0u;
+    // planes in walk order, bit j = the chunk's cell j: every plane was
+    // shifted once per iteration (itc of them); the lane walked n cells and
+    // the bits after them are not read
     const unsigned int shp = (unsigned int)(32 - itc) & 31u;
+    const unsigned int kf = itc ? __builtin_bitreverse32(kp) >> shp : 0u;
     const unsigned int yf = itc ? __builtin_bitreverse32(yp) >> shp : 0u;
     const unsigned int zf = itc ? __builtin_bitreverse32(zp) >> shp : 0u;
     const unsigned int cf = itc ? __builtin_bitreverse32(cp) >> shp : 0u;
@@ -345,6 +345,12 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
     if (threadIdx.x < kProbeBins) L.hist[threadIdx.x] = 0;
     if (threadIdx.x < 6) L.cnt[threadIdx.x] = 0;
     if (threadIdx.x == 0) L.pmax = 0;
+    // the ray slopes of the tile's 16 columns and 16 rows (the same division
+    // every pixel of a column or row would do)
+    if (threadIdx.x < kTile)
+        L.xn[threadIdx.x] = ((float)(tu + (int)threadIdx.x) - f.cx) / f.fx;
+    else if (threadIdx.x < 2 * kTile)
+        L.yn[threadIdx.x - kTile] = ((float)(tv + (int)threadIdx.x - kTile) - f.cy) / f.fy;
     __syncthreads();
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -377,10 +383,12 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
     // stepping down or still: exactly, for any cell a key can hold).
     int s0, s1, s2;
     float b0, b1, b2, f0, f1, f2, h0, h1, h2, tm0, tm1, tm2, g0, g1, g2, i0, i1, i2;
-    bool alive;
+    // Lane flags are kept as wavefront lane masks (bit k: lane k) in scalar
+    // registers; `lane_on` turns a mask into the lane's own condition.
+    unsigned long long alive;                 // lanes whose walk goes on
     auto load_walk = [&](const BandWalk& w, bool valid) __attribute__((always_inline)) {
         // (a lane that is not valid never walks: its values go unused)
-        alive = valid;
+        alive = __builtin_amdgcn_ballot_w64(valid);
         s0 = w.s0; s1 = w.s1; s2 = w.s2;
         f0 = (float)s0; f1 = (float)s1; f2 = (float)s2;
         b0 = (float)(w.k0 + (s0 > 0)); b1 = (float)(w.k1 + (s1 > 0)); b2 = (float)(w.k2 + (s2 > 0));
@@ -391,31 +399,34 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
     };
     // One step of the walk (every lane; a finished walk does not move).  The
     // stepped axis is the one whose boundary comes first (ties: x, then y).
+    // The masks of the lanes that stepped, and of those that stepped along y
+    // and along z; bc the boundary crossed.
     struct Step {
-        bool more, e0, e1, a1, a2;
-        float bc;                              // the boundary the step crosses
+        unsigned long long more, e0, e1, a1, a2;
+        float bc;
     };
     auto step = [&]() __attribute__((always_inline)) {
         Step st;
         const float tmin = fminf(fminf(tm0, tm1), tm2);
-        st.more = alive && tmin <= 1.0f;
-        st.e0 = tm0 == tmin;
-        st.e1 = tm1 == tmin;
-        const bool a0 = st.more && st.e0;
-        st.a1 = st.more && !st.e0 && st.e1;
-        st.a2 = st.more && !st.e0 && !st.e1;
-        st.bc = pick3(st.e0, st.e1, b0, b1, b2);
-        const float fc = pick3(st.e0, st.e1, f0, f1, f2);
-        const float gc = pick3(st.e0, st.e1, g0, g1, g2);
-        const float ic = pick3(st.e0, st.e1, i0, i1, i2);
+        st.more = alive & __builtin_amdgcn_ballot_w64(tmin <= 1.0f);
+        st.e0 = __builtin_amdgcn_ballot_w64(tm0 == tmin);
+        st.e1 = __builtin_amdgcn_ballot_w64(tm1 == tmin);
+        const unsigned long long a0 = st.more & st.e0;
+        st.a1 = st.more & ~st.e0 & st.e1;
+        st.a2 = st.more & ~st.e0 & ~st.e1;
+        const bool e0 = lane_on(st.e0), e1 = lane_on(st.e1);
+        st.bc = pick3(e0, e1, b0, b1, b2);
+        const float fc = pick3(e0, e1, f0, f1, f2);
+        const float gc = pick3(e0, e1, g0, g1, g2);
+        const float ic = pick3(e0, e1, i0, i1, i2);
         const float bn = st.bc + fc;           // the new cell's next boundary
         const float tn = (bn - gc) * ic;
-        b0 = a0 ? bn : b0;
-        b1 = st.a1 ? bn : b1;
-        b2 = st.a2 ? bn : b2;
-        tm0 = a0 ? tn : tm0;
-        tm1 = st.a1 ? tn : tm1;
-        tm2 = st.a2 ? tn : tm2;
+        b0 = lane_on(a0) ? bn : b0;
+        b1 = lane_on(st.a1) ? bn : b1;
+        b2 = lane_on(st.a2) ? bn : b2;
+        tm0 = lane_on(a0) ? tn : tm0;
+        tm1 = lane_on(st.a1) ? tn : tm1;
+        tm2 = lane_on(st.a2) ? tn : tm2;
         alive = st.more;
         return st;
     };
@@ -463,13 +474,14 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
     // boundary split in two records of the same block: the update adds both.
     int x, y, z;                              // the chunk's first cell
     unsigned int kp, yp, zp, cp;              // its planes
+    unsigned int nc;                          // cells this lane walked in the chunk
     auto walk_chunk = [&](int done) __attribute__((always_inline)) {
         x = (int)(b0 + h0 - 0.5f);            // the current cell (exact: integers and halves)
         y = (int)(b1 + h1 - 0.5f);
         z = (int)(b2 + h2 - 0.5f);
         float sa = 0.f, lo = 0.f, hi = 0.f, dl0 = 0.f, dl1 = 0.f, dl2 = 0.f;
         float sdf0;
-        bool keep = test_sdf(sdf0);           // the exact test at the chunk's first cell
+        unsigned long long keep = __builtin_amdgcn_ballot_w64(test_sdf(sdf0));   // the exact test at the chunk's first cell
         if constexpr (!kReproject) {
             sa = sdf0;
             dl0 = f0 * ax.r2 * vs;            // f (R vs), exact: f is -1, 0 or 1
@@ -484,30 +496,31 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
             lo = trunc - m;
             hi = trunc + m;
         }
-        kp = 1u;                              // the kept plane starts with a sentinel bit
-        yp = zp = cp = 0u;
+        kp = yp = zp = cp = nc = 0u;
         // the safety bound on cells per walk limits the chunk (uniform)
         const int lim = min(kChunkCells, max_visits - done);
         int itc = 0;                          // iterations of this chunk (uniform)
         for (; itc < lim; ++itc) {
-            if (!wave_any(alive)) break;
-            kp = alive ? kp + kp + (keep ? 1u : 0u) : kp;
+            if (!alive) break;
+            nc = count_in(nc, alive);         // a lane still walking is at its cell itc
+            kp = shift_in(kp, keep);
             const Step st = step();
-            yp = yp + yp + (st.a1 ? 1u : 0u);
-            zp = zp + zp + (st.a2 ? 1u : 0u);
+            yp = shift_in(yp, st.a1);
+            zp = shift_in(zp, st.a2);
             // the step leaves the block iff the boundary it crosses is a block face
-            const bool cr = st.more && __builtin_amdgcn_fractf(st.bc * 0.125f) == 0.0f;
-            cp = cp + cp + (cr ? 1u : 0u);
+            const unsigned long long cr =
+                st.more & __builtin_amdgcn_ballot_w64(__builtin_amdgcn_fractf(st.bc * 0.125f) == 0.0f);
+            cp = shift_in(cp, cr);
             if constexpr (kReproject) {
-                keep = test();
+                keep = __builtin_amdgcn_ballot_w64(test());
             } else {
-                sa = sa - (st.e0 ? dl0 : (st.e1 ? dl1 : dl2));
+                sa = sa - (lane_on(st.e0) ? dl0 : (lane_on(st.e1) ? dl1 : dl2));
                 const float as = fabsf(sa);
-                keep = as <= lo;
-                const bool unsure = st.more && !keep && as <= hi;
-                if (wave_any(unsure)) {       // rare: some lane is within the margin
-                    const bool ex = test();
-                    keep = unsure ? ex : keep;
+                keep = __builtin_amdgcn_ballot_w64(as <= lo);
+                const unsigned long long unsure = st.more & ~keep & __builtin_amdgcn_ballot_w64(as <= hi);
+                if (unsure) {                 // rare: some lane is within the margin
+                    const unsigned long long ex = __builtin_amdgcn_ballot_w64(test());
+                    keep = (keep & ~unsure) | (ex & unsure);
                 }
             }
         }
@@ -515,9 +528,9 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
         // Its last iteration took one more step; that step's bits sit after
         // the lane's last cell and no run reads them.
         if (done + lim >= max_visits) {
-            const unsigned int cut = (unsigned int)__popcll(__ballot(alive));
+            const unsigned int cut = (unsigned int)__popcll(alive);
             if (cut && lane == 0) atomicAdd(L.cnt + 4, cut);
-            alive = false;
+            alive = 0;
         }
         return itc;
     };
@@ -526,11 +539,10 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
         // first done steps replayed (the empty asm keeps the compiler from
         // hoisting the set-up out of the loop and holding its results)
         float dr = depth;
-        int ur, vr;
-        thread_pixel(tu, tv, ur, vr);
-        asm volatile("" : "+v"(dr), "+v"(ur), "+v"(vr));
+        float xr = L.xn[(wave & 1) * 8 + (lane & 7)], yr = L.yn[(wave >> 1) * 8 + (lane >> 3)];
+        asm volatile("" : "+v"(dr), "+v"(xr), "+v"(yr));
         BandWalk w;                           // (a pixel outside the image has depth 0: invalid)
-        const int cls = setup_walk(w, dr, ur, vr, f, vol.trunc, vol.inv_vs);
+        const int cls = setup_walk(w, dr, xr, yr, f, vol.trunc, vol.inv_vs);
         load_walk(w, cls == kValid);
         if (done == 0) {
             // point classes, counted once
@@ -556,8 +568,8 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
         }
         for (int i = 0; i < done; ++i) step();
         const int itc = walk_chunk(done);
-        const bool go_on = wave_any(alive);
-        cut_and_file(kp, yp, zp, cp, itc, x, y, z, (meta >> 29) & 1u ? -1 : 1, (meta >> 30) & 1u ? -1 : 1,
+        const bool go_on = alive != 0;
+        cut_and_file(kp, yp, zp, cp, (int)nc, itc, x, y, z, (meta >> 29) & 1u ? -1 : 1, (meta >> 30) & 1u ? -1 : 1,
                      (meta >> 31) & 1u ? -1 : 1, L, lane, part, vol, own, depth_bits, meta, frame_hi, n_upd);
         if (!go_on) break;
     }
