@@ -22,7 +22,7 @@ namespace {
 constexpr int kOwnerGridDefault = 2048;              // owner-update workgroups if the occupancy query fails
 constexpr int64_t kDefaultFramePixels = 1 << 20;    // owner-mode record buffers, per call
 constexpr int64_t kRunsPerPixel = 4;                // record capacity per pixel (a room frame needs ~2.7)
-constexpr int64_t kSegmentsPerPixel = 2;            // (wavefront, block) segments per pixel: a room
+constexpr int64_t kSegmentsPerPixel = 2;            // (filing, block) segments per pixel: a room
                                                     //   frame needs ~0.15, coarse 160 x 120 ones ~0.9
 
 // Owner-mode scratch layout: per-frame counters, per-table-entry arrays,

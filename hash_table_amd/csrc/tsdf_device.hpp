@@ -140,8 +140,8 @@ struct __align__(16) ItemDesc {
 
 // Per-frame counters of the owner update, in the caller's scratch buffer,
 // one set per frame parity.  Items and run records are reserved in
-// kParts partitions (wavefront w uses partition w mod kParts) so that no
-// single counter takes every wavefront's atomic.  The update hands blocks
+// kParts partitions (allocate workgroup w uses partition w mod kParts) so
+// that no single counter takes every workgroup's atomic.  The update hands blocks
 // out through one work counter per XCD, each in its own 128-byte line.
 constexpr int kParts = 64;
 constexpr int kXcds = 8;

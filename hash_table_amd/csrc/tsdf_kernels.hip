@@ -80,36 +80,37 @@ __device__ __forceinline__ void flush_hist(const unsigned int* s_hist, const uns
     if (t == kProbeBins && *s_pmax) atomicMax(c + kProbeMax, (unsigned long long)*s_pmax);
 }
 
-// order the wavefront's LDS accesses (LDS operations of one wavefront
-// complete in order once issued; this keeps the compiler from moving them)
-__device__ __forceinline__ void wave_lds_fence() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
-
 // ---------------------------------------------------------------------------
 // allocate.  Each lane walks its ray in chunks of up to kChunkCells cells and
 // cuts each chunk into runs, one per block the walk crosses; a lane holds
 // its runs with a kept voxel in kSlots register slots.  Full slots (or the
-// end of the chunk) are filed for the whole wavefront at once: the run keys
-// go into a per-wavefront LDS hash set, whose per-key run counter hands each
-// run its rank among the key's runs; one lane per distinct key probes the
-// global table and reserves the key's segment of run records; every lane
-// then writes the records of its own runs at the key's base + rank.  Also
-// counts the point classes and the kept (point, voxel) pairs.
+// end of the chunk) are filed for the whole workgroup (the 16 x 16 tile) at
+// once: the run keys go into an LDS hash set, whose per-key run counter
+// hands each run its rank among the key's runs; one thread per distinct key
+// probes the global table and adds the key's runs to its block counter, one
+// reservation takes the filing's segments (one per distinct key) and
+// records, and every lane then writes the records of its own runs at the
+// key's base + rank.  Neighbouring rays cross the same few blocks, so a
+// workgroup's filing has few distinct keys and each segment holds many runs.
+// Also counts the point classes and the kept (point, voxel) pairs.
 // ---------------------------------------------------------------------------
 constexpr int kSlots = 4;                         // runs a lane holds between filings
-constexpr int kSetCap = kSlots * 64;              // per-wavefront LDS set: room for every run of a filing
+constexpr int kSetCap = kSlots * kThreads;        // LDS set: room for every run of a filing
+constexpr int kSetBits = 10;
+static_assert(kSetCap == 1 << kSetBits, "set_slot yields kSetBits bits");
 constexpr unsigned int kNoBase = 0xFFFFFFFFu;     // runs not recorded (block rescanned)
 constexpr unsigned int kNoKeyBase = 0xFFFFFFFEu;  // runs of a key the full table refused
 
 struct AllocLds {
-    unsigned long long skey[kWaves][kSetCap];     // set: key (empty: all ones),
-    unsigned int scnt[kWaves][kSetCap];           //   its runs; after the reservation, its first record
-    unsigned char sslot[kWaves][kSetCap];         // set slots of the distinct keys, in insertion order
-    unsigned long long scode[kWaves][kSlots][64]; // the lanes' run codes, held here while the keys are filed
-    unsigned int nuniq[kWaves];
-    unsigned int nrec[kWaves];                    // records of a filing round, claimed so far
+    unsigned long long skey[kSetCap];             // set: key (empty: all ones),
+    unsigned int scnt[kSetCap];                   //   its runs; after the reservation, its first record
+    unsigned short sslot[kSetCap];                // set slots of the distinct keys, in insertion order
+    unsigned long long scode[kSlots][kThreads];   // the lanes' run codes, held here while the keys are filed
+    unsigned long long r0;                        // the filing's reservation: first segment << 32 | first record
+    unsigned int nuniq;                           // distinct keys of the filing
+    unsigned int nrun;                            // its runs
+    unsigned int nrec;                            // records handed to its keys so far
+    unsigned int votes[3];                        // workgroup_any, in rotation
     unsigned int hist[kProbeBins];
     unsigned int pmax;
     unsigned int cnt[6];
@@ -127,157 +128,180 @@ struct RunSlots {
 // Home slot of a block key in the LDS set (multiply-xor of the key's halves).
 __device__ __forceinline__ unsigned int set_slot(unsigned long long key) {
     const unsigned int lo = (unsigned int)key, hi = (unsigned int)(key >> 32);
-    return ((lo * 0x9E3779B1u) ^ (hi * 0x85EBCA77u)) >> 24;
+    return ((lo * 0x9E3779B1u) ^ (hi * 0x85EBCA77u)) >> (32 - kSetBits);
 }
-static_assert(kSetCap == 256, "set_slot yields 8 bits");
 
-// File the wavefront's pending runs (see above).  depth and meta: this
-// lane's point, for the records of its runs.  Must be called by the whole
-// wavefront.
-__device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, int lane, unsigned int part,
-                                          const VolumeArgs& vol, const OwnerArgs& own, unsigned int depth,
-                                          unsigned int meta, unsigned int frame_hi) {
-    bool any_pend = false;
-#pragma unroll
-    for (int q = 0; q < kSlots; ++q) any_pend = any_pend || S.pend[q];
-    if (!__any(any_pend)) return;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    unsigned long long* skey = L.skey[wave];
-    unsigned int* scnt = L.scnt[wave];
-    unsigned char* sslot = L.sslot[wave];
-    for (int i = lane; i < kSetCap; i += 64) {
-        skey[i] = kEmptyKey;
-        scnt[i] = 0;
-    }
-    if (lane == 0) L.nuniq[wave] = 0;
-    wave_lds_fence();
+// Whether p holds in any thread of the workgroup (one barrier).  Every
+// thread calls it with the same rnd, which it advances: call k votes in word
+// k mod 3 and clears the word of call k - 1 (read by every thread before
+// this call's barrier; written again only after the next call's).
+__device__ __forceinline__ bool workgroup_any(bool p, AllocLds& L, unsigned int& rnd) {
+    const unsigned int r = rnd % 3u;
+    if (__ballot(p) && (threadIdx.x & 63) == 0) L.votes[r] = 1u;
+    __syncthreads();
+    const bool any = L.votes[r] != 0u;
+    if (threadIdx.x == 0) L.votes[(r + 2u) % 3u] = 0u;
+    ++rnd;
+    return any;
+}
+
+// File the workgroup's pending runs (see above).  depth and meta: this
+// thread's point, for the records of its runs.  Must be called by the whole
+// workgroup after a barrier; the LDS set is empty on entry and again once the
+// next barrier has passed.
+__device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, unsigned int part, const VolumeArgs& vol,
+                                          const OwnerArgs& own, unsigned int depth, unsigned int meta,
+                                          unsigned int frame_hi) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // de-duplicate: each pending run finds (or enters) its key in the set
     // and takes a rank among the key's runs
-    unsigned int hr[kSlots];                      // per run: set slot | rank << 8
+    unsigned int hr[kSlots];                      // per run: set slot | rank << kSetBits
+    unsigned int wave_runs = 0;
 #pragma unroll
     for (int q = 0; q < kSlots; ++q) {
         hr[q] = 0;
-        if (!__any(S.pend[q])) continue;
+        const unsigned long long pm = __ballot(S.pend[q]);
+        if (!pm) continue;
+        wave_runs += (unsigned int)__popcll(pm);
         if (S.pend[q]) {
             const unsigned long long key = S.key[q];
             unsigned int h = set_slot(key);
             for (;;) {     // at most kSetCap distinct keys: the probe always finds room
-                const unsigned long long prev = atomicCAS(&skey[h], kEmptyKey, key);
+                const unsigned long long prev = atomicCAS(&L.skey[h], kEmptyKey, key);
                 if (prev == kEmptyKey) {
-                    sslot[atomicAdd(&L.nuniq[wave], 1u)] = (unsigned char)h;
+                    L.sslot[atomicAdd(&L.nuniq, 1u)] = (unsigned short)h;
                     break;
                 }
                 if (prev == key) break;
                 h = (h + 1) & (kSetCap - 1);
             }
-            hr[q] = h | (atomicAdd(&scnt[h], 1u) << 8);
-            L.scode[wave][q][lane] = S.code[q];
+            hr[q] = h | (atomicAdd(&L.scnt[h], 1u) << kSetBits);
+            L.scode[q][tid] = S.code[q];
         }
     }
-    wave_lds_fence();
-    const int nu = (int)L.nuniq[wave];
+    if (wave_runs && lane == 0) atomicAdd(&L.nrun, wave_runs);
+    __syncthreads();
+    const unsigned int nu = L.nuniq;
+    if (!nu) return;                              // (uniform) nothing pending: the set is still empty
     const unsigned long long below = (1ull << lane) - 1ull;
-    FrameCounters* fc = own.fc + own.parity;         // owner mode only
-    for (int d0 = 0; d0 < nu; d0 += 64) {           // wavefront-uniform: 64 distinct keys at a time
-        const int d = d0 + lane;
+    FrameCounters* fc = own.fc + own.parity;      // owner mode only
+    // one reservation for the filing: a segment per distinct key (key d
+    // takes the d-th) and a record per run (its return is awaited only
+    // where the segments are written)
+    unsigned long long r0 = 0;
+    if (own.build_items && tid == 0 && nu)
+        r0 = atomicAdd(&fc->part[part].segrec, ((unsigned long long)nu << 32) | L.nrun);
+    for (unsigned int d0 = 0; d0 < nu; d0 += kThreads) {   // workgroup-uniform: kThreads keys at a time
+        const unsigned int d = d0 + (unsigned int)tid;
         const bool has = d < nu;
-        unsigned int h = 0, slot = kNoSlot;
-        bool won = false;
-        if (has) {
-            h = sslot[d];
-            unsigned int probes;
-            slot = insert_key(vol, skey[h], won, probes);
-            hist_add(L.hist, &L.pmax, probes);
-        }
-        claim_pool_indices(vol, won, slot);
-        if (!own.build_items) continue;             // the ray-parallel update needs nothing more
-        // Segments and records: one reservation in the partition for the
-        // whole wavefront and, in the same round trip, one add per block on
-        // its counter (segments << 32 | runs).  The wavefront that finds a
-        // block's counter at zero is the first to touch it in this call and
-        // lists it for the update (the update zeroes the counter when it has
-        // finished the block); its new blocks take item numbers in the
-        // partition with one atomic.
-        const bool rsv = has && slot != kNoSlot;
-        const unsigned int runs = rsv ? scnt[h] : 0u;
-        // the key's runs within the wavefront's share of records (disjoint
-        // ranges; their order does not matter)
-        if (lane == 0) L.nrec[wave] = 0;
-        wave_lds_fence();
-        const unsigned int roff = rsv ? atomicAdd(&L.nrec[wave], runs) : 0u;
-        wave_lds_fence();
-        const unsigned int total = L.nrec[wave];
-        const unsigned long long rm = __ballot(rsv);
-        unsigned long long bc = 0, r0 = 0;
-        if (rsv) bc = atomicAdd(own.blk_count + slot, (1ull << 32) | runs);
-        if (rm && lane == 0) r0 = atomicAdd(&fc->part[part].segrec, ((unsigned long long)__popcll(rm) << 32) | total);
-        r0 = read_lane0(r0);
-        const bool first = rsv && bc == 0;
-        const unsigned long long fm = __ballot(first);
-        if (fm) {
-            unsigned int ib = 0;
-            if (lane == 0) ib = atomicAdd(&fc->part[part].items, (unsigned int)__popcll(fm));
-            ib = read_lane0(ib);
-            if (first) {
-                const unsigned int k = ib + (unsigned int)__popcll(fm & below);
-                if (k < own.item_part_cap)
-                    own.items[(size_t)part * own.item_part_cap + k] = slot;
-                else                                 // beyond the partition's share (rare)
-                    own.items_spill[atomicAdd(&fc->items_spill, 1u)] = slot;
+        unsigned int h = 0, slot = kNoSlot, runs = 0, roff = 0;
+        unsigned long long bc = 0;
+        if (d0 + (unsigned int)wave * 64u < nu) {           // (wavefront-uniform) this wavefront holds keys
+            bool won = false;
+            if (has) {
+                h = L.sslot[d];
+                unsigned int probes;
+                slot = insert_key(vol, L.skey[h], won, probes);
+                hist_add(L.hist, &L.pmax, probes);
+            }
+            claim_pool_indices(vol, won, slot);
+            if (own.build_items) {
+                // Each block's counter (segments << 32 | runs) takes one add
+                // per filing.  The workgroup that finds it at zero is the
+                // first to touch the block in this call and lists it for the
+                // update (the update zeroes the counter when it has finished
+                // the block); new blocks take item numbers in the partition
+                // with one atomic per wavefront.
+                const bool rsv = has && slot != kNoSlot;
+                if (has) runs = L.scnt[h];
+                if (rsv) {
+                    roff = atomicAdd(&L.nrec, runs);            // disjoint ranges; their order does not matter
+                    bc = atomicAdd(own.blk_count + slot, (1ull << 32) | runs);
+                }
+                const bool first = rsv && bc == 0;
+                const unsigned long long fm = __ballot(first);
+                if (fm) {
+                    unsigned int ib = 0;
+                    if (lane == 0) ib = atomicAdd(&fc->part[part].items, (unsigned int)__popcll(fm));
+                    ib = read_lane0(ib);
+                    if (first) {
+                        const unsigned int k = ib + (unsigned int)__popcll(fm & below);
+                        if (k < own.item_part_cap)
+                            own.items[(size_t)part * own.item_part_cap + k] = slot;
+                        else                                 // beyond the partition's share (rare)
+                            own.items_spill[atomicAdd(&fc->items_spill, 1u)] = slot;
+                    }
+                }
             }
         }
-        unsigned int rbase = kNoKeyBase;             // the full table refused the key: its kept visits are lost
-        if (rsv) {
-            const unsigned int seg = (unsigned int)(r0 >> 32) + (unsigned int)__popcll(rm & below);
-            const unsigned int rec = (unsigned int)r0 + roff;
+        if (!own.build_items) continue;                      // the ray-parallel update needs nothing more
+        if (d0 == 0 && tid == 0) L.r0 = r0;
+        __syncthreads();
+        if (has) {
+            const unsigned long long rr = L.r0;
+            const unsigned int seg = (unsigned int)(rr >> 32) + d;
+            const unsigned int rec = (unsigned int)rr + roff;
             Segment* segs = own.segs + (size_t)part * own.seg_part_cap;
-            if (seg < own.seg_part_cap && (unsigned long long)rec + runs <= own.rec_part_cap) {
-                Segment sg;
+            Segment sg;
+            sg.slot = kNoSlot;                               // void unless the key's runs are recorded
+            sg.rec_base = 0;
+            sg.block_off = 0;
+            sg.seg_pos = 0;
+            unsigned int rbase;
+            if (slot == kNoSlot) {
+                rbase = kNoKeyBase;                          // the full table refused the key: its kept visits are lost
+            } else if (seg < own.seg_part_cap && (unsigned long long)rec + runs <= own.rec_part_cap) {
                 sg.slot = slot;
                 sg.rec_base = part * own.rec_part_cap + rec;
                 sg.block_off = (unsigned int)bc & ~kSegOverflow;
                 sg.seg_pos = (unsigned int)(bc >> 32);
-                segs[seg] = sg;
                 rbase = sg.rec_base;
-            } else {                                 // out of space: the update rescans the block
-                if (seg < own.seg_part_cap) {        // the placing pass reads every reserved segment
-                    Segment sg;
-                    sg.slot = kNoSlot;
-                    sg.rec_base = 0;
-                    sg.block_off = 0;
-                    sg.seg_pos = 0;
-                    segs[seg] = sg;
-                }
+            } else {                                         // out of space: the update rescans the block
                 atomicOr(own.blk_count + slot, (unsigned long long)kSegOverflow);
                 rbase = kNoBase;
             }
+            if (seg < own.seg_part_cap) segs[seg] = sg;      // the placing pass reads every reserved segment
+            L.scnt[h] = rbase;                               // the key's runs are counted: keep its base instead
         }
-        if (has) scnt[h] = rbase;                    // the key's runs are counted: keep its base instead
     }
-    if (!own.build_items) return;
-    wave_lds_fence();
-    // every lane: the records of its runs
+    __syncthreads();
+    if (own.build_items) {
+        // every lane: the records of its runs
 #pragma unroll
-    for (int q = 0; q < kSlots; ++q) {
-        if (!S.pend[q]) continue;
-        const unsigned int b = scnt[hr[q] & 255u];
-        const unsigned long long code = L.scode[wave][q][lane];
-        if (b == kNoKeyBase) {
-            atomicAdd(L.cnt + 5, (unsigned int)code_kept(code));   // rare: counted at once
-        } else if (b != kNoBase) {
-            RunRecord r;
-            r.depth = depth;
-            r.meta = meta;
-            r.code_lo = (unsigned int)code;
-            r.code_hi = (unsigned int)(code >> 32) | frame_hi;
-            own.recs[b + (hr[q] >> 8)] = r;
+        for (int q = 0; q < kSlots; ++q) {
+            if (!S.pend[q]) continue;
+            const unsigned int b = L.scnt[hr[q] & (kSetCap - 1)];
+            const unsigned long long code = L.scode[q][tid];
+            if (b == kNoKeyBase) {
+                atomicAdd(L.cnt + 5, (unsigned int)code_kept(code));   // rare: counted at once
+            } else if (b != kNoBase) {
+                RunRecord r;
+                r.depth = depth;
+                r.meta = meta;
+                r.code_lo = (unsigned int)code;
+                r.code_hi = (unsigned int)(code >> 32) | frame_hi;
+                own.recs[b + (hr[q] >> kSetBits)] = r;
+            }
         }
+        __syncthreads();
+    }
+    // empty the set for the next filing (which starts after a barrier)
+    for (unsigned int d = (unsigned int)tid; d < nu; d += kThreads) {
+        const unsigned int h = L.sslot[d];
+        L.skey[h] = kEmptyKey;
+        L.scnt[h] = 0;
+    }
+    if (tid == 0) {
+        L.nuniq = 0;
+        L.nrun = 0;
+        L.nrec = 0;
     }
 }
 
 __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, unsigned int zp, unsigned int cp,
                                              int n, int itc, int x, int y, int z, int s0, int s1, int s2, AllocLds& L,
-                                             int lane, unsigned int part, const VolumeArgs& vol,
+                                             unsigned int& rnd, unsigned int part, const VolumeArgs& vol,
                                              const OwnerArgs& own, unsigned int depth_bits, unsigned int meta,
                                              unsigned int frame_hi, unsigned int& n_upd) {
     // planes in walk order, bit j = the chunk's cell j: every plane was
@@ -290,8 +314,8 @@ __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, u
     const unsigned int cf = itc ? __builtin_bitreverse32(cp) >> shp : 0u;
     // cut into runs: a run ends at a cell whose step leaves the block, or
     // at the lane's last cell of the chunk; up to kSlots runs per lane
-    // between filings
-    for (int j0 = 0; __any(j0 < n);) {
+    // between filings (workgroup-wide: every thread takes part in each)
+    for (int j0 = 0; workgroup_any(j0 < n, L, rnd);) {
         RunSlots S;
 #pragma unroll
         for (int q = 0; q < kSlots; ++q) {
@@ -323,7 +347,7 @@ __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, u
                 j0 += (int)len;
             }
         }
-        file_runs(S, L, lane, part, vol, own, depth_bits, meta, frame_hi);
+        file_runs(S, L, part, vol, own, depth_bits, meta, frame_hi);
     }
 }
 
@@ -344,7 +368,17 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
     if (!workgroup_tile(f, blockIdx.x - fi * B.tile_grid, tu, tv)) return;
     if (threadIdx.x < kProbeBins) L.hist[threadIdx.x] = 0;
     if (threadIdx.x < 6) L.cnt[threadIdx.x] = 0;
-    if (threadIdx.x == 0) L.pmax = 0;
+    if (threadIdx.x < 3) L.votes[threadIdx.x] = 0;
+    if (threadIdx.x == 0) {
+        L.pmax = 0;
+        L.nuniq = 0;
+        L.nrun = 0;
+        L.nrec = 0;
+    }
+    for (int i = threadIdx.x; i < kSetCap; i += kThreads) {
+        L.skey[i] = kEmptyKey;
+        L.scnt[i] = 0;
+    }
     // the ray slopes of the tile's 16 columns and 16 rows (the same division
     // every pixel of a column or row would do)
     if (threadIdx.x < kTile)
@@ -365,12 +399,12 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
     const unsigned int depth_bits = __float_as_uint(depth);
     const unsigned int frame_hi = ((unsigned int)fi >> 5) << (kFrameHighShift - 32);   // into the code's top bits
     unsigned int n_upd = 0;
-    // this wavefront's reservations: partitions in turn as if the call's
+    // this workgroup's reservations: partitions in turn as if the call's
     // frames were laid end to end by their tile counts (numbering by launch
     // index instead, every frame would start at a multiple of 8 workgroups
     // and the first tiles of many small frames would all fill the same few)
     const unsigned int wg = blockIdx.x - (unsigned int)fi * (unsigned int)B.tile_grid;
-    const unsigned int part = (((unsigned int)fi * (unsigned int)f.n_tiles + wg) * kWaves + wave) % kParts;
+    const unsigned int part = ((unsigned int)fi * (unsigned int)f.n_tiles + wg) % kParts;
     const int max_visits = f.max_visits;
     const float vs = vol.vs, trunc = vol.trunc;
     const DepthAxis ax = depth_axis(f);
@@ -534,44 +568,53 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
         }
         return itc;
     };
+    // The workgroup goes through the chunks together (its filings are
+    // collective); a wavefront whose walks have all ended skips the walk.
+    bool wave_on = true;
+    unsigned int rnd = 0;                     // workgroup_any's count (uniform)
     for (int done = 0;; done += kChunkCells) {
-        // the walk's state for this chunk: set up from the pixel, then the
-        // first done steps replayed (the empty asm keeps the compiler from
-        // hoisting the set-up out of the loop and holding its results)
-        float dr = depth;
-        float xr = L.xn[(wave & 1) * 8 + (lane & 7)], yr = L.yn[(wave >> 1) * 8 + (lane >> 3)];
-        asm volatile("" : "+v"(dr), "+v"(xr), "+v"(yr));
-        BandWalk w;                           // (a pixel outside the image has depth 0: invalid)
-        const int cls = setup_walk(w, dr, xr, yr, f, vol.trunc, vol.inv_vs);
-        load_walk(w, cls == kValid);
-        if (done == 0) {
-            // point classes, counted once
-            const unsigned int c_valid = (unsigned int)__popcll(__ballot(cls == kValid));
-            const unsigned int c_near = (unsigned int)__popcll(__ballot(cls == kNear));
-            const unsigned int c_oor = (unsigned int)__popcll(__ballot(cls == kOutside));
-            if (lane == 0) {
-                if (c_valid) atomicAdd(L.cnt + 0, c_valid);
-                if (c_near) atomicAdd(L.cnt + 1, c_near);
-                if (c_oor) atomicAdd(L.cnt + 2, c_oor);
-            }
-            // what the update needs of this point besides the run codes:
-            // colour (when the frame has it), frame of the batch and the
-            // directions of the stepping axes
-            if (cls == kValid) {
-                if (own.build_items && f.rgb) {
-                    const uint8_t* c = f.rgb + 3 * (size_t)pix;
-                    meta = (unsigned int)c[0] | ((unsigned int)c[1] << 8) | ((unsigned int)c[2] << 16);
+        int itc = 0;
+        kp = yp = zp = cp = nc = 0u;
+        x = y = z = 0;
+        if (wave_on) {
+            // the walk's state for this chunk: set up from the pixel, then the
+            // first done steps replayed (the empty asm keeps the compiler from
+            // hoisting the set-up out of the loop and holding its results)
+            float dr = depth;
+            float xr = L.xn[(wave & 1) * 8 + (lane & 7)], yr = L.yn[(wave >> 1) * 8 + (lane >> 3)];
+            asm volatile("" : "+v"(dr), "+v"(xr), "+v"(yr));
+            BandWalk w;                           // (a pixel outside the image has depth 0: invalid)
+            const int cls = setup_walk(w, dr, xr, yr, f, vol.trunc, vol.inv_vs);
+            load_walk(w, cls == kValid);
+            if (done == 0) {
+                // point classes, counted once
+                const unsigned int c_valid = (unsigned int)__popcll(__ballot(cls == kValid));
+                const unsigned int c_near = (unsigned int)__popcll(__ballot(cls == kNear));
+                const unsigned int c_oor = (unsigned int)__popcll(__ballot(cls == kOutside));
+                if (lane == 0) {
+                    if (c_valid) atomicAdd(L.cnt + 0, c_valid);
+                    if (c_near) atomicAdd(L.cnt + 1, c_near);
+                    if (c_oor) atomicAdd(L.cnt + 2, c_oor);
                 }
-                meta |= (((unsigned int)fi & 31u) << 24) | (w.s0 < 0 ? 1u << 29 : 0u) | (w.s1 < 0 ? 1u << 30 : 0u) |
-                        (w.s2 < 0 ? 1u << 31 : 0u);
+                // what the update needs of this point besides the run codes:
+                // colour (when the frame has it), frame of the batch and the
+                // directions of the stepping axes
+                if (cls == kValid) {
+                    if (own.build_items && f.rgb) {
+                        const uint8_t* c = f.rgb + 3 * (size_t)pix;
+                        meta = (unsigned int)c[0] | ((unsigned int)c[1] << 8) | ((unsigned int)c[2] << 16);
+                    }
+                    meta |= (((unsigned int)fi & 31u) << 24) | (w.s0 < 0 ? 1u << 29 : 0u) | (w.s1 < 0 ? 1u << 30 : 0u) |
+                            (w.s2 < 0 ? 1u << 31 : 0u);
+                }
             }
+            for (int i = 0; i < done; ++i) step();
+            itc = walk_chunk(done);
         }
-        for (int i = 0; i < done; ++i) step();
-        const int itc = walk_chunk(done);
-        const bool go_on = alive != 0;
+        wave_on = alive != 0;
         cut_and_file(kp, yp, zp, cp, (int)nc, itc, x, y, z, (meta >> 29) & 1u ? -1 : 1, (meta >> 30) & 1u ? -1 : 1,
-                     (meta >> 31) & 1u ? -1 : 1, L, lane, part, vol, own, depth_bits, meta, frame_hi, n_upd);
-        if (!go_on) break;
+                     (meta >> 31) & 1u ? -1 : 1, L, rnd, part, vol, own, depth_bits, meta, frame_hi, n_upd);
+        if (!workgroup_any(wave_on, L, rnd)) break;
     }
 
     const unsigned int c_upd = wave_sum(n_upd);
