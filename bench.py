@@ -115,6 +115,10 @@ def load_calls():
 # carries their digest; after any change the field is null until re-measured.
 MEASURED_TRAFFIC = {
     # (kernel, workload, most frames per call, update mode): (bytes per launch, source digest)
+    ("k_allocate", "room640x480", 128, "owner"): (1550696035, "915cb804f562dd8b"),
+    ("k_place_items", "room640x480", 128, "owner"): (6607236, "915cb804f562dd8b"),
+    ("k_place_segments", "room640x480", 128, "owner"): (273203122, "915cb804f562dd8b"),
+    ("k_update_owner", "room640x480", 128, "owner"): (1646373359, "915cb804f562dd8b"),
 }
 
 
@@ -164,9 +168,14 @@ def walk_ops(frames):
 # ---------------------------------------------------------------------------
 # the device: exclusivity, clocks, temperatures (sysfs; no GPU call)
 # ---------------------------------------------------------------------------
+TELEMETRY = True      # --no-telemetry: no amd-smi (e.g. under a profiler, whose preload reaches child processes)
+
+
 def _amd_smi(*args):
     """amd-smi's JSON output (run as a child process), or None."""
     import subprocess
+    if not TELEMETRY:
+        return None
     try:
         out = subprocess.run(["amd-smi", *args, "--json"], capture_output=True, text=True, timeout=30)
         text = out.stdout
@@ -533,7 +542,11 @@ def main():
                     help="refuse to run when another process holds the GPU")
     ap.add_argument("--sweep", action="store_true", help="also run the sweep cells (gated on stored counts)")
     ap.add_argument("--sweep-reps", type=int, default=20)
+    ap.add_argument("--no-telemetry", action="store_true",
+                    help="no amd-smi calls (exclusivity, clocks, temperatures), e.g. under rocprofv3")
     args = ap.parse_args()
+    global TELEMETRY
+    TELEMETRY = not args.no_telemetry
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the sharding design is described in DESIGN.md)", file=sys.stderr)

@@ -183,7 +183,6 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, unsigned int
     if (wave_runs && lane == 0) atomicAdd(&L.nrun, wave_runs);
     __syncthreads();
     const unsigned int nu = L.nuniq;
-    if (!nu) return;                              // (uniform) nothing pending: the set is still empty
     const unsigned long long below = (1ull << lane) - 1ull;
     FrameCounters* fc = own.fc + own.parity;      // owner mode only
     // one reservation for the filing: a segment per distinct key (key d
