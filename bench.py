@@ -672,21 +672,26 @@ def main():
         kt[name] = {"launches": v["launches"], "avg_us": round(v["total_ms"] * 1e3 / v["launches"], 3),
                     "share_of_kernel_time": round(v["total_ms"] / total_ms, 4)}
     out["kernel_times"] = kt
-    # roofline of the dominant kernel: the method's per-frame bytes over the
-    # frames its launch covers, against HBM; the ALU model beside it
-    per_launch = {"k_allocate": (fb_a, cb_a), "k_update_owner": (fb_u, cb_u)}
-    dom = max((k for k in per_launch if k in ktimes), key=lambda k: ktimes[k]["total_ms"])
+    # roofline of the dominant kernel against HBM, the ALU model beside it.
+    # Allocate: the method's per-frame bytes over the frames its launch
+    # covers.  Update: a batched call reads and writes each touched voxel once
+    # for all its frames, so its per-frame bytes (every frame's own
+    # read-modify-write) would exceed what the launch must move; it takes the
+    # call's compulsory bytes instead.
+    per_launch = {"k_allocate": fb_a, "k_update_owner": cb_u if cc else None}
+    dom = max((k for k in per_launch if k in ktimes and per_launch[k] is not None),
+              key=lambda k: ktimes[k]["total_ms"])
     launches = ktimes[dom]["launches"]
     avg_s = ktimes[dom]["total_ms"] * 1e-3 / launches
     launches_per_step = len(calls)                    # launches of each kernel per step
-    alg = per_launch[dom][0] / launches_per_step
+    alg = per_launch[dom] / launches_per_step
     achieved = alg / avg_s / 1e9
     out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                        "traffic": measured_traffic(dom, wl.name, args.batch, "owner"),
                        "algorithmic_bytes_per_launch": int(alg), "avg_launch_us": round(avg_s * 1e6, 3),
-                       "bytes": "per frame 4 P + 16 B_t + 16 B_n (allocate) / 7 P + 16 B_t + 40 U (update), "
-                                "summed over the launch's frames"}
+                       "bytes": "allocate: per frame 4 P + 16 B_t + 16 B_n, summed over the launch's frames; "
+                                "update: per call 7 P + 16 B_call + 20 U_fresh + 40 U_old"}
     ops = walk_ops(frames_of) / launches_per_step
     out["roofline_alu"] = {"kernel": "k_allocate", "bound": "alu",
                            "achieved": round(ops / (ktimes["k_allocate"]["total_ms"] * 1e-3 /

@@ -24,6 +24,8 @@ constexpr int64_t kDefaultFramePixels = 1 << 20;    // owner-mode record buffers
 constexpr int64_t kRunsPerPixel = 4;                // record capacity per pixel (a room frame needs ~2.7)
 constexpr int64_t kSegmentsPerPixel = 2;            // (filing, block) segments per pixel: a room
                                                     //   frame needs ~0.15, coarse 160 x 120 ones ~0.9
+constexpr int64_t kTilePixels = 256;                // an allocate workgroup's tile: it reserves in one
+                                                    //   partition, which holds at least a tile's share
 
 // Owner-mode scratch layout: per-frame counters, per-table-entry arrays,
 // then the per-frame segment and record buffers (kParts partitions each).
@@ -36,8 +38,9 @@ ScratchLayout scratch_layout(int64_t entries, int64_t frame_pixels) {
     ScratchLayout L;
     const int64_t px = frame_pixels > 0 ? frame_pixels : kDefaultFramePixels;
     L.item_part_cap = (unsigned int)std::max<int64_t>(64, entries / (kParts / 2));
-    L.seg_part_cap = (unsigned int)((kSegmentsPerPixel * px + kParts - 1) / kParts);
-    L.rec_part_cap = (unsigned int)((kRunsPerPixel * px + kParts - 1) / kParts);
+    const int64_t part_px = std::max<int64_t>((px + kParts - 1) / kParts, kTilePixels);
+    L.seg_part_cap = (unsigned int)(kSegmentsPerPixel * part_px);
+    L.rec_part_cap = (unsigned int)(kRunsPerPixel * part_px);
     size_t o = 0;
     L.fc = o;                         // 16-byte aligned pieces first
     o += 2 * sizeof(FrameCounters);

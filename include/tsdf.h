@@ -178,7 +178,8 @@ size_t tsdf_counters_bytes(void);
 
 /* Size of the scratch buffer a configuration needs (0 for TSDF_UPDATE_RAYS):
  * about 60 bytes per table entry plus 112 bytes per pixel of max_batch_pixels
- * (run records and their grouping by block).  0 for a NULL or invalid config. */
+ * (run records and their grouping by block; at least 16,384 pixels' worth).
+ * 0 for a NULL or invalid config. */
 size_t tsdf_scratch_bytes(const tsdf_config* config);
 
 /* Validate the configuration and buffers, then enqueue the initialisation of

@@ -43,7 +43,8 @@ def test_table_sizing_rule():
 
 def test_scratch_sizing():
     def expect(entries, px):
-        seg_part, rec_part = -(-2 * px // 64), -(-4 * px // 64)      # 2 segments, 4 runs per pixel
+        part_px = max(-(-px // 64), 256)                            # a partition holds at least a 16 x 16 tile
+        seg_part, rec_part = 2 * part_px, 4 * part_px                 # 2 segments, 4 runs per pixel
         item_part = max(64, entries // 32)
         counters = 64 * 128 + 128 + 8 * 32 * 4                      # per frame parity: partitions, totals, XCD fetch
         units = 8 * 8192                                              # split-block work units

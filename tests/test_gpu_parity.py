@@ -73,6 +73,20 @@ def test_sphere_wall_parity(name, mode):
     assert_parity(st, coords, arrays, o)
 
 
+@pytest.mark.parametrize("name", ["plane64x48", "spherewall320x240", "cube640x480"])
+def test_no_rescans_with_record_buffers_sized_for_the_call(name):
+    """Record buffers sized for exactly the call's pixels (as the benchmark
+    sizes them; small frames fill few of the record partitions, one per
+    16 x 16 tile): every run is recorded, no block is rescanned."""
+    wl = scenes.workload(name)
+    frames = list(wl.frames())
+    px = sum(f.width * f.height for f in frames)
+    _, st, coords, arrays, o = run_both(frames, wl.voxel_size, wl.trunc, wl.pool_capacity, batch=len(frames),
+                                        max_batch_pixels=px)
+    assert st["fallback_blocks"] == 0
+    assert_parity(st, coords, arrays, o)
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_cube_contention_parity(mode):
     wl = scenes.workload("cube640x480")
