@@ -115,7 +115,8 @@ __device__ __forceinline__ int record_frame(unsigned int meta, unsigned long lon
     return (int)(((meta >> 24) & 31u) | ((unsigned int)(code >> kFrameHighShift) << 5));
 }
 
-// A wavefront's runs through one block, as recorded by allocate.  One
+// One filing's runs through one block (an allocate workgroup's tile), as
+// recorded by allocate.  One
 // 64-bit atomic on the block's counter (segments << 32 | runs) gives both
 // the segment's position among the block's segments and its first run's
 // position among the block's runs, so in segment order block_off is the

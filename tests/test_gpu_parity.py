@@ -273,7 +273,7 @@ def test_load_factor_parity(target, mode):
     ha = st["probe_hist_alloc"]
     mean_a = float((ha * bins).sum() / ha.sum())
     # the histogram counts every probe sequence (one per distinct key and
-    # wavefront): at least one slot each, and at most the longest sequence
+    # workgroup filing): at least one slot each, and at most the longest sequence
     # the final layout allows
     disp = table_displacements(table, o.block_coords())
     say(f"  allocate probes: mean {mean_a:.3f} (Knuth's insertion expectation "
