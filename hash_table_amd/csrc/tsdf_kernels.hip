@@ -1062,10 +1062,13 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                         const unsigned long long c = (unsigned long long)(rr.meta & 0xFFu) |
                                                      ((unsigned long long)((rr.meta >> 8) & 0xFFu) << 21) |
                                                      ((unsigned long long)((rr.meta >> 16) & 0xFFu) << 42);
-                        const int d0 = (rr.meta >> 29) & 1u ? -1 : 1;
-                        const int d1 = (rr.meta >> 30) & 1u ? -1 : 1;
-                        const int d2 = (rr.meta >> 31) & 1u ? -1 : 1;
-                        const float f0 = (float)d0, f1 = (float)d1, f2 = (float)d2;
+                        // the axis directions, as voxel-index steps (a step
+                        // along x, y or z adds d0, d0 + dy or d0 + dz) and
+                        // as floats
+                        const bool n0 = (rr.meta >> 29) & 1u, n1 = (rr.meta >> 30) & 1u, n2 = (rr.meta >> 31) & 1u;
+                        const int d0 = n0 ? -1 : 1;
+                        const int dy = (n1 ? -8 : 8) - d0, dz = (n2 ? -64 : 64) - d0;
+                        const float f0 = n0 ? -1.0f : 1.0f, f1 = n1 ? -1.0f : 1.0f, f2 = n2 ? -1.0f : 1.0f;
                         const int e = code_entry(code), cells = code_cells(code);
                         // the cell's centre in voxels, k + 1/2 per axis (exact:
                         // integers and halves), and its voxel within the block
@@ -1076,9 +1079,8 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                         int j = e;
                         const unsigned int ys = code_ysteps(code), zs = code_zsteps(code);
                         // q counts the cells every active lane has done (the
-                        // same in all of them): step q's bits are tested
-                        // against one wavefront-uniform mask
-                        for (int q = 0;;) {
+                        // same in all of them, a scalar)
+                        for (int q = 0; q < cells; ++q) {
                             float sdf;
                             if (kReproject ? centre_test_reproject_at(x0, x1, x2, dep, ax, s_proj[rf], vol.vs, vol.trunc, sdf)
                                            : centre_test_at(x0, x1, x2, dep, ax, vol.vs, vol.trunc, sdf)) {
@@ -1086,13 +1088,18 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                                 atomicAdd(L.tw + sum_slot(j), (1ull << kCountShift) + tq);
                                 atomicAdd(L.rgb + sum_slot(j), c);
                             }
-                            const unsigned int bit = 1u << q;
-                            if (++q >= cells) break;
-                            const bool sy = (ys & bit) != 0u, sz = (zs & bit) != 0u;
-                            x0 = (sy || sz) ? x0 : x0 + f0;
-                            x1 = sy ? x1 + f1 : x1;
-                            x2 = sz ? x2 + f2 : x2;
-                            j += sy ? 8 * d1 : (sz ? 64 * d2 : d0);
+                            // the step after cell q: bit q of the planes (after
+                            // the run's last cell both are 0, an x step whose
+                            // cell is never used).  The coordinates move by
+                            // exactly 0 or +-1, so the fused multiply-add rounds
+                            // nothing.
+                            const int by = (int)__builtin_amdgcn_ubfe(ys, (unsigned int)q, 1u);
+                            const int bz = (int)__builtin_amdgcn_ubfe(zs, (unsigned int)q, 1u);
+                            const int bx = 1 - by - bz;
+                            x0 = __builtin_fmaf((float)bx, f0, x0);
+                            x1 = __builtin_fmaf((float)by, f1, x1);
+                            x2 = __builtin_fmaf((float)bz, f2, x2);
+                            j += d0 + by * dy + bz * dz;
                         }
                     }
                     __syncthreads();                         // s_run is rewritten next
