@@ -1231,12 +1231,62 @@ __global__ __launch_bounds__(kRescanThreads) void k_update_rescan(BatchArgs B, V
 // ray-parallel update: walk, test, look the block up once per block run of
 // the ray, add with five no-return f32 atomics into the SoA pool.
 // ---------------------------------------------------------------------------
+// Per-wavefront staging of block-index lookups: a small LDS hash map from
+// block key to pool index.  A lane entering a block takes the index from the
+// map; when the key is not there yet, the lanes that need it in the same
+// step enter it with an LDS compare-exchange, the one that entered it looks
+// it up in the table, and after a wavefront fence every one of them reads
+// the index.  A wavefront's rays cross a few blocks, so most runs need no
+// table probe at all.  A full map (more than kLookupCap distinct keys in a
+// wavefront) sends the lane to the table directly.
+constexpr int kLookupCap = 64;
+
+struct LookupLds {
+    unsigned long long key[kWaves][kLookupCap];
+    unsigned int idx[kWaves][kLookupCap];
+};
+
+__device__ __forceinline__ unsigned int staged_lookup(LookupLds& M, int wave, const VolumeArgs& vol,
+                                                      unsigned long long key, unsigned int* s_hist,
+                                                      unsigned int* s_pmax) {
+    unsigned long long* mk = M.key[wave];
+    unsigned int* mi = M.idx[wave];
+    unsigned int h = set_slot(key) & (kLookupCap - 1), n = 0;
+    bool won = false, found = false;
+    for (; n < (unsigned int)kLookupCap; ++n) {
+        const unsigned long long prev = atomicCAS(&mk[h], kEmptyKey, key);
+        if (prev == kEmptyKey) {
+            won = true;
+            break;
+        }
+        if (prev == key) {
+            found = true;
+            break;
+        }
+        h = (h + 1) & (kLookupCap - 1);
+    }
+    unsigned int idx = kNoIndex;
+    if (won || !found) {                     // the entering lane, or a full map: the table
+        unsigned int probes;
+        idx = lookup_key(vol, key, probes);
+        hist_add(s_hist, s_pmax, probes);
+        if (won) mi[h] = idx;
+    }
+    // the entries written in this step are visible to the whole wavefront
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (found) idx = mi[h];
+    return idx;
+}
+
 __global__ __launch_bounds__(kThreads) void k_update_rays(BatchArgs B, VolumeArgs vol) {
     const int fi = blockIdx.x / B.tile_grid;
     const FrameArgs f = batch_frame(B, fi);
     __shared__ unsigned int s_hist[kProbeBins];
     __shared__ unsigned int s_pmax;
     __shared__ unsigned int s_miss;
+    __shared__ LookupLds M;
     int tu, tv;
     if (!workgroup_tile(f, blockIdx.x - fi * B.tile_grid, tu, tv)) return;
     if (threadIdx.x < kProbeBins) s_hist[threadIdx.x] = 0;
@@ -1244,8 +1294,10 @@ __global__ __launch_bounds__(kThreads) void k_update_rays(BatchArgs B, VolumeArg
         s_pmax = 0;
         s_miss = 0;
     }
+    for (int i = threadIdx.x; i < kWaves * kLookupCap; i += kThreads) (&M.key[0][0])[i] = kEmptyKey;
     __syncthreads();
 
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int u, v;
     thread_pixel(tu, tv, u, v);
     BandWalk w;
@@ -1273,10 +1325,8 @@ __global__ __launch_bounds__(kThreads) void k_update_rays(BatchArgs B, VolumeArg
                               : centre_test(w, f, vol.vs, vol.trunc, sdf)) {
                 const unsigned long long key = block_key(w.k0, w.k1, w.k2);
                 if (key != cur) {
-                    unsigned int probes;
-                    idx = lookup_key(vol, key, probes);
+                    idx = staged_lookup(M, wave, vol, key, s_hist, &s_pmax);
                     cur = key;
-                    hist_add(s_hist, &s_pmax, probes);
                 }
                 if (idx != kNoIndex) {
                     const size_t off = (size_t)idx * kBlockVoxels + voxel_in_block(w.k0, w.k1, w.k2);
