@@ -460,6 +460,21 @@ def test_random_frames_parity(seed, W, H, mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+def test_filing_with_many_distinct_blocks(mode):
+    """Wide-angle rays at random depths 1-10 m: the rays of one 16 x 16 tile
+    cross ~900 distinct blocks, so a single workgroup filing holds far more
+    than 256 distinct keys (it takes them 256 at a time)."""
+    frames = [scenes.random_frame(seed, W=16, H=16, depth_range=(1.0, 10.0), fx=4.0, translation_scale=0.3)
+              for seed in (11, 12)]
+    frames.append(scenes.random_frame(13, W=32, H=32, depth_range=(1.0, 10.0), fx=8.0, translation_scale=0.3))
+    _, st, coords, arrays, o = run_both(frames[:1], 0.01, 0.04, 1 << 16, mode=mode)
+    assert st["pool_used"] > 800                 # one tile: its filings pass 256 keys at a time
+    assert_parity(st, coords, arrays, o)
+    _, st, coords, arrays, o = run_both(frames, 0.01, 0.04, 1 << 16, mode=mode, batch=3)
+    assert_parity(st, coords, arrays, o)
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_long_walks_parity(mode):
     """Bands many voxels deep, so walks run through several of allocate's
     31-cell chunks: every chunk after the first is filed separately and
