@@ -531,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
         }
         kp = yp = zp = cp = nc = 0u;
         // the safety bound on cells per walk limits the chunk (uniform)
-        const int lim = min(kChunkCells, max_visits - done);
+        const int lim = __builtin_amdgcn_readfirstlane(min(kChunkCells, max_visits - done));
         int itc = 0;                          // iterations of this chunk (uniform)
         for (; itc < lim; ++itc) {
             if (!alive) break;
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
             if constexpr (kReproject) {
                 keep = __builtin_amdgcn_ballot_w64(test());
             } else {
-                sa = sa - (lane_on(st.e0) ? dl0 : (lane_on(st.e1) ? dl1 : dl2));
+                sa = sa - pick3(lane_on(st.e0), lane_on(st.e1), dl0, dl1, dl2);
                 const float as = fabsf(sa);
                 keep = __builtin_amdgcn_ballot_w64(as <= lo);
                 const unsigned long long unsure = st.more & ~keep & __builtin_amdgcn_ballot_w64(as <= hi);
