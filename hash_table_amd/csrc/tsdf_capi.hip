@@ -30,7 +30,7 @@ constexpr int64_t kTilePixels = 256;                // an allocate workgroup's t
 // Owner-mode scratch layout: per-frame counters, per-table-entry arrays,
 // then the per-frame segment and record buffers (kParts partitions each).
 struct ScratchLayout {
-    size_t fc, desc, segs, recs, units, seg_list, blk_count, items, items_spill, item_of, rescan, bytes;
+    size_t fc, desc, segs, recs, units, seg_list, blk_count, items, items_spill, seg_first_of, rescan, bytes;
     unsigned int item_part_cap, seg_part_cap, rec_part_cap;
 };
 
@@ -60,7 +60,7 @@ ScratchLayout scratch_layout(int64_t entries, int64_t frame_pixels) {
     o += 4 * (size_t)kParts * L.item_part_cap;
     L.items_spill = o;
     o += 4 * (size_t)entries;
-    L.item_of = o;
+    L.seg_first_of = o;
     o += 4 * (size_t)entries;
     L.rescan = o;
     o += 4 * (size_t)entries;
@@ -224,7 +224,7 @@ OwnerArgs owner_args_at(const tsdf_volume* h, unsigned int serial, void* scratch
     o.fc = reinterpret_cast<FrameCounters*>(base + L.fc);
     o.items = reinterpret_cast<unsigned int*>(base + L.items);
     o.items_spill = reinterpret_cast<unsigned int*>(base + L.items_spill);
-    o.item_of = reinterpret_cast<unsigned int*>(base + L.item_of);
+    o.seg_first_of = reinterpret_cast<unsigned int*>(base + L.seg_first_of);
     o.blk_count = reinterpret_cast<unsigned long long*>(base + L.blk_count);
     o.rescan = reinterpret_cast<unsigned int*>(base + L.rescan);
     o.desc = reinterpret_cast<ItemDesc*>(base + L.desc);

@@ -187,7 +187,8 @@ struct OwnerArgs {
     FrameCounters* fc;         // [2] by frame parity
     unsigned int* items;       // [kParts * item_part_cap] first-touched slots, by partition
     unsigned int* items_spill; // [table entries] slots beyond a partition's share
-    unsigned int* item_of;     // [table entries] slot -> its item this frame
+    unsigned int* seg_first_of;  // [table entries] slot -> its first place in the segment list this call
+                                 //   (kNoSlot: the block is rescanned)
     unsigned long long* blk_count;  // [table entries] segments << 32 | runs (| kSegOverflow) per slot
     unsigned int* rescan;      // [table entries] items whose runs did not fit
     ItemDesc* desc;            // [table entries] per item

@@ -769,7 +769,7 @@ __global__ __launch_bounds__(kThreads) void k_place_items(VolumeArgs vol, OwnerA
                 }
             }
             own.desc[j] = d;
-            own.item_of[slot] = j;
+            own.seg_first_of[slot] = (rc & kSegOverflow) ? kNoSlot : d.seg_first;
             if (rc & kSegOverflow) own.rescan[atomicAdd(&fc.n_rescan, 1u)] = j;
         }
         __syncthreads();
@@ -788,9 +788,9 @@ __global__ __launch_bounds__(kThreads) void k_place_segments(VolumeArgs vol, Own
         const int p = find_partition(s_pre, j);
         const Segment sg = own.segs[(size_t)p * own.seg_part_cap + (j - s_pre[p])];
         if (sg.slot == kNoSlot) continue;                       // refused for lack of space
-        const ItemDesc& d = own.desc[own.item_of[sg.slot]];
-        if (d.rec_count & kSegOverflow) continue;               // the block is rescanned
-        own.seg_list[d.seg_first + sg.seg_pos] = make_uint2(sg.rec_base, sg.block_off);
+        const unsigned int first = own.seg_first_of[sg.slot];
+        if (first == kNoSlot) continue;                         // the block is rescanned
+        own.seg_list[first + sg.seg_pos] = make_uint2(sg.rec_base, sg.block_off);
     }
 }
 
