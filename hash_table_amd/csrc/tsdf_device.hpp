@@ -65,67 +65,60 @@ constexpr unsigned int kSegOverflow = 0x80000000u;   // block's runs did not all
 constexpr float kNearPlane = 1e-4f;                 // block corners closer than this: whole image
 
 // One run of a walk inside one block, as allocate records it for the
-// update (16 bytes):
-//   depth     the point's depth (f32 bits)
-//   meta      colour R | G << 8 | B << 16, frame of the batch << 24 (its low
-//             5 bits), axis direction bits << 29 (bit set: that axis steps
-//             by -1)
-//   code      first cell (voxel index in the block, 9 bits) | cells - 1 << 9
-//             (5 bits) | y-step plane << 14 (21 bits) | z-step plane << 35
-//             (21 bits) | kept cells << 56 (6 bits) | frame of the batch >> 5
-//             << 62 (its high 2 bits)
-// Bit q of the y-step (z-step) plane is set when the run's step q, the one
-// from its cell q to cell q + 1, moves along y (z); a step with neither bit
-// moves along x.  The walk is monotonic on every axis and a block spans 8
-// cells per axis, so a run takes at most 7 + 7 + 7 = 21 steps (22 cells):
-// 21-bit planes and 5 bits of cell count always suffice.  The update
-// enumerates the run's cells from the code alone: it never repeats the
-// walk's arithmetic.
-struct __align__(16) RunRecord {
+// update (12 bytes):
+//   depth  the point's depth (f32 bits)
+//   w1     colour R | G << 8 | B << 16, axis direction bits << 24 (bit set:
+//          that axis steps by -1), cells - 1 << 27 (4 bits)
+//   w2     first cell (voxel index in the block, 9 bits) | y-step plane << 9
+//          (11 bits) | z-step plane << 20 (11 bits)
+// The frame of the batch is the run's segment's (a filing holds one tile of
+// one frame).  Bit q of the y-step (z-step) plane is set when the run's
+// step q, the one from its cell q to cell q + 1, moves along y (z); a step
+// with neither bit moves along x.  A run holds at most kMaxRunCells cells:
+// the walk is monotonic on every axis and a block spans 8 cells per axis,
+// so a walk's stretch through a block has at most 22 cells, and a stretch
+// longer than kMaxRunCells is recorded as several runs of the same block.
+// The update enumerates a run's cells from the record alone: it never
+// repeats the walk's arithmetic.
+struct RunRecord {
     unsigned int depth;
-    unsigned int meta;
-    unsigned int code_lo;
-    unsigned int code_hi;
+    unsigned int w1;
+    unsigned int w2;
 };
+static_assert(sizeof(RunRecord) == 12, "12-byte run records");
 
-constexpr int kStepShift = 14;
-constexpr int kPlaneBits = 21;
-constexpr int kKeptShift = 56;
+constexpr int kMaxRunCells = 12;
+constexpr int kPlaneBits = kMaxRunCells - 1;
 
-__device__ __forceinline__ unsigned long long run_code(unsigned int entry, unsigned int cells, unsigned int ysteps,
-                                                       unsigned int zsteps, unsigned int kept) {
-    return (unsigned long long)(entry | ((cells - 1) << 9)) | ((unsigned long long)ysteps << kStepShift) |
-           ((unsigned long long)zsteps << (kStepShift + kPlaneBits)) | ((unsigned long long)kept << kKeptShift);
+__device__ __forceinline__ unsigned int run_w1(unsigned int colour_dirs, unsigned int cells) {
+    return colour_dirs | ((cells - 1u) << 27);
 }
-__device__ __forceinline__ unsigned long long record_code(const RunRecord& r) {
-    return (unsigned long long)r.code_lo | ((unsigned long long)r.code_hi << 32);
+__device__ __forceinline__ unsigned int run_w2(unsigned int entry, unsigned int ysteps, unsigned int zsteps) {
+    return entry | (ysteps << 9) | (zsteps << (9 + kPlaneBits));
 }
-__device__ __forceinline__ int code_entry(unsigned long long c) { return (int)(c & 511u); }
-__device__ __forceinline__ int code_cells(unsigned long long c) { return (int)((c >> 9) & 31u) + 1; }
-__device__ __forceinline__ unsigned int code_ysteps(unsigned long long c) {
-    return (unsigned int)(c >> kStepShift) & ((1u << kPlaneBits) - 1u);
+__device__ __forceinline__ int run_cells(unsigned int w1) { return (int)((w1 >> 27) & 15u) + 1; }
+__device__ __forceinline__ int run_entry(unsigned int w2) { return (int)(w2 & 511u); }
+__device__ __forceinline__ unsigned int run_ysteps(unsigned int w2) { return (w2 >> 9) & ((1u << kPlaneBits) - 1u); }
+__device__ __forceinline__ unsigned int run_zsteps(unsigned int w2) {
+    return (w2 >> (9 + kPlaneBits)) & ((1u << kPlaneBits) - 1u);
 }
-__device__ __forceinline__ unsigned int code_zsteps(unsigned long long c) {
-    return (unsigned int)(c >> (kStepShift + kPlaneBits)) & ((1u << kPlaneBits) - 1u);
-}
-__device__ __forceinline__ int code_kept(unsigned long long c) { return (int)((c >> kKeptShift) & 63u); }
-constexpr int kFrameHighShift = 62;
-// The frame (of the batch) a record belongs to: 5 bits in meta, 2 in the code.
-__device__ __forceinline__ int record_frame(unsigned int meta, unsigned long long code) {
-    return (int)(((meta >> 24) & 31u) | ((unsigned int)(code >> kFrameHighShift) << 5));
-}
+
+// A segment's position among its block's segments and the frame of its
+// filing share a word (so do the runs before it and the frame in the
+// block-ordered segment list): positions and run offsets below 2^25.
+constexpr int kSegFrameShift = 25;
+constexpr unsigned int kSegPosMask = (1u << kSegFrameShift) - 1u;
 
 // One filing's runs through one block (an allocate workgroup's tile), as
-// recorded by allocate.  One
-// 64-bit atomic on the block's counter (segments << 32 | runs) gives both
-// the segment's position among the block's segments and its first run's
-// position among the block's runs, so in segment order block_off is the
-// running total of the runs before it.
+// recorded by allocate.  One 64-bit atomic on the block's counter
+// (segments << 32 | runs) gives both the segment's position among the
+// block's segments and its first run's position among the block's runs, so
+// in segment order block_off is the running total of the runs before it.
 struct __align__(16) Segment {
     unsigned int slot;        // table slot of the block (kNoSlot: refused for lack of space)
     unsigned int rec_base;    // its first record in the record buffer
     unsigned int block_off;   // runs of the block's earlier segments
-    unsigned int seg_pos;     // its position among the block's segments
+    unsigned int seg_pos;     // its position among the block's segments | frame << kSegFrameShift
 };
 
 // A block touched by the call, as the owner update reads it.
@@ -193,7 +186,8 @@ struct OwnerArgs {
     unsigned int* rescan;      // [table entries] items whose runs did not fit
     ItemDesc* desc;            // [table entries] per item
     Segment* segs;             // [kParts * seg_part_cap] allocate order
-    uint2* seg_list;           // [kParts * seg_part_cap] (rec_base, block_off), grouped by block
+    uint2* seg_list;           // [kParts * seg_part_cap] (rec_base, block_off | frame << kSegFrameShift),
+                               //   grouped by block
     RunRecord* recs;           // [kParts * rec_part_cap] allocate order (read in place)
     uint2* units;              // [kMaxUnits] (item, chunk >= 1) of split blocks
     unsigned int unit_target;  // work units a call aims for (<= kMaxUnits): blocks with more
@@ -224,7 +218,7 @@ struct FrameArgs {
 // kernel arguments; the others (a call of more frames) in a device table
 // the library fills before the call's kernels (`more`, frame kArgFrames
 // first).
-constexpr int kMaxBatch = 128;              // 7-bit frame index in the run records
+constexpr int kMaxBatch = 128;              // 7-bit frame index beside a segment's position
 constexpr int kArgFrames = 32;
 struct BatchArgs {
     FrameArgs f[kArgFrames];

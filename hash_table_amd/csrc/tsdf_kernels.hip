@@ -11,7 +11,8 @@
 //
 //   * owner update (default): allocate cuts every walk into runs, one per
 //     block it crosses, and records each run with a kept voxel (depth,
-//     colour, frame, first cell and the axis of each step: 16 bytes); the
+//     colour, first cell and the axis of each step: 12 bytes; the frame
+//     goes with the run's segment); the
 //     records are grouped by block, and one workgroup per block enumerates
 //     the cells of each of its runs (no walk arithmetic repeated), sums the
 //     block's contributions in LDS and then read-modify-writes the five
@@ -145,13 +146,14 @@ __device__ __forceinline__ bool workgroup_any(bool p, AllocLds& L, unsigned int&
     return any;
 }
 
-// File the workgroup's pending runs (see above).  depth and meta: this
-// thread's point, for the records of its runs.  Must be called by the whole
+// File the workgroup's pending runs (see above).  depth and colour_dirs:
+// this thread's point, for the records of its runs; frame: the workgroup's
+// frame of the batch, for its segments.  Must be called by the whole
 // workgroup after a barrier; the LDS set is empty on entry and again once the
 // next barrier has passed.
 __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, unsigned int part, const VolumeArgs& vol,
-                                          const OwnerArgs& own, unsigned int depth, unsigned int meta,
-                                          unsigned int frame_hi) {
+                                          const OwnerArgs& own, unsigned int depth, unsigned int colour_dirs,
+                                          unsigned int frame) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // de-duplicate: each pending run finds (or enters) its key in the set
@@ -250,13 +252,15 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, unsigned int
             unsigned int rbase;
             if (slot == kNoSlot) {
                 rbase = kNoKeyBase;                          // the full table refused the key: its kept visits are lost
-            } else if (seg < own.seg_part_cap && (unsigned long long)rec + runs <= own.rec_part_cap) {
+            } else if (seg < own.seg_part_cap && (unsigned long long)rec + runs <= own.rec_part_cap &&
+                       (unsigned int)(bc >> 32) <= kSegPosMask && ((unsigned int)bc & ~kSegOverflow) + runs <= kSegPosMask) {
                 sg.slot = slot;
                 sg.rec_base = part * own.rec_part_cap + rec;
                 sg.block_off = (unsigned int)bc & ~kSegOverflow;
-                sg.seg_pos = (unsigned int)(bc >> 32);
+                sg.seg_pos = (unsigned int)(bc >> 32) | (frame << kSegFrameShift);
                 rbase = sg.rec_base;
-            } else {                                         // out of space: the update rescans the block
+            } else {                                         // out of space (or a block's lists out of range):
+                                                             // the update rescans the block
                 atomicOr(own.blk_count + slot, (unsigned long long)kSegOverflow);
                 rbase = kNoBase;
             }
@@ -271,15 +275,14 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, unsigned int
         for (int q = 0; q < kSlots; ++q) {
             if (!S.pend[q]) continue;
             const unsigned int b = L.scnt[hr[q] & (kSetCap - 1)];
-            const unsigned long long code = L.scode[q][tid];
+            const unsigned long long code = L.scode[q][tid];     // w2 | (cells | kept << 8) << 32
             if (b == kNoKeyBase) {
-                atomicAdd(L.cnt + 5, (unsigned int)code_kept(code));   // rare: counted at once
+                atomicAdd(L.cnt + 5, (unsigned int)(code >> 40));   // rare: its kept cells counted at once
             } else if (b != kNoBase) {
                 RunRecord r;
                 r.depth = depth;
-                r.meta = meta;
-                r.code_lo = (unsigned int)code;
-                r.code_hi = (unsigned int)(code >> 32) | frame_hi;
+                r.w1 = run_w1(colour_dirs, (unsigned int)(code >> 32) & 255u);
+                r.w2 = (unsigned int)code;
                 own.recs[b + (hr[q] >> kSetBits)] = r;
             }
         }
@@ -301,8 +304,8 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, unsigned int
 __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, unsigned int zp, unsigned int cp,
                                              int n, int itc, int x, int y, int z, int s0, int s1, int s2, AllocLds& L,
                                              unsigned int& rnd, unsigned int part, const VolumeArgs& vol,
-                                             const OwnerArgs& own, unsigned int depth_bits, unsigned int meta,
-                                             unsigned int frame_hi, unsigned int& n_upd) {
+                                             const OwnerArgs& own, unsigned int depth_bits, unsigned int colour_dirs,
+                                             unsigned int frame, unsigned int& n_upd) {
     // planes in walk order, bit j = the chunk's cell j: every plane was
     // shifted once per iteration (itc of them); the lane walked n cells and
     // the bits after them are not read
@@ -311,9 +314,10 @@ __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, u
     const unsigned int yf = itc ? __builtin_bitreverse32(yp) >> shp : 0u;
     const unsigned int zf = itc ? __builtin_bitreverse32(zp) >> shp : 0u;
     const unsigned int cf = itc ? __builtin_bitreverse32(cp) >> shp : 0u;
-    // cut into runs: a run ends at a cell whose step leaves the block, or
-    // at the lane's last cell of the chunk; up to kSlots runs per lane
-    // between filings (workgroup-wide: every thread takes part in each)
+    // cut into runs: a run ends at a cell whose step leaves the block, at
+    // its kMaxRunCells-th cell, or at the lane's last cell of the chunk; up
+    // to kSlots runs per lane between filings (workgroup-wide: every thread
+    // takes part in each)
     for (int j0 = 0; workgroup_any(j0 < n, L, rnd);) {
         RunSlots S;
 #pragma unroll
@@ -328,16 +332,19 @@ __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, u
             if (j0 < n) {
                 const unsigned int rest = cf >> j0;
                 const unsigned int tz = rest ? (unsigned int)__builtin_ctz(rest) : 32u;
-                const unsigned int e = min(tz, (unsigned int)(n - 1 - j0));   // steps inside the run
+                const unsigned int e = min(min(tz, (unsigned int)(n - 1 - j0)),   // steps inside the run
+                                           (unsigned int)(kMaxRunCells - 1));
                 const unsigned int len = e + 1;                                 // its cells
                 const unsigned int kept = __popc(__builtin_amdgcn_ubfe(kf, j0, len));
                 const unsigned int ys = __builtin_amdgcn_ubfe(yf, j0, e);
                 const unsigned int zs = __builtin_amdgcn_ubfe(zf, j0, e);
                 S.key[q] = block_key(x, y, z);
-                S.code[q] = run_code((unsigned int)voxel_in_block(x, y, z), len, ys, zs, kept);
+                // the record's w2, with the cell count and the kept cells above it
+                S.code[q] = (unsigned long long)run_w2((unsigned int)voxel_in_block(x, y, z), ys, zs) |
+                            ((unsigned long long)(len | (kept << 8)) << 32);
                 S.pend[q] = kept > 0;
                 n_upd += kept;
-                // the next run's first cell: the run's steps and the one leaving it
+                // the next run's first cell: the run's steps and the one after it
                 const int cy = __popc(__builtin_amdgcn_ubfe(yf, j0, len));
                 const int cz = __popc(__builtin_amdgcn_ubfe(zf, j0, len));
                 x += __mul24(s0, (int)len - cy - cz);
@@ -346,7 +353,7 @@ __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, u
                 j0 += (int)len;
             }
         }
-        file_runs(S, L, part, vol, own, depth_bits, meta, frame_hi);
+        file_runs(S, L, part, vol, own, depth_bits, colour_dirs, frame);
     }
 }
 
@@ -394,9 +401,8 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
     float depth = 0.0f;
     const bool in_image = u < f.width && v < f.height;
     if (in_image) depth = f.depth[pix];
-    unsigned int meta = 0;
+    unsigned int meta = 0;                    // colour | axis direction bits << 24 (a record's w1 without its length)
     const unsigned int depth_bits = __float_as_uint(depth);
-    const unsigned int frame_hi = ((unsigned int)fi >> 5) << (kFrameHighShift - 32);   // into the code's top bits
     unsigned int n_upd = 0;
     // this workgroup's reservations: partitions in turn as if the call's
     // frames were laid end to end by their tile counts (numbering by launch
@@ -596,23 +602,22 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
                     if (c_oor) atomicAdd(L.cnt + 2, c_oor);
                 }
                 // what the update needs of this point besides the run codes:
-                // colour (when the frame has it), frame of the batch and the
-                // directions of the stepping axes
+                // colour (when the frame has it) and the directions of the
+                // stepping axes (the frame of the batch goes with the segments)
                 if (cls == kValid) {
                     if (own.build_items && f.rgb) {
                         const uint8_t* c = f.rgb + 3 * (size_t)pix;
                         meta = (unsigned int)c[0] | ((unsigned int)c[1] << 8) | ((unsigned int)c[2] << 16);
                     }
-                    meta |= (((unsigned int)fi & 31u) << 24) | (w.s0 < 0 ? 1u << 29 : 0u) | (w.s1 < 0 ? 1u << 30 : 0u) |
-                            (w.s2 < 0 ? 1u << 31 : 0u);
+                    meta |= (w.s0 < 0 ? 1u << 24 : 0u) | (w.s1 < 0 ? 1u << 25 : 0u) | (w.s2 < 0 ? 1u << 26 : 0u);
                 }
             }
             for (int i = 0; i < done; ++i) step();
             itc = walk_chunk(done);
         }
         wave_on = alive != 0;
-        cut_and_file(kp, yp, zp, cp, (int)nc, itc, x, y, z, (meta >> 29) & 1u ? -1 : 1, (meta >> 30) & 1u ? -1 : 1,
-                     (meta >> 31) & 1u ? -1 : 1, L, rnd, part, vol, own, depth_bits, meta, frame_hi, n_upd);
+        cut_and_file(kp, yp, zp, cp, (int)nc, itc, x, y, z, (meta >> 24) & 1u ? -1 : 1, (meta >> 25) & 1u ? -1 : 1,
+                     (meta >> 26) & 1u ? -1 : 1, L, rnd, part, vol, own, depth_bits, meta, (unsigned int)fi, n_upd);
         if (!workgroup_any(wave_on, L, rnd)) break;
     }
 
@@ -790,7 +795,8 @@ __global__ __launch_bounds__(kThreads) void k_place_segments(VolumeArgs vol, Own
         if (sg.slot == kNoSlot) continue;                       // refused for lack of space
         const unsigned int first = own.seg_first_of[sg.slot];
         if (first == kNoSlot) continue;                         // the block is rescanned
-        own.seg_list[first + sg.seg_pos] = make_uint2(sg.rec_base, sg.block_off);
+        own.seg_list[first + (sg.seg_pos & kSegPosMask)] =
+            make_uint2(sg.rec_base, sg.block_off | (sg.seg_pos & ~kSegPosMask));   // (the frame rides along)
     }
 }
 
@@ -919,6 +925,14 @@ __device__ __forceinline__ void flush_atomic(OwnerLds& L, const VolumeArgs& vol,
     }
 }
 
+// A run as the update stages it in LDS: its record and its segment's frame.
+struct __align__(16) StagedRun {
+    unsigned int depth;
+    unsigned int w1;
+    unsigned int w2;
+    unsigned int frame;
+};
+
 // kReproject: the reprojection reading of the occlusion test (as in k_allocate).
 template <bool kReproject>
 __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_owner(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
@@ -928,7 +942,8 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
     __shared__ unsigned int s_item[2];                      // alternates: read k while k + 1 is written
     __shared__ unsigned int s_rec[kSegWindow];
     __shared__ unsigned int s_off[kSegWindow + 1];
-    __shared__ RunRecord s_run[kSubRuns];                   // staged runs, sorted by length
+    __shared__ unsigned char s_frm[kSegWindow];             // each segment's frame of the batch
+    __shared__ StagedRun s_run[kSubRuns];                   // staged runs, sorted by length
     __shared__ unsigned int s_hist[kLengths];               // staged runs of each length
     __shared__ unsigned int s_hbase[kLengths];              // first place of each length in the order
     const int tid = threadIdx.x;
@@ -989,9 +1004,11 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                 if (i < wn) {
                     const uint2 e = own.seg_list[d.seg_first + w0 + i];
                     s_rec[i] = e.x;
-                    s_off[i] = e.y;
+                    s_off[i] = e.y & kSegPosMask;
+                    s_frm[i] = (unsigned char)(e.y >> kSegFrameShift);
                 } else {
-                    s_off[i] = w0 + wn < d.seg_count ? own.seg_list[d.seg_first + w0 + wn].y : d.rec_count;
+                    s_off[i] = w0 + wn < d.seg_count ? own.seg_list[d.seg_first + w0 + wn].y & kSegPosMask
+                                                     : d.rec_count;
                 }
             }
             __syncthreads();
@@ -1010,7 +1027,7 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                 for (unsigned int b0 = c0; b0 < c1; b0 += kSubRuns) {
                     const unsigned int nb = min(c1 - b0, (unsigned int)kSubRuns);
                     const unsigned int p0 = (unsigned int)tid * kRunsPerThread;
-                    RunRecord rec[kRunsPerThread];
+                    StagedRun rec[kRunsPerThread];
                     unsigned int rank[kRunsPerThread];
 #pragma unroll
                     for (int i = 0; i < kRunsPerThread; ++i) rank[i] = kNoRank;
@@ -1026,20 +1043,19 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                         for (int i = 0; i < kRunsPerThread; ++i) {
                             if (p0 + i < nb) {
                                 while (r >= s_off[si + 1]) ++si;   // s_off[wn] = wr1 > r ends it
-                                rec[i] = own.recs[s_rec[si] + (r - s_off[si])];
+                                const RunRecord hr = own.recs[s_rec[si] + (r - s_off[si])];
+                                rec[i].depth = hr.depth;
+                                rec[i].w1 = hr.w1;
+                                rec[i].w2 = hr.w2;
+                                rec[i].frame = s_frm[si];
                                 ++r;
                             }
                         }
 #pragma unroll
                         for (int i = 0; i < kRunsPerThread; ++i) {
-                            if (p0 + i < nb) {
-                                const unsigned long long code = record_code(rec[i]);
-                                if (store) rank[i] = atomicAdd(s_hist + code_cells(code) - 1, 1u);
-                                else misses += (unsigned int)code_kept(code);
-                            }
+                            if (p0 + i < nb) rank[i] = atomicAdd(s_hist + run_cells(rec[i].w1) - 1, 1u);
                         }
                     }
-                    if (!store) continue;                    // (uniform) a refused block: counted above
                     __syncthreads();
                     if (tid < 64) {                          // each length's first place in the order
                         const unsigned int h = tid < kLengths ? s_hist[tid] : 0u;
@@ -1051,25 +1067,24 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
 #pragma unroll
                     for (int i = 0; i < kRunsPerThread; ++i)
                         if (rank[i] != kNoRank)
-                            s_run[s_hbase[code_cells(record_code(rec[i])) - 1] + rank[i]] = rec[i];
+                            s_run[s_hbase[run_cells(rec[i].w1) - 1] + rank[i]] = rec[i];
                     __syncthreads();
                     for (unsigned int p = (unsigned int)tid; p < nb; p += kUpdateThreads) {
-                        const RunRecord rr = s_run[p];
-                        const unsigned long long code = record_code(rr);
+                        const StagedRun rr = s_run[p];
                         const float dep = __uint_as_float(rr.depth);
-                        const int rf = record_frame(rr.meta, code);
+                        const int rf = (int)rr.frame;
                         const DepthAxis ax = s_axis[rf];
-                        const unsigned long long c = (unsigned long long)(rr.meta & 0xFFu) |
-                                                     ((unsigned long long)((rr.meta >> 8) & 0xFFu) << 21) |
-                                                     ((unsigned long long)((rr.meta >> 16) & 0xFFu) << 42);
+                        const unsigned long long c = (unsigned long long)(rr.w1 & 0xFFu) |
+                                                     ((unsigned long long)((rr.w1 >> 8) & 0xFFu) << 21) |
+                                                     ((unsigned long long)((rr.w1 >> 16) & 0xFFu) << 42);
                         // the axis directions, as voxel-index steps (a step
                         // along x, y or z adds d0, d0 + dy or d0 + dz) and
                         // as floats
-                        const bool n0 = (rr.meta >> 29) & 1u, n1 = (rr.meta >> 30) & 1u, n2 = (rr.meta >> 31) & 1u;
+                        const bool n0 = (rr.w1 >> 24) & 1u, n1 = (rr.w1 >> 25) & 1u, n2 = (rr.w1 >> 26) & 1u;
                         const int d0 = n0 ? -1 : 1;
                         const int dy = (n1 ? -8 : 8) - d0, dz = (n2 ? -64 : 64) - d0;
                         const float f0 = n0 ? -1.0f : 1.0f, f1 = n1 ? -1.0f : 1.0f, f2 = n2 ? -1.0f : 1.0f;
-                        const int e = code_entry(code), cells = code_cells(code);
+                        const int e = run_entry(rr.w2), cells = run_cells(rr.w1);
                         // the cell's centre in voxels, k + 1/2 per axis (exact:
                         // integers and halves), and its voxel within the block
                         // (a run stays in its block)
@@ -1077,16 +1092,20 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                         float x1 = (float)(lo1 + ((e >> 3) & 7)) + 0.5f;
                         float x2 = (float)(lo2 + (e >> 6)) + 0.5f;
                         int j = e;
-                        const unsigned int ys = code_ysteps(code), zs = code_zsteps(code);
+                        const unsigned int ys = run_ysteps(rr.w2), zs = run_zsteps(rr.w2);
                         // q counts the cells every active lane has done (the
                         // same in all of them, a scalar)
                         for (int q = 0; q < cells; ++q) {
                             float sdf;
                             if (kReproject ? centre_test_reproject_at(x0, x1, x2, dep, ax, s_proj[rf], vol.vs, vol.trunc, sdf)
                                            : centre_test_at(x0, x1, x2, dep, ax, vol.vs, vol.trunc, sdf)) {
-                                const unsigned int tq = (unsigned int)(__float2int_rn(sdf * tsdf_scale) + (1 << 25));
-                                atomicAdd(L.tw + sum_slot(j), (1ull << kCountShift) + tq);
-                                atomicAdd(L.rgb + sum_slot(j), c);
+                                if (store) {
+                                    const unsigned int tq = (unsigned int)(__float2int_rn(sdf * tsdf_scale) + (1 << 25));
+                                    atomicAdd(L.tw + sum_slot(j), (1ull << kCountShift) + tq);
+                                    atomicAdd(L.rgb + sum_slot(j), c);
+                                } else {
+                                    ++misses;                // (uniform) a block refused a pool index: counted
+                                }
                             }
                             // the step after cell q: bit q of the planes (after
                             // the run's last cell both are 0, an x step whose

@@ -177,7 +177,7 @@ int64_t tsdf_table_entries_for(int64_t pool_capacity);
 size_t tsdf_counters_bytes(void);
 
 /* Size of the scratch buffer a configuration needs (0 for TSDF_UPDATE_RAYS):
- * about 60 bytes per table entry plus 112 bytes per pixel of max_batch_pixels
+ * about 60 bytes per table entry plus 96 bytes per pixel of max_batch_pixels
  * (run records and their grouping by block; at least 16,384 pixels' worth).
  * 0 for a NULL or invalid config. */
 size_t tsdf_scratch_bytes(const tsdf_config* config);
@@ -236,7 +236,7 @@ tsdf_status tsdf_integrate_batch(tsdf_volume* volume, const tsdf_frame* frames, 
  * Limit (TSDF_ELIMIT, nothing enqueued): in owner mode the work lists of the
  * call must fit the array: tsdf_scratch_bytes of the volume's config with
  * max_batch_pixels set to the call's total pixels, i.e. about 60 bytes per
- * table entry plus 112 per pixel, at most TSDF_NOALLOC_SCRATCH_BYTES.
+ * table entry plus 96 per pixel, at most TSDF_NOALLOC_SCRATCH_BYTES.
  * Ray-parallel volumes need no work lists.  Up to TSDF_MAX_BATCH frames.
  * Every call on one GPU shares that GPU's array, which keeps the previous
  * call's contents (each call clears what it needs): calls that overlap in

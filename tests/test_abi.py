@@ -48,7 +48,7 @@ def test_scratch_sizing():
         item_part = max(64, entries // 32)
         counters = 64 * 128 + 128 + 8 * 32 * 4                      # per frame parity: partitions, totals, XCD fetch
         units = 8 * 8192                                              # split-block work units
-        return (2 * counters + 32 * entries + 16 * 64 * seg_part + 16 * 64 * rec_part + units + 8 * 64 * seg_part
+        return (2 * counters + 32 * entries + 16 * 64 * seg_part + 12 * 64 * rec_part + units + 8 * 64 * seg_part
                 + 8 * entries + 4 * 64 * item_part + 12 * entries)
     owner = tsdf.tsdf_config(0.01, 0.04, 4096, 0, tsdf.TSDF_UPDATE_OWNER, 1000)
     assert tsdf.tsdf_scratch_bytes(owner) == expect(8192, 1000)
