@@ -11,13 +11,13 @@
 //
 //   * owner update (default): allocate cuts every walk into runs, one per
 //     block it crosses, and records each run with a kept voxel (depth,
-//     colour, first cell and the axis of each step: 12 bytes; the frame
-//     goes with the run's segment); the
-//     records are grouped by block, and one workgroup per block enumerates
-//     the cells of each of its runs (no walk arithmetic repeated), sums the
-//     block's contributions in LDS and then read-modify-writes the five
-//     pool arrays with plain coalesced loads and stores: a block has one
-//     writer per call, so no device-scope float atomics are needed.  A block
+//     colour, first cell and the axis of each step: 12 bytes; the frame goes
+//     with the run's segment); the records are grouped by block, and one
+//     workgroup per block enumerates the cells of each of its runs (no walk
+//     arithmetic repeated), sums the block's contributions in LDS and then
+//     read-modify-writes the five pool arrays with plain coalesced loads and
+//     stores: a block has one writer per call, so no device-scope float
+//     atomics are needed.  A block
 //     whose runs did not fit the record buffers is rescanned from the pixel
 //     rectangle its band can be seen through.
 //   * ray-parallel update: the shape the paper describes (one thread per
