@@ -433,13 +433,22 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
         b0 = (float)(w.k0 + (s0 > 0)); b1 = (float)(w.k1 + (s1 > 0)); b2 = (float)(w.k2 + (s2 > 0));
         h0 = s0 > 0 ? -0.5f : 0.5f; h1 = s1 > 0 ? -0.5f : 0.5f; h2 = s2 > 0 ? -0.5f : 0.5f;
         tm0 = w.tm0; tm1 = w.tm1; tm2 = w.tm2;
-        g0 = w.gA0; g1 = w.gA1; g2 = w.gA2;
-        i0 = w.inv0; i1 = w.inv1; i2 = w.inv2;
+        // an axis that does not move: start -inf and reciprocal +inf, so
+        // that (b - g) i, recomputed every step, stays +inf
+        g0 = s0 != 0 ? w.gA0 : -__builtin_inff();
+        g1 = s1 != 0 ? w.gA1 : -__builtin_inff();
+        g2 = s2 != 0 ? w.gA2 : -__builtin_inff();
+        i0 = s0 != 0 ? w.inv0 : __builtin_inff();
+        i1 = s1 != 0 ? w.inv1 : __builtin_inff();
+        i2 = s2 != 0 ? w.inv2 : __builtin_inff();
     };
     // One step of the walk (every lane; a finished walk does not move).  The
-    // stepped axis is the one whose boundary comes first (ties: x, then y).
-    // The masks of the lanes that stepped, and of those that stepped along y
-    // and along z; bc the boundary crossed.
+    // stepped axis is the one whose boundary comes first (ties: x, then y);
+    // its next boundary moves on by one cell, and every axis's crossing
+    // parameter is then (b - g) i of its next boundary b (the same value as
+    // before for an axis that did not step).  The masks of the lanes that
+    // stepped, and of those that stepped along y and along z; bc the
+    // boundary crossed.
     struct Step {
         unsigned long long more, e0, e1, a1, a2;
         float bc;
@@ -455,17 +464,12 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
         st.a2 = st.more & ~st.e0 & ~st.e1;
         const bool e0 = lane_on(st.e0), e1 = lane_on(st.e1);
         st.bc = pick3(e0, e1, b0, b1, b2);
-        const float fc = pick3(e0, e1, f0, f1, f2);
-        const float gc = pick3(e0, e1, g0, g1, g2);
-        const float ic = pick3(e0, e1, i0, i1, i2);
-        const float bn = st.bc + fc;           // the new cell's next boundary
-        const float tn = (bn - gc) * ic;
-        b0 = lane_on(a0) ? bn : b0;
-        b1 = lane_on(st.a1) ? bn : b1;
-        b2 = lane_on(st.a2) ? bn : b2;
-        tm0 = lane_on(a0) ? tn : tm0;
-        tm1 = lane_on(st.a1) ? tn : tm1;
-        tm2 = lane_on(st.a2) ? tn : tm2;
+        b0 = lane_on(a0) ? b0 + f0 : b0;
+        b1 = lane_on(st.a1) ? b1 + f1 : b1;
+        b2 = lane_on(st.a2) ? b2 + f2 : b2;
+        tm0 = (b0 - g0) * i0;
+        tm1 = (b1 - g1) * i1;
+        tm2 = (b2 - g2) * i2;
         alive = st.more;
         return st;
     };
@@ -606,7 +610,9 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
                 // stepping axes (the frame of the batch goes with the segments)
                 if (cls == kValid) {
                     if (own.build_items && f.rgb) {
-                        const uint8_t* c = f.rgb + 3 * (size_t)pix;
+                        unsigned int px = pix;       // (opaque: the address is formed here, not held from the start)
+                        asm volatile("" : "+v"(px));
+                        const uint8_t* c = f.rgb + 3 * (size_t)px;
                         meta = (unsigned int)c[0] | ((unsigned int)c[1] << 8) | ((unsigned int)c[2] << 16);
                     }
                     meta |= (w.s0 < 0 ? 1u << 24 : 0u) | (w.s1 < 0 ? 1u << 25 : 0u) | (w.s2 < 0 ? 1u << 26 : 0u);
