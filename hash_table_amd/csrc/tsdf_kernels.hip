@@ -106,7 +106,7 @@ struct AllocLds {
     unsigned long long skey[kSetCap];             // set: key (empty: all ones),
     unsigned int scnt[kSetCap];                   //   its runs; after the reservation, its first record
     unsigned short sslot[kSetCap];                // set slots of the distinct keys, in insertion order
-    unsigned long long scode[kSlots][kThreads];   // the lanes' run codes, held here while the keys are filed
+    unsigned long long scode[kSlots][kThreads];   // the lanes' RunSlots codes, held here while the keys are filed
     unsigned long long r0;                        // the filing's reservation: first segment << 32 | first record
     unsigned int nuniq;                           // distinct keys of the filing
     unsigned int nrun;                            // its runs
@@ -119,7 +119,9 @@ struct AllocLds {
 };
 
 // A lane's runs since the last filing: slot q holds its q-th run (pend: a
-// run with a kept voxel waiting to be filed).
+// run with a kept voxel waiting to be filed): its block key, and its
+// record's w2 with the cell count and the kept cells above it
+// (w2 | (cells | kept << 8) << 32).
 struct RunSlots {
     unsigned long long key[kSlots];
     unsigned long long code[kSlots];
