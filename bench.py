@@ -767,7 +767,35 @@ def main():
         out["cells"] = config_cells(R, scenes, host_room, args)
     if not args.no_microbench:
         log("microbenchmarks")
-        out["microbench"] = microbench(torch, tsdf, stream)
+        mb = out["microbench"] = microbench(torch, tsdf, stream)
+        # the path against the measured ceilings: copy bandwidth, and the
+        # atomic rates of the matching pattern
+        t_upd = ktimes["k_update_owner"]["total_ms"] * 1e-3 / ktimes["k_update_owner"]["launches"]
+        lds_per_clk = 2.0 * vox / launches_per_step / t_upd / 2.4e9 / 256    # two 64-bit LDS adds per voxel update
+        ar = {
+            "path_compulsory_frac_of_copy": round(out["path_roofline"]["achieved"] / mb["copy_GBps"], 5)
+            if "path_roofline" in out else None,
+            "k_update_owner": {"lds_u64_adds_per_clk_per_cu": round(lds_per_clk, 3),
+                               "peak_random": mb["lds_add_u64_random_per_clk_per_cu"],
+                               "peak_distinct": mb["lds_add_u64_distinct_per_clk_per_cu"],
+                               "frac_of_random": round(lds_per_clk / mb["lds_add_u64_random_per_clk_per_cu"], 4),
+                               "adds": "2 per voxel update (signed distance | count, colour), integer 64-bit"},
+            "effective_bytes_40V": {"bytes_per_step": 40 * vox,
+                                    "GBps": round(40 * vox * args.steps / wall / 1e9, 1),
+                                    "note": "40 bytes per voxel update, as a per-visit read-modify-write would move: "
+                                            "an effective figure, not traffic"},
+        }
+        if not args.no_variants and "rays_batch1" in out["variants"]["results"]:
+            t_rays = out["variants"]["results"]["rays_batch1"]["step_ms"]["median"] * 1e-3
+            g = 5.0 * vox / t_rays / 1e9
+            # neighbouring rays add to neighbouring voxels, so the pattern lies
+            # between the random rate and the coalesced one; the roof is the latter
+            ar["rays_batch1"] = {"f32_atomics_Gops": round(g, 2),
+                                 "peak_coalesced_Gops": mb["atomic_add_f32_coalesced_Gops"],
+                                 "random_Gops": mb["atomic_add_f32_random_Gops"],
+                                 "frac": round(g / mb["atomic_add_f32_coalesced_Gops"], 4),
+                                 "atomics": "5 f32 adds per voxel update; step time includes allocate"}
+        out["atomic_roofline"] = ar
     if args.sweep:
         log("sweep cells")
         out["sweep"] = sweep(R, scenes, args)
