@@ -912,6 +912,18 @@ __device__ __forceinline__ void flush_owner(OwnerLds& L, const VolumeArgs& vol, 
     }
 }
 
+// A block refused a pool index: its kept cells (counted, not stored), and
+// the sums cleared for the next pass.
+__device__ __forceinline__ unsigned int count_and_clear(OwnerLds& L) {
+    unsigned int n = 0;
+    for (int j = threadIdx.x; j < kBlockVoxels; j += kUpdateThreads) {
+        n += (unsigned int)(L.tw[sum_slot(j)] >> kCountShift);
+        L.tw[sum_slot(j)] = 0;
+        L.rgb[sum_slot(j)] = 0;
+    }
+    return n;
+}
+
 // The same for one work unit of a split block: other workgroups add to the
 // same voxels, so the sums go in with no-return float atomics (weights stay
 // exact: integer-valued floats far below 2^24).
@@ -1081,7 +1093,7 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                         const StagedRun rr = s_run[p];
                         const float dep = __uint_as_float(rr.depth);
                         const int rf = (int)rr.frame;
-                        const DepthAxis ax = s_axis[rf];
+                        const DepthAxis ax = s_axis[__umul24(rr.frame, 1u)];    // (a 24-bit index: a cheap multiply)
                         const unsigned long long c = (unsigned long long)(rr.w1 & 0xFFu) |
                                                      ((unsigned long long)((rr.w1 >> 8) & 0xFFu) << 21) |
                                                      ((unsigned long long)((rr.w1 >> 16) & 0xFFu) << 42);
@@ -1107,13 +1119,9 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                             float sdf;
                             if (kReproject ? centre_test_reproject_at(x0, x1, x2, dep, ax, s_proj[rf], vol.vs, vol.trunc, sdf)
                                            : centre_test_at(x0, x1, x2, dep, ax, vol.vs, vol.trunc, sdf)) {
-                                if (store) {
-                                    const unsigned int tq = (unsigned int)(__float2int_rn(sdf * tsdf_scale) + (1 << 25));
-                                    atomicAdd(L.tw + sum_slot(j), (1ull << kCountShift) + tq);
-                                    atomicAdd(L.rgb + sum_slot(j), c);
-                                } else {
-                                    ++misses;                // (uniform) a block refused a pool index: counted
-                                }
+                                const unsigned int tq = (unsigned int)(__float2int_rn(sdf * tsdf_scale) + (1 << 25));
+                                atomicAdd(L.tw + sum_slot(j), (1ull << kCountShift) + tq);
+                                atomicAdd(L.rgb + sum_slot(j), c);
                             }
                             // the step after cell q: bit q of the planes (after
                             // the run's last cell both are 0, an x step whose
@@ -1132,12 +1140,12 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                     __syncthreads();                         // s_run is rewritten next
                 }
                 __syncthreads();
-                if (store) {
-                    if (split)
-                        flush_atomic(L, vol, base);
-                    else
-                        flush_owner(L, vol, base, fresh);
-                }
+                if (!store)
+                    misses += count_and_clear(L);            // refused a pool index: its kept cells are lost
+                else if (split)
+                    flush_atomic(L, vol, base);
+                else
+                    flush_owner(L, vol, base, fresh);
                 fresh = false;                               // a later pass adds to what this one wrote
                 __syncthreads();
             }
