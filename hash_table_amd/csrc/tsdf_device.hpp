@@ -249,6 +249,41 @@ __device__ __forceinline__ FrameArgs batch_frame(const BatchArgs& b, int i) {
     return f;
 }
 
+// A pointer into memory that no kernel writes while it is read (the kernel
+// arguments, the frame table), in the constant address space: a load through
+// it at a wavefront-uniform address is a scalar load.
+template <class T>
+using ConstRef = const __attribute__((address_space(4))) T*;
+template <class T>
+__device__ __forceinline__ ConstRef<T> const_ref(const T* p) {
+    return (ConstRef<T>)p;
+}
+// The same pointer, opaque to the optimiser: loads through the result happen
+// where they are written, so a value needed at several places of a long
+// kernel is loaded again (a few scalar loads) instead of being held in scalar
+// registers in between (which, with the scalar register file full, spills it
+// into lanes of a vector register: vector instructions for every use).
+template <class T>
+__device__ __forceinline__ ConstRef<T> reload(ConstRef<T> p) {
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    return p + __builtin_amdgcn_readfirstlane(z);
+}
+
+// The object a constant-address pointer points to (its fields are loaded
+// where the copy's fields are used; unused fields are not loaded).
+template <class T>
+__device__ __forceinline__ T load_ref(ConstRef<T> p) {
+    T v;
+    __builtin_memcpy(&v, (const T*)p, sizeof(T));
+    return v;
+}
+
+// Frame i of the batch as a constant-address pointer (i wavefront-uniform).
+__device__ __forceinline__ ConstRef<FrameArgs> frame_ref(const BatchArgs& b, int i) {
+    return i < kArgFrames ? const_ref(b.f + i) : const_ref(b.more + (i - kArgFrames));
+}
+
 struct VolumeArgs {
     Entry* table;
     unsigned int mask;               // table_entries - 1

@@ -153,9 +153,11 @@ __device__ __forceinline__ bool workgroup_any(bool p, AllocLds& L, unsigned int&
 // frame of the batch, for its segments.  Must be called by the whole
 // workgroup after a barrier; the LDS set is empty on entry and again once the
 // next barrier has passed.
-__device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, unsigned int part, const VolumeArgs& vol,
-                                          const OwnerArgs& own, unsigned int depth, unsigned int colour_dirs,
+__device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, unsigned int part, ConstRef<VolumeArgs> vref,
+                                          ConstRef<OwnerArgs> oref, unsigned int depth, unsigned int colour_dirs,
                                           unsigned int frame) {
+    const VolumeArgs vol = load_ref(reload(vref));         // (loaded per filing, not held through the walk)
+    const OwnerArgs own = load_ref(reload(oref));
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // de-duplicate: each pending run finds (or enters) its key in the set
@@ -305,8 +307,8 @@ __device__ __forceinline__ void file_runs(RunSlots& S, AllocLds& L, unsigned int
 
 __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, unsigned int zp, unsigned int cp,
                                              int n, int itc, int x, int y, int z, int s0, int s1, int s2, AllocLds& L,
-                                             unsigned int& rnd, unsigned int part, const VolumeArgs& vol,
-                                             const OwnerArgs& own, unsigned int depth_bits, unsigned int colour_dirs,
+                                             unsigned int& rnd, unsigned int part, ConstRef<VolumeArgs> vref,
+                                             ConstRef<OwnerArgs> oref, unsigned int depth_bits, unsigned int colour_dirs,
                                              unsigned int frame, unsigned int& n_upd) {
     // planes in walk order, bit j = the chunk's cell j: every plane was
     // shifted once per iteration (itc of them); the lane walked n cells and
@@ -355,7 +357,7 @@ __device__ __forceinline__ void cut_and_file(unsigned int kp, unsigned int yp, u
                 j0 += (int)len;
             }
         }
-        file_runs(S, L, part, vol, own, depth_bits, colour_dirs, frame);
+        file_runs(S, L, part, vref, oref, depth_bits, colour_dirs, frame);
     }
 }
 
@@ -365,7 +367,13 @@ template <bool kReproject>
 __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArgs vol, OwnerArgs own) {
     __shared__ AllocLds L;
     const int fi = blockIdx.x / B.tile_grid;                 // frame of this workgroup
-    const FrameArgs f = batch_frame(B, fi);
+    // The frame and the volume's and the update's arguments are read with
+    // scalar loads where they are used: the walk's masks fill the scalar
+    // registers, and values held through it would be spilled.
+    const ConstRef<FrameArgs> fr = frame_ref(B, fi);
+    const ConstRef<VolumeArgs> vref = const_ref(&vol);
+    const ConstRef<OwnerArgs> oref = const_ref(&own);
+    const FrameArgs f = load_ref(fr);                                // (the set-up's fields)
     if (blockIdx.x == 0 && own.build_items) {
         // clear the next frame's counters (their last users finished before
         // this kernel started)
@@ -414,7 +422,6 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
     const unsigned int part = ((unsigned int)fi * (unsigned int)f.n_tiles + wg) % kParts;
     const int max_visits = f.max_visits;
     const float vs = vol.vs, trunc = vol.trunc;
-    const DepthAxis ax = depth_axis(f);
 
     // Walk state in registers, per axis: the index of the next cell boundary
     // the walk will cross and the step (both as floats holding integers,
@@ -477,13 +484,14 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
     };
     const float dd = depth;
     const Projection proj = projection(f);
-    auto test_sdf = [&](float& sdf) __attribute__((always_inline)) {         // the centre test of the walk's current cell
+    const DepthAxis ax_all = depth_axis(f);  // (the reprojection walk tests every cell: held)
+    auto test_sdf = [&](const DepthAxis& ax, float& sdf) __attribute__((always_inline)) {   // the centre test of the walk's current cell
         return kReproject ? centre_test_reproject_at(b0 + h0, b1 + h1, b2 + h2, dd, ax, proj, vs, trunc, sdf)
                           : centre_test_at(b0 + h0, b1 + h1, b2 + h2, dd, ax, vs, trunc, sdf);
     };
     auto test = [&]() __attribute__((always_inline)) {
         float sdf;
-        return test_sdf(sdf);
+        return test_sdf(kReproject ? ax_all : depth_axis(load_ref(reload(fr))), sdf);   // (band walk: rare, loaded here)
     };
     // Stepped sdf (band test alone).  A step moves the centre by one voxel
     // along one axis, which changes d - zc by the pose's depth-axis entry
@@ -504,8 +512,8 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
     // m = 2^-20 (r (sum |X| + sum |t| + 80 vs) + d + 2 |sdf0|) covers the sum
     // with room for the rounding of m itself, and 2^-22 trunc covers that
     // of trunc -+ m.
-    const float t_abs = (fabsf(ax.t0) + fabsf(ax.t1)) + fabsf(ax.t2);
-    const float r_max = fmaxf(fmaxf(fabsf(ax.r2), fabsf(ax.r5)), fmaxf(fabsf(ax.r8), 1.0f));
+    const float t_abs = (fabsf(ax_all.t0) + fabsf(ax_all.t1)) + fabsf(ax_all.t2);
+    const float r_max = fmaxf(fmaxf(fabsf(ax_all.r2), fabsf(ax_all.r5)), fmaxf(fabsf(ax_all.r8), 1.0f));
 
     // The walk goes in chunks of up to kChunkCells cells.  All lanes start
     // together, so a lane's cell index within the chunk is the (uniform)
@@ -520,13 +528,13 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
     int x, y, z;                              // the chunk's first cell
     unsigned int kp, yp, zp, cp;              // its planes
     unsigned int nc;                          // cells this lane walked in the chunk
-    auto walk_chunk = [&](int done) __attribute__((always_inline)) {
+    auto walk_chunk = [&](int done, const DepthAxis& ax) __attribute__((always_inline)) {
         x = (int)(b0 + h0 - 0.5f);            // the current cell (exact: integers and halves)
         y = (int)(b1 + h1 - 0.5f);
         z = (int)(b2 + h2 - 0.5f);
         float sa = 0.f, lo = 0.f, hi = 0.f, dl0 = 0.f, dl1 = 0.f, dl2 = 0.f;
         float sdf0;
-        unsigned long long keep = __builtin_amdgcn_ballot_w64(test_sdf(sdf0));   // the exact test at the chunk's first cell
+        unsigned long long keep = __builtin_amdgcn_ballot_w64(test_sdf(ax, sdf0));   // the exact test at the chunk's first cell
         if constexpr (!kReproject) {
             sa = sdf0;
             dl0 = f0 * ax.r2 * vs;            // f (R vs), exact: f is -1, 0 or 1
@@ -595,7 +603,9 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
             float xr = L.xn[(wave & 1) * 8 + (lane & 7)], yr = L.yn[(wave >> 1) * 8 + (lane >> 3)];
             asm volatile("" : "+v"(dr), "+v"(xr), "+v"(yr));
             BandWalk w;                           // (a pixel outside the image has depth 0: invalid)
-            const int cls = setup_walk(w, dr, xr, yr, f, vol.trunc, vol.inv_vs);
+            const FrameArgs fc = load_ref(reload(fr));
+            const VolumeArgs vc = load_ref(reload(vref));
+            const int cls = setup_walk(w, dr, xr, yr, fc, vc.trunc, vc.inv_vs);
             load_walk(w, cls == kValid);
             if (done == 0) {
                 // point classes, counted once
@@ -611,21 +621,21 @@ __global__ __launch_bounds__(kThreads, 7) void k_allocate(BatchArgs B, VolumeArg
                 // colour (when the frame has it) and the directions of the
                 // stepping axes (the frame of the batch goes with the segments)
                 if (cls == kValid) {
-                    if (own.build_items && f.rgb) {
+                    if (load_ref(reload(oref)).build_items && fc.rgb) {
                         unsigned int px = pix;       // (opaque: the address is formed here, not held from the start)
                         asm volatile("" : "+v"(px));
-                        const uint8_t* c = f.rgb + 3 * (size_t)px;
+                        const uint8_t* c = fc.rgb + 3 * (size_t)px;
                         meta = (unsigned int)c[0] | ((unsigned int)c[1] << 8) | ((unsigned int)c[2] << 16);
                     }
                     meta |= (w.s0 < 0 ? 1u << 24 : 0u) | (w.s1 < 0 ? 1u << 25 : 0u) | (w.s2 < 0 ? 1u << 26 : 0u);
                 }
             }
             for (int i = 0; i < done; ++i) step();
-            itc = walk_chunk(done);
+            itc = walk_chunk(done, depth_axis(fc));
         }
         wave_on = alive != 0;
         cut_and_file(kp, yp, zp, cp, (int)nc, itc, x, y, z, (meta >> 24) & 1u ? -1 : 1, (meta >> 25) & 1u ? -1 : 1,
-                     (meta >> 26) & 1u ? -1 : 1, L, rnd, part, vol, own, depth_bits, meta, (unsigned int)fi, n_upd);
+                     (meta >> 26) & 1u ? -1 : 1, L, rnd, part, vref, oref, depth_bits, meta, (unsigned int)fi, n_upd);
         if (!workgroup_any(wave_on, L, rnd)) break;
     }
 
