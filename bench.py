@@ -115,10 +115,10 @@ def load_calls():
 # carries their digest; after any change the field is null until re-measured.
 MEASURED_TRAFFIC = {
     # (kernel, workload, most frames per call, update mode): (bytes per launch, source digest)
-    ("k_allocate", "room640x480", 128, "owner"): (1264218621, "113db45839a5893d"),
-    ("k_place_items", "room640x480", 128, "owner"): (6604211, "113db45839a5893d"),
-    ("k_place_segments", "room640x480", 128, "owner"): (260115326, "113db45839a5893d"),
-    ("k_update_owner", "room640x480", 128, "owner"): (1392521957, "113db45839a5893d"),
+    ("k_allocate", "room640x480", 128, "owner"): (1264368139, "ee7173c6bba865dc"),
+    ("k_place_items", "room640x480", 128, "owner"): (6606120, "ee7173c6bba865dc"),
+    ("k_place_segments", "room640x480", 128, "owner"): (260322543, "ee7173c6bba865dc"),
+    ("k_update_owner", "room640x480", 128, "owner"): (1392674085, "ee7173c6bba865dc"),
 }
 
 
@@ -730,6 +730,25 @@ def main():
                 out["path_roofline"]["measured_traffic_per_step"] / (cb_a + cb_u), 2)
     out["loss_counters"] = {k: st_main[k] for k in ("pool_overflow", "table_full", "update_misses", "walk_guard")}
     out["device"]["telemetry_after_headline"] = telemetry()
+    if TELEMETRY:
+        # the clocks with the GPU at work: steps of the headline queued for
+        # half a second (the clocks ramp up), then amd-smi run (a child
+        # process, in a thread) while this thread keeps queueing them
+        import threading
+        sample = []
+        th = threading.Thread(target=lambda: sample.append(telemetry()))
+        n_load, t_load = 0, time.perf_counter()
+        while time.perf_counter() - t_load < 0.5:
+            step(vol, calls, arrays)
+            n_load += 1
+        th.start()
+        while th.is_alive():
+            step(vol, calls, arrays)
+            n_load += 1
+        torch.cuda.synchronize()
+        out["device"]["telemetry_under_load"] = (dict(sample[0], steps_queued=n_load,
+                                                      seconds=round(time.perf_counter() - t_load, 2))
+                                                 if sample else None)
 
     # ---- the headline configuration and its variants, interleaved and rotated ----
     if not args.no_variants:
@@ -756,7 +775,9 @@ def main():
                                           "first_half_ms": round(first * 1e3, 4), "second_half_ms": round(second * 1e3, 4),
                                           "drift": round(second / first - 1.0, 4)}
         out["variants"] = {"rounds": args.rounds, "order": "rotated each round", "results": rot,
-                           "telemetry_per_round": clocks}
+                           "telemetry_per_round": clocks,
+                           "telemetry_note": "sampled after each round, with the GPU idle (its clocks may "
+                                             "read low); device.telemetry_under_load is the clock at work"}
         for v in variants:
             if v != ("owner", args.batch):
                 del setups[v]
