@@ -970,9 +970,8 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
     __shared__ DepthAxis s_axis[kMaxBatch];                 // per-record frame lookups from LDS
     __shared__ Projection s_proj[kMaxBatch];
     __shared__ unsigned int s_item[2];                      // alternates: read k while k + 1 is written
-    __shared__ unsigned int s_rec[kSegWindow];
-    __shared__ unsigned int s_off[kSegWindow + 1];
-    __shared__ unsigned char s_frm[kSegWindow];             // each segment's frame of the batch
+    // the window's segments: first record, and runs before it | frame << kSegFrameShift
+    __shared__ uint2 s_seg[kSegWindow + 1];
     __shared__ StagedRun s_run[kSubRuns];                   // staged runs, sorted by length
     __shared__ unsigned int s_hist[kLengths];               // staged runs of each length
     __shared__ unsigned int s_hbase[kLengths];              // first place of each length in the order
@@ -1027,23 +1026,21 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
         const int lo0 = bx * 8, lo1 = by * 8, lo2 = bz * 8;
         const size_t base = (size_t)d.idx * kBlockVoxels;
         // the block's segments, a window at a time: segment i holds runs
-        // [s_off[i], s_off[i + 1]) of the block, stored from s_rec[i] on
+        // [off(i), off(i + 1)) of the block (off: the low kSegFrameShift bits
+        // of s_seg[i].y), stored from s_seg[i].x on
         for (unsigned int w0 = 0; w0 < d.seg_count; w0 += kSegWindow) {
             const unsigned int wn = min(d.seg_count - w0, (unsigned int)kSegWindow);
             for (unsigned int i = tid; i <= wn; i += kUpdateThreads) {
                 if (i < wn) {
-                    const uint2 e = own.seg_list[d.seg_first + w0 + i];
-                    s_rec[i] = e.x;
-                    s_off[i] = e.y & kSegPosMask;
-                    s_frm[i] = (unsigned char)(e.y >> kSegFrameShift);
+                    s_seg[i] = own.seg_list[d.seg_first + w0 + i];
                 } else {
-                    s_off[i] = w0 + wn < d.seg_count ? own.seg_list[d.seg_first + w0 + wn].y & kSegPosMask
-                                                     : d.rec_count;
+                    s_seg[i] = make_uint2(0u, w0 + wn < d.seg_count ? own.seg_list[d.seg_first + w0 + wn].y & kSegPosMask
+                                                                    : d.rec_count);
                 }
             }
             __syncthreads();
-            const unsigned int wr0 = max(s_off[0], r_lo), wr1 = min(s_off[wn], r_hi);
-            const bool past = s_off[wn] >= r_hi;             // (uniform) no later window holds this unit's runs
+            const unsigned int wr0 = max(s_seg[0].y & kSegPosMask, r_lo), wr1 = min(s_seg[wn].y, r_hi);
+            const bool past = s_seg[wn].y >= r_hi;           // (uniform) no later window holds this unit's runs
             for (unsigned int c0 = wr0; c0 < wr1; c0 += kChunkRuns) {
                 const unsigned int c1 = min(wr1, c0 + kChunkRuns);
                 // The chunk's runs go through LDS kSubRuns at a time: each
@@ -1066,18 +1063,23 @@ __global__ __launch_bounds__(kUpdateThreads, kReproject ? 5 : 7) void k_update_o
                         unsigned int lo = 0, hi = wn - 1;    // last segment starting at or before r
                         while (lo < hi) {
                             const unsigned int m = (lo + hi + 1) >> 1;
-                            if (s_off[m] <= r) lo = m; else hi = m - 1;
+                            if ((s_seg[m].y & kSegPosMask) <= r) lo = m; else hi = m - 1;
                         }
                         unsigned int si = lo;
+                        uint2 cur = s_seg[si];                // segment si, and where the next one starts
+                        unsigned int next = s_seg[si + 1].y & kSegPosMask;
 #pragma unroll
                         for (int i = 0; i < kRunsPerThread; ++i) {
                             if (p0 + i < nb) {
-                                while (r >= s_off[si + 1]) ++si;   // s_off[wn] = wr1 > r ends it
-                                const RunRecord hr = own.recs[s_rec[si] + (r - s_off[si])];
+                                while (r >= next) {           // (the sentinel s_seg[wn] = wr1 > r ends it)
+                                    cur = s_seg[++si];
+                                    next = s_seg[si + 1].y & kSegPosMask;
+                                }
+                                const RunRecord hr = own.recs[cur.x + (r - (cur.y & kSegPosMask))];
                                 rec[i].depth = hr.depth;
                                 rec[i].w1 = hr.w1;
                                 rec[i].w2 = hr.w2;
-                                rec[i].frame = s_frm[si];
+                                rec[i].frame = cur.y >> kSegFrameShift;
                                 ++r;
                             }
                         }
