@@ -869,8 +869,8 @@ __global__ __launch_bounds__(kThreads) void k_discard_items(VolumeArgs vol, Owne
 constexpr unsigned int kChunkRuns = 8191;
 constexpr int kSegWindow = 256;                      // segments of a block held in LDS at once
 constexpr int kUpdateThreads = 256;                  // workgroup of the owner update
-constexpr int kRunsPerThread = 2;                    // runs each thread stages (2: 22 KB of LDS and
-                                                     // 71 VGPRs, 7 workgroups per CU)
+constexpr int kRunsPerThread = 2;                    // runs each thread stages (2: 22.3 KB of LDS and
+                                                     // 72 VGPRs, 7 workgroups per CU)
 constexpr int kSubRuns = kUpdateThreads * kRunsPerThread;   // runs staged in LDS at a time
 constexpr int kLengths = 32;                         // run lengths a record can state (5 bits)
 constexpr unsigned int kNoRank = 0xFFFFFFFFu;
