@@ -769,8 +769,8 @@ def main():
             clocks.append(telemetry())
         rot = {}
         for v, ts in times.items():
-            h = len(ts) // 2
-            first, second = statistics.median(ts[:h]), statistics.median(ts[h:])
+            h = len(ts) // 2                  # (one round: no halves to compare)
+            first, second = (statistics.median(ts[:h]), statistics.median(ts[h:])) if h else (ts[0], ts[0])
             rot[f"{v[0]}_batch{v[1]}"] = {"step_ms": dist(ts, 1e3, 4), "points_per_s": round(pts / statistics.median(ts), 1),
                                           "first_half_ms": round(first * 1e3, 4), "second_half_ms": round(second * 1e3, 4),
                                           "drift": round(second / first - 1.0, 4)}
